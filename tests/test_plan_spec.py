@@ -1,0 +1,161 @@
+"""The reference plan procedure: a hand-worked example and invariants."""
+import numpy as np
+import pytest
+
+from oracle.plan_spec import PlanSpecError, plan_spec
+from workloads import config_lengths
+
+
+def _indptr(lens, ps=16):
+    n = [-(-int(L) // ps) for L in lens]
+    return np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+
+
+def test_hand_worked_decode_plan():
+    # Three requests of 4, 2, 5 full pages (the page lists of the worked CSR
+    # example), 2 kv heads, target 1*8 tiles: units = 2*11 = 22, P = ceil(22/8) = 3.
+    lens = [64, 32, 80]
+    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=8)
+    assert p["chunk_pages"] == 3 and p["num_slots"] == 4
+    expect = [
+        [0, 0, 0, 1, 0, 48, 0, 2], [0, 1, 0, 1, 0, 48, 0, 2],
+        [2, 0, 2, 3, 0, 48, 2, 2], [2, 1, 2, 3, 0, 48, 2, 2],
+        [1, 0, 1, 2, 0, 32, -1, 1], [1, 1, 1, 2, 0, 32, -1, 1],
+        [2, 0, 2, 3, 48, 80, 3, 2], [2, 1, 2, 3, 48, 80, 3, 2],
+        [0, 0, 0, 1, 48, 64, 1, 2], [0, 1, 0, 1, 48, 64, 1, 2],
+    ]
+    assert p["tiles"].tolist() == expect
+    assert p["merge"].tolist() == [[0, 0, 2, 0], [2, 2, 2, 0]]
+    # target 4: P = 6 pages, nothing splits; longest request first
+    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=4)
+    assert p["chunk_pages"] == 6 and p["num_slots"] == 0 and p["merge"].shape == (0, 4)
+    assert [t[0] for t in p["tiles"].tolist()] == [2, 2, 0, 0, 1, 1]
+
+
+def test_hand_worked_append_plan():
+    # one request, kv 40, 40 new rows (pure prefill), qo_tile 16, causal:
+    # q tiles rows [0,16) vis 16, [16,32) vis 32, [32,40) vis 40 -> 1+2+3 = 6 pages;
+    # 1 kv head, target 4 -> P = 2 pages: C = 1, 1, 2.
+    p = plan_spec([0, 3], [40], 1, 4, 1, 128, 16, max_batch=1, qo_indptr=[0, 40], causal=True,
+                  max_qo_tokens=40, num_cu=1, tiles_per_cu=4, qo_tile=16)
+    assert p["chunk_pages"] == 2
+    assert p["tiles"].tolist() == [
+        [0, 0, 16, 32, 0, 32, -1, 1],
+        [0, 0, 0, 16, 0, 16, -1, 1],
+        [0, 0, 32, 40, 0, 32, 0, 2],
+        [0, 0, 32, 40, 32, 40, 1, 2],
+    ]
+    assert p["num_slots"] == 16
+    assert p["merge"].tolist() == [[r, (r - 32) * 2, 2, 0] for r in range(32, 40)]
+
+
+def check_invariants(p, lens, Hkv, ps=16, qo_indptr=None, causal=False, qo_tile=1):
+    tiles = p["tiles"]
+    cost = (tiles[:, 5] - tiles[:, 4]).astype(np.int64) * (tiles[:, 3] - tiles[:, 2])
+    assert np.all(np.diff(cost) <= 0), "not in descending cost order"
+    assert np.all(tiles[:, 4] % ps == 0), "chunk begin not page aligned"
+    cover = {}
+    for b, h, q0, q1, t0, t1, s0, C in tiles.tolist():
+        cover.setdefault((b, h, q0, q1), []).append((t0, t1, s0, C))
+    B = len(lens)
+    rows_seen = {}
+    for (b, h, q0, q1), parts in cover.items():
+        parts.sort()
+        L = int(lens[b])
+        if qo_indptr is None:
+            assert (q0, q1) == (b, b + 1)
+            vis = L
+        else:
+            ql = qo_indptr[b + 1] - qo_indptr[b]
+            vis = min(L, L - ql + (q1 - qo_indptr[b])) if causal else L
+        assert parts[0][0] == 0 and parts[-1][1] == max(vis, 0)
+        for (a0, a1, _, _), (b0, b1, _, _) in zip(parts[:-1], parts[1:]):
+            assert a1 == b0, "chunks must tile the key range"
+        C = parts[0][3]
+        assert len(parts) == C and all(x[3] == C for x in parts)
+        if C == 1:
+            assert parts[0][2] == -1
+        for r in range(q0, q1):
+            rows_seen[(r, h)] = rows_seen.get((r, h), 0) + 1
+    nrows = B if qo_indptr is None else int(qo_indptr[-1])
+    for r in range(nrows):
+        for h in range(Hkv):
+            assert rows_seen.get((r, h), 0) == 1, "each (row, kv head) in exactly one q tile"
+    used = set()
+    for r, s0, C, _ in p["merge"].tolist():
+        for s in range(s0, s0 + C):
+            assert s not in used
+            used.add(s)
+    assert used == set(range(p["num_slots"]))
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_decode_configs(k):
+    lens = config_lengths(k, np.random.default_rng(k))["kv_lens"]
+    Hkv = 32 if k == 1 else 8
+    p = plan_spec(_indptr(lens), lens, len(lens), 32, Hkv, 128, 16, max_batch=len(lens))
+    check_invariants(p, lens, Hkv)
+    assert len(p["tiles"]) <= p["knobs"]["max_tiles"]
+
+
+def test_append_config5_and_cascade_prefix():
+    lens = [4608] * 16
+    qo = np.concatenate([[0], np.cumsum([512] * 16)])
+    p = plan_spec(_indptr(lens), lens, 16, 32, 8, 128, 16, max_batch=16, qo_indptr=qo,
+                  causal=True, max_qo_tokens=8192)
+    check_invariants(p, lens, 8, qo_indptr=qo, causal=True)
+    assert p["num_slots"] == 0 and len(p["tiles"]) == 16 * 8 * 16
+    p = plan_spec([0, 1024], [16384], 1, 32, 8, 128, 16, max_batch=1, qo_indptr=[0, 256],
+                  causal=False, max_qo_tokens=256)
+    check_invariants(p, [16384], 8, qo_indptr=[0, 256], causal=False)
+    assert p["chunk_pages"] == 128 and len(p["tiles"]) == 512
+
+
+def test_random_geometries():
+    rng = np.random.default_rng(0)
+    for it in range(300):
+        B = int(rng.integers(0, 9))
+        lens = rng.integers(0, 300, size=B)
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        knobs = dict(num_cu=int(rng.integers(1, 9)), tiles_per_cu=int(rng.integers(1, 5)),
+                     min_chunk_pages=int(rng.integers(1, 4)))
+        if it % 2:
+            p = plan_spec(_indptr(lens), lens, B, G * Hkv, Hkv, 128, 16, max_batch=max(B, 1),
+                          **knobs)
+            check_invariants(p, lens, Hkv)
+        else:
+            ql = np.minimum(rng.integers(0, 70, size=B), lens)
+            qo = np.concatenate([[0], np.cumsum(ql)]).astype(np.int64)
+            causal = bool(rng.integers(0, 2))
+            qt = int(rng.choice([8, 16, 32]))
+            p = plan_spec(_indptr(lens), lens, B, G * Hkv, Hkv, 128, 16, max_batch=max(B, 1),
+                          qo_indptr=qo, causal=causal, max_qo_tokens=max(int(qo[-1]), 1),
+                          qo_tile=qt, **knobs)
+            check_invariants(p, lens, Hkv, qo_indptr=qo, causal=causal, qo_tile=qt)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(lens=[33], indptr=[0, 2]), "INVALID"),      # 33 tokens need 3 pages
+    (dict(lens=[32], indptr=[0, 3]), "INVALID"),      # 3 pages but only 32 tokens
+    (dict(lens=[5], indptr=[0, 0]), "INVALID"),       # tokens without pages
+    (dict(lens=[16], indptr=[1, 2]), "INVALID"),      # indptr must start at 0
+    (dict(Hq=12, Hkv=8), "INVALID"),                  # non-integer group
+    (dict(D=64), "UNSUPPORTED"),
+    (dict(Hq=48, Hkv=3), "UNSUPPORTED"),              # group 16
+    (dict(max_batch=0), "INVALID"),
+])
+def test_errors(bad, code):
+    args = dict(lens=[16], indptr=[0, 1], Hq=8, Hkv=2, D=128, max_batch=1)
+    args.update(bad)
+    with pytest.raises(PlanSpecError) as e:
+        plan_spec(args["indptr"], args["lens"], len(args["lens"]), args["Hq"], args["Hkv"],
+                  args["D"], 16, max_batch=args["max_batch"])
+    assert e.value.code == code
+
+
+def test_capacity_error():
+    lens = [160] * 4
+    with pytest.raises(PlanSpecError) as e:
+        plan_spec(_indptr(lens), lens, 4, 8, 8, 128, 16, max_batch=4, max_tiles=16)
+    assert e.value.code == "CAPACITY"

@@ -1,0 +1,17 @@
+"""Seeded synthetic inputs for paged-KV attention.
+
+This package only draws random numbers and lays them out as a paged KV cache
+(page pool, CSR page table, queries). It holds none of the attention
+arithmetic: both the fp64 oracle and the GPU path consume the same stored
+bytes that it produces.
+"""
+from .gen import (  # noqa: F401
+    Workload,
+    make_config,
+    config_lengths,
+    make_workload,
+    make_cascade,
+    csr_from_page_lists,
+    to_storage_bits,
+    CONFIG_NAMES,
+)
