@@ -1,0 +1,219 @@
+/*
+ * fa.h -- C ABI of the paged-KV attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is described on these pages (cited by title and
+ * section):
+ *
+ *  [Guide]    "FlashInfer: GPU Kernels for LLM Inference (2026 Guide)":
+ *             "What FlashInfer is" (block-sparse KV format; load-balanced
+ *             scheduling that stays compatible with graphs), "Cascade attention
+ *             for shared prefixes" (merge_state / merge_states), "Quickstart"
+ *             (plan step with static geometry before graph capture, run step
+ *             with per-launch tensors; NHD layout by default).
+ *  [DeepDive] "FlashInfer: The Attention Kernel Library That Proves the
+ *             Bottleneck in LLM Inference Was Never the Model. It Was the
+ *             Memory Access Pattern.": "Snippet One: Paged KV-Cache Attention
+ *             and MLA" (page pool, CSR page table, last_page_len, caller-owned
+ *             workspace buffer, plan arguments), "It In Action" step 1 (a
+ *             per-step plan builds the tile-to-request map), "Why This Design
+ *             Works" (static launch geometry, dynamic assignment).
+ *
+ * Conventions shared by every entry point:
+ *  - Every call returns fa_status; nothing throws and nothing aborts.
+ *  - The library never allocates or frees device memory. Every device buffer
+ *    (queries, pages, page tables, outputs, workspace) is owned by the caller
+ *    and must stay alive until the work enqueued on `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream. Run
+ *    calls (fa_decode, fa_append, fa_merge_state, fa_merge_states) only
+ *    enqueue kernels: no synchronisation, no allocation, no host-to-device
+ *    copy, and their launch shapes depend only on the fa_geometry a plan was
+ *    made with. They may therefore be captured in a hipGraph, and a captured
+ *    graph stays valid when fa_plan is called again with the same geometry and
+ *    workspace pointers (the plan rewrites the device workspace the graph
+ *    reads). fa_plan itself copies to the device and refuses to run on a
+ *    capturing stream.
+ *  - Scores use natural-log log-sum-exp (`lse = log(sum_j exp(s_j))`) and
+ *    `s_j = sm_scale * <q, k_j>`; `sm_scale <= 0` selects 1/sqrt(head_dim).
+ *  - Query head h reads kv head h / (num_qo_heads / num_kv_heads).
+ *  - Supported: head_dim 128, page_size 16, num_qo_heads / num_kv_heads in
+ *    {1, 2, 4, 8}, fp16 or bf16 q / K / V / out with fp32 accumulation. Other
+ *    shapes return FA_ERR_UNSUPPORTED.
+ */
+#ifndef PAGED_KV_FA_H_
+#define PAGED_KV_FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fa_status;
+#define FA_OK 0
+#define FA_ERR_INVALID (-1)     /* bad argument, inconsistent page table, misaligned pointer */
+#define FA_ERR_UNSUPPORTED (-2) /* head_dim / page_size / group size / dtype not built */
+#define FA_ERR_WORKSPACE (-3)   /* a workspace is missing or smaller than fa_workspace_size */
+#define FA_ERR_CAPACITY (-4)    /* more tiles / partial states / merge rows than the geometry allows */
+#define FA_ERR_HIP (-5)         /* a HIP runtime call failed (fa_last_error names it) */
+#define FA_ERR_CAPTURING (-6)   /* fa_plan called on a stream that is capturing a graph */
+#define FA_ERR_NOT_PLANNED (-7) /* run call with a plan that has no device upload */
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1, FA_F32 = 2 } fa_dtype;
+typedef enum { FA_MODE_DECODE = 0, FA_MODE_APPEND = 1 } fa_mode;
+
+/* Static geometry: fixed for the life of a captured graph. Zero knobs take
+ * defaults; the resolved values are reported by fa_plan_info. */
+typedef struct {
+  int32_t mode;            /* fa_mode: decode (one query row per request) or append */
+  int32_t dtype;           /* fa_dtype of q, K/V pages and out (FA_F16 or FA_BF16) */
+  int32_t max_batch;       /* upper bound on the number of requests */
+  int32_t max_qo_tokens;   /* append: upper bound on packed query rows; ignored for decode */
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;        /* 128 */
+  int32_t page_size;       /* 16 */
+  /* plan knobs (0 = default) */
+  int32_t num_cu;          /* compute units to spread tiles over (default 256) */
+  int32_t tiles_per_cu;    /* tiles wanted per compute unit (default 8 decode, 2 append) */
+  int32_t min_chunk_pages; /* smallest split-KV chunk in pages (default 1) */
+  int32_t qo_tile;         /* append: query rows per tile (default 32); decode: 1 */
+  int32_t max_tiles;       /* capacities; default = worst case of the plan procedure */
+  int32_t max_partials;
+  int32_t max_merge;
+  int32_t reserved[9];
+} fa_geometry;
+
+/* Caller-allocated plan object. Zero it before first use; release the HIP
+ * event it may hold with fa_plan_destroy. Not shared between streams that run
+ * concurrently. */
+typedef struct {
+  uint64_t opaque[64];
+} fa_plan_t;
+
+typedef struct {
+  int32_t num_tiles;       /* work tiles in the current plan */
+  int32_t num_merge;       /* query rows whose state is split over several tiles */
+  int32_t num_slots;       /* fp32 partial states in use */
+  int32_t chunk_pages;     /* split-KV chunk length in pages */
+  int32_t batch;
+  int32_t num_rows;        /* query rows (batch for decode) */
+  int32_t causal;
+  int32_t uploaded;        /* 1 if the plan was copied to a device workspace */
+  fa_geometry resolved;    /* geometry with every default filled in */
+} fa_plan_stats;
+
+/* Host and device workspace sizes in bytes for a geometry. Either output may
+ * be NULL. Errors: FA_ERR_INVALID / FA_ERR_UNSUPPORTED for a bad geometry. */
+fa_status fa_workspace_size(const fa_geometry* geom, size_t* host_bytes, size_t* device_bytes);
+
+/* Build the split-KV work plan on the host ([Guide] "What FlashInfer is",
+ * idea 3; [DeepDive] "It In Action" step 1) and copy it into `dev_ws` on
+ * `stream`.
+ *
+ *  kv_indptr_h  host int32 [batch+1]: CSR offsets of each request's pages in
+ *               kv_indices (must start at 0 and be non-decreasing).
+ *  kv_lens_h    host int32 [batch]: valid tokens per request; must satisfy
+ *               (n_b-1)*page_size < kv_len <= n_b*page_size for n_b pages, or
+ *               0 with no pages.
+ *  qo_indptr_h  host int32 [batch+1] for append (packed query rows of each
+ *               request), NULL for decode.
+ *  causal       append: row i of a request with qo_len new rows sees keys
+ *               0 .. kv_len - qo_len + i (its new tokens are already in the
+ *               pages); ignored for decode.
+ *  host_ws      caller host memory of fa_workspace_size's host_bytes (pinned
+ *               memory recommended). fa_plan waits for its own previous copy
+ *               out of it before writing it again.
+ *  dev_ws       caller device memory of device_bytes, 256-byte aligned, or
+ *               NULL to plan on the host only (no HIP call is made; the plan
+ *               can then be inspected but not run).
+ * Errors: FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_CAPACITY,
+ * FA_ERR_CAPTURING, FA_ERR_HIP. On error the previous plan is unusable. */
+fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
+                  const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
+                  int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
+                  size_t dev_ws_bytes, void* stream);
+
+/* Summary of the current plan. */
+fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats);
+
+/* Host copies of the current plan, valid until the next fa_plan on this plan:
+ * tiles int32 [num_tiles][8] = {request, kv_head, row_begin, row_end,
+ * key_begin, key_end, slot0 (-1 = write the final output), n_chunks}; merge
+ * int32 [num_merge][4] = {row, first_slot, n_slots, 0}. */
+fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t* num_tiles,
+                        const int32_t** merge_h, int32_t* num_merge);
+
+/* Release the HIP event a plan keeps for reusing its host workspace. */
+fa_status fa_plan_destroy(fa_plan_t* plan);
+
+/* Batched decode over the paged KV cache ([DeepDive] "Snippet One", batch
+ * decode wrapper plan/run; [Guide] "Quickstart").
+ *
+ *  q            device [batch, num_qo_heads, head_dim], geometry dtype, contiguous.
+ *  k_pages, v_pages  device page pools; element (page, slot, kv_head, d) of K is
+ *               k_pages[page*page_stride + slot*token_stride + kv_head*head_stride + d]
+ *               (strides in elements, d contiguous). The combined pool
+ *               [num_pages, 2, page_size, num_kv_heads, head_dim] is
+ *               k_pages = pool, v_pages = pool + page_size*num_kv_heads*head_dim,
+ *               page_stride = 2*page_size*num_kv_heads*head_dim,
+ *               token_stride = num_kv_heads*head_dim, head_stride = head_dim.
+ *               Pointers 16-byte aligned, strides multiples of 8.
+ *  kv_indices_d, kv_indptr_d, last_page_len_d  device int32 CSR page table
+ *               (same content as given to fa_plan; last_page_len in [1, page_size]).
+ *  out          device [batch, num_qo_heads, head_dim], geometry dtype.
+ *  lse          device fp32 [batch, num_qo_heads] or NULL.
+ * A request with no keys gets out = 0 and lse = -inf. Requests whose keys were
+ * split by the plan are combined with the log-sum-exp merge in a second kernel
+ * on the same stream. Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
+fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
+                    const void* v_pages, int64_t page_stride, int64_t token_stride,
+                    int64_t head_stride, const int32_t* kv_indices_d, const int32_t* kv_indptr_d,
+                    const int32_t* last_page_len_d, float sm_scale, void* out, float* lse,
+                    void* stream);
+
+/* Append / prefill over the paged KV cache, causal or not as planned ([Guide]
+ * "Features (from the repository README)": prefill and append kernels). The
+ * new tokens' K/V must already be in the pages.
+ *
+ *  q            device [num_rows, num_qo_heads, head_dim] packed rows
+ *               (request b owns rows qo_indptr[b] .. qo_indptr[b+1]-1).
+ *  qo_indptr_d  device int32 [batch+1], same content as given to fa_plan.
+ *  out / lse    device [num_rows, num_qo_heads, head_dim] / fp32 [num_rows, num_qo_heads].
+ * Other arguments as fa_decode. Errors as fa_decode. */
+fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indptr_d,
+                    const void* k_pages, const void* v_pages, int64_t page_stride,
+                    int64_t token_stride, int64_t head_stride, const int32_t* kv_indices_d,
+                    const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
+                    void* out, float* lse, void* stream);
+
+/* Merge two attention states computed over disjoint key sets ([Guide]
+ * "Cascade attention for shared prefixes"):
+ *   s = log(exp(s_a) + exp(s_b)),  v = exp(s_a - s) v_a + exp(s_b - s) v_b.
+ *  v_a, v_b, v_out  device [n, heads, head_dim] in `dtype` (FA_F16, FA_BF16, FA_F32).
+ *  s_a, s_b, s_out  device fp32 [n, heads]; -inf marks an empty state.
+ * v_out / s_out may alias v_a / s_a. head_dim must be a multiple of 8 and the
+ * pointers 16-byte aligned. Errors: FA_ERR_INVALID, FA_ERR_HIP. */
+fa_status fa_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                         void* v_out, float* s_out, int64_t n, int32_t heads, int32_t head_dim,
+                         int32_t dtype, void* stream);
+
+/* Merge k states per row ([Guide] "Cascade attention for shared prefixes"):
+ *  v  device [n, k, heads, head_dim] in `dtype`; s device fp32 [n, k, heads];
+ *  v_out device [n, heads, head_dim] in `dtype`; s_out fp32 [n, heads] or NULL.
+ * All states -inf gives v = 0, s = -inf. Errors: FA_ERR_INVALID, FA_ERR_HIP. */
+fa_status fa_merge_states(const void* v, const float* s, int64_t n, int32_t k, int32_t heads,
+                          int32_t head_dim, int32_t dtype, void* v_out, float* s_out,
+                          void* stream);
+
+/* Static description of a status code. */
+const char* fa_status_string(fa_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_FA_H_ */

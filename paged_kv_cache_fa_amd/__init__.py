@@ -1,0 +1,214 @@
+"""Paged-KV attention for AMD Instinct MI355X (gfx950): Python binding.
+
+A thin ctypes layer over the C ABI in ``include/fa.h`` (``libpkfa.so``, built
+from ``csrc/`` by ``build.py``). It only marshals arguments: every step of the
+computation runs in the library's HIP kernels. Device buffers are torch
+tensors (used for memory and streams only); there is no CPU fallback — if the
+library is missing, the import of any entry point raises.
+
+Entry points (same names as the C ABI): ``workspace_size``, ``plan`` (returns a
+``Plan``), ``decode``, ``append``, ``merge_state``, ``merge_states``.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import (FA_BF16, FA_F16, FA_F32, FA_MODE_APPEND, FA_MODE_DECODE, FAError,  # noqa: F401
+                   Geometry, PlanStats, PlanT, check, load)
+
+_DTYPE_CODES = {"bf16": FA_BF16, "fp16": FA_F16, "fp32": FA_F32}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dt) -> int:
+    """Map "bf16"/"fp16"/"fp32" or a torch dtype to the ABI dtype code."""
+    if isinstance(dt, str):
+        return _DTYPE_CODES[dt]
+    torch = _torch()
+    return {torch.bfloat16: FA_BF16, torch.float16: FA_F16, torch.float32: FA_F32}[dt]
+
+
+def geometry(mode: str, dtype, max_batch: int, num_qo_heads: int, num_kv_heads: int,
+             head_dim: int = 128, page_size: int = 16, max_qo_tokens: int = 0,
+             **knobs) -> Geometry:
+    g = Geometry()
+    g.mode = FA_MODE_APPEND if mode == "append" else FA_MODE_DECODE
+    g.dtype = dtype_code(dtype)
+    g.max_batch = max_batch
+    g.max_qo_tokens = max_qo_tokens
+    g.num_qo_heads = num_qo_heads
+    g.num_kv_heads = num_kv_heads
+    g.head_dim = head_dim
+    g.page_size = page_size
+    for k, v in knobs.items():
+        setattr(g, k, int(v))
+    return g
+
+
+def workspace_size(geom: Geometry):
+    """(host_bytes, device_bytes) for a geometry."""
+    lib = load()
+    h, d = ctypes.c_size_t(), ctypes.c_size_t()
+    check(lib.fa_workspace_size(ctypes.byref(geom), ctypes.byref(h), ctypes.byref(d)))
+    return h.value, d.value
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        torch = _torch()
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _i32(a) -> np.ndarray:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+class Plan:
+    """A plan object plus its host and device workspaces.
+
+    ``device=None`` plans on the host only (inspectable, not runnable). The
+    host workspace is pinned memory when a GPU is used.
+    """
+
+    def __init__(self, geom: Geometry, device=None):
+        lib = load()
+        self.geom = geom
+        self.device = device
+        self._plan = PlanT()
+        hb, db = workspace_size(geom)
+        self.host_bytes, self.dev_bytes = hb, db
+        if device is None:
+            self.host_ws = np.zeros(hb, dtype=np.uint8)
+            self.dev_ws = None
+        else:
+            torch = _torch()
+            self.host_ws = torch.empty(hb, dtype=torch.uint8, pin_memory=True)
+            self.dev_ws = torch.empty(db + 256, dtype=torch.uint8, device=device)
+            off = (-self.dev_ws.data_ptr()) % 256
+            self.dev_ws = self.dev_ws[off: off + db]
+        self._lib = lib
+        self._keep = None
+
+    def plan(self, kv_indptr, kv_lens, qo_indptr=None, causal: bool = False, stream=None):
+        kv_indptr, kv_lens, qo_indptr = _i32(kv_indptr), _i32(kv_lens), _i32(qo_indptr)
+        self._keep = (kv_indptr, kv_lens, qo_indptr)
+        batch = int(kv_lens.shape[0])
+        check(self._lib.fa_plan(ctypes.byref(self._plan), ctypes.byref(self.geom),
+                                _ptr(kv_indptr), _ptr(kv_lens), batch,
+                                _ptr(qo_indptr) if qo_indptr is not None else None, int(causal),
+                                _ptr(self.host_ws), self.host_bytes,
+                                _ptr(self.dev_ws) if self.dev_ws is not None else None,
+                                self.dev_bytes if self.dev_ws is not None else 0,
+                                _stream(stream) if self.dev_ws is not None else None))
+        return self
+
+    def info(self) -> PlanStats:
+        st = PlanStats()
+        check(self._lib.fa_plan_info(ctypes.byref(self._plan), ctypes.byref(st)))
+        return st
+
+    def tiles(self):
+        """(tiles int32 [n, 8], merge int32 [m, 4]) host copies of the current plan."""
+        tp, mp = ctypes.c_void_p(), ctypes.c_void_p()
+        nt, nm = ctypes.c_int32(), ctypes.c_int32()
+        check(self._lib.fa_plan_tiles(ctypes.byref(self._plan), ctypes.byref(tp),
+                                      ctypes.byref(nt), ctypes.byref(mp), ctypes.byref(nm)))
+        t = np.ctypeslib.as_array(ctypes.cast(tp, ctypes.POINTER(ctypes.c_int32)),
+                                  shape=(max(nt.value, 1) * 8,))[: nt.value * 8]
+        m = np.ctypeslib.as_array(ctypes.cast(mp, ctypes.POINTER(ctypes.c_int32)),
+                                  shape=(max(nm.value, 1) * 4,))[: nm.value * 4]
+        return t.reshape(-1, 8).copy(), m.reshape(-1, 4).copy()
+
+    def __del__(self):
+        try:
+            self._lib.fa_plan_destroy(ctypes.byref(self._plan))
+        except Exception:
+            pass
+
+
+def plan(geom: Geometry, kv_indptr, kv_lens, qo_indptr=None, causal: bool = False,
+         device=None, stream=None) -> Plan:
+    """Build a plan (and upload it when ``device`` is given)."""
+    return Plan(geom, device).plan(kv_indptr, kv_lens, qo_indptr, causal, stream)
+
+
+def _alloc_out(q, out, lse, rows, heads):
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(rows, heads, dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def decode(p: Plan, q, k_pages, v_pages, page_stride: int, token_stride: int, head_stride: int,
+           kv_indices, kv_indptr, last_page_len, sm_scale: float = 0.0, out=None, lse=None,
+           stream=None):
+    """Batched paged decode (see fa_decode). Returns (out, lse)."""
+    out, lse = _alloc_out(q, out, lse, q.shape[0], q.shape[1])
+    check(p._lib.fa_decode(ctypes.byref(p._plan), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                           page_stride, token_stride, head_stride, _ptr(kv_indices),
+                           _ptr(kv_indptr), _ptr(last_page_len), float(sm_scale), _ptr(out),
+                           _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def append(p: Plan, q, qo_indptr, k_pages, v_pages, page_stride: int, token_stride: int,
+           head_stride: int, kv_indices, kv_indptr, last_page_len, sm_scale: float = 0.0,
+           out=None, lse=None, stream=None):
+    """Append / prefill over the paged cache (see fa_append). Returns (out, lse)."""
+    out, lse = _alloc_out(q, out, lse, q.shape[0], q.shape[1])
+    check(p._lib.fa_append(ctypes.byref(p._plan), _ptr(q), _ptr(qo_indptr), _ptr(k_pages),
+                           _ptr(v_pages), page_stride, token_stride, head_stride,
+                           _ptr(kv_indices), _ptr(kv_indptr), _ptr(last_page_len),
+                           float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
+    """Merge two states [n, heads, D] / [n, heads] (see fa_merge_state)."""
+    torch = _torch()
+    n, heads, d = v_a.shape
+    if v_out is None:
+        v_out = torch.empty_like(v_a)
+    if s_out is None:
+        s_out = torch.empty_like(s_a)
+    check(load().fa_merge_state(_ptr(v_a), _ptr(s_a), _ptr(v_b), _ptr(s_b), _ptr(v_out),
+                                _ptr(s_out), n, heads, d, dtype_code(v_a.dtype), _stream(stream)))
+    return v_out, s_out
+
+
+def merge_states(v, s, v_out=None, s_out=None, stream=None):
+    """Merge k states per row: v [n, k, heads, D], s [n, k, heads] (see fa_merge_states)."""
+    torch = _torch()
+    n, k, heads, d = v.shape
+    if v_out is None:
+        v_out = torch.empty(n, heads, d, dtype=v.dtype, device=v.device)
+    if s_out is None:
+        s_out = torch.empty(n, heads, dtype=torch.float32, device=v.device)
+    check(load().fa_merge_states(_ptr(v), _ptr(s), n, k, heads, d, dtype_code(v.dtype),
+                                 _ptr(v_out), _ptr(s_out), _stream(stream)))
+    return v_out, s_out

@@ -1,0 +1,331 @@
+// C ABI: argument validation, plan upload and kernel launches.
+//
+// Plan/run split as described in [Guide] "FlashInfer: GPU Kernels for LLM
+// Inference (2026 Guide)", section "Quickstart" (plan with static geometry
+// before graph capture, run with per-launch tensors) and [DeepDive]
+// "FlashInfer: The Attention Kernel Library That Proves the Bottleneck ...",
+// sections "Snippet One" (caller-owned workspace buffer, plan arguments) and
+// "Why This Design Works" (static launch shape, dynamic tile assignment; a
+// re-plan does not invalidate the captured launch). Run calls enqueue kernels
+// only; their grids depend on the resolved geometry alone.
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <string.h>
+
+#include "kernels.h"
+#include "plan_internal.h"
+
+namespace pkfa {
+const char* last_error();
+}
+
+using namespace pkfa;
+
+namespace {
+
+fa_status hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s", what, hipGetErrorString(e));
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+fa_status check_run_args(const PlanImpl* pl, int want_mode, const void* q, const void* k,
+                          const void* v, int64_t page_stride, int64_t token_stride,
+                          int64_t head_stride, const int32_t* kv_indices, const int32_t* kv_indptr,
+                          const int32_t* last_page_len, const void* out) {
+  if (!pl || pl->magic != kPlanMagic || !pl->planned) {
+    set_error("plan object was not filled by fa_plan");
+    return FA_ERR_INVALID;
+  }
+  if (!pl->uploaded) {
+    set_error("plan was built without a device workspace");
+    return FA_ERR_NOT_PLANNED;
+  }
+  if (pl->geom.mode != want_mode) {
+    set_error(want_mode == FA_MODE_DECODE ? "plan was made for append, not decode"
+                                          : "plan was made for decode, not append");
+    return FA_ERR_INVALID;
+  }
+  if (!q || !k || !v || !kv_indices || !kv_indptr || !last_page_len || !out) {
+    set_error("NULL tensor argument");
+    return FA_ERR_INVALID;
+  }
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) {
+    set_error("q, K/V pages and out must be 16-byte aligned");
+    return FA_ERR_INVALID;
+  }
+  const int D = pl->geom.head_dim;
+  if (page_stride <= 0 || token_stride < D || head_stride < D || (page_stride & 7) ||
+      (token_stride & 7) || (head_stride & 7) ||
+      (int64_t)token_stride * 2 * pl->geom.page_size > 0x7fffffffLL) {
+    set_error("strides must be positive multiples of 8 elements with token/head stride >= "
+              "head_dim");
+    return FA_ERR_INVALID;
+  }
+  return FA_OK;
+}
+
+AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const void* v,
+                       int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                       const int32_t* kv_indices, const int32_t* kv_indptr,
+                       const int32_t* last_page_len, const int32_t* qo_indptr, float sm_scale,
+                       void* out, float* lse) {
+  const uint8_t* ws = static_cast<const uint8_t*>(pl->dev_ws);
+  AttnParams p;
+  p.header = reinterpret_cast<const int32_t*>(ws + pl->lay.header);
+  p.tiles = reinterpret_cast<const int32_t*>(ws + pl->lay.tiles);
+  p.merge = reinterpret_cast<const int32_t*>(ws + pl->lay.merge);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.page_stride = page_stride;
+  p.token_stride = token_stride;
+  p.head_stride = head_stride;
+  p.kv_indices = kv_indices;
+  p.kv_indptr = kv_indptr;
+  p.last_page_len = last_page_len;
+  p.qo_indptr = qo_indptr;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.part_o = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl->lay.dev_part_o);
+  p.part_lse = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl->lay.dev_part_lse);
+  const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)pl->geom.head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.num_qo_heads = pl->geom.num_qo_heads;
+  p.causal = pl->causal;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_CAPACITY: return "plan capacity exceeded";
+    case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_CAPTURING: return "stream is capturing a graph";
+    case FA_ERR_NOT_PLANNED: return "plan has no device upload";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return pkfa::last_error(); }
+
+fa_status fa_workspace_size(const fa_geometry* geom, size_t* host_bytes, size_t* device_bytes) {
+  fa_geometry g;
+  const fa_status st = resolve_geometry(geom, &g);
+  if (st != FA_OK) return st;
+  const Layout lay = compute_layout(g);
+  if (host_bytes) *host_bytes = lay.host_bytes;
+  if (device_bytes) *device_bytes = lay.dev_bytes;
+  return FA_OK;
+}
+
+fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
+                  const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
+                  int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
+                  size_t dev_ws_bytes, void* stream) {
+  if (!plan) {
+    set_error("plan is NULL");
+    return FA_ERR_INVALID;
+  }
+  PlanImpl* pl = impl(plan);
+  if (pl->magic != kPlanMagic) {
+    memset(plan, 0, sizeof(*plan));
+    pl->magic = kPlanMagic;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dev_ws) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone) {
+      set_error("fa_plan copies to the device and cannot be captured; plan before capture");
+      return FA_ERR_CAPTURING;
+    }
+    // the previous copy out of host_ws must finish before host_ws is rewritten
+    if (pl->upload_event) {
+      e = hipEventSynchronize(static_cast<hipEvent_t>(pl->upload_event));
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    }
+  }
+  pl->planned = 0;
+  pl->uploaded = 0;
+  fa_geometry g;
+  fa_status st = resolve_geometry(geom, &g);
+  if (st != FA_OK) return st;
+  st = build_plan(pl, g, kv_indptr_h, kv_lens_h, batch, qo_indptr_h, causal, host_ws,
+                  host_ws_bytes);
+  if (st != FA_OK) return st;
+  pl->planned = 1;
+  pl->dev_ws = dev_ws;
+  if (!dev_ws) return FA_OK;
+  if (dev_ws_bytes < pl->lay.dev_bytes || (reinterpret_cast<uintptr_t>(dev_ws) & 255)) {
+    pl->planned = 0;
+    set_error("device workspace needs %zu bytes, 256-byte aligned", pl->lay.dev_bytes);
+    return FA_ERR_WORKSPACE;
+  }
+  const size_t bytes = pl->lay.tiles + (size_t)pl->num_tiles * kTileInts * 4;
+  hipError_t e = hipMemcpyAsync(dev_ws, host_ws, bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) {
+    pl->planned = 0;
+    return hip_fail(e, "hipMemcpyAsync (plan upload)");
+  }
+  if (!pl->upload_event) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      pl->planned = 0;
+      return hip_fail(e, "hipEventCreateWithFlags");
+    }
+    pl->upload_event = ev;
+  }
+  e = hipEventRecord(static_cast<hipEvent_t>(pl->upload_event), s);
+  if (e != hipSuccess) {
+    pl->planned = 0;
+    return hip_fail(e, "hipEventRecord");
+  }
+  pl->uploaded = 1;
+  return FA_OK;
+}
+
+fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats) {
+  const PlanImpl* pl = plan ? impl(plan) : nullptr;
+  if (!pl || pl->magic != kPlanMagic || !pl->planned || !stats) {
+    set_error("plan object was not filled by fa_plan");
+    return FA_ERR_INVALID;
+  }
+  memset(stats, 0, sizeof(*stats));
+  stats->num_tiles = pl->num_tiles;
+  stats->num_merge = pl->num_merge;
+  stats->num_slots = pl->num_slots;
+  stats->chunk_pages = pl->chunk_pages;
+  stats->batch = pl->batch;
+  stats->num_rows = pl->num_rows;
+  stats->causal = pl->causal;
+  stats->uploaded = pl->uploaded;
+  stats->resolved = pl->geom;
+  return FA_OK;
+}
+
+fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t* num_tiles,
+                        const int32_t** merge_h, int32_t* num_merge) {
+  const PlanImpl* pl = plan ? impl(plan) : nullptr;
+  if (!pl || pl->magic != kPlanMagic || !pl->planned) {
+    set_error("plan object was not filled by fa_plan");
+    return FA_ERR_INVALID;
+  }
+  const uint8_t* ws = static_cast<const uint8_t*>(pl->host_ws);
+  if (tiles_h) *tiles_h = reinterpret_cast<const int32_t*>(ws + pl->lay.tiles);
+  if (num_tiles) *num_tiles = pl->num_tiles;
+  if (merge_h) *merge_h = reinterpret_cast<const int32_t*>(ws + pl->lay.merge);
+  if (num_merge) *num_merge = pl->num_merge;
+  return FA_OK;
+}
+
+fa_status fa_plan_destroy(fa_plan_t* plan) {
+  if (!plan) return FA_OK;
+  PlanImpl* pl = impl(plan);
+  if (pl->magic == kPlanMagic && pl->upload_event) {
+    hipEventDestroy(static_cast<hipEvent_t>(pl->upload_event));
+  }
+  memset(plan, 0, sizeof(*plan));
+  return FA_OK;
+}
+
+fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
+                    const void* v_pages, int64_t page_stride, int64_t token_stride,
+                    int64_t head_stride, const int32_t* kv_indices_d, const int32_t* kv_indptr_d,
+                    const int32_t* last_page_len_d, float sm_scale, void* out, float* lse,
+                    void* stream) {
+  const PlanImpl* pl = plan ? impl(plan) : nullptr;
+  fa_status st = check_run_args(pl, FA_MODE_DECODE, q, k_pages, v_pages, page_stride,
+                                token_stride, head_stride, kv_indices_d, kv_indptr_d,
+                                last_page_len_d, out);
+  if (st != FA_OK) return st;
+  const AttnParams p = make_params(pl, q, k_pages, v_pages, page_stride, token_stride,
+                                   head_stride, kv_indices_d, kv_indptr_d, last_page_len_d,
+                                   nullptr, sm_scale, out, lse);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
+  hipError_t e = launch_decode(p, pl->geom.dtype, G, pl->geom.max_tiles, s);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  e = launch_merge_partials(p, pl->geom.dtype, pl->geom.max_merge, s);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return FA_OK;
+}
+
+fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indptr_d,
+                    const void* k_pages, const void* v_pages, int64_t page_stride,
+                    int64_t token_stride, int64_t head_stride, const int32_t* kv_indices_d,
+                    const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
+                    void* out, float* lse, void* stream) {
+  const PlanImpl* pl = plan ? impl(plan) : nullptr;
+  fa_status st = check_run_args(pl, FA_MODE_APPEND, q, k_pages, v_pages, page_stride,
+                                token_stride, head_stride, kv_indices_d, kv_indptr_d,
+                                last_page_len_d, out);
+  if (st != FA_OK) return st;
+  if (!qo_indptr_d) {
+    set_error("qo_indptr is NULL");
+    return FA_ERR_INVALID;
+  }
+  const AttnParams p = make_params(pl, q, k_pages, v_pages, page_stride, token_stride,
+                                   head_stride, kv_indices_d, kv_indptr_d, last_page_len_d,
+                                   qo_indptr_d, sm_scale, out, lse);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
+  hipError_t e = launch_append(p, pl->geom.dtype, G, pl->geom.max_tiles, s);
+  if (e == hipErrorNotSupported) {
+    set_error("append kernel not built for this group size");
+    return FA_ERR_UNSUPPORTED;
+  }
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  e = launch_merge_partials(p, pl->geom.dtype, pl->geom.max_merge, s);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return FA_OK;
+}
+
+fa_status fa_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                         void* v_out, float* s_out, int64_t n, int32_t heads, int32_t head_dim,
+                         int32_t dtype, void* stream) {
+  if (n < 0 || heads <= 0 || head_dim <= 0 || (head_dim & 7) ||
+      (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_F32)) {
+    set_error("merge_state: bad sizes or dtype");
+    return FA_ERR_INVALID;
+  }
+  if (n == 0) return FA_OK;
+  if (!v_a || !s_a || !v_b || !s_b || !v_out || !aligned16(v_a) || !aligned16(v_b) ||
+      !aligned16(v_out)) {
+    set_error("merge_state: NULL or misaligned buffer");
+    return FA_ERR_INVALID;
+  }
+  hipError_t e = launch_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, n, heads, head_dim, dtype,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e, "merge_state kernel launch");
+}
+
+fa_status fa_merge_states(const void* v, const float* s, int64_t n, int32_t k, int32_t heads,
+                          int32_t head_dim, int32_t dtype, void* v_out, float* s_out,
+                          void* stream) {
+  if (n < 0 || k < 0 || heads <= 0 || head_dim <= 0 || (head_dim & 7) ||
+      (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_F32)) {
+    set_error("merge_states: bad sizes or dtype");
+    return FA_ERR_INVALID;
+  }
+  if (n == 0) return FA_OK;
+  if ((k > 0 && (!v || !s || !aligned16(v))) || !v_out || !aligned16(v_out)) {
+    set_error("merge_states: NULL or misaligned buffer");
+    return FA_ERR_INVALID;
+  }
+  hipError_t e = launch_merge_states(v, s, n, k, heads, head_dim, dtype, v_out, s_out,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e, "merge_states kernel launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Kernel parameter blocks and launchers (host side of the kernels).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pkfa {
+
+// One work tile = {request, kv_head, row_begin, row_end, key_begin, key_end,
+// slot0, n_chunks} (int32 x 8), read from the device workspace.
+struct AttnParams {
+  const int32_t* header;      // {num_tiles, num_merge, ...}
+  const int32_t* tiles;
+  const int32_t* merge;
+  const uint16_t* q;          // [rows, Hq, 128]
+  const uint16_t* k;          // page pools (16-bit elements)
+  const uint16_t* v;
+  int64_t page_stride, token_stride, head_stride;  // elements
+  const int32_t* kv_indices;
+  const int32_t* kv_indptr;
+  const int32_t* last_page_len;
+  const int32_t* qo_indptr;   // append only
+  uint16_t* out;              // [rows, Hq, 128]
+  float* lse;                 // [rows, Hq] natural log, may be null
+  float* part_o;              // [slots, Hq, 128] fp32
+  float* part_lse;            // [slots, Hq] log2 units
+  float scale_log2;           // sm_scale * log2(e)
+  int32_t num_qo_heads;
+  int32_t causal;
+};
+
+hipError_t launch_decode(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
+hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
+hipError_t launch_merge_partials(const AttnParams& p, int dtype, int max_merge, hipStream_t s);
+hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
+                              void* vo, float* so, int64_t n, int heads, int head_dim, int dtype,
+                              hipStream_t s);
+hipError_t launch_merge_states(const void* v, const float* s, int64_t n, int k, int heads,
+                               int head_dim, int dtype, void* vo, float* so, hipStream_t st);
+
+}  // namespace pkfa

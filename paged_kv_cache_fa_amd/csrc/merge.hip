@@ -1,0 +1,213 @@
+// Log-sum-exp merge of attention states on gfx950.
+//
+// [Guide] "FlashInfer: GPU Kernels for LLM Inference (2026 Guide)", section
+// "Cascade attention for shared prefixes": states computed over disjoint key
+// sets are combined by merge_state / merge_states. For states (v_c, s_c):
+//   s = log(sum_c exp(s_c)),   v = sum_c exp(s_c - s) v_c,
+// evaluated here as a running (online) merge in fp32 so any number of states
+// streams through registers; a state with s = -inf contributes nothing and
+// all-empty input gives (0, -inf).
+//
+// These kernels are HBM-bound elementwise passes: each thread owns 8
+// consecutive elements of one (row, head), loads 16/32 bytes per state and
+// writes its 8 outputs once.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkfa {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive values of type DT (FA_F32 or a 16-bit type) <-> fp32.
+template <int DT>
+struct Vec8 {
+  __device__ __forceinline__ static void load(const void* base, int64_t idx, float (&x)[8]) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = Elt<DT>::lo(u[i]);
+      x[2 * i + 1] = Elt<DT>::hi(u[i]);
+    }
+  }
+  __device__ __forceinline__ static void store(void* base, int64_t idx, const float (&x)[8]) {
+    u32x4 u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = Elt<DT>::pack(x[2 * i], x[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + idx) = u;
+  }
+};
+
+template <>
+struct Vec8<FA_F32> {
+  __device__ __forceinline__ static void load(const void* base, int64_t idx, float (&x)[8]) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  __device__ __forceinline__ static void store(void* base, int64_t idx, const float (&x)[8]) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);
+    p[0] = make_float4(x[0], x[1], x[2], x[3]);
+    p[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
+};
+
+// Running merge state in log2 units.
+struct Online {
+  float m = kNegInf, sum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  __device__ __forceinline__ void add(float s2, const float (&v)[8]) {
+    if (s2 == kNegInf) return;
+    const float mn = fmaxf(m, s2);
+    const float f = fast_exp2(m - mn);  // m = -inf -> 0
+    const float w = fast_exp2(s2 - mn);
+    sum = sum * f + w;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] * f + w * v[i];
+    m = mn;
+  }
+  __device__ __forceinline__ void finish(float (&out)[8], float& lse2) const {
+    const bool live = sum > 0.f;
+    const float inv = live ? 1.f / sum : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = acc[i] * inv;
+    lse2 = live ? m + fast_log2(sum) : kNegInf;
+  }
+};
+
+// Split-KV reduction: merge entry i = {row, first_slot, n_slots}; partial
+// states are fp32 [slots, Hq, 128] with log2-unit lse.
+template <int DT>
+__global__ __launch_bounds__(256) void merge_partials_kernel(AttnParams p) {
+  const int i = blockIdx.x;
+  if (i >= p.header[1]) return;
+  const int32_t* e = p.merge + i * 4;
+  const int row = e[0], s0 = e[1], C = e[2];
+  const int Hq = p.num_qo_heads;
+  for (int it = threadIdx.x; it < Hq * 16; it += 256) {
+    const int h = it >> 4, d = (it & 15) * 8;
+    Online st;
+    for (int c = 0; c < C; ++c) {
+      const int64_t sl = (int64_t)(s0 + c) * Hq + h;
+      const float s2 = p.part_lse[sl];
+      float v[8];
+      Vec8<FA_F32>::load(p.part_o, sl * 128 + d, v);
+      st.add(s2, v);
+    }
+    float o[8], lse2;
+    st.finish(o, lse2);
+    Vec8<DT>::store(p.out, ((int64_t)row * Hq + h) * 128 + d, o);
+    if (d == 0 && p.lse) p.lse[(int64_t)row * Hq + h] = lse2 * kLn2;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void merge_state_kernel(const void* va, const float* sa,
+                                                          const void* vb, const float* sb,
+                                                          void* vo, float* so, int64_t n, int heads,
+                                                          int head_dim) {
+  const int chunks = head_dim / 8;
+  const int64_t total = n * heads * chunks;
+  for (int64_t it = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; it < total;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rh = it / chunks;
+    const int64_t idx = rh * head_dim + (it % chunks) * 8;
+    float a[8], b[8];
+    Vec8<DT>::load(va, idx, a);
+    Vec8<DT>::load(vb, idx, b);
+    const float s_a = sa[rh], s_b = sb[rh];
+    Online st;
+    st.add(s_a * kLog2e, a);
+    st.add(s_b * kLog2e, b);
+    float o[8], lse2;
+    st.finish(o, lse2);
+    Vec8<DT>::store(vo, idx, o);
+    if (so && (it % chunks) == 0) so[rh] = lse2 * kLn2;
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void merge_states_kernel(const void* v, const float* s, int64_t n,
+                                                           int k, int heads, int head_dim, void* vo,
+                                                           float* so) {
+  const int chunks = head_dim / 8;
+  const int64_t total = n * heads * chunks;
+  for (int64_t it = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; it < total;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rh = it / chunks;  // row * heads + head
+    const int64_t row = rh / heads, h = rh % heads;
+    const int d = (int)(it % chunks) * 8;
+    Online st;
+    for (int c = 0; c < k; ++c) {
+      const int64_t sh = (row * k + c) * heads + h;
+      float x[8];
+      Vec8<DT>::load(v, sh * head_dim + d, x);
+      st.add(s[sh] * kLog2e, x);
+    }
+    float o[8], lse2;
+    st.finish(o, lse2);
+    Vec8<DT>::store(vo, rh * head_dim + d, o);
+    if (so && d == 0) so[rh] = lse2 * kLn2;
+  }
+}
+
+int grid_for(int64_t total) {
+  const int64_t blocks = (total + 255) / 256;
+  return (int)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_merge_partials(const AttnParams& p, int dtype, int max_merge, hipStream_t s) {
+  if (max_merge <= 0) return hipSuccess;
+  if (dtype == FA_BF16)
+    hipLaunchKernelGGL(merge_partials_kernel<FA_BF16>, dim3(max_merge), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(merge_partials_kernel<FA_F16>, dim3(max_merge), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
+                              void* vo, float* so, int64_t n, int heads, int head_dim, int dtype,
+                              hipStream_t s) {
+  const int64_t total = n * heads * (head_dim / 8);
+  if (total <= 0) return hipSuccess;
+  const int grid = grid_for(total);
+  switch (dtype) {
+    case FA_BF16:
+      hipLaunchKernelGGL(merge_state_kernel<FA_BF16>, dim3(grid), dim3(256), 0, s, va, sa, vb, sb,
+                         vo, so, n, heads, head_dim);
+      break;
+    case FA_F16:
+      hipLaunchKernelGGL(merge_state_kernel<FA_F16>, dim3(grid), dim3(256), 0, s, va, sa, vb, sb,
+                         vo, so, n, heads, head_dim);
+      break;
+    default:
+      hipLaunchKernelGGL(merge_state_kernel<FA_F32>, dim3(grid), dim3(256), 0, s, va, sa, vb, sb,
+                         vo, so, n, heads, head_dim);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_states(const void* v, const float* sv, int64_t n, int k, int heads,
+                               int head_dim, int dtype, void* vo, float* so, hipStream_t s) {
+  const int64_t total = n * heads * (head_dim / 8);
+  if (total <= 0) return hipSuccess;
+  const int grid = grid_for(total);
+  switch (dtype) {
+    case FA_BF16:
+      hipLaunchKernelGGL(merge_states_kernel<FA_BF16>, dim3(grid), dim3(256), 0, s, v, sv, n, k,
+                         heads, head_dim, vo, so);
+      break;
+    case FA_F16:
+      hipLaunchKernelGGL(merge_states_kernel<FA_F16>, dim3(grid), dim3(256), 0, s, v, sv, n, k,
+                         heads, head_dim, vo, so);
+      break;
+    default:
+      hipLaunchKernelGGL(merge_states_kernel<FA_F32>, dim3(grid), dim3(256), 0, s, v, sv, n, k,
+                         heads, head_dim, vo, so);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkfa

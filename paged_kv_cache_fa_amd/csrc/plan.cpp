@@ -1,0 +1,296 @@
+// Split-KV work planner: host-only, integer-only.
+//
+// [Guide] "FlashInfer: GPU Kernels for LLM Inference (2026 Guide)", section
+// "What FlashInfer is" (idea 3: plan the split of uneven requests so the load
+// is even while the launch stays static for graphs) and [DeepDive] "FlashInfer:
+// The Attention Kernel Library That Proves the Bottleneck ...", section "It In
+// Action" step 1 (a per-step plan computes only tile assignments). The pages
+// give no algorithm; this planner fixes one:
+//
+//  * a q tile is up to qo_tile query rows of one request (one row in decode);
+//    its visible keys are kv_len, or for causal append the keys seen by its
+//    last row, kv_len - qo_len + row_end;
+//  * with units = num_kv_heads * sum(visible pages) and target = num_cu *
+//    tiles_per_cu tiles, every q tile is cut into chunks of
+//    P = max(min_chunk_pages, ceil(units / target)) pages, so all tiles cost
+//    about the same and there are about `target` of them;
+//  * a q tile cut into C > 1 chunks gets C fp32 partial states per row, merged
+//    afterwards by log-sum-exp; otherwise its tile writes the output directly;
+//  * tiles are ordered by descending cost (rows x keys), stable on
+//    (request, q tile, chunk, kv head), so in-order dispatch starts the
+//    longest tiles first.
+//
+// The launch shapes depend only on the capacities derived from the geometry,
+// never on the lengths, which is what keeps a captured graph valid across plans.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "plan_internal.h"
+
+namespace pkfa {
+
+namespace {
+thread_local char g_err[512] = "";
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+const char* last_error() { return g_err; }
+
+fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
+  if (!in || !out) {
+    set_error("geometry is NULL");
+    return FA_ERR_INVALID;
+  }
+  fa_geometry g = *in;
+  if (g.mode != FA_MODE_DECODE && g.mode != FA_MODE_APPEND) {
+    set_error("unknown mode %d", g.mode);
+    return FA_ERR_INVALID;
+  }
+  if (g.max_batch <= 0 || g.num_qo_heads <= 0 || g.num_kv_heads <= 0 ||
+      g.num_qo_heads % g.num_kv_heads != 0) {
+    set_error("need max_batch > 0 and num_qo_heads a positive multiple of num_kv_heads");
+    return FA_ERR_INVALID;
+  }
+  if (g.mode == FA_MODE_APPEND && g.max_qo_tokens <= 0) {
+    set_error("append geometry needs max_qo_tokens > 0");
+    return FA_ERR_INVALID;
+  }
+  if (g.num_cu < 0 || g.tiles_per_cu < 0 || g.min_chunk_pages < 0 || g.qo_tile < 0 ||
+      g.max_tiles < 0 || g.max_partials < 0 || g.max_merge < 0) {
+    set_error("negative plan knob");
+    return FA_ERR_INVALID;
+  }
+  const int G = g.num_qo_heads / g.num_kv_heads;
+  if (g.head_dim != kSupportedHeadDim || g.page_size != kSupportedPageSize ||
+      !(G == 1 || G == 2 || G == 4 || G == 8) || (g.dtype != FA_F16 && g.dtype != FA_BF16)) {
+    set_error("unsupported: head_dim %d page_size %d group %d dtype %d (built: 128, 16, "
+              "{1,2,4,8}, fp16/bf16)", g.head_dim, g.page_size, G, g.dtype);
+    return FA_ERR_UNSUPPORTED;
+  }
+  const bool app = g.mode == FA_MODE_APPEND;
+  if (!app) g.max_qo_tokens = 0;
+  if (!g.num_cu) g.num_cu = 256;
+  if (!g.tiles_per_cu) g.tiles_per_cu = app ? 2 : 8;
+  if (!g.min_chunk_pages) g.min_chunk_pages = 1;
+  g.qo_tile = app ? (g.qo_tile ? g.qo_tile : 32) : 1;
+  if (app && g.qo_tile != 32) {
+    set_error("append kernels are built for qo_tile 32");
+    return FA_ERR_UNSUPPORTED;
+  }
+  const int64_t target = (int64_t)g.num_cu * g.tiles_per_cu;
+  const int64_t nqt = app ? (int64_t)g.max_batch + cdiv(g.max_qo_tokens, g.qo_tile)
+                          : (int64_t)g.max_batch;
+  int64_t mt = g.max_tiles ? g.max_tiles : target + (int64_t)g.num_kv_heads * nqt;
+  int64_t mp = g.max_partials ? g.max_partials : 2 * (int64_t)g.qo_tile * cdiv(target, g.num_kv_heads);
+  int64_t mm = g.max_merge ? g.max_merge : (int64_t)g.qo_tile * cdiv(target, g.num_kv_heads);
+  if (mt > (1 << 26) || mp > (1 << 26) || mm > (1 << 26)) {
+    set_error("capacities too large");
+    return FA_ERR_INVALID;
+  }
+  g.max_tiles = (int32_t)mt;
+  g.max_partials = (int32_t)mp;
+  g.max_merge = (int32_t)mm;
+  *out = g;
+  return FA_OK;
+}
+
+Layout compute_layout(const fa_geometry& g) {
+  Layout L;
+  L.header = 0;
+  L.merge = kHeaderInts * 4;
+  L.tiles = align_up(L.merge + (size_t)g.max_merge * kMergeInts * 4, 64);
+  L.upload_end = L.tiles + (size_t)g.max_tiles * kTileInts * 4;
+  L.dev_part_lse = align_up(L.upload_end, 256);
+  L.dev_part_o = align_up(L.dev_part_lse + (size_t)g.max_partials * g.num_qo_heads * 4, 256);
+  L.dev_bytes = align_up(L.dev_part_o + (size_t)g.max_partials * g.num_qo_heads * g.head_dim * 4, 256);
+  L.host_unsorted = align_up(L.upload_end, 64);
+  L.host_order = L.host_unsorted + (size_t)g.max_tiles * kTileInts * 4;
+  L.host_cost = align_up(L.host_order + (size_t)g.max_tiles * 4, 8);
+  L.host_bytes = L.host_cost + (size_t)g.max_tiles * 8;
+  return L;
+}
+
+fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr,
+                     const int32_t* kv_lens, int32_t batch, const int32_t* qo_indptr,
+                     int32_t causal, void* host_ws, size_t host_ws_bytes) {
+  const bool app = g.mode == FA_MODE_APPEND;
+  const int ps = g.page_size;
+  if (batch < 0 || batch > g.max_batch) {
+    set_error("batch %d outside [0, %d]", batch, g.max_batch);
+    return FA_ERR_INVALID;
+  }
+  if (batch > 0 && (!kv_indptr || !kv_lens)) {
+    set_error("kv_indptr / kv_lens is NULL");
+    return FA_ERR_INVALID;
+  }
+  if (app != (qo_indptr != nullptr)) {
+    set_error(app ? "append plan needs qo_indptr" : "decode plan takes no qo_indptr");
+    return FA_ERR_INVALID;
+  }
+  if (kv_indptr && kv_indptr[0] != 0) {
+    set_error("kv_indptr[0] must be 0");
+    return FA_ERR_INVALID;
+  }
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+    const int64_t L = kv_lens[b];
+    if (n < 0) {
+      set_error("kv_indptr decreases at request %d", b);
+      return FA_ERR_INVALID;
+    }
+    if (n == 0 ? L != 0 : !((n - 1) * ps < L && L <= n * ps)) {
+      set_error("request %d: kv_len %lld inconsistent with %lld pages", b, (long long)L,
+                (long long)n);
+      return FA_ERR_INVALID;
+    }
+  }
+  if (app) {
+    if (qo_indptr[0] != 0) {
+      set_error("qo_indptr[0] must be 0");
+      return FA_ERR_INVALID;
+    }
+    for (int b = 0; b < batch; ++b) {
+      const int64_t ql = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+      if (ql < 0) {
+        set_error("qo_indptr decreases at request %d", b);
+        return FA_ERR_INVALID;
+      }
+      if (causal && ql > kv_lens[b]) {
+        set_error("request %d: causal qo_len %lld exceeds kv_len %d", b, (long long)ql, kv_lens[b]);
+        return FA_ERR_INVALID;
+      }
+    }
+    if (qo_indptr[batch] > g.max_qo_tokens) {
+      set_error("%d query rows exceed max_qo_tokens %d", qo_indptr[batch], g.max_qo_tokens);
+      return FA_ERR_INVALID;
+    }
+  }
+  const Layout lay = compute_layout(g);
+  if (!host_ws || host_ws_bytes < lay.host_bytes) {
+    set_error("host workspace needs %zu bytes", lay.host_bytes);
+    return FA_ERR_WORKSPACE;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(host_ws);
+  int32_t* header = reinterpret_cast<int32_t*>(ws + lay.header);
+  int32_t* merge = reinterpret_cast<int32_t*>(ws + lay.merge);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
+  int32_t* unsorted = reinterpret_cast<int32_t*>(ws + lay.host_unsorted);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + lay.host_order);
+  int64_t* cost = reinterpret_cast<int64_t*>(ws + lay.host_cost);
+
+  // Visit q tiles in (request, tile) order; fn(b, row0, row1, visible_keys).
+  const int qt = g.qo_tile;
+  auto for_each_qtile = [&](auto&& fn) {
+    for (int b = 0; b < batch; ++b) {
+      const int64_t L = kv_lens[b];
+      if (!app) {
+        fn(b, (int64_t)b, (int64_t)b + 1, L);
+        continue;
+      }
+      const int64_t r0 = qo_indptr[b], r1 = qo_indptr[b + 1], ql = r1 - r0;
+      for (int64_t t0 = 0; t0 < ql; t0 += qt) {
+        const int64_t t1 = std::min(ql, t0 + qt);
+        const int64_t vis = causal ? std::min(L, L - ql + t1) : L;
+        fn(b, r0 + t0, r0 + t1, vis);
+      }
+    }
+  };
+
+  int64_t units = 0;
+  for_each_qtile([&](int, int64_t, int64_t, int64_t vis) { units += cdiv(vis, ps); });
+  units *= g.num_kv_heads;
+  const int64_t target = (int64_t)g.num_cu * g.tiles_per_cu;
+  const int64_t P = std::max<int64_t>(g.min_chunk_pages, cdiv(units, target));
+
+  int64_t ntiles = 0, nmerge = 0, slots = 0;
+  bool over = false;
+  for_each_qtile([&](int b, int64_t q0, int64_t q1, int64_t vis) {
+    const int64_t C = std::max<int64_t>(1, cdiv(cdiv(vis, ps), P));
+    int64_t base = -1;
+    if (C > 1) {
+      base = slots;
+      slots += C * (q1 - q0);
+      for (int64_t r = q0; r < q1; ++r) {
+        if (nmerge < g.max_merge && base + (r - q0) * C + C <= g.max_partials) {
+          int32_t* m = merge + nmerge * kMergeInts;
+          m[0] = (int32_t)r;
+          m[1] = (int32_t)(base + (r - q0) * C);
+          m[2] = (int32_t)C;
+          m[3] = 0;
+        }
+        ++nmerge;
+      }
+    }
+    for (int64_t c = 0; c < C; ++c) {
+      const int64_t k0 = c * P * ps, k1 = std::min((c + 1) * P * ps, vis);
+      for (int h = 0; h < g.num_kv_heads; ++h) {
+        if (ntiles >= g.max_tiles) {
+          over = true;
+          ++ntiles;
+          continue;
+        }
+        int32_t* t = unsorted + ntiles * kTileInts;
+        t[0] = b;
+        t[1] = h;
+        t[2] = (int32_t)q0;
+        t[3] = (int32_t)q1;
+        t[4] = (int32_t)k0;
+        t[5] = (int32_t)k1;
+        t[6] = C > 1 ? (int32_t)(base + c) : -1;
+        t[7] = (int32_t)C;
+        cost[ntiles] = (k1 - k0) * (q1 - q0);
+        ++ntiles;
+      }
+    }
+  });
+  if (over || ntiles > g.max_tiles) {
+    set_error("%lld tiles exceed max_tiles %d", (long long)ntiles, g.max_tiles);
+    return FA_ERR_CAPACITY;
+  }
+  if (slots > g.max_partials) {
+    set_error("%lld partial states exceed max_partials %d", (long long)slots, g.max_partials);
+    return FA_ERR_CAPACITY;
+  }
+  if (nmerge > g.max_merge) {
+    set_error("%lld merge rows exceed max_merge %d", (long long)nmerge, g.max_merge);
+    return FA_ERR_CAPACITY;
+  }
+  for (int64_t i = 0; i < ntiles; ++i) order[i] = (int32_t)i;
+  std::stable_sort(order, order + ntiles, [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+  for (int64_t i = 0; i < ntiles; ++i)
+    memcpy(tiles + i * kTileInts, unsorted + (int64_t)order[i] * kTileInts, kTileInts * 4);
+
+  memset(header, 0, kHeaderInts * 4);
+  header[0] = (int32_t)ntiles;
+  header[1] = (int32_t)nmerge;
+  header[2] = batch;
+  header[3] = app ? qo_indptr[batch] : batch;
+  header[4] = app ? causal : 0;
+  header[5] = (int32_t)P;
+
+  p->num_tiles = (int32_t)ntiles;
+  p->num_merge = (int32_t)nmerge;
+  p->num_slots = (int32_t)slots;
+  p->chunk_pages = (int32_t)P;
+  p->batch = batch;
+  p->num_rows = header[3];
+  p->causal = header[4];
+  p->geom = g;
+  p->lay = lay;
+  p->host_ws = host_ws;
+  return FA_OK;
+}
+
+}  // namespace pkfa

@@ -1,0 +1,53 @@
+// Internal plan object and workspace layout. Host-only C++ (no HIP headers),
+// so the planner builds and is tested with a plain host compiler too.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+
+namespace pkfa {
+
+constexpr uint32_t kPlanMagic = 0x70666131u;  // "pfa1"
+constexpr int kTileInts = 8;                   // {b, h, row0, row1, key0, key1, slot0, nchunk}
+constexpr int kMergeInts = 4;                  // {row, slot0, nslot, 0}
+constexpr int kHeaderInts = 16;                // {num_tiles, num_merge, batch, num_rows, causal, chunk_pages, ...}
+constexpr int kSupportedHeadDim = 128;
+constexpr int kSupportedPageSize = 16;
+
+// Byte offsets of the regions inside the host and device workspaces.
+struct Layout {
+  size_t header, merge, tiles, upload_end;  // upload image (same offsets in host and device ws)
+  size_t dev_part_lse, dev_part_o, dev_bytes;
+  size_t host_unsorted, host_order, host_cost, host_bytes;
+};
+
+struct PlanImpl {
+  uint32_t magic;
+  int32_t planned;    // 1 after a successful fa_plan
+  int32_t uploaded;   // 1 if the plan was copied into a device workspace
+  int32_t num_tiles, num_merge, num_slots, chunk_pages, batch, num_rows, causal;
+  fa_geometry geom;   // resolved
+  Layout lay;
+  void* host_ws;
+  void* dev_ws;
+  void* upload_event;  // hipEvent_t recorded after the copy out of host_ws
+};
+static_assert(sizeof(PlanImpl) <= sizeof(fa_plan_t), "plan object too large");
+
+inline PlanImpl* impl(fa_plan_t* p) { return reinterpret_cast<PlanImpl*>(p); }
+inline const PlanImpl* impl(const fa_plan_t* p) { return reinterpret_cast<const PlanImpl*>(p); }
+
+// Fill default knobs and check the geometry. Returns FA_OK or an error code.
+fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out);
+Layout compute_layout(const fa_geometry& g);
+
+// Build the plan into the host workspace (upload image + scratch). Host only.
+fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr,
+                     const int32_t* kv_lens, int32_t batch, const int32_t* qo_indptr,
+                     int32_t causal, void* host_ws, size_t host_ws_bytes);
+
+void set_error(const char* fmt, ...);
+
+}  // namespace pkfa

@@ -1,0 +1,83 @@
+"""Helpers for GPU tests: upload a seeded workload, run the library, compare."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import paged_kv_cache_fa_amd as fa
+
+OUT_TOL = 2e-2     # max-abs on out (16-bit outputs, fp32 accumulation)
+LSE_TOL = 1e-3     # max-abs on lse (natural log)
+
+
+def torch_dtype(name):
+    import torch
+    return {"bf16": torch.bfloat16, "fp16": torch.float16}[name]
+
+
+class DevWorkload:
+    """Device copies of a workload's stored bytes (pool, q, page tables)."""
+
+    def __init__(self, wl, device="cuda"):
+        import torch
+        self.wl = wl
+        dt = torch_dtype(wl.dtype)
+        self.device = device
+        self.pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
+        self.q = torch.from_numpy(wl.q.view(np.int16)).to(device).view(dt)
+        self.kv_indptr = torch.from_numpy(wl.kv_indptr).to(device)
+        self.kv_indices = torch.from_numpy(wl.kv_indices).to(device)
+        self.last_page_len = torch.from_numpy(wl.last_page_len).to(device)
+        self.qo_indptr = (torch.from_numpy(wl.qo_indptr).to(device)
+                          if wl.qo_indptr is not None else None)
+        if wl.prefix_indptr is not None:
+            self.prefix_indptr = torch.from_numpy(wl.prefix_indptr).to(device)
+            self.prefix_indices = torch.from_numpy(wl.prefix_indices).to(device)
+            self.prefix_last_page_len = torch.from_numpy(wl.prefix_last_page_len).to(device)
+        _, _, ps, hkv, d = wl.pool.shape
+        self.strides = (2 * ps * hkv * d, hkv * d, d)
+
+    @property
+    def k(self):
+        return self.pool[:, 0]
+
+    @property
+    def v(self):
+        return self.pool[:, 1]
+
+
+def decode_geometry(wl, **knobs):
+    return fa.geometry("decode", wl.dtype, max(wl.batch, 1), wl.num_qo_heads, wl.num_kv_heads,
+                       **knobs)
+
+
+def run_decode(dw: DevWorkload, plan=None, out=None, lse=None, **knobs):
+    wl = dw.wl
+    if plan is None:
+        plan = fa.Plan(decode_geometry(wl, **knobs), device=dw.device)
+        plan.plan(wl.kv_indptr, wl.kv_lens)
+    out, lse = fa.decode(plan, dw.q, dw.k, dw.v, *dw.strides, dw.kv_indices, dw.kv_indptr,
+                         dw.last_page_len, out=out, lse=lse)
+    return plan, out, lse
+
+
+def to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def oracle_decode(wl, requests=None):
+    return oracle.decode(wl.q, wl.pool, wl.dtype, wl.kv_indptr, wl.kv_indices, wl.last_page_len,
+                         wl.page_size, requests=requests)
+
+
+def assert_close(out, lse, ref_out, ref_lse, out_tol=OUT_TOL, lse_tol=LSE_TOL, what=""):
+    out = np.asarray(out, np.float64)
+    lse = np.asarray(lse, np.float64)
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    assert np.array_equal(np.isneginf(lse), np.isneginf(ref_lse)), f"{what}: -inf pattern"
+    e_out = float(np.max(np.abs(out - ref_out))) if out.size else 0.0
+    fin = np.isfinite(ref_lse)
+    e_lse = float(np.max(np.abs(lse[fin] - ref_lse[fin]))) if fin.any() else 0.0
+    assert e_out <= out_tol, f"{what}: out max-abs {e_out} > {out_tol}"
+    assert e_lse <= lse_tol, f"{what}: lse max-abs {e_lse} > {lse_tol}"
+    return e_out, e_lse

@@ -1,0 +1,169 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-only plan is bit-identical to the reference plan procedure."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_fa_amd as fa
+from oracle.plan_spec import PlanSpecError, plan_spec
+from workloads import config_lengths
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    declared = _declared_symbols()
+    assert declared == sorted(fa._lib.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = fa.load()
+    assert lib.fa_status_string(0) == b"ok"
+    assert lib.fa_status_string(-6) == b"stream is capturing a graph"
+
+
+def _indptr(lens, ps=16):
+    n = [-(-int(L) // ps) for L in lens]
+    return np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+
+
+def _geom(mode, max_batch, Hq, Hkv, max_qo=0, **knobs):
+    return fa.geometry(mode, "bf16", max_batch, Hq, Hkv, max_qo_tokens=max_qo, **knobs)
+
+
+def _compare(g, lens, qo_indptr=None, causal=False, **spec_knobs):
+    p = fa.Plan(g)           # host-only plan: no HIP call is made
+    p.plan(_indptr(lens), np.asarray(lens, np.int32), qo_indptr, causal)
+    st = p.info()
+    r = st.resolved
+    knobs = dict(num_cu=r.num_cu, tiles_per_cu=r.tiles_per_cu, min_chunk_pages=r.min_chunk_pages,
+                 qo_tile=r.qo_tile, max_tiles=r.max_tiles, max_partials=r.max_partials,
+                 max_merge=r.max_merge)
+    spec = plan_spec(_indptr(lens), lens, len(lens), g.num_qo_heads, g.num_kv_heads, 128, 16,
+                     max_batch=g.max_batch, qo_indptr=qo_indptr, causal=causal,
+                     max_qo_tokens=g.max_qo_tokens, **knobs)
+    tiles, merge = p.tiles()
+    assert np.array_equal(tiles, spec["tiles"])
+    assert np.array_equal(merge, spec["merge"])
+    assert st.chunk_pages == spec["chunk_pages"] and st.num_slots == spec["num_slots"]
+    assert st.uploaded == 0
+    return st
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_plan_bit_exact_decode_configs(k):
+    lens = config_lengths(k, np.random.default_rng(k))["kv_lens"]
+    Hkv = 32 if k == 1 else 8
+    _compare(_geom("decode", len(lens), 32, Hkv), lens)
+
+
+def test_plan_default_knobs_match_the_spec_defaults():
+    from oracle.plan_spec import default_knobs
+    for mode, mb, mq, hkv in (("decode", 64, 0, 8), ("append", 16, 8192, 8), ("decode", 3, 0, 1)):
+        p = fa.Plan(_geom(mode, mb, 8 * hkv if hkv < 8 else 32, hkv, mq))
+        lens = [16] * mb
+        qo = np.arange(mb + 1, dtype=np.int32) if mode == "append" else None
+        p.plan(_indptr(lens), np.asarray(lens, np.int32), qo, False)
+        r = p.info().resolved
+        d = default_knobs(hkv, mb, mq, mode == "append")
+        assert (r.num_cu, r.tiles_per_cu, r.min_chunk_pages, r.qo_tile, r.max_tiles,
+                r.max_partials, r.max_merge) == tuple(d[k] for k in (
+                    "num_cu", "tiles_per_cu", "min_chunk_pages", "qo_tile", "max_tiles",
+                    "max_partials", "max_merge"))
+
+
+def test_plan_bit_exact_append_and_cascade_prefix():
+    lens = [4608] * 16
+    qo = np.concatenate([[0], np.cumsum([512] * 16)]).astype(np.int32)
+    _compare(_geom("append", 16, 32, 8, 8192), lens, qo, True)
+    _compare(_geom("append", 1, 32, 8, 256), [16384], np.array([0, 256], np.int32), False)
+
+
+def test_plan_bit_exact_random():
+    rng = np.random.default_rng(1)
+    for it in range(400):
+        B = int(rng.integers(0, 12))
+        lens = rng.integers(0, 700, size=B)
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        knobs = dict(num_cu=int(rng.integers(1, 40)), tiles_per_cu=int(rng.integers(1, 9)),
+                     min_chunk_pages=int(rng.integers(1, 5)))
+        if it % 2:
+            _compare(_geom("decode", max(B, 1) + int(rng.integers(0, 3)), G * Hkv, Hkv, **knobs),
+                     lens)
+        else:
+            ql = np.minimum(rng.integers(0, 100, size=B), lens)
+            causal = bool(rng.integers(0, 2))
+            if not causal:
+                ql = rng.integers(0, 100, size=B)
+            qo = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+            _compare(_geom("append", max(B, 1), G * Hkv, Hkv, max(int(qo[-1]), 1), **knobs),
+                     lens, qo, causal)
+
+
+@pytest.mark.parametrize("lens,indptr,hq,hkv,code", [
+    ([33], [0, 2], 8, 2, "INVALID"),
+    ([32], [0, 3], 8, 2, "INVALID"),
+    ([5], [0, 0], 8, 2, "INVALID"),
+    ([16], [1, 2], 8, 2, "INVALID"),
+    ([16], [0, 1], 12, 8, "INVALID"),
+    ([16], [0, 1], 48, 3, "UNSUPPORTED"),
+])
+def test_plan_error_codes_match_spec(lens, indptr, hq, hkv, code):
+    g = _geom("decode", 1, hq, hkv)
+    with pytest.raises(fa.FAError) as e:
+        fa.Plan(g).plan(np.asarray(indptr, np.int32), np.asarray(lens, np.int32))
+    assert e.value.code == code
+    with pytest.raises(PlanSpecError) as e2:
+        plan_spec(indptr, lens, 1, hq, hkv, 128, 16, max_batch=1)
+    assert e2.value.code == code
+
+
+def test_geometry_errors():
+    with pytest.raises(fa.FAError) as e:
+        fa.workspace_size(fa.geometry("decode", "bf16", 4, 32, 8, head_dim=64))
+    assert e.value.code == "UNSUPPORTED"
+    with pytest.raises(fa.FAError) as e:
+        fa.workspace_size(fa.geometry("append", "bf16", 4, 32, 8))   # max_qo_tokens missing
+    assert e.value.code == "INVALID"
+    g = fa.geometry("decode", "bf16", 4, 32, 8)
+    p = fa.Plan(g)
+    lib = fa.load()
+    small = np.zeros(16, np.uint8)
+    st = lib.fa_plan(ctypes.byref(p._plan), ctypes.byref(g), _indptr([16]).ctypes.data,
+                     np.array([16], np.int32).ctypes.data, 1, None, 0, small.ctypes.data, 16,
+                     None, 0, None)
+    assert st == fa._lib.FA_ERR_WORKSPACE
+
+
+def test_capacity_error():
+    g = _geom("decode", 4, 8, 8, max_tiles=16)
+    with pytest.raises(fa.FAError) as e:
+        fa.Plan(g).plan(_indptr([160] * 4), np.array([160] * 4, np.int32))
+    assert e.value.code == "CAPACITY"
+
+
+def test_run_calls_reject_host_only_plans():
+    g = _geom("decode", 1, 8, 2)
+    p = fa.Plan(g).plan(_indptr([16]), np.array([16], np.int32))
+    lib = fa.load()
+    buf = np.zeros(4096, np.uint16)
+    ptr = buf.ctypes.data
+    st = lib.fa_decode(ctypes.byref(p._plan), ptr, ptr, ptr, 2048, 256, 128, ptr, ptr, ptr, 0.0,
+                       ptr, None, None)
+    assert st == fa._lib.FA_ERR_NOT_PLANNED
+    st = lib.fa_append(ctypes.byref(p._plan), ptr, ptr, ptr, ptr, 2048, 256, 128, ptr, ptr, ptr,
+                       0.0, ptr, None, None)
+    assert st == fa._lib.FA_ERR_NOT_PLANNED
