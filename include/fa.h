@@ -75,7 +75,7 @@ typedef struct {
   int32_t page_size;       /* 16 */
   /* plan knobs (0 = default) */
   int32_t num_cu;          /* compute units to spread tiles over (default 256) */
-  int32_t tiles_per_cu;    /* tiles wanted per compute unit (default 8 decode, 2 append) */
+  int32_t tiles_per_cu;    /* decode: worker waves per compute unit (default 4); append: tiles per CU (default 2) */
   int32_t min_chunk_pages; /* smallest split-KV chunk in pages (default 1) */
   int32_t qo_tile;         /* append: query rows per tile (default 32); decode: 1 */
   int32_t max_tiles;       /* capacities; default = worst case of the plan procedure */
@@ -100,6 +100,7 @@ typedef struct {
   int32_t num_rows;        /* query rows (batch for decode) */
   int32_t causal;
   int32_t uploaded;        /* 1 if the plan was copied to a device workspace */
+  int32_t num_workers;     /* decode: worker waves (num_cu * tiles_per_cu); append: 0 */
   fa_geometry resolved;    /* geometry with every default filled in */
 } fa_plan_stats;
 
@@ -137,12 +138,19 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
 /* Summary of the current plan. */
 fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats);
 
-/* Host copies of the current plan, valid until the next fa_plan on this plan:
- * tiles int32 [num_tiles][8] = {request, kv_head, row_begin, row_end,
- * key_begin, key_end, slot0 (-1 = write the final output), n_chunks}; merge
- * int32 [num_merge][4] = {row, first_slot, n_slots, 0}. */
+/* Host copies of the current plan, valid until the next fa_plan on this plan.
+ * tiles int32 [num_tiles][8]:
+ *   decode  {request, kv_head, row, first_slot, key_begin, key_end, slot, n_pieces},
+ *           listed worker by worker; worker w runs tiles worker_ptr[w] ..
+ *           worker_ptr[w+1]-1 (worker_ptr int32 [num_workers+1]);
+ *   append  {request, kv_head, row_begin, row_end, key_begin, key_end, slot0, n_chunks},
+ *           one workgroup each, longest first; worker_ptr is NULL.
+ * A slot of -1 means the tile writes the final output. merge int32
+ * [num_merge][4] = {first row, kv_head, first_slot, n_states} per split unit.
+ * Any output pointer may be NULL. */
 fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t* num_tiles,
-                        const int32_t** merge_h, int32_t* num_merge);
+                        const int32_t** merge_h, int32_t* num_merge,
+                        const int32_t** worker_ptr_h, int32_t* num_workers);
 
 /* Release the HIP event a plan keeps for reusing its host workspace. */
 fa_status fa_plan_destroy(fa_plan_t* plan);

@@ -1,37 +1,52 @@
 """Split-KV work plan, reference procedure — oracle (test infrastructure only).
 
 [Guide, "What FlashInfer is", idea 3] and [DeepDive, "The Architecture,
-Unpacked" and "It In Action", step 1]: requests of very different lengths are
-cut into tiles that are spread evenly over the compute units; the launch
-shape is fixed while the tile assignment changes from step to step, so a
+Unpacked", "It In Action" step 1 and "Why This Design Works"]: requests of
+very different lengths are cut into pieces spread evenly over the GPU; the
+launch shape is fixed while the assignment changes from step to step, so a
 captured graph stays valid. The pages give no algorithm, so this module fixes
-one integer-only procedure; the library's planner must produce exactly the
-same tile list (bit-exact), and the attention result does not depend on the
+one integer-only procedure per mode; the library's planner must produce the
+same arrays bit for bit, and the attention result does not depend on the
 choice.
 
-Units. A *q tile* is a run of at most ``qo_tile`` query rows of one request
-(``qo_tile = 1`` for decode: one row per request). Its visible key count is
-``vis = kv_len`` (decode / non-causal) or ``min(kv_len, kv_len - qo_len + i1)``
-(causal, ``i1`` = request-relative end of the tile's rows). Its cost in
-page-units is ``vis_pages = ceil(vis / page_size)``.
+A *unit* is one kv head of one q tile. A q tile is one request in decode, or
+up to ``qo_tile`` query rows of one request in append; its visible key count
+is ``vis = kv_len`` (decode, non-causal) or ``min(kv_len, kv_len - qo_len +
+i1)`` (causal; ``i1`` = request-relative end of its rows), and its cost in
+pages is ``ceil(vis / page_size)``. Units are ordered (q tile, kv head).
 
-Procedure:
+Decode — balanced contiguous split over ``S = num_cu * tiles_per_cu``
+worker waves:
 
-1. ``units = num_kv_heads * sum(vis_pages)`` over all q tiles.
-2. ``target = num_cu * tiles_per_cu``;
+1. Lay the units' pages end to end (``W`` pages in total); worker w owns
+   pages ``[floor(w W / S), floor((w+1) W / S))``.
+2. Every maximal run of one unit inside one worker's range, cut further into
+   runs of at most ``MAX_PIECE_PAGES`` (128) pages, is a piece (tile)
+   ``[b, kv_head, b, base, key0, key1, slot, C]`` where ``C`` is the unit's
+   piece count; a unit with no pages gets one empty piece in the first worker
+   whose range ends after the unit's offset (else the last).
+3. Pieces are listed in worker order; ``worker_ptr[w]`` is worker w's first.
+4. Units with ``C > 1`` get ``C`` partial slots (unit order, running count):
+   piece i of the unit writes slot ``base + i``; ``base = slot = -1`` when
+   ``C == 1``. Merge entry per split unit: ``(b, kv_head, base, C)``.
+
+Append — uniform chunks:
+
+1. ``target = num_cu * tiles_per_cu``; ``units = num_kv_heads * sum(cost)``;
    ``P = max(min_chunk_pages, ceil(units / target))`` pages per chunk.
-3. Each q tile is split into ``C = max(1, ceil(vis_pages / P))`` chunks;
-   chunk c covers keys ``[c*P*ps, min((c+1)*P*ps, vis))``.
-4. Q tiles are visited in order (request, tile). A tile with ``C > 1`` gets
-   ``C * rows`` partial slots starting at the running count ``base``; the
-   state of row r for chunk c goes to slot ``base + (r - q_begin)*C + c``,
-   and every such row gets a merge entry ``(r, base + (r - q_begin)*C, C)``.
-5. Tiles are emitted in order (request, q tile, chunk, kv head) as
-   ``[b, kv_head, q_begin, q_end, tok_begin, tok_end, slot0, C]`` with
-   ``slot0 = base + c`` (or -1 when ``C == 1``), then stably sorted by
-   descending cost ``(tok_end - tok_begin) * (q_end - q_begin)`` so that
-   in-order dispatch starts the longest tiles first.
-6. More tiles, slots or merge entries than the capacities is an error.
+2. Each q tile splits into ``C = max(1, ceil(cost / P))`` chunks; chunk c
+   covers keys ``[c P ps, min((c+1) P ps, vis))``.
+3. Units with ``C > 1`` get ``C * rows`` slots (unit order, running count
+   ``base``); chunk c of the unit writes row r to slot
+   ``base + c*rows + (r - q0)``. Merge entry per split unit:
+   ``(q0, kv_head, base, C)``.
+4. Tiles ``[b, kv_head, q0, q1, key0, key1, slot0, C]`` with
+   ``slot0 = base + c*rows`` (-1 when ``C == 1``) are emitted in order
+   (request, q tile, kv head, chunk) and stably sorted by descending cost
+   ``(key1 - key0) * (q1 - q0)``, so in-order dispatch starts the longest
+   first.
+
+More tiles, slots or merge entries than the capacities is an error.
 """
 from __future__ import annotations
 
@@ -42,6 +57,7 @@ import numpy as np
 SUPPORTED_HEAD_DIM = (128,)
 SUPPORTED_PAGE_SIZE = (16,)
 SUPPORTED_GROUP = (1, 2, 4, 8)
+MAX_PIECE_PAGES = 128
 
 
 class PlanSpecError(Exception):
@@ -62,14 +78,20 @@ def default_knobs(num_kv_heads: int, max_batch: int, max_qo_tokens: int, is_appe
                   max_merge: int = 0) -> dict:
     """Fill zero knobs with defaults; capacities are the worst case of the procedure."""
     num_cu = num_cu or 256
-    tiles_per_cu = tiles_per_cu or (2 if is_append else 8)
+    tiles_per_cu = tiles_per_cu or (2 if is_append else 4)
     min_chunk_pages = min_chunk_pages or 1
     qo_tile = (qo_tile or 32) if is_append else 1
     target = num_cu * tiles_per_cu
-    n_qtiles = (max_batch + _cdiv(max_qo_tokens, qo_tile)) if is_append else max_batch
-    max_tiles = max_tiles or (target + num_kv_heads * n_qtiles)
-    max_partials = max_partials or (2 * qo_tile * _cdiv(target, num_kv_heads))
-    max_merge = max_merge or (qo_tile * _cdiv(target, num_kv_heads))
+    if is_append:
+        n_qtiles = max_batch + _cdiv(max_qo_tokens, qo_tile)
+        max_tiles = max_tiles or (target + num_kv_heads * n_qtiles)
+        max_partials = max_partials or (2 * qo_tile * target)
+        max_merge = max_merge or target
+    else:
+        units = max_batch * num_kv_heads
+        max_tiles = max_tiles or (2 * target + units)
+        max_partials = max_partials or (2 * target + units)
+        max_merge = max_merge or units
     return dict(num_cu=num_cu, tiles_per_cu=tiles_per_cu, min_chunk_pages=min_chunk_pages,
                 qo_tile=qo_tile, max_tiles=max_tiles, max_partials=max_partials,
                 max_merge=max_merge)
@@ -110,11 +132,96 @@ def validate(kv_indptr, kv_lens, batch, num_qo_heads, num_kv_heads, head_dim, pa
             raise PlanSpecError("INVALID", "too many query rows for max_qo_tokens")
 
 
+def _decode_plan(kv_lens, batch, Hkv, ps, k):
+    S = k["num_cu"] * k["tiles_per_cu"]
+    units = [(b, h, int(kv_lens[b])) for b in range(batch) for h in range(Hkv)]
+    cost = [_cdiv(L, ps) for (_, _, L) in units]
+    W = sum(cost)
+    pieces = []                          # (worker, unit, page0, page1)
+    w, E, O = 0, W // S, 0
+    for u, c in enumerate(cost):
+        if c == 0:
+            while E <= O and w < S - 1:
+                w += 1
+                E = (w + 1) * W // S
+            pieces.append((w, u, 0, 0))
+            continue
+        pos = O
+        while pos < O + c:
+            while E <= pos:
+                w += 1
+                E = (w + 1) * W // S
+            end = min(E, O + c)
+            q = pos
+            while q < end:
+                e2 = min(end, q + MAX_PIECE_PAGES)
+                pieces.append((w, u, q - O, e2 - O))
+                q = e2
+            pos = end
+        O += c
+    npieces = [0] * len(units)
+    for (_, u, _, _) in pieces:
+        npieces[u] += 1
+    base, slots, merge = [-1] * len(units), 0, []
+    for u, n in enumerate(npieces):
+        if n > 1:
+            base[u] = slots
+            slots += n
+            merge.append((units[u][0], units[u][1], base[u], n))
+    seen = [0] * len(units)
+    tiles = []
+    for (w, u, p0, p1) in pieces:
+        b, h, L = units[u]
+        C = npieces[u]
+        slot = base[u] + seen[u] if C > 1 else -1
+        seen[u] += 1
+        tiles.append((b, h, b, base[u], p0 * ps, min(p1 * ps, L), slot, C))
+    wptr = [0] * (S + 1)
+    for (w, _, _, _) in pieces:
+        wptr[w + 1] += 1
+    for i in range(S):
+        wptr[i + 1] += wptr[i]
+    return tiles, merge, slots, wptr, _cdiv(W, S)
+
+
+def _append_plan(kv_lens, batch, Hkv, ps, qo_indptr, causal, k):
+    qtiles = []                         # (b, q0, q1, vis)
+    for b in range(batch):
+        L = int(kv_lens[b])
+        r0, r1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        ql = r1 - r0
+        for t0 in range(0, ql, k["qo_tile"]):
+            t1 = min(ql, t0 + k["qo_tile"])
+            vis = min(L, L - ql + t1) if causal else L
+            qtiles.append((b, r0 + t0, r0 + t1, vis))
+    units = Hkv * sum(_cdiv(v, ps) for (_, _, _, v) in qtiles)
+    target = k["num_cu"] * k["tiles_per_cu"]
+    P = max(k["min_chunk_pages"], _cdiv(units, target))
+    tiles, merge, slots = [], [], 0
+    for (b, q0, q1, vis) in qtiles:
+        C = max(1, _cdiv(_cdiv(vis, ps), P))
+        rows = q1 - q0
+        for h in range(Hkv):
+            base = -1
+            if C > 1:
+                base = slots
+                slots += C * rows
+                merge.append((q0, h, base, C))
+            for c in range(C):
+                t0 = c * P * ps
+                t1 = min((c + 1) * P * ps, vis)
+                tiles.append((b, h, q0, q1, t0, t1, base + c * rows if C > 1 else -1, C))
+    order = sorted(range(len(tiles)),
+                   key=lambda i: -((tiles[i][5] - tiles[i][4]) * (tiles[i][3] - tiles[i][2])))
+    return [tiles[i] for i in order], merge, slots, None, P
+
+
 def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
               num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
               max_batch: int, qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
               max_qo_tokens: int = 0, **knobs) -> dict:
-    """Reference plan. Returns tiles ``int32 [n, 8]``, merge ``int32 [m, 4]`` and scalars."""
+    """Reference plan: tiles ``int32 [n, 8]``, merge ``int32 [m, 4]``, worker_ptr
+    ``int32 [S+1]`` (decode) and scalars."""
     kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     is_append = qo_indptr is not None
@@ -122,48 +229,20 @@ def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
              max_batch, None if qo_indptr is None else np.asarray(qo_indptr, np.int64), causal,
              max_qo_tokens)
     k = default_knobs(num_kv_heads, max_batch, max_qo_tokens, is_append, **knobs)
-    ps = page_size
-    qtiles = []                     # (b, q_begin, q_end, vis)
-    for b in range(batch):
-        L = int(kv_lens[b])
-        if not is_append:
-            qtiles.append((b, b, b + 1, L))
-            continue
-        r0, r1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
-        ql = r1 - r0
-        for t0 in range(0, ql, k["qo_tile"]):
-            t1 = min(ql, t0 + k["qo_tile"])
-            vis = min(L, L - ql + t1) if causal else L
-            qtiles.append((b, r0 + t0, r0 + t1, vis))
-    units = num_kv_heads * sum(_cdiv(v, ps) for (_, _, _, v) in qtiles)
-    target = k["num_cu"] * k["tiles_per_cu"]
-    P = max(k["min_chunk_pages"], _cdiv(units, target))
-    tiles, merge = [], []
-    slots = 0
-    for (b, q0, q1, vis) in qtiles:
-        C = max(1, _cdiv(_cdiv(vis, ps), P))
-        base = -1
-        if C > 1:
-            base = slots
-            slots += C * (q1 - q0)
-            for r in range(q0, q1):
-                merge.append((r, base + (r - q0) * C, C, 0))
-        for c in range(C):
-            t0 = c * P * ps
-            t1 = min((c + 1) * P * ps, vis)
-            for h in range(num_kv_heads):
-                tiles.append((b, h, q0, q1, t0, t1, base + c if C > 1 else -1, C))
-    order = sorted(range(len(tiles)),
-                   key=lambda i: -((tiles[i][5] - tiles[i][4]) * (tiles[i][3] - tiles[i][2])))
-    tiles = [tiles[i] for i in order]
+    if is_append:
+        tiles, merge, slots, wptr, P = _append_plan(kv_lens, batch, num_kv_heads, page_size,
+                                                    np.asarray(qo_indptr, np.int64), causal, k)
+    else:
+        tiles, merge, slots, wptr, P = _decode_plan(kv_lens, batch, num_kv_heads, page_size, k)
     if len(tiles) > k["max_tiles"]:
         raise PlanSpecError("CAPACITY", "too many tiles")
     if slots > k["max_partials"]:
         raise PlanSpecError("CAPACITY", "too many partial slots")
     if len(merge) > k["max_merge"]:
-        raise PlanSpecError("CAPACITY", "too many merge rows")
+        raise PlanSpecError("CAPACITY", "too many merge entries")
     return dict(
         tiles=np.asarray(tiles, dtype=np.int32).reshape(-1, 8),
         merge=np.asarray(merge, dtype=np.int32).reshape(-1, 4),
-        chunk_pages=P, target=target, num_slots=slots, knobs=k,
+        worker_ptr=None if wptr is None else np.asarray(wptr, dtype=np.int32),
+        chunk_pages=P, target=k["num_cu"] * k["tiles_per_cu"], num_slots=slots, knobs=k,
     )

@@ -130,17 +130,26 @@ class Plan:
         check(self._lib.fa_plan_info(ctypes.byref(self._plan), ctypes.byref(st)))
         return st
 
-    def tiles(self):
-        """(tiles int32 [n, 8], merge int32 [m, 4]) host copies of the current plan."""
-        tp, mp = ctypes.c_void_p(), ctypes.c_void_p()
-        nt, nm = ctypes.c_int32(), ctypes.c_int32()
+    def tiles(self, with_workers: bool = False):
+        """Host copies of the current plan: (tiles int32 [n, 8], merge int32 [m, 4])
+        and, with ``with_workers``, worker_ptr int32 [workers+1] (None for append)."""
+        tp, mp, wp = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        nt, nm, nw = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         check(self._lib.fa_plan_tiles(ctypes.byref(self._plan), ctypes.byref(tp),
-                                      ctypes.byref(nt), ctypes.byref(mp), ctypes.byref(nm)))
-        t = np.ctypeslib.as_array(ctypes.cast(tp, ctypes.POINTER(ctypes.c_int32)),
-                                  shape=(max(nt.value, 1) * 8,))[: nt.value * 8]
-        m = np.ctypeslib.as_array(ctypes.cast(mp, ctypes.POINTER(ctypes.c_int32)),
-                                  shape=(max(nm.value, 1) * 4,))[: nm.value * 4]
-        return t.reshape(-1, 8).copy(), m.reshape(-1, 4).copy()
+                                      ctypes.byref(nt), ctypes.byref(mp), ctypes.byref(nm),
+                                      ctypes.byref(wp), ctypes.byref(nw)))
+
+        def arr(ptr, n):
+            if n == 0:
+                return np.zeros(0, np.int32)
+            return np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctypes.c_int32)),
+                                         shape=(n,)).copy()
+        t = arr(tp, nt.value * 8).reshape(-1, 8)
+        m = arr(mp, nm.value * 4).reshape(-1, 4)
+        if not with_workers:
+            return t, m
+        w = arr(wp, nw.value + 1) if nw.value else None
+        return t, m, w
 
     def __del__(self):
         try:

@@ -46,7 +46,7 @@ class PlanT(ctypes.Structure):
 class PlanStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tiles", "num_merge", "num_slots", "chunk_pages", "batch", "num_rows", "causal",
-        "uploaded")] + [("resolved", Geometry)]
+        "uploaded", "num_workers")] + [("resolved", Geometry)]
 
 
 _lib = None
@@ -77,7 +77,7 @@ def load(path: str = LIB_PATH):
         "fa_plan": [PP, GP, P, P, I32, P, I32, P, SZ, P, SZ, P],
         "fa_plan_info": [PP, ctypes.POINTER(PlanStats)],
         "fa_plan_tiles": [PP, ctypes.POINTER(P), ctypes.POINTER(I32), ctypes.POINTER(P),
-                          ctypes.POINTER(I32)],
+                          ctypes.POINTER(I32), ctypes.POINTER(P), ctypes.POINTER(I32)],
         "fa_plan_destroy": [PP],
         "fa_decode": [PP, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
         "fa_append": [PP, P, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],

@@ -75,6 +75,7 @@ AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const v
   AttnParams p;
   p.header = reinterpret_cast<const int32_t*>(ws + pl->lay.header);
   p.tiles = reinterpret_cast<const int32_t*>(ws + pl->lay.tiles);
+  p.worker_ptr = reinterpret_cast<const int32_t*>(ws + pl->lay.worker_ptr);
   p.merge = reinterpret_cast<const int32_t*>(ws + pl->lay.merge);
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -90,9 +91,11 @@ AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const v
   p.lse = lse;
   p.part_o = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl->lay.dev_part_o);
   p.part_lse = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl->lay.dev_part_lse);
+  p.counters = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + pl->lay.dev_counters);
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)pl->geom.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.num_qo_heads = pl->geom.num_qo_heads;
+  p.num_kv_heads = pl->geom.num_kv_heads;
   p.causal = pl->causal;
   return p;
 }
@@ -171,8 +174,21 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
     set_error("device workspace needs %zu bytes, 256-byte aligned", pl->lay.dev_bytes);
     return FA_ERR_WORKSPACE;
   }
+  // Arrival counters return to zero at the end of every run call; clear them
+  // once per device workspace (fresh memory holds garbage).
+  const size_t cbytes = pl->lay.dev_part_lse - pl->lay.dev_counters;
+  hipError_t e = hipSuccess;
+  if (pl->zeroed_ws != dev_ws || pl->zeroed_bytes < cbytes) {
+    e = hipMemsetAsync(static_cast<uint8_t*>(dev_ws) + pl->lay.dev_counters, 0, cbytes, s);
+    if (e != hipSuccess) {
+      pl->planned = 0;
+      return hip_fail(e, "hipMemsetAsync (arrival counters)");
+    }
+    pl->zeroed_ws = dev_ws;
+    pl->zeroed_bytes = cbytes;
+  }
   const size_t bytes = pl->lay.tiles + (size_t)pl->num_tiles * kTileInts * 4;
-  hipError_t e = hipMemcpyAsync(dev_ws, host_ws, bytes, hipMemcpyHostToDevice, s);
+  e = hipMemcpyAsync(dev_ws, host_ws, bytes, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) {
     pl->planned = 0;
     return hip_fail(e, "hipMemcpyAsync (plan upload)");
@@ -210,12 +226,14 @@ fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats) {
   stats->num_rows = pl->num_rows;
   stats->causal = pl->causal;
   stats->uploaded = pl->uploaded;
+  stats->num_workers = pl->num_workers;
   stats->resolved = pl->geom;
   return FA_OK;
 }
 
 fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t* num_tiles,
-                        const int32_t** merge_h, int32_t* num_merge) {
+                        const int32_t** merge_h, int32_t* num_merge,
+                        const int32_t** worker_ptr_h, int32_t* num_workers) {
   const PlanImpl* pl = plan ? impl(plan) : nullptr;
   if (!pl || pl->magic != kPlanMagic || !pl->planned) {
     set_error("plan object was not filled by fa_plan");
@@ -226,6 +244,10 @@ fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t*
   if (num_tiles) *num_tiles = pl->num_tiles;
   if (merge_h) *merge_h = reinterpret_cast<const int32_t*>(ws + pl->lay.merge);
   if (num_merge) *num_merge = pl->num_merge;
+  if (worker_ptr_h)
+    *worker_ptr_h = pl->num_workers ? reinterpret_cast<const int32_t*>(ws + pl->lay.worker_ptr)
+                                    : nullptr;
+  if (num_workers) *num_workers = pl->num_workers;
   return FA_OK;
 }
 
@@ -254,11 +276,8 @@ fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
                                    nullptr, sm_scale, out, lse);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
-  hipError_t e = launch_decode(p, pl->geom.dtype, G, pl->geom.max_tiles, s);
-  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-  e = launch_merge_partials(p, pl->geom.dtype, pl->geom.max_merge, s);
-  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  return FA_OK;
+  const hipError_t e = launch_decode(p, pl->geom.dtype, G, pl->num_workers, s);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "decode kernel launch");
 }
 
 fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indptr_d,

@@ -6,13 +6,14 @@
 // Bottleneck ...", section "Snippet One: Paged KV-Cache Attention and MLA":
 // page pool, CSR page list, last_page_len), split into key chunks by the
 // planner ([Guide] "FlashInfer: GPU Kernels for LLM Inference (2026 Guide)",
-// section "What FlashInfer is", idea 3). A chunk's state (out, lse) is either
-// final or an fp32 partial merged later by log-sum-exp ([Guide] section
-// "Cascade attention for shared prefixes").
+// section "What FlashInfer is", idea 3). Chunks of one request are combined by
+// the log-sum-exp merge ([Guide] section "Cascade attention for shared
+// prefixes").
 //
 // MI355X design (decode is HBM-bound, so no MFMA):
-//  * one wave64 per tile {request, kv head, key chunk}; 4 independent waves
-//    per 256-thread workgroup, no barriers;
+//  * one wave64 per worker; the planner gives every worker a contiguous,
+//    equal share of all (request, kv head) pages, as pieces {request, kv head,
+//    key range}; 4 independent waves per 256-thread workgroup, no barriers;
 //  * all G = Hq/Hkv query heads of the kv head are packed in the wave (GQA),
 //    so each K/V byte is read from HBM once for all of them;
 //  * lane = 8 x row-group + segment: row group r (0..7) owns tokens r and r+8
@@ -22,12 +23,21 @@
 //  * loads go through a per-page buffer resource whose size stops at the
 //    last valid token, so slots past last_page_len read as zero without any
 //    memory access and without branches;
+//  * a ring of NBUF pages in registers: page j+NBUF-1 is requested while page
+//    j is consumed;
 //  * scores: packed 2-element dot products (v_dot2_f32_bf16 / _f16) and an
-//    8-lane DPP sum; every row group keeps its own online-softmax state
-//    (running max in log2 units, sum, 16 fp32 accumulators per head), merged
-//    across the 8 row groups once at the end;
-//  * the next page is loaded while the current one is consumed, and page ids
-//    are fetched 64 at a time one batch ahead.
+//    8-lane DPP sum; P*V: the two tokens a lane holds are paired per element
+//    (v_perm) and multiplied with the packed probabilities by the same dot2,
+//    accumulating in fp32;
+//  * each row group keeps its own online-softmax state (reference max in log2
+//    units, sum, 16 fp32 accumulators per head); the reference is only moved
+//    (and the accumulators rescaled) when a wave-wide vote finds a score more
+//    than 2^8 above it, so most pages skip the rescale;
+//  * a (request, kv head) cut into several pieces: each piece writes an fp32
+//    partial state, then the last wave to arrive (an agent-scope counter per
+//    split unit) merges all pieces and writes the final output, so one launch
+//    does the whole decode. The counter is reset by that wave, so the kernel
+//    can be replayed from a graph.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,6 +46,9 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
+constexpr int kCoherent = 16;          // cache policy sc1: device-coherent access
+
 struct PageRegs {
   u32x4 k[4];  // token r lo/hi, token r+8 lo/hi
   u32x4 v[4];
@@ -43,6 +56,12 @@ struct PageRegs {
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+
+// The fp32 partial outputs [slots][G][128] as one buffer (byte offsets < 2^31:
+// the planner's capacities keep slots * G * 512 below that).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p.part_o, 0, 0x7fffffff, 0x00020000);
 }
 
 __device__ __forceinline__ void load_page(PageRegs& pr, const AttnParams& p, int pid, int hk,
@@ -75,53 +94,201 @@ __device__ __forceinline__ void consume_page(const PageRegs& pr, const u32x4 (&q
       x = E::dot2(qhi[g][i], pr.k[1][i], x);
       y = E::dot2(qhi[g][i], pr.k[3][i], y);
     }
-    sa[g] = va ? octet_sum(x) * scale : kNegInf;
-    sb[g] = vb ? octet_sum(y) * scale : kNegInf;
+    const float xs = octet_sum(x) * scale;
+    const float ys = octet_sum(y) * scale;
+    sa[g] = va ? xs : kNegInf;
+    sb[g] = vb ? ys : kNegInf;
   }
-  float va_f[16], vb_f[16];
+  bool need = false;
+#pragma unroll
+  for (int g = 0; g < G; ++g) need |= fmaxf(sa[g], sb[g]) > m[g] + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(m[g], fmaxf(sa[g], sb[g]));
+      const float alpha = fast_exp2(m[g] - (mn == kNegInf ? 0.f : mn));
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[g][e] *= alpha;
+      m[g] = mn;
+    }
+  }
+  // element e of tokens r and r+8 side by side: (A_e, B_e)
+  uint32_t pv[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    va_f[2 * i] = E::lo(pr.v[0][i]);
-    va_f[2 * i + 1] = E::hi(pr.v[0][i]);
-    va_f[8 + 2 * i] = E::lo(pr.v[1][i]);
-    va_f[8 + 2 * i + 1] = E::hi(pr.v[1][i]);
-    vb_f[2 * i] = E::lo(pr.v[2][i]);
-    vb_f[2 * i + 1] = E::hi(pr.v[2][i]);
-    vb_f[8 + 2 * i] = E::lo(pr.v[3][i]);
-    vb_f[8 + 2 * i + 1] = E::hi(pr.v[3][i]);
+    pv[2 * i] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x05040100u);
+    pv[2 * i + 1] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x07060302u);
+    pv[8 + 2 * i] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x05040100u);
+    pv[8 + 2 * i + 1] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x07060302u);
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float mn = fmaxf(m[g], fmaxf(sa[g], sb[g]));
-    const float ms = mn == kNegInf ? 0.f : mn;
-    const float alpha = fast_exp2(m[g] - ms);
+    const float ms = m[g] == kNegInf ? 0.f : m[g];
     const float pa = fast_exp2(sa[g] - ms);
     const float pb = fast_exp2(sb[g] - ms);
-    l[g] = l[g] * alpha + pa + pb;
+    l[g] += pa + pb;
+    const uint32_t pp = E::pack(pa, pb);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[g][e] = acc[g][e] * alpha + pa * va_f[e] + pb * vb_f[e];
+    for (int e = 0; e < 16; ++e) acc[g][e] = E::dot2(pp, pv[e], acc[g][e]);
+  }
+}
+
+// Merge the 8 row-group states of the wave (lanes that differ in bits 3..5).
+template <int G>
+__device__ __forceinline__ void merge_row_groups(float (&m)[G], float (&l)[G],
+                                                 float (&acc)[G][16]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = m[g];
+    M = fmaxf(M, xor_shfl(M, 8));
+    M = fmaxf(M, xor_shfl(M, 16));
+    M = fmaxf(M, xor_shfl(M, 32));
+    const float f = fast_exp2(m[g] - (M == kNegInf ? 0.f : M));
+    float L = l[g] * f;
+    L += xor_shfl(L, 8);
+    L += xor_shfl(L, 16);
+    L += xor_shfl(L, 32);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float a = acc[g][e] * f;
+      a += xor_shfl(a, 8);
+      a += xor_shfl(a, 16);
+      a += xor_shfl(a, 32);
+      acc[g][e] = a;
+    }
+    m[g] = M;
+    l[g] = L;
+  }
+}
+
+// Online merge of the fp32 partial states in slots base .. base+C-1 (slot
+// layout [slot][G][128], piece c taken by row group c % 8). The partials were
+// published by other waves with device-coherent stores; they are read back
+// with device-coherent loads (sc1).
+template <int G>
+__device__ __forceinline__ void gather_partials(const AttnParams& p, int64_t base, int C, int r,
+                                                int s, float (&m)[G], float (&l)[G],
+                                                float (&acc)[G][16]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
+  }
+  // one resource over the whole partial array: row groups read different slots
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
+  auto load_state = [&](int c, int g, float& s2, float (&v)[16]) {
+    const int64_t sh = (base + c) * G + g;
+    s2 = __hip_atomic_load(p.part_lse + sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t o = (uint32_t)sh * 512u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, o + (i < 2 ? 32 * s : 256 + 32 * s) + 16 * (i & 1), 0, kCoherent);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[4 * i + k] = __uint_as_float(raw[k]);
+    }
+  };
+  auto add_state = [&](int g, float s2, const float (&v)[16]) {
+    const float mn = fmaxf(m[g], s2);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float f = fast_exp2(m[g] - ms);
+    const float w = fast_exp2(s2 - ms);
+    l[g] = l[g] * f + w;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = acc[g][e] * f + w * v[e];
     m[g] = mn;
+  };
+  // two chunks per row group per round, both requested before either is used
+  for (int c = r; c < C; c += 16) {
+    const bool two = c + 8 < C;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float sa2, sb2 = kNegInf, va[16], vb[16];
+      load_state(c, g, sa2, va);
+      if (two) load_state(c + 8, g, sb2, vb);
+      add_state(g, sa2, va);
+      if (two) add_state(g, sb2, vb);
+    }
   }
 }
 
 template <int DT, int G>
-__global__ __launch_bounds__(256) void decode_kernel(AttnParams p) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int tile_id = blockIdx.x * 4 + wave;
-  if (tile_id >= p.header[0]) return;
-  const int32_t* t = p.tiles + tile_id * 8;
-  const int b = t[0], hk = t[1], row = t[2], slot0 = t[6];
-  const int key0 = t[4];
-  const int pbeg = p.kv_indptr[b];
-  const int npages_req = p.kv_indptr[b + 1] - pbeg;
-  const int kv_len = npages_req > 0 ? (npages_req - 1) * 16 + p.last_page_len[b] : 0;
-  const int key1 = min(t[5], kv_len);
+__device__ __forceinline__ void write_final(const AttnParams& p, int row, int hk, int r, int s,
+                                            const float (&m)[G], const float (&l)[G],
+                                            const float (&acc)[G][16]) {
+  const int Hq = p.num_qo_heads;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (r != g) continue;  // row group g writes head g of the group
+    const int h = hk * G + g;
+    const bool live = l[g] > 0.f;
+    const float inv = live ? 1.f / l[g] : 0.f;
+    uint16_t* op = p.out + ((int64_t)row * Hq + h) * 128;
+    u32x4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = Elt<DT>::pack(acc[g][2 * i] * inv, acc[g][2 * i + 1] * inv);
+      hi[i] = Elt<DT>::pack(acc[g][8 + 2 * i] * inv, acc[g][8 + 2 * i + 1] * inv);
+    }
+    *reinterpret_cast<u32x4*>(op + s * 8) = lo;
+    *reinterpret_cast<u32x4*>(op + 64 + s * 8) = hi;
+    if (s == 0 && p.lse)
+      p.lse[(int64_t)row * Hq + h] = live ? (m[g] + fast_log2(l[g])) * kLn2 : kNegInf;
+  }
+}
+
+// Publish a chunk's normalised state with device-coherent stores (sc1), so a
+// wave on any XCD can read it after the arrival counter says it is complete.
+template <int G>
+__device__ __forceinline__ void write_partial(const AttnParams& p, int64_t slot, int r, int s,
+                                              const float (&m)[G], const float (&l)[G],
+                                              const float (&acc)[G][16]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (r != g) continue;
+    const int64_t sh = slot * G + g;
+    const bool live = l[g] > 0.f;
+    const float inv = live ? 1.f / l[g] : 0.f;
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
+    const uint32_t o = (uint32_t)sh * 512u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[k] = __float_as_uint(acc[g][4 * i + k] * inv);
+      __builtin_amdgcn_raw_buffer_store_b128(u, rs, o + (i < 2 ? 32 * s : 256 + 32 * s) + 16 * (i & 1),
+                                             0, kCoherent);
+    }
+    if (s == 0)
+      __hip_atomic_store(p.part_lse + sh, live ? m[g] + fast_log2(l[g]) : kNegInf, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// One piece: keys [key0, key1) of kv head hk of request b, for its G q heads.
+template <int DT, int G, int NBUF>
+__device__ __forceinline__ void decode_piece(const AttnParams& p, const int32_t* t, int lane) {
+  // Everything that addresses memory is made wave-uniform explicitly (loaded
+  // once per piece by a few lanes, then v_readlane into scalar registers):
+  // the compiler cannot prove these loads uniform across the pieces' stores,
+  // and a per-lane buffer resource would turn every page load into a loop.
+  const int tv = t[lane & 7];
+  const int b = __builtin_amdgcn_readlane(tv, 0), hk = __builtin_amdgcn_readlane(tv, 1);
+  const int row = __builtin_amdgcn_readlane(tv, 2), base = __builtin_amdgcn_readlane(tv, 3);
+  const int key0 = __builtin_amdgcn_readlane(tv, 4);
+  const int slot = __builtin_amdgcn_readlane(tv, 6), npieces = __builtin_amdgcn_readlane(tv, 7);
+  const int pv3 = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
+  const int pbeg = __builtin_amdgcn_readlane(pv3, 0);
+  const int npages_req = __builtin_amdgcn_readlane(pv3, 1) - pbeg;
+  const int kv_len = npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(pv3, 2) : 0;
+  const int key1 = min(__builtin_amdgcn_readlane(tv, 5), kv_len);
   const int Hq = p.num_qo_heads;
 
   const int r = lane >> 3;
   const int s = lane & 7;
-  // byte offsets inside a page (relative to the kv head's row of slot 0)
   const uint32_t ts2 = (uint32_t)p.token_stride * 2u;
   const uint32_t off[4] = {r * ts2 + s * 16u, r * ts2 + 128u + s * 16u, (r + 8) * ts2 + s * 16u,
                            (r + 8) * ts2 + 128u + s * 16u};
@@ -144,103 +311,108 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnParams p) {
 
   const int first_page = key0 >> 4;
   const int npg = key1 > key0 ? ((key1 + 15) >> 4) - first_page : 0;
+  // Page ids of the piece (at most 128 pages, a planner guarantee) are fetched
+  // once, before any K/V load is in flight (lane i holds pages i and i+64),
+  // and handed to the scalar unit with v_readlane: waiting on a load later
+  // would drain the in-order load counter.
   const int32_t* ids_base = p.kv_indices + pbeg + first_page;
-  int ids = lane < npg ? ids_base[lane] : 0;
-  int ids_next = lane + 64 < npg ? ids_base[64 + lane] : 0;
+  const int ids0 = lane < npg ? ids_base[lane] : 0;
+  const int ids1 = lane + 64 < npg ? ids_base[lane + 64] : 0;
+  asm volatile("" ::"v"(ids0), "v"(ids1));  // both arrive before the page loop starts
   auto page_id = [&](int j) -> int {
-    if (j > 0 && (j & 63) == 0) {
-      ids = ids_next;
-      ids_next = j + 64 + lane < npg ? ids_base[j + 64 + lane] : 0;
-    }
-    return __builtin_amdgcn_readlane(ids, j & 63);
+    return j < 64 ? __builtin_amdgcn_readlane(ids0, j & 63)
+                  : __builtin_amdgcn_readlane(ids1, j & 63);
   };
   // bytes of the page that hold valid tokens (a buffer load past them returns 0)
   auto page_bytes = [&](int j) -> uint32_t {
-    const int valid = min(16, key1 - (first_page + j) * 16);
-    return (uint32_t)valid * ts2;
+    return (uint32_t)min(16, key1 - (first_page + j) * 16) * ts2;
   };
   const float scale = p.scale_log2;
 
-  PageRegs A, B;
-  if (npg > 0) load_page(A, p, page_id(0), hk, page_bytes(0), off);
-  for (int j = 0; j < npg; j += 2) {
-    if (j + 1 < npg) load_page(B, p, page_id(j + 1), hk, page_bytes(j + 1), off);
-    {
-      const int tb = (first_page + j) * 16;
-      consume_page<DT, G>(A, qlo, qhi, m, l, acc, scale, tb + r < key1, tb + r + 8 < key1);
-    }
-    if (j + 1 >= npg) break;
-    if (j + 2 < npg) load_page(A, p, page_id(j + 2), hk, page_bytes(j + 2), off);
-    {
-      const int tb = (first_page + j + 1) * 16;
-      consume_page<DT, G>(B, qlo, qhi, m, l, acc, scale, tb + r < key1, tb + r + 8 < key1);
-    }
-  }
-
-  // merge the 8 row-group states (lanes that differ in bits 3..5)
+  PageRegs buf[NBUF];
+  int j = 0;
+  if (npg >= 2 * NBUF) {
+    // Steady state: every page touched here is full and has a successor, so
+    // all loads (prologue included) are unconditional and the next page id is
+    // fetched one page ahead; the compiler then keeps NBUF-1 pages in flight.
+    const uint32_t full = 16u * ts2;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float M = m[g];
-    M = fmaxf(M, xor_shfl(M, 8));
-    M = fmaxf(M, xor_shfl(M, 16));
-    M = fmaxf(M, xor_shfl(M, 32));
-    const float Ms = M == kNegInf ? 0.f : M;
-    const float f = fast_exp2(m[g] - Ms);
-    float L = l[g] * f;
-    L += xor_shfl(L, 8);
-    L += xor_shfl(L, 16);
-    L += xor_shfl(L, 32);
+    for (int u = 0; u < NBUF - 1; ++u) load_page(buf[u], p, page_id(u), hk, full, off);
+    int nid = page_id(NBUF - 1);
+    auto ring_pass = [&](int j0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float a = acc[g][e] * f;
-      a += xor_shfl(a, 8);
-      a += xor_shfl(a, 16);
-      a += xor_shfl(a, 32);
-      acc[g][e] = a;
-    }
-    m[g] = M;
-    l[g] = L;
-  }
-
-  // row group g writes head g of the group
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (r != g) continue;
-    const int h = hk * G + g;
-    const bool live = l[g] > 0.f;
-    const float inv = live ? 1.f / l[g] : 0.f;
-    const float lse2 = live ? m[g] + fast_log2(l[g]) : kNegInf;  // log2 units
-    if (slot0 < 0) {
-      uint16_t* op = p.out + ((int64_t)row * Hq + h) * 128;
-      u32x4 lo, hi;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = Elt<DT>::pack(acc[g][2 * i] * inv, acc[g][2 * i + 1] * inv);
-        hi[i] = Elt<DT>::pack(acc[g][8 + 2 * i] * inv, acc[g][8 + 2 * i + 1] * inv);
+      for (int u = 0; u < NBUF; ++u) {
+        const int jn = j0 + u + NBUF - 1;
+        const int pid = nid;
+        nid = page_id(jn + 1);
+        load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, off);
+        consume_page<DT, G>(buf[u], qlo, qhi, m, l, acc, scale, true, true);
       }
-      *reinterpret_cast<u32x4*>(op + s * 8) = lo;
-      *reinterpret_cast<u32x4*>(op + 64 + s * 8) = hi;
-      if (s == 0 && p.lse) p.lse[(int64_t)row * Hq + h] = lse2 * kLn2;
-    } else {
-      float* op = p.part_o + ((int64_t)slot0 * Hq + h) * 128;
-      float4* o4 = reinterpret_cast<float4*>(op + s * 8);
-      o4[0] = make_float4(acc[g][0] * inv, acc[g][1] * inv, acc[g][2] * inv, acc[g][3] * inv);
-      o4[1] = make_float4(acc[g][4] * inv, acc[g][5] * inv, acc[g][6] * inv, acc[g][7] * inv);
-      float4* o4h = reinterpret_cast<float4*>(op + 64 + s * 8);
-      o4h[0] = make_float4(acc[g][8] * inv, acc[g][9] * inv, acc[g][10] * inv, acc[g][11] * inv);
-      o4h[1] = make_float4(acc[g][12] * inv, acc[g][13] * inv, acc[g][14] * inv, acc[g][15] * inv);
-      if (s == 0) p.part_lse[(int64_t)slot0 * Hq + h] = lse2;
+    };
+    // The first pass is peeled so that the q loads are waited for there; in
+    // the loop only K/V page loads are then outstanding at the loop header
+    // and the compiler's wait counts keep NBUF-1 pages in flight.
+    ring_pass(0);
+    for (j = NBUF; j + 2 * NBUF - 1 < npg; j += NBUF) ring_pass(j);
+  } else {
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u)
+      if (u < npg) load_page(buf[u], p, page_id(u), hk, page_bytes(u), off);
+  }
+  // Tail: at most 2*NBUF-1 pages, the last one possibly partial.
+  for (; j < npg; j += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int jj = j + u;
+      if (jj >= npg) break;
+      const int jn = jj + NBUF - 1;
+      if (jn < npg) load_page(buf[(u + NBUF - 1) % NBUF], p, page_id(jn), hk, page_bytes(jn), off);
+      const int tb = (first_page + jj) * 16;
+      consume_page<DT, G>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1, tb + r + 8 < key1);
     }
   }
+  merge_row_groups<G>(m, l, acc);
+
+  if (slot < 0) {
+    write_final<DT, G>(p, row, hk, r, s, m, l, acc);
+    return;
+  }
+  // split unit: publish this piece; the last piece to arrive merges them all
+  write_partial<G>(p, slot, r, s, m, l, acc);
+  int32_t* counter = p.counters + base;
+  // the coherent stores above must have completed before the arrival is counted
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, 64);
+  if (prev != npieces - 1) return;
+  if (lane == 0) *counter = 0;
+  gather_partials<G>(p, base, npieces, r, s, m, l, acc);
+  merge_row_groups<G>(m, l, acc);
+  write_final<DT, G>(p, row, hk, r, s, m, l, acc);
+}
+
+// One wave per worker: its pieces are tiles worker_ptr[w] .. worker_ptr[w+1]-1,
+// a contiguous, equal share of all pages (4 independent waves per workgroup).
+template <int DT, int G, int NBUF>
+__global__ __launch_bounds__(256, (G <= 4 ? 2 : 1)) void decode_kernel(AttnParams p) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + wave;
+  if (w >= p.header[6]) return;
+  const int t1 = p.worker_ptr[w + 1];
+  for (int t = p.worker_ptr[w]; t < t1; ++t) decode_piece<DT, G, NBUF>(p, p.tiles + t * 8, lane);
 }
 
 template <int DT>
 hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: hipLaunchKernelGGL((decode_kernel<DT, 1>), dim3(grid), dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<DT, 2>), dim3(grid), dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<DT, 4>), dim3(grid), dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<DT, 8>), dim3(grid), dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<DT, 1, 3>), dim3(grid), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<DT, 2, 3>), dim3(grid), dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<DT, 4, 3>), dim3(grid), dim3(256), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<DT, 8, 2>), dim3(grid), dim3(256), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -248,8 +420,8 @@ hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s) {
-  const int grid = (max_tiles + 3) / 4;
+hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s) {
+  const int grid = (workers + 3) / 4;
   if (grid <= 0) return hipSuccess;
   return dtype == FA_BF16 ? launch_dt<FA_BF16>(p, group, grid, s)
                           : launch_dt<FA_F16>(p, group, grid, s);

@@ -11,6 +11,7 @@ namespace pkfa {
 struct AttnParams {
   const int32_t* header;      // {num_tiles, num_merge, ...}
   const int32_t* tiles;
+  const int32_t* worker_ptr;  // decode: [workers+1] tile ranges per worker wave
   const int32_t* merge;
   const uint16_t* q;          // [rows, Hq, 128]
   const uint16_t* k;          // page pools (16-bit elements)
@@ -22,14 +23,16 @@ struct AttnParams {
   const int32_t* qo_indptr;   // append only
   uint16_t* out;              // [rows, Hq, 128]
   float* lse;                 // [rows, Hq] natural log, may be null
-  float* part_o;              // [slots, Hq, 128] fp32
-  float* part_lse;            // [slots, Hq] log2 units
+  float* part_o;              // [slots, G, 128] fp32 partial outputs (normalised)
+  float* part_lse;            // [slots, G] partial lse in log2 units
+  int32_t* counters;          // [slots] arrivals per split unit, indexed by its first slot
   float scale_log2;           // sm_scale * log2(e)
   int32_t num_qo_heads;
+  int32_t num_kv_heads;
   int32_t causal;
 };
 
-hipError_t launch_decode(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s);
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
 hipError_t launch_merge_partials(const AttnParams& p, int dtype, int max_merge, hipStream_t s);
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,

@@ -3,25 +3,26 @@
 // [Guide] "FlashInfer: GPU Kernels for LLM Inference (2026 Guide)", section
 // "What FlashInfer is" (idea 3: plan the split of uneven requests so the load
 // is even while the launch stays static for graphs) and [DeepDive] "FlashInfer:
-// The Attention Kernel Library That Proves the Bottleneck ...", section "It In
-// Action" step 1 (a per-step plan computes only tile assignments). The pages
-// give no algorithm; this planner fixes one:
+// The Attention Kernel Library That Proves the Bottleneck ...", sections "It In
+// Action" step 1 (a per-step plan computes only tile assignments) and "Why This
+// Design Works" (static launch, dynamic assignment). The pages give no
+// algorithm; this planner fixes one per mode. A *unit* is one kv head of one
+// q tile (a request in decode, up to qo_tile query rows in append).
 //
-//  * a q tile is up to qo_tile query rows of one request (one row in decode);
-//    its visible keys are kv_len, or for causal append the keys seen by its
-//    last row, kv_len - qo_len + row_end;
-//  * with units = num_kv_heads * sum(visible pages) and target = num_cu *
-//    tiles_per_cu tiles, every q tile is cut into chunks of
-//    P = max(min_chunk_pages, ceil(units / target)) pages, so all tiles cost
-//    about the same and there are about `target` of them;
-//  * a q tile cut into C > 1 chunks gets C fp32 partial states per row, merged
-//    afterwards by log-sum-exp; otherwise its tile writes the output directly;
-//  * tiles are ordered by descending cost (rows x keys), stable on
-//    (request, q tile, chunk, kv head), so in-order dispatch starts the
-//    longest tiles first.
+// Decode (HBM-bound, one wave per worker): the units' pages are laid end to
+// end and cut into num_cu * tiles_per_cu equal contiguous shares, one per
+// worker wave, so every wave streams the same number of pages (+-1) in a
+// single round; runs longer than 128 pages are cut further (a wave keeps the
+// ids of one piece in two registers). A unit cut into C > 1 pieces gets C fp32
+// partial states, combined by log-sum-exp by the last piece to finish.
 //
-// The launch shapes depend only on the capacities derived from the geometry,
-// never on the lengths, which is what keeps a captured graph valid across plans.
+// Append (MFMA-bound, one workgroup per tile): every q tile is cut into
+// chunks of P = max(min_chunk_pages, ceil(units / target)) pages, so tiles
+// cost about the same; tiles are ordered by descending cost so in-order
+// dispatch starts the longest first.
+//
+// Launch shapes depend only on capacities derived from the geometry, never on
+// the lengths, which keeps a captured graph valid across plans.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -82,7 +83,7 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
   const bool app = g.mode == FA_MODE_APPEND;
   if (!app) g.max_qo_tokens = 0;
   if (!g.num_cu) g.num_cu = 256;
-  if (!g.tiles_per_cu) g.tiles_per_cu = app ? 2 : 8;
+  if (!g.tiles_per_cu) g.tiles_per_cu = app ? 2 : 4;
   if (!g.min_chunk_pages) g.min_chunk_pages = 1;
   g.qo_tile = app ? (g.qo_tile ? g.qo_tile : 32) : 1;
   if (app && g.qo_tile != 32) {
@@ -90,11 +91,22 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
     return FA_ERR_UNSUPPORTED;
   }
   const int64_t target = (int64_t)g.num_cu * g.tiles_per_cu;
-  const int64_t nqt = app ? (int64_t)g.max_batch + cdiv(g.max_qo_tokens, g.qo_tile)
-                          : (int64_t)g.max_batch;
-  int64_t mt = g.max_tiles ? g.max_tiles : target + (int64_t)g.num_kv_heads * nqt;
-  int64_t mp = g.max_partials ? g.max_partials : 2 * (int64_t)g.qo_tile * cdiv(target, g.num_kv_heads);
-  int64_t mm = g.max_merge ? g.max_merge : (int64_t)g.qo_tile * cdiv(target, g.num_kv_heads);
+  int64_t mt, mp, mm;
+  if (app) {
+    const int64_t nqt = (int64_t)g.max_batch + cdiv(g.max_qo_tokens, g.qo_tile);
+    mt = g.max_tiles ? g.max_tiles : target + (int64_t)g.num_kv_heads * nqt;
+    mp = g.max_partials ? g.max_partials : 2 * (int64_t)g.qo_tile * target;
+    mm = g.max_merge ? g.max_merge : target;
+  } else {
+    const int64_t units = (int64_t)g.max_batch * g.num_kv_heads;
+    mt = g.max_tiles ? g.max_tiles : 2 * target + units;
+    mp = g.max_partials ? g.max_partials : 2 * target + units;
+    mm = g.max_merge ? g.max_merge : units;
+  }
+  if (target > (1 << 22)) {
+    set_error("num_cu * tiles_per_cu too large");
+    return FA_ERR_INVALID;
+  }
   if (mt > (1 << 26) || mp > (1 << 26) || mm > (1 << 26)) {
     set_error("capacities too large");
     return FA_ERR_INVALID;
@@ -108,19 +120,208 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
 
 Layout compute_layout(const fa_geometry& g) {
   Layout L;
+  const int G = g.num_qo_heads / g.num_kv_heads;
+  L.workers = g.mode == FA_MODE_DECODE ? g.num_cu * g.tiles_per_cu : 0;
   L.header = 0;
   L.merge = kHeaderInts * 4;
-  L.tiles = align_up(L.merge + (size_t)g.max_merge * kMergeInts * 4, 64);
+  L.worker_ptr = L.merge + (size_t)g.max_merge * kMergeInts * 4;
+  L.tiles = align_up(L.worker_ptr + (size_t)(L.workers + 1) * 4, 64);
   L.upload_end = L.tiles + (size_t)g.max_tiles * kTileInts * 4;
-  L.dev_part_lse = align_up(L.upload_end, 256);
-  L.dev_part_o = align_up(L.dev_part_lse + (size_t)g.max_partials * g.num_qo_heads * 4, 256);
-  L.dev_bytes = align_up(L.dev_part_o + (size_t)g.max_partials * g.num_qo_heads * g.head_dim * 4, 256);
+  L.dev_counters = align_up(L.upload_end, 256);
+  L.dev_part_lse = align_up(L.dev_counters + (size_t)g.max_partials * 4, 256);
+  L.dev_part_o = align_up(L.dev_part_lse + (size_t)g.max_partials * G * 4, 256);
+  L.dev_bytes = align_up(L.dev_part_o + (size_t)g.max_partials * G * g.head_dim * 4, 256);
   L.host_unsorted = align_up(L.upload_end, 64);
   L.host_order = L.host_unsorted + (size_t)g.max_tiles * kTileInts * 4;
   L.host_cost = align_up(L.host_order + (size_t)g.max_tiles * 4, 8);
-  L.host_bytes = L.host_cost + (size_t)g.max_tiles * 8;
+  L.host_units = L.host_cost + (size_t)g.max_tiles * 8;
+  L.host_bytes = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 2 * 4;
   return L;
 }
+
+namespace {
+
+fa_status capacity_error(const char* what, int64_t n, int32_t cap) {
+  set_error("%lld %s exceed the capacity %d", (long long)n, what, cap);
+  return FA_ERR_CAPACITY;
+}
+
+// Decode: balanced contiguous split of the units' pages over the workers.
+fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, const int32_t* kv_lens,
+                      int32_t batch, int64_t* ntiles_out, int64_t* nmerge_out, int64_t* slots_out,
+                      int64_t* per_worker_out) {
+  const int ps = g.page_size, Hkv = g.num_kv_heads;
+  const int64_t S = lay.workers;
+  const int64_t nunits = (int64_t)batch * Hkv;
+  int32_t* merge = reinterpret_cast<int32_t*>(ws + lay.merge);
+  int32_t* wptr = reinterpret_cast<int32_t*>(ws + lay.worker_ptr);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
+  int32_t* npieces = reinterpret_cast<int32_t*>(ws + lay.host_units);
+  int32_t* base = npieces + (size_t)g.max_batch * Hkv;
+  int64_t W = 0;
+  for (int b = 0; b < batch; ++b) W += cdiv(kv_lens[b], ps) * Hkv;
+
+  // Walk the cut points once; emit(worker, unit, page0, page1) per piece.
+  auto walk = [&](auto&& emit) {
+    int64_t w = 0, E = W / S, O = 0;
+    for (int64_t u = 0; u < nunits; ++u) {
+      const int64_t c = cdiv(kv_lens[u / Hkv], ps);
+      if (c == 0) {
+        while (E <= O && w < S - 1) {
+          ++w;
+          E = (w + 1) * W / S;
+        }
+        emit(w, u, (int64_t)0, (int64_t)0);
+        continue;
+      }
+      for (int64_t pos = O; pos < O + c;) {
+        while (E <= pos) {
+          ++w;
+          E = (w + 1) * W / S;
+        }
+        const int64_t end = std::min(E, O + c);
+        for (int64_t q = pos; q < end; q += kMaxPiecePages)
+          emit(w, u, q - O, std::min(end, q + kMaxPiecePages) - O);
+        pos = end;
+      }
+      O += c;
+    }
+  };
+  int64_t ntiles = 0;
+  for (int64_t u = 0; u < nunits; ++u) npieces[u] = 0;
+  walk([&](int64_t, int64_t u, int64_t, int64_t) {
+    ++npieces[u];
+    ++ntiles;
+  });
+  if (ntiles > g.max_tiles) return capacity_error("tiles", ntiles, g.max_tiles);
+  int64_t slots = 0, nmerge = 0;
+  for (int64_t u = 0; u < nunits; ++u) {
+    base[u] = -1;
+    if (npieces[u] > 1) {
+      base[u] = (int32_t)slots;
+      slots += npieces[u];
+      if (nmerge < g.max_merge) {
+        int32_t* m = merge + nmerge * kMergeInts;
+        m[0] = (int32_t)(u / Hkv);
+        m[1] = (int32_t)(u % Hkv);
+        m[2] = base[u];
+        m[3] = npieces[u];
+      }
+      ++nmerge;
+    }
+  }
+  if (slots > g.max_partials) return capacity_error("partial states", slots, g.max_partials);
+  if (nmerge > g.max_merge) return capacity_error("merge entries", nmerge, g.max_merge);
+  for (int64_t w = 0; w <= S; ++w) wptr[w] = 0;
+  int64_t i = 0;
+  for (int64_t u = 0; u < nunits; ++u) npieces[u] = 0;  // reused: pieces seen so far
+  walk([&](int64_t w, int64_t u, int64_t p0, int64_t p1) {
+    const int b = (int)(u / Hkv);
+    const int64_t L = kv_lens[b];
+    int32_t* t = tiles + i * kTileInts;
+    const bool split = base[u] >= 0;
+    t[0] = b;
+    t[1] = (int32_t)(u % Hkv);
+    t[2] = b;
+    t[3] = base[u];
+    t[4] = (int32_t)(p0 * ps);
+    t[5] = (int32_t)std::min(p1 * ps, L);
+    t[6] = split ? base[u] + npieces[u] : -1;
+    ++npieces[u];
+    ++wptr[w + 1];
+    ++i;
+  });
+  // piece counts are complete now: fill C
+  for (int64_t k = 0; k < ntiles; ++k) {
+    int32_t* t = tiles + k * kTileInts;
+    t[7] = npieces[(int64_t)t[0] * Hkv + t[1]];
+  }
+  for (int64_t w = 0; w < S; ++w) wptr[w + 1] += wptr[w];
+  *ntiles_out = ntiles;
+  *nmerge_out = nmerge;
+  *slots_out = slots;
+  *per_worker_out = S > 0 ? cdiv(W, S) : 0;
+  return FA_OK;
+}
+
+// Append: uniform chunks of P pages, LPT order.
+fa_status plan_append(const fa_geometry& g, const Layout& lay, uint8_t* ws, const int32_t* kv_lens,
+                      int32_t batch, const int32_t* qo_indptr, int32_t causal, int64_t* ntiles_out,
+                      int64_t* nmerge_out, int64_t* slots_out, int64_t* P_out) {
+  const int ps = g.page_size, Hkv = g.num_kv_heads, qt = g.qo_tile;
+  int32_t* merge = reinterpret_cast<int32_t*>(ws + lay.merge);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
+  int32_t* unsorted = reinterpret_cast<int32_t*>(ws + lay.host_unsorted);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + lay.host_order);
+  int64_t* cost = reinterpret_cast<int64_t*>(ws + lay.host_cost);
+  // Visit q tiles in (request, tile) order; fn(b, row0, row1, visible_keys).
+  auto for_each_qtile = [&](auto&& fn) {
+    for (int b = 0; b < batch; ++b) {
+      const int64_t L = kv_lens[b];
+      const int64_t r0 = qo_indptr[b], r1 = qo_indptr[b + 1], ql = r1 - r0;
+      for (int64_t t0 = 0; t0 < ql; t0 += qt) {
+        const int64_t t1 = std::min(ql, t0 + qt);
+        const int64_t vis = causal ? std::min(L, L - ql + t1) : L;
+        fn(b, r0 + t0, r0 + t1, vis);
+      }
+    }
+  };
+  int64_t units = 0;
+  for_each_qtile([&](int, int64_t, int64_t, int64_t vis) { units += cdiv(vis, ps); });
+  units *= Hkv;
+  const int64_t target = (int64_t)g.num_cu * g.tiles_per_cu;
+  const int64_t P = std::max<int64_t>(g.min_chunk_pages, cdiv(units, target));
+  int64_t ntiles = 0, nmerge = 0, slots = 0;
+  for_each_qtile([&](int b, int64_t q0, int64_t q1, int64_t vis) {
+    const int64_t C = std::max<int64_t>(1, cdiv(cdiv(vis, ps), P));
+    const int64_t rows = q1 - q0;
+    for (int h = 0; h < Hkv; ++h) {
+      int64_t base = -1;
+      if (C > 1) {
+        base = slots;
+        slots += C * rows;
+        if (nmerge < g.max_merge) {
+          int32_t* m = merge + nmerge * kMergeInts;
+          m[0] = (int32_t)q0;
+          m[1] = h;
+          m[2] = (int32_t)base;
+          m[3] = (int32_t)C;
+        }
+        ++nmerge;
+      }
+      for (int64_t c = 0; c < C; ++c) {
+        if (ntiles < g.max_tiles) {
+          const int64_t k0 = c * P * ps, k1 = std::min((c + 1) * P * ps, vis);
+          int32_t* t = unsorted + ntiles * kTileInts;
+          t[0] = b;
+          t[1] = h;
+          t[2] = (int32_t)q0;
+          t[3] = (int32_t)q1;
+          t[4] = (int32_t)k0;
+          t[5] = (int32_t)k1;
+          t[6] = C > 1 ? (int32_t)(base + c * rows) : -1;
+          t[7] = (int32_t)C;
+          cost[ntiles] = (k1 - k0) * rows;
+        }
+        ++ntiles;
+      }
+    }
+  });
+  if (ntiles > g.max_tiles) return capacity_error("tiles", ntiles, g.max_tiles);
+  if (slots > g.max_partials) return capacity_error("partial states", slots, g.max_partials);
+  if (nmerge > g.max_merge) return capacity_error("merge entries", nmerge, g.max_merge);
+  for (int64_t i = 0; i < ntiles; ++i) order[i] = (int32_t)i;
+  std::stable_sort(order, order + ntiles, [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+  for (int64_t i = 0; i < ntiles; ++i)
+    memcpy(tiles + i * kTileInts, unsorted + (int64_t)order[i] * kTileInts, kTileInts * 4);
+  *ntiles_out = ntiles;
+  *nmerge_out = nmerge;
+  *slots_out = slots;
+  *P_out = P;
+  return FA_OK;
+}
+
+}  // namespace
 
 fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr,
                      const int32_t* kv_lens, int32_t batch, const int32_t* qo_indptr,
@@ -184,94 +385,11 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
   }
   uint8_t* ws = static_cast<uint8_t*>(host_ws);
   int32_t* header = reinterpret_cast<int32_t*>(ws + lay.header);
-  int32_t* merge = reinterpret_cast<int32_t*>(ws + lay.merge);
-  int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
-  int32_t* unsorted = reinterpret_cast<int32_t*>(ws + lay.host_unsorted);
-  int32_t* order = reinterpret_cast<int32_t*>(ws + lay.host_order);
-  int64_t* cost = reinterpret_cast<int64_t*>(ws + lay.host_cost);
-
-  // Visit q tiles in (request, tile) order; fn(b, row0, row1, visible_keys).
-  const int qt = g.qo_tile;
-  auto for_each_qtile = [&](auto&& fn) {
-    for (int b = 0; b < batch; ++b) {
-      const int64_t L = kv_lens[b];
-      if (!app) {
-        fn(b, (int64_t)b, (int64_t)b + 1, L);
-        continue;
-      }
-      const int64_t r0 = qo_indptr[b], r1 = qo_indptr[b + 1], ql = r1 - r0;
-      for (int64_t t0 = 0; t0 < ql; t0 += qt) {
-        const int64_t t1 = std::min(ql, t0 + qt);
-        const int64_t vis = causal ? std::min(L, L - ql + t1) : L;
-        fn(b, r0 + t0, r0 + t1, vis);
-      }
-    }
-  };
-
-  int64_t units = 0;
-  for_each_qtile([&](int, int64_t, int64_t, int64_t vis) { units += cdiv(vis, ps); });
-  units *= g.num_kv_heads;
-  const int64_t target = (int64_t)g.num_cu * g.tiles_per_cu;
-  const int64_t P = std::max<int64_t>(g.min_chunk_pages, cdiv(units, target));
-
-  int64_t ntiles = 0, nmerge = 0, slots = 0;
-  bool over = false;
-  for_each_qtile([&](int b, int64_t q0, int64_t q1, int64_t vis) {
-    const int64_t C = std::max<int64_t>(1, cdiv(cdiv(vis, ps), P));
-    int64_t base = -1;
-    if (C > 1) {
-      base = slots;
-      slots += C * (q1 - q0);
-      for (int64_t r = q0; r < q1; ++r) {
-        if (nmerge < g.max_merge && base + (r - q0) * C + C <= g.max_partials) {
-          int32_t* m = merge + nmerge * kMergeInts;
-          m[0] = (int32_t)r;
-          m[1] = (int32_t)(base + (r - q0) * C);
-          m[2] = (int32_t)C;
-          m[3] = 0;
-        }
-        ++nmerge;
-      }
-    }
-    for (int64_t c = 0; c < C; ++c) {
-      const int64_t k0 = c * P * ps, k1 = std::min((c + 1) * P * ps, vis);
-      for (int h = 0; h < g.num_kv_heads; ++h) {
-        if (ntiles >= g.max_tiles) {
-          over = true;
-          ++ntiles;
-          continue;
-        }
-        int32_t* t = unsorted + ntiles * kTileInts;
-        t[0] = b;
-        t[1] = h;
-        t[2] = (int32_t)q0;
-        t[3] = (int32_t)q1;
-        t[4] = (int32_t)k0;
-        t[5] = (int32_t)k1;
-        t[6] = C > 1 ? (int32_t)(base + c) : -1;
-        t[7] = (int32_t)C;
-        cost[ntiles] = (k1 - k0) * (q1 - q0);
-        ++ntiles;
-      }
-    }
-  });
-  if (over || ntiles > g.max_tiles) {
-    set_error("%lld tiles exceed max_tiles %d", (long long)ntiles, g.max_tiles);
-    return FA_ERR_CAPACITY;
-  }
-  if (slots > g.max_partials) {
-    set_error("%lld partial states exceed max_partials %d", (long long)slots, g.max_partials);
-    return FA_ERR_CAPACITY;
-  }
-  if (nmerge > g.max_merge) {
-    set_error("%lld merge rows exceed max_merge %d", (long long)nmerge, g.max_merge);
-    return FA_ERR_CAPACITY;
-  }
-  for (int64_t i = 0; i < ntiles; ++i) order[i] = (int32_t)i;
-  std::stable_sort(order, order + ntiles, [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
-  for (int64_t i = 0; i < ntiles; ++i)
-    memcpy(tiles + i * kTileInts, unsorted + (int64_t)order[i] * kTileInts, kTileInts * 4);
-
+  int64_t ntiles = 0, nmerge = 0, slots = 0, P = 0;
+  fa_status st = app ? plan_append(g, lay, ws, kv_lens, batch, qo_indptr, causal, &ntiles, &nmerge,
+                                   &slots, &P)
+                     : plan_decode(g, lay, ws, kv_lens, batch, &ntiles, &nmerge, &slots, &P);
+  if (st != FA_OK) return st;
   memset(header, 0, kHeaderInts * 4);
   header[0] = (int32_t)ntiles;
   header[1] = (int32_t)nmerge;
@@ -279,6 +397,7 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
   header[3] = app ? qo_indptr[batch] : batch;
   header[4] = app ? causal : 0;
   header[5] = (int32_t)P;
+  header[6] = lay.workers;
 
   p->num_tiles = (int32_t)ntiles;
   p->num_merge = (int32_t)nmerge;
@@ -287,6 +406,7 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
   p->batch = batch;
   p->num_rows = header[3];
   p->causal = header[4];
+  p->num_workers = lay.workers;
   p->geom = g;
   p->lay = lay;
   p->host_ws = host_ws;

@@ -11,28 +11,37 @@ namespace pkfa {
 
 constexpr uint32_t kPlanMagic = 0x70666131u;  // "pfa1"
 constexpr int kTileInts = 8;                   // {b, h, row0, row1, key0, key1, slot0, nchunk}
-constexpr int kMergeInts = 4;                  // {row, slot0, nslot, 0}
-constexpr int kHeaderInts = 16;                // {num_tiles, num_merge, batch, num_rows, causal, chunk_pages, ...}
+constexpr int kMergeInts = 4;                  // {row0, kv_head, base slot, n_chunks}
+constexpr int kHeaderInts = 16;  // {num_tiles, num_merge, batch, num_rows, causal, chunk_pages, num_workers, ...}
 constexpr int kSupportedHeadDim = 128;
 constexpr int kSupportedPageSize = 16;
+constexpr int kMaxPiecePages = 128;  // decode pieces: the kernel holds 128 page ids per wave
 
 // Byte offsets of the regions inside the host and device workspaces.
+// Upload image (same offsets in host and device workspace):
+//   header | merge [max_merge][4] | worker_ptr [workers+1] | tiles [max_tiles][8]
+// Device only: arrival counters [max_partials] (zero between calls), partial
+// lse [max_partials][G] (log2 units), partial out [max_partials][G][head_dim].
+// Host only: scratch for sorting tiles and per-unit counts.
 struct Layout {
-  size_t header, merge, tiles, upload_end;  // upload image (same offsets in host and device ws)
-  size_t dev_part_lse, dev_part_o, dev_bytes;
-  size_t host_unsorted, host_order, host_cost, host_bytes;
+  size_t header, merge, worker_ptr, tiles, upload_end;
+  size_t dev_counters, dev_part_lse, dev_part_o, dev_bytes;
+  size_t host_unsorted, host_order, host_cost, host_units, host_bytes;
+  int32_t workers;
 };
 
 struct PlanImpl {
   uint32_t magic;
   int32_t planned;    // 1 after a successful fa_plan
   int32_t uploaded;   // 1 if the plan was copied into a device workspace
-  int32_t num_tiles, num_merge, num_slots, chunk_pages, batch, num_rows, causal;
+  int32_t num_tiles, num_merge, num_slots, chunk_pages, batch, num_rows, causal, num_workers;
   fa_geometry geom;   // resolved
   Layout lay;
   void* host_ws;
   void* dev_ws;
   void* upload_event;  // hipEvent_t recorded after the copy out of host_ws
+  void* zeroed_ws;     // device workspace whose counters were cleared
+  size_t zeroed_bytes;
 };
 static_assert(sizeof(PlanImpl) <= sizeof(fa_plan_t), "plan object too large");
 

@@ -54,9 +54,13 @@ def _compare(g, lens, qo_indptr=None, causal=False, **spec_knobs):
     spec = plan_spec(_indptr(lens), lens, len(lens), g.num_qo_heads, g.num_kv_heads, 128, 16,
                      max_batch=g.max_batch, qo_indptr=qo_indptr, causal=causal,
                      max_qo_tokens=g.max_qo_tokens, **knobs)
-    tiles, merge = p.tiles()
+    tiles, merge, wptr = p.tiles(with_workers=True)
     assert np.array_equal(tiles, spec["tiles"])
     assert np.array_equal(merge, spec["merge"])
+    if spec["worker_ptr"] is None:
+        assert wptr is None and st.num_workers == 0
+    else:
+        assert np.array_equal(wptr, spec["worker_ptr"])
     assert st.chunk_pages == spec["chunk_pages"] and st.num_slots == spec["num_slots"]
     assert st.uploaded == 0
     return st
@@ -149,7 +153,7 @@ def test_geometry_errors():
 
 
 def test_capacity_error():
-    g = _geom("decode", 4, 8, 8, max_tiles=16)
+    g = _geom("decode", 4, 8, 8, max_tiles=16, num_cu=64)
     with pytest.raises(fa.FAError) as e:
         fa.Plan(g).plan(_indptr([160] * 4), np.array([160] * 4, np.int32))
     assert e.value.code == "CAPACITY"

@@ -13,29 +13,34 @@ def _indptr(lens, ps=16):
 
 def test_hand_worked_decode_plan():
     # Three requests of 4, 2, 5 full pages (the page lists of the worked CSR
-    # example), 2 kv heads, target 1*8 tiles: units = 2*11 = 22, P = ceil(22/8) = 3.
+    # example), 2 kv heads -> units of 4,4,2,2,5,5 pages (W = 22) laid end to
+    # end; 4 workers own pages [0,5) [5,11) [11,16) [16,22).
     lens = [64, 32, 80]
-    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=8)
-    assert p["chunk_pages"] == 3 and p["num_slots"] == 4
-    expect = [
-        [0, 0, 0, 1, 0, 48, 0, 2], [0, 1, 0, 1, 0, 48, 0, 2],
-        [2, 0, 2, 3, 0, 48, 2, 2], [2, 1, 2, 3, 0, 48, 2, 2],
-        [1, 0, 1, 2, 0, 32, -1, 1], [1, 1, 1, 2, 0, 32, -1, 1],
-        [2, 0, 2, 3, 48, 80, 3, 2], [2, 1, 2, 3, 48, 80, 3, 2],
-        [0, 0, 0, 1, 48, 64, 1, 2], [0, 1, 0, 1, 48, 64, 1, 2],
-    ]
-    assert p["tiles"].tolist() == expect
-    assert p["merge"].tolist() == [[0, 0, 2, 0], [2, 2, 2, 0]]
-    # target 4: P = 6 pages, nothing splits; longest request first
     p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=4)
-    assert p["chunk_pages"] == 6 and p["num_slots"] == 0 and p["merge"].shape == (0, 4)
-    assert [t[0] for t in p["tiles"].tolist()] == [2, 2, 0, 0, 1, 1]
+    assert p["tiles"].tolist() == [
+        [0, 0, 0, -1, 0, 64, -1, 1],                                   # worker 0
+        [0, 1, 0, 0, 0, 16, 0, 2],
+        [0, 1, 0, 0, 16, 64, 1, 2],                                    # worker 1
+        [1, 0, 1, -1, 0, 32, -1, 1],
+        [1, 1, 1, 2, 0, 16, 2, 2],
+        [1, 1, 1, 2, 16, 32, 3, 2],                                    # worker 2
+        [2, 0, 2, 4, 0, 64, 4, 2],
+        [2, 0, 2, 4, 64, 80, 5, 2],                                    # worker 3
+        [2, 1, 2, -1, 0, 80, -1, 1],
+    ]
+    assert p["worker_ptr"].tolist() == [0, 2, 5, 7, 9]
+    assert p["merge"].tolist() == [[0, 1, 0, 2], [1, 1, 2, 2], [2, 0, 4, 2]]
+    assert p["num_slots"] == 6 and p["chunk_pages"] == 6
+    # one worker: every unit is one piece, nothing to merge
+    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=1)
+    assert p["num_slots"] == 0 and p["merge"].shape == (0, 4)
+    assert p["worker_ptr"].tolist() == [0, 6]
 
 
 def test_hand_worked_append_plan():
     # one request, kv 40, 40 new rows (pure prefill), qo_tile 16, causal:
     # q tiles rows [0,16) vis 16, [16,32) vis 32, [32,40) vis 40 -> 1+2+3 = 6 pages;
-    # 1 kv head, target 4 -> P = 2 pages: C = 1, 1, 2.
+    # 1 kv head, target 4 -> P = 2 pages: C = 1, 1, 2; the split unit has 8 rows.
     p = plan_spec([0, 3], [40], 1, 4, 1, 128, 16, max_batch=1, qo_indptr=[0, 40], causal=True,
                   max_qo_tokens=40, num_cu=1, tiles_per_cu=4, qo_tile=16)
     assert p["chunk_pages"] == 2
@@ -43,13 +48,46 @@ def test_hand_worked_append_plan():
         [0, 0, 16, 32, 0, 32, -1, 1],
         [0, 0, 0, 16, 0, 16, -1, 1],
         [0, 0, 32, 40, 0, 32, 0, 2],
-        [0, 0, 32, 40, 32, 40, 1, 2],
+        [0, 0, 32, 40, 32, 40, 8, 2],
     ]
-    assert p["num_slots"] == 16
-    assert p["merge"].tolist() == [[r, (r - 32) * 2, 2, 0] for r in range(32, 40)]
+    assert p["num_slots"] == 16 and p["worker_ptr"] is None
+    assert p["merge"].tolist() == [[32, 0, 0, 2]]
 
 
-def check_invariants(p, lens, Hkv, ps=16, qo_indptr=None, causal=False, qo_tile=1):
+def _pages(k0, k1, ps=16):
+    return -(-k1 // ps) - k0 // ps
+
+
+def check_decode_invariants(p, lens, Hkv, ps=16):
+    tiles, wptr = p["tiles"], p["worker_ptr"]
+    S = len(wptr) - 1
+    assert wptr[0] == 0 and wptr[-1] == len(tiles) and np.all(np.diff(wptr) >= 0)
+    W = sum(-(-int(L) // ps) for L in lens) * Hkv
+    for w in range(S):
+        load = sum(_pages(t[4], t[5], ps) for t in tiles[wptr[w]:wptr[w + 1]].tolist())
+        assert load == (w + 1) * W // S - w * W // S, "worker load must be its exact share"
+    by_unit = {}
+    for t in tiles.tolist():
+        by_unit.setdefault((t[0], t[1]), []).append(t)
+    assert sorted(by_unit) == [(b, h) for b in range(len(lens)) for h in range(Hkv)]
+    slots = set()
+    for (b, h), parts in by_unit.items():
+        L = int(lens[b])
+        C = len(parts)
+        assert parts[0][4] == 0 and parts[-1][5] == L
+        for a, c in zip(parts[:-1], parts[1:]):
+            assert a[5] == c[4] and c[4] % ps == 0
+        for i, t in enumerate(parts):
+            assert t[2] == b and t[7] == C
+            if C == 1:
+                assert t[3] == -1 and t[6] == -1
+            else:
+                assert t[6] == t[3] + i
+                slots.add(t[6])
+    assert slots == set(range(p["num_slots"]))
+
+
+def check_append_invariants(p, lens, Hkv, qo_indptr, causal, ps=16):
     tiles = p["tiles"]
     cost = (tiles[:, 5] - tiles[:, 4]).astype(np.int64) * (tiles[:, 3] - tiles[:, 2])
     assert np.all(np.diff(cost) <= 0), "not in descending cost order"
@@ -57,17 +95,13 @@ def check_invariants(p, lens, Hkv, ps=16, qo_indptr=None, causal=False, qo_tile=
     cover = {}
     for b, h, q0, q1, t0, t1, s0, C in tiles.tolist():
         cover.setdefault((b, h, q0, q1), []).append((t0, t1, s0, C))
-    B = len(lens)
     rows_seen = {}
+    used = set()
     for (b, h, q0, q1), parts in cover.items():
         parts.sort()
         L = int(lens[b])
-        if qo_indptr is None:
-            assert (q0, q1) == (b, b + 1)
-            vis = L
-        else:
-            ql = qo_indptr[b + 1] - qo_indptr[b]
-            vis = min(L, L - ql + (q1 - qo_indptr[b])) if causal else L
+        ql = qo_indptr[b + 1] - qo_indptr[b]
+        vis = min(L, L - ql + (q1 - qo_indptr[b])) if causal else L
         assert parts[0][0] == 0 and parts[-1][1] == max(vis, 0)
         for (a0, a1, _, _), (b0, b1, _, _) in zip(parts[:-1], parts[1:]):
             assert a1 == b0, "chunks must tile the key range"
@@ -75,17 +109,17 @@ def check_invariants(p, lens, Hkv, ps=16, qo_indptr=None, causal=False, qo_tile=
         assert len(parts) == C and all(x[3] == C for x in parts)
         if C == 1:
             assert parts[0][2] == -1
+        else:
+            for c, x in enumerate(parts):
+                assert x[2] == parts[0][2] + c * (q1 - q0)
+                for r in range(q1 - q0):
+                    assert x[2] + r not in used
+                    used.add(x[2] + r)
         for r in range(q0, q1):
             rows_seen[(r, h)] = rows_seen.get((r, h), 0) + 1
-    nrows = B if qo_indptr is None else int(qo_indptr[-1])
-    for r in range(nrows):
+    for r in range(int(qo_indptr[-1])):
         for h in range(Hkv):
             assert rows_seen.get((r, h), 0) == 1, "each (row, kv head) in exactly one q tile"
-    used = set()
-    for r, s0, C, _ in p["merge"].tolist():
-        for s in range(s0, s0 + C):
-            assert s not in used
-            used.add(s)
     assert used == set(range(p["num_slots"]))
 
 
@@ -94,7 +128,7 @@ def test_decode_configs(k):
     lens = config_lengths(k, np.random.default_rng(k))["kv_lens"]
     Hkv = 32 if k == 1 else 8
     p = plan_spec(_indptr(lens), lens, len(lens), 32, Hkv, 128, 16, max_batch=len(lens))
-    check_invariants(p, lens, Hkv)
+    check_decode_invariants(p, lens, Hkv)
     assert len(p["tiles"]) <= p["knobs"]["max_tiles"]
 
 
@@ -103,11 +137,11 @@ def test_append_config5_and_cascade_prefix():
     qo = np.concatenate([[0], np.cumsum([512] * 16)])
     p = plan_spec(_indptr(lens), lens, 16, 32, 8, 128, 16, max_batch=16, qo_indptr=qo,
                   causal=True, max_qo_tokens=8192)
-    check_invariants(p, lens, 8, qo_indptr=qo, causal=True)
+    check_append_invariants(p, lens, 8, qo, True)
     assert p["num_slots"] == 0 and len(p["tiles"]) == 16 * 8 * 16
     p = plan_spec([0, 1024], [16384], 1, 32, 8, 128, 16, max_batch=1, qo_indptr=[0, 256],
                   causal=False, max_qo_tokens=256)
-    check_invariants(p, [16384], 8, qo_indptr=[0, 256], causal=False)
+    check_append_invariants(p, [16384], 8, [0, 256], False)
     assert p["chunk_pages"] == 128 and len(p["tiles"]) == 512
 
 
@@ -123,7 +157,7 @@ def test_random_geometries():
         if it % 2:
             p = plan_spec(_indptr(lens), lens, B, G * Hkv, Hkv, 128, 16, max_batch=max(B, 1),
                           **knobs)
-            check_invariants(p, lens, Hkv)
+            check_decode_invariants(p, lens, Hkv)
         else:
             ql = np.minimum(rng.integers(0, 70, size=B), lens)
             qo = np.concatenate([[0], np.cumsum(ql)]).astype(np.int64)
@@ -132,7 +166,7 @@ def test_random_geometries():
             p = plan_spec(_indptr(lens), lens, B, G * Hkv, Hkv, 128, 16, max_batch=max(B, 1),
                           qo_indptr=qo, causal=causal, max_qo_tokens=max(int(qo[-1]), 1),
                           qo_tile=qt, **knobs)
-            check_invariants(p, lens, Hkv, qo_indptr=qo, causal=causal, qo_tile=qt)
+            check_append_invariants(p, lens, Hkv, qo, causal)
 
 
 @pytest.mark.parametrize("bad,code", [
@@ -157,5 +191,5 @@ def test_errors(bad, code):
 def test_capacity_error():
     lens = [160] * 4
     with pytest.raises(PlanSpecError) as e:
-        plan_spec(_indptr(lens), lens, 4, 8, 8, 128, 16, max_batch=4, max_tiles=16)
+        plan_spec(_indptr(lens), lens, 4, 8, 8, 128, 16, max_batch=4, max_tiles=16, num_cu=64)
     assert e.value.code == "CAPACITY"
