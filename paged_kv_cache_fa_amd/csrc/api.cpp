@@ -299,15 +299,12 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
                                    qo_indptr_d, sm_scale, out, lse);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
-  hipError_t e = launch_append(p, pl->geom.dtype, G, pl->geom.max_tiles, s);
+  const hipError_t e = launch_append(p, pl->geom.dtype, G, pl->geom.max_tiles, s);
   if (e == hipErrorNotSupported) {
     set_error("append kernel not built for this group size");
     return FA_ERR_UNSUPPORTED;
   }
-  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
-  e = launch_merge_partials(p, pl->geom.dtype, pl->geom.max_merge, s);
-  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  return FA_OK;
+  return e == hipSuccess ? FA_OK : hip_fail(e, "append kernel launch");
 }
 
 fa_status fa_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,

@@ -34,7 +34,6 @@ struct AttnParams {
 
 hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s);
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
-hipError_t launch_merge_partials(const AttnParams& p, int dtype, int max_merge, hipStream_t s);
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
                               void* vo, float* so, int64_t n, int heads, int head_dim, int dtype,
                               hipStream_t s);

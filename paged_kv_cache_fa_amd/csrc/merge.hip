@@ -75,32 +75,6 @@ struct Online {
   }
 };
 
-// Split-KV reduction: merge entry i = {row, first_slot, n_slots}; partial
-// states are fp32 [slots, Hq, 128] with log2-unit lse.
-template <int DT>
-__global__ __launch_bounds__(256) void merge_partials_kernel(AttnParams p) {
-  const int i = blockIdx.x;
-  if (i >= p.header[1]) return;
-  const int32_t* e = p.merge + i * 4;
-  const int row = e[0], s0 = e[1], C = e[2];
-  const int Hq = p.num_qo_heads;
-  for (int it = threadIdx.x; it < Hq * 16; it += 256) {
-    const int h = it >> 4, d = (it & 15) * 8;
-    Online st;
-    for (int c = 0; c < C; ++c) {
-      const int64_t sl = (int64_t)(s0 + c) * Hq + h;
-      const float s2 = p.part_lse[sl];
-      float v[8];
-      Vec8<FA_F32>::load(p.part_o, sl * 128 + d, v);
-      st.add(s2, v);
-    }
-    float o[8], lse2;
-    st.finish(o, lse2);
-    Vec8<DT>::store(p.out, ((int64_t)row * Hq + h) * 128 + d, o);
-    if (d == 0 && p.lse) p.lse[(int64_t)row * Hq + h] = lse2 * kLn2;
-  }
-}
-
 template <int DT>
 __global__ __launch_bounds__(256) void merge_state_kernel(const void* va, const float* sa,
                                                           const void* vb, const float* sb,
@@ -157,15 +131,6 @@ int grid_for(int64_t total) {
 }
 
 }  // namespace
-
-hipError_t launch_merge_partials(const AttnParams& p, int dtype, int max_merge, hipStream_t s) {
-  if (max_merge <= 0) return hipSuccess;
-  if (dtype == FA_BF16)
-    hipLaunchKernelGGL(merge_partials_kernel<FA_BF16>, dim3(max_merge), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(merge_partials_kernel<FA_F16>, dim3(max_merge), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
 
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
                               void* vo, float* so, int64_t n, int heads, int head_dim, int dtype,

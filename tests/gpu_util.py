@@ -81,3 +81,23 @@ def assert_close(out, lse, ref_out, ref_lse, out_tol=OUT_TOL, lse_tol=LSE_TOL, w
     assert e_out <= out_tol, f"{what}: out max-abs {e_out} > {out_tol}"
     assert e_lse <= lse_tol, f"{what}: lse max-abs {e_lse} > {lse_tol}"
     return e_out, e_lse
+
+
+def append_geometry(wl, **knobs):
+    return fa.geometry("append", wl.dtype, max(wl.batch, 1), wl.num_qo_heads, wl.num_kv_heads,
+                       max_qo_tokens=max(wl.rows, 1), **knobs)
+
+
+def run_append(dw: DevWorkload, plan=None, out=None, lse=None, **knobs):
+    wl = dw.wl
+    if plan is None:
+        plan = fa.Plan(append_geometry(wl, **knobs), device=dw.device)
+        plan.plan(wl.kv_indptr, wl.kv_lens, wl.qo_indptr, wl.causal)
+    out, lse = fa.append(plan, dw.q, dw.qo_indptr, dw.k, dw.v, *dw.strides, dw.kv_indices,
+                         dw.kv_indptr, dw.last_page_len, out=out, lse=lse)
+    return plan, out, lse
+
+
+def oracle_append(wl, rows=None):
+    return oracle.append(wl.q, wl.qo_indptr, wl.pool, wl.dtype, wl.kv_indptr, wl.kv_indices,
+                         wl.last_page_len, wl.page_size, causal=wl.causal, rows=rows)
