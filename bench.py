@@ -1,23 +1,32 @@
-"""Benchmark: paged decode HBM throughput on one MI355X.
+"""Benchmark: paged-KV attention hot path on one MI355X.
 
-One step = one pass of the decode hot path over one batch: the host plan
-(split-KV tiles, uploaded to the device workspace) followed by the decode
-kernel and the log-sum-exp merge of split requests. The headline workload is
-batch 64 with GQA (32 q / 8 kv heads, head_dim 128, bf16, page 16, kv_len
-uniform in [512, 4096], pages scattered by a seeded permutation); the batch-128
-skewed workload (4 x 32768 + 124 log-normal lengths) is reported alongside.
+Headline (the JSON ``value``): batched paged decode, batch 64, GQA 32 q / 8 kv
+heads, head_dim 128, bf16, page 16, kv_len uniform in [512, 4096], pages
+scattered by a seeded permutation. One step = the host plan (balanced
+split-KV work list, uploaded to the device workspace) + the decode kernel
+(which also merges split requests). ``value`` is the achieved algorithmic
+HBM bandwidth of the step in GB/s: bytes of the valid K/V of every request,
+plus q, out and lse, divided by the wall time per step.
 
-Inputs are synthetic (seeded N(0,1)), already resident in HBM before the timed
+Reported alongside in the same JSON line:
+  * ``batch128``: the skewed batch-128 decode (4 x 32768 + 124 log-normal);
+  * ``cascade``: batch 256 sharing a 16384-token prefix (prefix pass on MFMA +
+    suffix decode + merge_state), as HBM GB/s with the prefix counted once;
+  * ``append``: causal append of 16 x 512 rows onto 4096 cached tokens, as
+    MFMA utilisation (584.2 GFLOP of unmasked work per step);
+  * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
+    from HIP events on its stream), with HBM traffic from rocprofv3 counters
+    when the stored counter summary matches the current kernel source;
+  * ``cpu_baseline``: the fp64 numpy oracle on the host cores.
+
+Inputs are synthetic (seeded N(0,1)), resident in HBM before the timed
 region; steps rotate over enough copies of the page pool (>= 1 GiB in total)
-that the 256 MB Infinity Cache cannot serve them.
-
-Prints one JSON line. ``value`` is the achieved algorithmic HBM bandwidth in
-GB/s of the whole step (bytes of valid K/V + q + out + lse, divided by the
-wall time per step).
+that the 256 MB Infinity Cache cannot hold them.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,33 +39,86 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2516.6  # bf16 dense: 256 CU x 4096 FLOP/clk x 2.4 GHz
 METRIC = "paged decode achieved HBM GB/s (% of peak) and tokens/sec at batch 64/128"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_batch64_hbm_counters.txt")
+
+
+def kv_bytes(lens, hkv, d=128, elt=2) -> int:
+    return int(np.asarray(lens, np.int64).sum()) * hkv * d * 2 * elt
+
+
+def io_bytes(rows, hq, d=128, elt=2) -> int:
+    return rows * hq * d * elt * 2 + rows * hq * 4
 
 
 def algorithmic_bytes(wl) -> int:
-    """Valid K/V bytes of every request plus q, out and lse."""
-    elt = 2
-    kv = int(wl.kv_lens.astype(np.int64).sum()) * wl.num_kv_heads * wl.head_dim * 2 * elt
-    q = wl.rows * wl.num_qo_heads * wl.head_dim * elt
-    return kv + 2 * q + wl.rows * wl.num_qo_heads * 4
+    """Valid K/V bytes of every request (a shared prefix once) plus q, out, lse."""
+    b = kv_bytes(wl.kv_lens, wl.num_kv_heads) + io_bytes(wl.rows, wl.num_qo_heads)
+    if wl.prefix_len:
+        b += kv_bytes([wl.prefix_len], wl.num_kv_heads)
+    return b
 
 
-class DecodeBench:
+def append_flops(wl) -> float:
+    """4 * head_dim FLOPs per unmasked (query row, key) pair and query head."""
+    pairs = 0
+    for b in range(wl.batch):
+        ql = int(wl.qo_indptr[b + 1] - wl.qo_indptr[b])
+        L = int(wl.kv_lens[b])
+        if wl.causal:
+            pairs += sum(L - ql + i + 1 for i in range(ql))
+        else:
+            pairs += ql * L
+    return float(pairs) * wl.num_qo_heads * 4 * wl.head_dim
+
+
+def _dev(wl, device, min_rotation_bytes):
+    import torch
+    dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
+    pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
+    copies = max(1, math.ceil(min_rotation_bytes / max(1, pool.numel() * 2)))
+    pools = [pool] + [pool.clone() for _ in range(copies - 1)]
+    q = torch.from_numpy(wl.q.view(np.int16)).to(device).view(dt)
+    _, _, ps, hkv, d = wl.pool.shape
+    return pools, q, (2 * ps * hkv * d, hkv * d, d)
+
+
+def _i32(a, device):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+class Timed:
+    """Run steps; time the whole step and one named kernel call with HIP events."""
+
+    def run(self, steps: int, warmup: int):
+        import torch
+        for i in range(warmup):
+            self.step(i, None)
+        torch.cuda.synchronize()
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            self.step(warmup + i, kev[i])
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in kev]))
+
+
+class DecodeBench(Timed):
     def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, **knobs):
         import torch
         import paged_kv_cache_fa_amd as fa
-        self.fa = fa
-        self.wl = wl
-        dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
-        pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
-        copies = max(1, math.ceil(min_rotation_bytes / max(1, pool.numel() * 2)))
-        self.pools = [pool] + [pool.clone() for _ in range(copies - 1)]
-        self.q = torch.from_numpy(wl.q.view(np.int16)).to(device).view(dt)
-        self.kv_indptr = torch.from_numpy(wl.kv_indptr).to(device)
-        self.kv_indices = torch.from_numpy(wl.kv_indices).to(device)
-        self.last = torch.from_numpy(wl.last_page_len).to(device)
-        _, _, ps, hkv, d = wl.pool.shape
-        self.strides = (2 * ps * hkv * d, hkv * d, d)
+        self.fa, self.wl = fa, wl
+        self.pools, self.q, self.strides = _dev(wl, device, min_rotation_bytes)
+        self.kv_indptr = _i32(wl.kv_indptr, device)
+        self.kv_indices = _i32(wl.kv_indices, device)
+        self.last = _i32(wl.last_page_len, device)
         geom = fa.geometry("decode", wl.dtype, wl.batch, wl.num_qo_heads, wl.num_kv_heads, **knobs)
         self.plan = fa.Plan(geom, device=device)
         self.out = torch.empty_like(self.q)
@@ -74,50 +136,122 @@ class DecodeBench:
         if ev is not None:
             ev[1].record()
 
-    def run(self, steps: int, warmup: int):
+
+class AppendBench(Timed):
+    def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, **knobs):
         import torch
-        for i in range(warmup):
-            self.step(i)
-        torch.cuda.synchronize()
-        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record()
-        for i in range(steps):
-            self.step(warmup + i, kev[i])
-        t1.record()
-        torch.cuda.synchronize()
-        step_ms = t0.elapsed_time(t1) / steps
-        kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
-        return step_ms, kernel_ms
+        import paged_kv_cache_fa_amd as fa
+        self.fa, self.wl = fa, wl
+        self.pools, self.q, self.strides = _dev(wl, device, min_rotation_bytes)
+        self.kv_indptr = _i32(wl.kv_indptr, device)
+        self.kv_indices = _i32(wl.kv_indices, device)
+        self.last = _i32(wl.last_page_len, device)
+        self.qo_indptr = _i32(wl.qo_indptr, device)
+        geom = fa.geometry("append", wl.dtype, wl.batch, wl.num_qo_heads, wl.num_kv_heads,
+                           max_qo_tokens=wl.rows, **knobs)
+        self.plan = fa.Plan(geom, device=device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(wl.rows, wl.num_qo_heads, dtype=torch.float32, device=device)
+
+    def step(self, i: int, ev=None):
+        wl = self.wl
+        pool = self.pools[i % len(self.pools)]
+        self.plan.plan(wl.kv_indptr, wl.kv_lens, wl.qo_indptr, wl.causal)
+        if ev is not None:
+            ev[0].record()
+        self.fa.append(self.plan, self.q, self.qo_indptr, pool[:, 0], pool[:, 1], *self.strides,
+                       self.kv_indices, self.kv_indptr, self.last, out=self.out, lse=self.lse)
+        if ev is not None:
+            ev[1].record()
 
 
-def cpu_baseline(wl, budget_s: float = 15.0) -> dict:
-    """The fp64 oracle on the host cores over a bounded sample of requests."""
+class CascadeBench(Timed):
+    """Prefix pass (non-causal append over the shared prefix) + suffix decode +
+    merge_state; the timed kernel is the prefix pass."""
+
+    def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30):
+        import torch
+        import paged_kv_cache_fa_amd as fa
+        self.fa, self.wl = fa, wl
+        B = wl.batch
+        self.pools, self.q, self.strides = _dev(wl, device, min_rotation_bytes)
+        self.kv_indptr = _i32(wl.kv_indptr, device)
+        self.kv_indices = _i32(wl.kv_indices, device)
+        self.last = _i32(wl.last_page_len, device)
+        self.p_indptr = _i32(wl.prefix_indptr, device)
+        self.p_indices = _i32(wl.prefix_indices, device)
+        self.p_last = _i32(wl.prefix_last_page_len, device)
+        self.qo = _i32([0, B], device)
+        gp = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads, max_qo_tokens=B)
+        gs = fa.geometry("decode", wl.dtype, B, wl.num_qo_heads, wl.num_kv_heads)
+        self.pplan = fa.Plan(gp, device=device)
+        self.splan = fa.Plan(gs, device=device)
+        mk = lambda: (torch.empty_like(self.q),
+                      torch.empty(B, wl.num_qo_heads, dtype=torch.float32, device=device))
+        self.op, self.lp = mk()
+        self.os, self.ls = mk()
+        self.out, self.lse = mk()
+
+    def step(self, i: int, ev=None):
+        wl, fa = self.wl, self.fa
+        pool = self.pools[i % len(self.pools)]
+        k, v = pool[:, 0], pool[:, 1]
+        self.pplan.plan(wl.prefix_indptr, [wl.prefix_len], [0, wl.batch], False)
+        self.splan.plan(wl.kv_indptr, wl.kv_lens)
+        if ev is not None:
+            ev[0].record()
+        fa.append(self.pplan, self.q, self.qo, k, v, *self.strides, self.p_indices, self.p_indptr,
+                  self.p_last, out=self.op, lse=self.lp)
+        if ev is not None:
+            ev[1].record()
+        fa.decode(self.splan, self.q, k, v, *self.strides, self.kv_indices, self.kv_indptr,
+                  self.last, out=self.os, lse=self.ls)
+        fa.merge_state(self.op, self.lp, self.os, self.ls, self.out, self.lse)
+
+
+def stored_traffic(kernel_src: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    fields = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
+    """The fp64 oracle on the host cores, repeated over the batch for >= min_seconds."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
-        cores = 1
-    reqs, t_used, done_bytes = [], 0.0, 0
+        cores = len(os.sched_getaffinity(0))
     per_tok = wl.num_kv_heads * wl.head_dim * 2 * 2
-    t_start = time.perf_counter()
-    for b in range(wl.batch):
-        t = time.perf_counter()
-        oracle.decode(wl.q, wl.pool, wl.dtype, wl.kv_indptr, wl.kv_indices, wl.last_page_len,
-                      wl.page_size, requests=[b])
-        t_used += time.perf_counter() - t
-        reqs.append(b)
-        done_bytes += int(wl.kv_lens[b]) * per_tok + wl.num_qo_heads * wl.head_dim * 2 * 2
-        if time.perf_counter() - t_start > budget_s:
-            break
+    done_bytes, done_req, t_used, passes = 0, 0, 0.0, 0
+    while t_used < min_seconds and passes < 20:
+        for b in range(wl.batch):
+            t = time.perf_counter()
+            oracle.decode(wl.q, wl.pool, wl.dtype, wl.kv_indptr, wl.kv_indices, wl.last_page_len,
+                          wl.page_size, requests=[b])
+            t_used += time.perf_counter() - t
+            done_bytes += int(wl.kv_lens[b]) * per_tok + io_bytes(1, wl.num_qo_heads)
+            done_req += 1
+        passes += 1
     return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle over requests 0..{len(reqs) - 1} of {wl.batch} "
-                      f"({len(reqs) / t_used:.2f} requests/s, {t_used:.1f} s)"}
+            "sample": f"fp64 numpy oracle over all {wl.batch} requests of the same workload, "
+                      f"{passes} pass(es): {done_req / t_used:.1f} requests/s "
+                      f"({done_req / t_used * 1:.1f} tokens/s), {t_used:.1f} s"}
 
 
 def main():
@@ -125,18 +259,27 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="2 = batch 64 (headline), 3 = batch 128")
+    ap.add_argument("--config", type=int, default=2, help="decode workload for the headline (1-3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-batch128", action="store_true")
-    ap.add_argument("--knob", action="append", default=[], help="plan knob name=value")
+    ap.add_argument("--only-headline", action="store_true", help="skip batch128/cascade/append")
+    ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB device copy first (scales rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              "(DESIGN.md describes how it would shard).", file=sys.stderr)
         sys.exit(2)
     import torch
     from workloads import CONFIG_NAMES, make_config
     knobs = {k: int(v) for k, v in (s.split("=") for s in args.knob)}
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     wl = make_config(args.config)
     b = DecodeBench(wl, **knobs)
@@ -145,6 +288,7 @@ def main():
     gbs = nbytes / (step_ms * 1e-3) / 1e9
     kgbs = nbytes / (kernel_ms * 1e-3) / 1e9
     st = b.plan.info()
+    traffic = stored_traffic(os.path.join(ROOT, "paged_kv_cache_fa_amd", "csrc", "decode.hip"))
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -163,28 +307,51 @@ def main():
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "page_size": wl.page_size, "kv_tokens": int(wl.kv_lens.sum()),
                    "algorithmic_bytes": nbytes, "pool_copies": len(b.pools),
-                   "tiles": st.num_tiles, "merge_rows": st.num_merge,
-                   "chunk_pages": st.chunk_pages},
+                   "tiles": st.num_tiles, "split_units": st.num_merge,
+                   "workers": st.num_workers, "pages_per_worker": st.chunk_pages},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(wl.batch / (step_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel + merge_partials_kernel (one fa_decode call)",
-                     "kernel_ms": round(kernel_ms, 5)},
+                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel (one fa_decode call)",
+                     "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes},
     }
     del b
     torch.cuda.empty_cache()
-    if args.config == 2 and not args.no_batch128:
-        wl3 = make_config(3)
-        b3 = DecodeBench(wl3, **knobs)
+    if not args.only_headline:
+        w3 = make_config(3)
+        b3 = DecodeBench(w3, **knobs)
         s3, k3 = b3.run(args.steps, args.warmup)
-        n3 = algorithmic_bytes(wl3)
+        n3 = algorithmic_bytes(w3)
         line["batch128"] = {"workload": f"config3: {CONFIG_NAMES[3]}",
                             "GB/s": round(n3 / (s3 * 1e-3) / 1e9, 2),
                             "pct_of_hbm_peak": round(100 * n3 / (s3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                             "tokens_per_s": round(128 / (s3 * 1e-3), 1),
                             "ms_per_step": round(s3, 5), "kernel_ms": round(k3, 5)}
-        del b3, wl3
+        del b3, w3
+        torch.cuda.empty_cache()
+        w4 = make_config(4)
+        b4 = CascadeBench(w4)
+        s4, k4 = b4.run(max(5, args.steps // 2), max(2, args.warmup // 2))
+        n4 = algorithmic_bytes(w4)
+        line["cascade"] = {"workload": f"config4: {CONFIG_NAMES[4]}",
+                           "GB/s": round(n4 / (s4 * 1e-3) / 1e9, 2),
+                           "pct_of_hbm_peak": round(100 * n4 / (s4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                           "tokens_per_s": round(256 / (s4 * 1e-3), 1),
+                           "ms_per_step": round(s4, 5), "prefix_pass_ms": round(k4, 5),
+                           "algorithmic_bytes": n4}
+        del b4, w4
+        torch.cuda.empty_cache()
+        w5 = make_config(5)
+        b5 = AppendBench(w5)
+        s5, k5 = b5.run(max(5, args.steps // 2), max(2, args.warmup // 2))
+        f5 = append_flops(w5)
+        line["append"] = {"workload": f"config5: {CONFIG_NAMES[5]}",
+                          "TFLOP/s": round(f5 / (k5 * 1e-3) / 1e12, 1),
+                          "mfma_utilisation": round(f5 / (k5 * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+                          "flops": f5, "kernel_ms": round(k5, 5), "ms_per_step": round(s5, 5),
+                          "tokens_per_s": round(w5.rows / (s5 * 1e-3), 1)}
+        del b5, w5
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

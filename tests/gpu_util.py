@@ -101,3 +101,32 @@ def run_append(dw: DevWorkload, plan=None, out=None, lse=None, **knobs):
 def oracle_append(wl, rows=None):
     return oracle.append(wl.q, wl.qo_indptr, wl.pool, wl.dtype, wl.kv_indptr, wl.kv_indices,
                          wl.last_page_len, wl.page_size, causal=wl.causal, rows=rows)
+
+
+def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, **knobs):
+    """Shared-prefix pass (non-causal append of every request's query over the
+    prefix) + private-suffix decode + merge_state. Returns (out, lse, plans)."""
+    import torch
+    wl = dw.wl
+    B = wl.batch
+    if prefix_plan is None:
+        g = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads,
+                        max_qo_tokens=B, **knobs.get("prefix", {}))
+        prefix_plan = fa.Plan(g, device=dw.device)
+        prefix_plan.plan(wl.prefix_indptr, [wl.prefix_len], [0, B], False)
+    if suffix_plan is None:
+        suffix_plan = fa.Plan(decode_geometry(wl, **knobs.get("suffix", {})), device=dw.device)
+        suffix_plan.plan(wl.kv_indptr, wl.kv_lens)
+    qo = torch.tensor([0, B], dtype=torch.int32, device=dw.device)
+    o_p, l_p = fa.append(prefix_plan, dw.q, qo, dw.k, dw.v, *dw.strides, dw.prefix_indices,
+                         dw.prefix_indptr, dw.prefix_last_page_len)
+    o_s, l_s = fa.decode(suffix_plan, dw.q, dw.k, dw.v, *dw.strides, dw.kv_indices, dw.kv_indptr,
+                         dw.last_page_len)
+    out, lse = fa.merge_state(o_p, l_p, o_s, l_s)
+    return out, lse, (prefix_plan, suffix_plan)
+
+
+def oracle_cascade(wl, requests=None):
+    return oracle.cascade(wl.q, wl.pool, wl.dtype, wl.prefix_indptr, wl.prefix_indices,
+                          wl.prefix_last_page_len, wl.kv_indptr, wl.kv_indices, wl.last_page_len,
+                          wl.page_size, requests=requests)

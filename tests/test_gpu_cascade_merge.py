@@ -1,0 +1,118 @@
+"""GPU parity: merge_state / merge_states kernels and the cascade path."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle  # noqa: E402
+from gpu_util import (DevWorkload, assert_close, oracle_cascade, run_cascade,  # noqa: E402
+                      to_f64, torch_dtype)
+from workloads import make_cascade, make_config, to_storage_bits  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _states(rng, shape, dtype, empty_frac=0.1):
+    import torch
+    v = rng.standard_normal(shape + (128,)).astype(np.float32)
+    s = (rng.standard_normal(shape) * 3).astype(np.float32)
+    s[rng.random(shape) < empty_frac] = -np.inf
+    if dtype == "fp32":
+        vt = torch.from_numpy(v).cuda()
+        v64 = v.astype(np.float64)
+    else:
+        bits = to_storage_bits(v, dtype)
+        vt = torch.from_numpy(bits.view(np.int16)).cuda().view(torch_dtype(dtype))
+        v64 = oracle.upcast(bits, dtype)
+    return vt, torch.from_numpy(s).cuda(), v64, s.astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+def test_merge_state(dtype):
+    import paged_kv_cache_fa_amd as fa
+    rng = np.random.default_rng(1)
+    va, sa, va64, sa64 = _states(rng, (37, 8), dtype)
+    vb, sb, vb64, sb64 = _states(rng, (37, 8), dtype)
+    sb[0, 0] = -np.inf
+    sa[0, 0] = -np.inf          # both empty -> (0, -inf)
+    sa64[0, 0] = sb64[0, 0] = -np.inf
+    vo, so = fa.merge_state(va, sa, vb, sb)
+    ro, rs = oracle.merge_state(va64, sa64, vb64, sb64)
+    tol = 2e-2 if dtype != "fp32" else 1e-5
+    assert_close(to_f64(vo), so.cpu().numpy().astype(np.float64), ro, rs, out_tol=tol,
+                 what=f"merge_state {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("k", [1, 3, 17])
+def test_merge_states(dtype, k):
+    import paged_kv_cache_fa_amd as fa
+    rng = np.random.default_rng(k)
+    v, s, v64, s64 = _states(rng, (23, k, 4), dtype)
+    vo, so = fa.merge_states(v, s)
+    ro, rs = oracle.merge_states(np.moveaxis(v64, 1, 2), np.moveaxis(s64, 1, 2))
+    tol = 2e-2 if dtype != "fp32" else 1e-5
+    assert_close(to_f64(vo), so.cpu().numpy().astype(np.float64), ro, rs, out_tol=tol,
+                 what=f"merge_states {dtype} k={k}")
+
+
+def test_merge_recovers_unsplit_attention():
+    """Two decode passes over disjoint halves of each request's keys, merged on
+    the GPU, equal the oracle over the whole request."""
+    import torch
+    import paged_kv_cache_fa_amd as fa
+    from workloads import make_workload
+    from gpu_util import run_decode, oracle_decode
+    lens = [640, 1024, 48]
+    wl = make_workload(lens, 32, 8, "bf16", 17, mode="test")
+    # first half: pages [0, n/2), second half: the rest, as two page tables
+    halves = []
+    for part in (0, 1):
+        lists, L2 = [], []
+        for b, L in enumerate(lens):
+            pages = wl.kv_indices[wl.kv_indptr[b]: wl.kv_indptr[b + 1]]
+            n = len(pages)
+            cut = n // 2
+            sel = pages[:cut] if part == 0 else pages[cut:]
+            lists.append(sel)
+            L2.append(cut * 16 if part == 0 else L - cut * 16)
+        import copy
+        w2 = copy.copy(wl)
+        w2.kv_indptr = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+        w2.kv_indices = np.concatenate(lists).astype(np.int32)
+        w2.kv_lens = np.array(L2, np.int32)
+        w2.last_page_len = np.array([0 if x == 0 else x - 16 * ((x - 1) // 16) for x in L2],
+                                    np.int32)
+        dw = DevWorkload(w2)
+        _, o, l_ = run_decode(dw)
+        halves.append((o, l_))
+    out, lse = fa.merge_state(halves[0][0], halves[0][1], halves[1][0], halves[1][1])
+    ref = oracle_decode(wl)
+    assert_close(to_f64(out), lse.cpu().numpy().astype(np.float64), *ref, what="split+merge")
+
+
+def test_cascade_small():
+    wl = make_cascade(256, [5, 16, 17, 300, 1], 32, 8, "bf16", 21, mode="test")
+    dw = DevWorkload(wl)
+    out, lse, _ = run_cascade(dw, prefix={"num_cu": 4}, suffix={"num_cu": 4})
+    ref = oracle_cascade(wl)
+    assert_close(to_f64(out), to_f64(lse), *ref, what="cascade small")
+    direct = oracle.cascade_direct(wl.q, wl.pool, wl.dtype, wl.prefix_indptr, wl.prefix_indices,
+                                   wl.prefix_last_page_len, wl.kv_indptr, wl.kv_indices,
+                                   wl.last_page_len, wl.page_size)
+    assert_close(to_f64(out), to_f64(lse), *direct, what="cascade vs direct")
+
+
+def test_config4_full_size():
+    print("[config 4] generating", flush=True)
+    wl = make_config(4, mode="test")
+    dw = DevWorkload(wl)
+    out, lse, plans = run_cascade(dw)
+    print(f"[config 4] prefix tiles {plans[0].info().num_tiles} suffix tiles "
+          f"{plans[1].info().num_tiles}", flush=True)
+    reqs = list(range(0, 256, 5)) + [255]
+    ref = oracle_cascade(wl, requests=reqs)
+    e = assert_close(to_f64(out)[reqs], to_f64(lse)[reqs], *ref, what="config 4")
+    print(f"[config 4] {len(reqs)} requests: max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
