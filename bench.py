@@ -262,6 +262,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="decode workload for the headline (1-3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip batch128/cascade/append")
+    ap.add_argument("--parts", default="batch128,cascade,append",
+                    help="comma list of the secondary workloads to run after the headline")
     ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device copy first (scales rocprofv3 byte counters)")
@@ -318,7 +320,8 @@ def main():
     }
     del b
     torch.cuda.empty_cache()
-    if not args.only_headline:
+    parts = set() if args.only_headline else set(filter(None, args.parts.split(",")))
+    if "batch128" in parts:
         w3 = make_config(3)
         b3 = DecodeBench(w3, **knobs)
         s3, k3 = b3.run(args.steps, args.warmup)
@@ -330,6 +333,7 @@ def main():
                             "ms_per_step": round(s3, 5), "kernel_ms": round(k3, 5)}
         del b3, w3
         torch.cuda.empty_cache()
+    if "cascade" in parts:
         w4 = make_config(4)
         b4 = CascadeBench(w4)
         s4, k4 = b4.run(max(5, args.steps // 2), max(2, args.warmup // 2))
@@ -342,6 +346,7 @@ def main():
                            "algorithmic_bytes": n4}
         del b4, w4
         torch.cuda.empty_cache()
+    if "append" in parts:
         w5 = make_config(5)
         b5 = AppendBench(w5)
         s5, k5 = b5.run(max(5, args.steps // 2), max(2, args.warmup // 2))

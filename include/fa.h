@@ -77,7 +77,8 @@ typedef struct {
   int32_t num_cu;          /* compute units to spread tiles over (default 256) */
   int32_t tiles_per_cu;    /* decode: worker waves per compute unit (default 4); append: tiles per CU (default 2) */
   int32_t min_chunk_pages; /* smallest split-KV chunk in pages (default 1) */
-  int32_t qo_tile;         /* append: query rows per tile (default 32); decode: 1 */
+  int32_t qo_tile;         /* append: query rows per tile, 1..128/G (default 128/G,
+                              G = num_qo_heads / num_kv_heads); decode: 1 */
   int32_t max_tiles;       /* capacities; default = worst case of the plan procedure */
   int32_t max_partials;
   int32_t max_merge;

@@ -75,12 +75,17 @@ def _cdiv(a: int, b: int) -> int:
 def default_knobs(num_kv_heads: int, max_batch: int, max_qo_tokens: int, is_append: bool,
                   num_cu: int = 0, tiles_per_cu: int = 0, min_chunk_pages: int = 0,
                   qo_tile: int = 0, max_tiles: int = 0, max_partials: int = 0,
-                  max_merge: int = 0) -> dict:
-    """Fill zero knobs with defaults; capacities are the worst case of the procedure."""
+                  max_merge: int = 0, group: int = 1) -> dict:
+    """Fill zero knobs with defaults; capacities are the worst case of the procedure.
+
+    An append q tile holds at most ``128 / group`` rows (the library's tiles
+    have 128 query columns = group heads x rows); that is also the default."""
     num_cu = num_cu or 256
     tiles_per_cu = tiles_per_cu or (2 if is_append else 4)
     min_chunk_pages = min_chunk_pages or 1
-    qo_tile = (qo_tile or 32) if is_append else 1
+    qo_tile = (qo_tile or 128 // group) if is_append else 1
+    if is_append and qo_tile > 128 // group:
+        raise PlanSpecError("UNSUPPORTED", "qo_tile larger than 128 / group")
     target = num_cu * tiles_per_cu
     if is_append:
         n_qtiles = max_batch + _cdiv(max_qo_tokens, qo_tile)
@@ -228,7 +233,8 @@ def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
     validate(kv_indptr, kv_lens, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
              max_batch, None if qo_indptr is None else np.asarray(qo_indptr, np.int64), causal,
              max_qo_tokens)
-    k = default_knobs(num_kv_heads, max_batch, max_qo_tokens, is_append, **knobs)
+    k = default_knobs(num_kv_heads, max_batch, max_qo_tokens, is_append,
+                      group=num_qo_heads // num_kv_heads, **knobs)
     if is_append:
         tiles, merge, slots, wptr, P = _append_plan(kv_lens, batch, num_kv_heads, page_size,
                                                     np.asarray(qo_indptr, np.int64), causal, k)

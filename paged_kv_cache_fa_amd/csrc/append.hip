@@ -11,24 +11,36 @@
 // for shared prefixes").
 //
 // MI355X design (the work is a dense contraction, so it runs on MFMA):
-//  * one workgroup per tile {request, kv head, 32 query rows, key chunk},
-//    one wave per query head of the kv head's group (GQA): the G waves share
-//    every K/V block staged in LDS;
-//  * K/V blocks of 64 keys are fetched with 16-byte global loads one block
-//    ahead into registers and stored to a double-buffered LDS; V is written
-//    transposed (4 keys x 8 dims per thread, regrouped with v_perm) so the
-//    PV operand reads 4 consecutive keys per dim;
+//  * one 256-thread workgroup (4 waves) per tile {request, kv head, up to
+//    128/G query positions, key chunk}. The tile's 128 query columns are the
+//    G heads of the kv head's group x 128/G positions (GQA packing): every
+//    K/V block staged in LDS feeds all of them. Wave w owns columns
+//    32w .. 32w+31;
+//  * blocks of 64 keys: each thread fetches 16 bytes of 4 token rows of K and
+//    of V (one row from each of the block's 4 pages, so every load's page is
+//    uniform across the workgroup) through a per-page buffer resource that
+//    ends at the last valid token: keys past the end read as zero. The
+//    registers are written to a double-buffered LDS after the current block's
+//    math, one barrier per block;
+//  * inside a block, key k sits in LDS slot 4 (k mod 16) + k / 16, so one
+//    thread's 4 rows form 4 consecutive slots: V is stored transposed
+//    (dim-major, 4 slots per 8-byte store) without any exchange. The
+//    contraction over keys is order-free, and the mask maps slots back to
+//    keys. V^T rows are XOR-swizzled in 8-byte units so that both the
+//    transposing stores and the MFMA operand reads hit distinct banks;
 //  * scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_{bf16,f16}: each lane then owns one query column and
-//    16 of its 32 keys per tile, so the online-softmax max / sum need one
-//    cross-lane exchange (lanes l and l^32) and the rescale of the output
-//    accumulators is lane-local;
+//    v_mfma_f32_32x32x16_{bf16,f16}: a lane owns one query column and 16 of
+//    every 32 slots, so the online-softmax max / sum need one exchange
+//    (lanes l and l^32) and the output rescale is lane-local. The reference
+//    max only moves (with a rescale) when a wave-wide vote sees a score more
+//    than 2^8 above it, so most blocks skip the rescale;
 //  * O^T += V^T P^T reuses the score registers (rounded to the input type) as
-//    the B operand; the contraction index (keys) is permuted identically in
-//    both operands, so the result is unaffected;
-//  * a chunked (split) query tile writes fp32 partial states; the last
-//    workgroup of the split (agent-scope counter, reset by that workgroup)
-//    merges them by log-sum-exp.
+//    the B operand;
+//  * blocks that need no mask (all keys valid and below the first row's
+//    causal limit) skip the masking step;
+//  * a chunked (split) tile writes fp32 partial states; the last workgroup of
+//    the split (agent-scope counter, reset by that workgroup) merges them by
+//    log-sum-exp.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -41,13 +53,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
+constexpr int kThreads = 256;
 constexpr int kBlockKeys = 64;
-constexpr int kKStride = 136;  // 16-bit elements per K row in LDS (128 dims + 8 pad)
-constexpr int kVStride = 68;   // 16-bit elements per V^T row in LDS (64 keys + 4 pad)
+constexpr int kKStride = 136;  // 16-bit elements per K slot row in LDS (128 dims + 8 pad)
 constexpr int kKElems = kBlockKeys * kKStride;
-constexpr int kVElems = 128 * kVStride;
+constexpr int kVElems = 128 * kBlockKeys;  // V^T: 128 dim rows x 64 slots (swizzled)
 constexpr int kBufElems = kKElems + kVElems;
-constexpr int kCoherent = 16;  // cache policy sc1: device-coherent access
+constexpr int kCoherent = 16;          // cache policy sc1: device-coherent access
+constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
 
 template <int DT>
 struct Mfma;
@@ -70,31 +83,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p)
   return __builtin_amdgcn_make_buffer_rsrc((void*)p.part_o, 0, 0x7fffffff, 0x00020000);
 }
 
-// One thread's share of a K/V block: tasks of 4 consecutive keys x 8 dims.
-template <int TPT>
-struct Stage {
-  u32x4 k[TPT][4];
-  u32x4 v[TPT][4];
-};
+// 8-byte unit (4 slots) swizzle of V^T row d; depends on d mod 32 only, so a
+// lane's operand reads for the 4 dim tiles differ by immediate offsets. With
+// x = d mod 32 it is 4 (x / 8) ^ (x mod 4) ^ 8 ((x / 4) mod 2): the 16 rows
+// read together (x = jq) get distinct units, and so do the 16 stores issued
+// together (4 rows 8 apart x 4 token rows).
+__device__ __forceinline__ int vswz(int d) { return ((d >> 1) & 12) ^ (d & 3) ^ ((d & 4) << 1); }
 
-template <int G>
-struct Geo {
-  static constexpr int kThreads = 64 * G;
-  static constexpr int kTasks = (kBlockKeys / 4) * (128 / 8);  // 256
-  static constexpr int kTPT = kTasks >= kThreads ? kTasks / kThreads : 1;
-};
+// Key (0..63 within the block) held in register r of score tile kt by a lane
+// of half h: slot 32 kt + 8 (r / 4) + 4 h + r % 4, key = slot / 4 + 16 (slot % 4).
+__device__ __forceinline__ constexpr int reg_key(int kt, int r, int h) {
+  return 8 * kt + 2 * (r >> 2) + h + 16 * (r & 3);
+}
 
 template <int DT, int G>
-__global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
-  using GE = Geo<G>;
-  constexpr int TPT = GE::kTPT;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void append_kernel(AttnParams p) {
+  constexpr int PT = 128 / G;  // query positions per tile
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBufElems];
   __shared__ int s_flag;
 
   const int tile_id = blockIdx.x;
   if (tile_id >= p.header[0]) return;
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // query head within the group
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int jq = lane & 31, h = lane >> 5;
 
@@ -118,17 +130,19 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
   const int key1 = min(__builtin_amdgcn_readlane(tv, 5), kv_len);
   const int rows = q1 - q0;
   const int Hq = p.num_qo_heads;
-  const int head = hk * G + wave;
 
-  // this lane's query column: row q0 + jq, absolute position qpos
-  const bool qvalid = jq < rows;
-  const int qpos = p.causal ? kv_len - qo_len + (q0 + jq - qo_beg) : 0x7fffffff;
+  // this lane's query column: head hk*G + g, row q0 + pos
+  const int col = 32 * wave + jq;
+  const int g = col / PT, pos = col % PT;
+  const int head = hk * G + g;
+  const bool qvalid = pos < rows;
   const int qpos_min = p.causal ? kv_len - qo_len + (q0 - qo_beg) : 0x7fffffff;
+  const int qpos = p.causal ? qpos_min + pos : 0x7fffffff;
 
   // Q^T operand: 8 blocks of 16 dims, this lane supplies dims 16 kb + 8 h .. +8
   u32x4 qf[8];
   {
-    const uint16_t* qp = p.q + ((int64_t)(q0 + jq) * Hq + head) * 128 + 8 * h;
+    const uint16_t* qp = p.q + ((int64_t)(q0 + pos) * Hq + head) * 128 + 8 * h;
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb)
       qf[kb] = qvalid ? *reinterpret_cast<const u32x4*>(qp + 16 * kb) : u32x4{0, 0, 0, 0};
@@ -143,85 +157,64 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
   const float scale = p.scale_log2;
 
   const int nblocks = key1 > key0 ? (key1 - key0 + kBlockKeys - 1) / kBlockKeys : 0;
-  const int first_page = key0 >> 4;
+  const int first_page = key0 >> 4;  // chunks start on a page boundary
 
-  // --- K/V staging ---------------------------------------------------------
-  // task tk: key group kg = tk >> 4 (keys 4kg..4kg+3), dim group dg = tk & 15
-  auto page_of = [&](int blk, int tk) -> int {
-    const int pg = first_page + blk * (kBlockKeys / 16) + ((tk >> 4) >> 2);
-    return pg < npages_req ? p.kv_indices[pbeg + pg] : 0;
+  // --- K/V staging: thread = (token row tr of each of the 4 pages, dims 8 dg..) --
+  // tid bits [1:0] and [5:4] give dg, bits [3:2] and [7:6] give tr: a wave
+  // reads 4 whole token rows per load, and 16 lanes that store together cover
+  // 4 dg x 4 tr (conflict-free V^T stores under vswz).
+  const int dg = (tid & 3) | ((tid >> 2) & 12), tr = ((tid >> 2) & 3) | ((tid >> 4) & 12);
+  const uint32_t row_bytes = (uint32_t)p.token_stride * 2u;
+  const uint32_t ld_off = (uint32_t)tr * row_bytes + 16u * dg;
+  const int64_t head_off = (int64_t)hk * p.head_stride;
+  u32x4 stk[4], stv[4];
+  int pid[4];
+  // page ids of a block: lanes 0..3 load them, then every lane takes them as
+  // wave-uniform values (so the buffer resources below stay scalar)
+  auto load_pids = [&](int blk) {
+    const int pg = first_page + blk * 4 + (lane & 3);
+    const int v = pg < npages_req ? p.kv_indices[pbeg + pg] : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pid[i] = __builtin_amdgcn_readlane(v, i);
   };
-  auto fetch = [&](Stage<TPT>& st, int blk, const int (&pid)[TPT]) {
+  auto fetch = [&](int blk) {
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int tk = tid + i * GE::kThreads;
-      const bool active = tk < GE::kTasks;
-      const int kg = (tk >> 4) & 15, dg = tk & 15;
-      const int kbase = key0 + blk * kBlockKeys + 4 * kg;
-      const int64_t pbase = (int64_t)pid[i] * p.page_stride + (int64_t)hk * p.head_stride + 8 * dg;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = kbase + kk;
-        const int64_t off = pbase + (int64_t)(key & 15) * p.token_stride;
-        if (active && key < key1) {
-          st.k[i][kk] = *reinterpret_cast<const u32x4*>(p.k + off);
-          st.v[i][kk] = *reinterpret_cast<const u32x4*>(p.v + off);
-        } else {
-          st.k[i][kk] = u32x4{0, 0, 0, 0};
-          st.v[i][kk] = u32x4{0, 0, 0, 0};
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int kstart = key0 + blk * kBlockKeys + 16 * i;
+      const int nbytes =
+          __builtin_amdgcn_readfirstlane(min(max(key1 - kstart, 0), 16) * (int)row_bytes);
+      const int64_t base = (int64_t)pid[i] * p.page_stride + head_off;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + base), 0, nbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + base), 0, nbytes, 0x00020000);
+      stk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ld_off, 0, 0);
+      stv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ld_off, 0, 0);
     }
   };
-  auto store = [&](const Stage<TPT>& st, int buf) {
+  auto store = [&](int buf) {
     uint16_t* sk = smem + buf * kBufElems;
     uint16_t* sv = sk + kKElems;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int tk = tid + i * GE::kThreads;
-      if (tk >= GE::kTasks) continue;
-      const int kg = (tk >> 4) & 15, dg = tk & 15;
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(sk + (4 * tr + i) * kKStride + 8 * dg) = stk[i];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        *reinterpret_cast<u32x4*>(sk + (4 * kg + kk) * kKStride + 8 * dg) = st.k[i][kk];
-      // transpose 4 keys x 8 dims -> 8 dims x 4 keys
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = st.v[i][0][w], a1 = st.v[i][1][w], a2 = st.v[i][2][w], a3 = st.v[i][3][w];
-        const u32x2 lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                          __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-        const u32x2 hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                          __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-        const int d = 8 * dg + 2 * w;
-        *reinterpret_cast<u32x2*>(sv + d * kVStride + 4 * kg) = lo;
-        *reinterpret_cast<u32x2*>(sv + (d + 1) * kVStride + 4 * kg) = hi;
-      }
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = stv[0][w], a1 = stv[1][w], a2 = stv[2][w], a3 = stv[3][w];
+      const u32x2 lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                        __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                        __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+      const int d = 8 * dg + 2 * w;
+      *reinterpret_cast<u32x2*>(sv + d * kBlockKeys + 4 * (tr ^ vswz(d))) = lo;
+      *reinterpret_cast<u32x2*>(sv + (d + 1) * kBlockKeys + 4 * (tr ^ vswz(d + 1))) = hi;
     }
   };
 
-  Stage<TPT> st;
-  int pid_cur[TPT], pid_next[TPT];
-  if (nblocks > 0) {
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) pid_cur[i] = page_of(0, tid + i * GE::kThreads);
-    fetch(st, 0, pid_cur);
-    store(st, 0);
-  }
-  __syncthreads();
-
-  for (int blk = 0; blk < nblocks; ++blk) {
-    const int buf = blk & 1;
-    const bool more = blk + 1 < nblocks;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) pid_next[i] = page_of(blk + 1, tid + i * GE::kThreads);
-      fetch(st, blk + 1, pid_next);
-    }
+  // one block of 64 keys from LDS buffer buf
+  auto block = [&](int buf, int blk, bool need_mask) {
     const uint16_t* sk = smem + buf * kBufElems;
     const uint16_t* sv = sk + kKElems;
-    const int kb0 = key0 + blk * kBlockKeys;
-
-    // S^T = K Q^T for two tiles of 32 keys
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -232,43 +225,46 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
       for (int kb = 0; kb < 8; ++kb)
         s[kt] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(krow + 16 * kb), qf[kb], s[kt]);
     }
-    // scale, mask, block max: register r of tile kt holds key 32 kt + 8 (r/4) + 4 h + r%4
-    const bool need_mask = kb0 + kBlockKeys > key1 || kb0 + kBlockKeys - 1 > qpos_min;
+    if (need_mask) {  // wave-uniform
+      const int kb0 = key0 + blk * kBlockKeys;
+      const int lim = min(key1 - 1, qpos) - kb0;  // last visible key of this column, in-block
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kt][r] = reg_key(kt, r, h) > lim ? kNegInf : s[kt][r];
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[kt][r] * scale;
-        if (need_mask) {
-          const int key = kb0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= key1 || key > qpos) x = kNegInf;
-        }
-        s[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = fmaxf(mx, xor_shfl(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float ms = mn == kNegInf ? 0.f : mn;
-    const float alpha = fast_exp2(m - ms);
+    const float mxs = mx * scale;
+    const bool need = mxs > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m - mxs) : 1.f;
+      m = need ? mxs : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float ms = m == kNegInf ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(s[kt][r] - ms);
+        const float e = fast_exp2(__builtin_fmaf(s[kt][r], scale, -ms));
         s[kt][r] = e;
         rs += e;
       }
     rs += xor_shfl(rs, 32);
-    l = l * alpha + rs;
-    m = mn;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    l += rs;
 
-    // O^T += V^T P^T over 4 key blocks of 16 (keys permuted alike in both operands)
+    // O^T += V^T P^T over 4 slot groups of 16
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -277,32 +273,49 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pb[e] = Elt<DT>::pack(s[kt][8 * kh + 2 * e], s[kt][8 * kh + 2 * e + 1]);
-        const int kofs = 32 * kt + 16 * kh + 4 * h;
+        const int u0 = 8 * kt + 4 * kh + h;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const uint16_t* vrow = sv + (32 * db + jq) * kVStride + kofs;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+          const int d = 32 * db + jq;
+          const uint16_t* vrow = sv + d * kBlockKeys;
+          const int sw = vswz(d);
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 4 * (u0 ^ sw));
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 4 * ((u0 + 2) ^ sw));
           o[db] = Mfma<DT>::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
         }
       }
+  };
 
+  if (nblocks > 0) {
+    load_pids(0);
+    fetch(0);
+    store(0);
+    if (nblocks > 1) load_pids(1);
+  }
+  __syncthreads();
+
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const int buf = blk & 1;
+    const bool more = blk + 1 < nblocks;
     if (more) {
-      store(st, buf ^ 1);
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) pid_cur[i] = pid_next[i];
+      fetch(blk + 1);
+      if (blk + 2 < nblocks) load_pids(blk + 2);
     }
+    const int kb0 = key0 + blk * kBlockKeys;
+    const bool need_mask = kb0 + kBlockKeys > key1 || kb0 + kBlockKeys - 1 > qpos_min;
+    block(buf, blk, need_mask);
+    if (more) store(buf ^ 1);
     __syncthreads();
   }
 
   // --- epilogue --------------------------------------------------------------
-  // register r of o[db] holds dim 32 db + 8 (r/4) + 4 h + r%4 of query jq
+  // register r of o[db] holds dim 32 db + 8 (r/4) + 4 h + r%4 of this column
   const bool live = l > 0.f;
   const float inv = live ? 1.f / l : 0.f;
   const float lse2 = live ? m + fast_log2(l) : kNegInf;
   if (slot0 < 0) {
     if (qvalid) {
-      uint16_t* op = p.out + ((int64_t)(q0 + jq) * Hq + head) * 128;
+      uint16_t* op = p.out + ((int64_t)(q0 + pos) * Hq + head) * 128;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -311,15 +324,15 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
                            Elt<DT>::pack(o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv)};
           *reinterpret_cast<u32x2*>(op + 32 * db + 8 * rg + 4 * h) = w;
         }
-      if (h == 0 && p.lse) p.lse[(int64_t)(q0 + jq) * Hq + head] = lse2 * kLn2;
+      if (h == 0 && p.lse) p.lse[(int64_t)(q0 + pos) * Hq + head] = lse2 * kLn2;
     }
     return;
   }
 
-  // split tile: publish the partial state of every row with device-coherent stores
+  // split tile: publish the partial state of every column with device-coherent stores
   const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
   if (qvalid) {
-    const int64_t sh = (int64_t)(slot0 + jq) * G + wave;
+    const int64_t sh = (int64_t)(slot0 + pos) * G + g;
     const uint32_t ob = (uint32_t)sh * 512u;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -349,14 +362,14 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
   __syncthreads();
   if (!s_flag || !qvalid) return;
 
-  // last workgroup of the split: merge the chunks of every row; lane (h, jq)
-  // owns dims 64 h .. 64 h + 63 of row q0 + jq
+  // last workgroup of the split: merge the chunks of every column; lane (h, jq)
+  // owns dims 64 h .. 64 h + 63 of its column
   float acc[64];
 #pragma unroll
   for (int i = 0; i < 64; ++i) acc[i] = 0.f;
   float gm = kNegInf, gl = 0.f;
   for (int c = 0; c < nchunk; ++c) {
-    const int64_t sh = (int64_t)(base + c * rows + jq) * G + wave;
+    const int64_t sh = (int64_t)(base + c * rows + pos) * G + g;
     const float s2 = __hip_atomic_load(p.part_lse + sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t ob = (uint32_t)sh * 512u + 256u * h;
     u32x4 raw[16];
@@ -373,7 +386,7 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
   }
   const bool glive = gl > 0.f;
   const float ginv = glive ? 1.f / gl : 0.f;
-  uint16_t* op = p.out + ((int64_t)(q0 + jq) * Hq + head) * 128 + 64 * h;
+  uint16_t* op = p.out + ((int64_t)(q0 + pos) * Hq + head) * 128 + 64 * h;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     u32x4 w;
@@ -382,16 +395,16 @@ __global__ __launch_bounds__(64 * G) void append_kernel(AttnParams p) {
     *reinterpret_cast<u32x4*>(op + 8 * i) = w;
   }
   if (h == 0 && p.lse)
-    p.lse[(int64_t)(q0 + jq) * Hq + head] = glive ? (gm + fast_log2(gl)) * kLn2 : kNegInf;
+    p.lse[(int64_t)(q0 + pos) * Hq + head] = glive ? (gm + fast_log2(gl)) * kLn2 : kNegInf;
 }
 
 template <int DT>
 hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: hipLaunchKernelGGL((append_kernel<DT, 1>), dim3(grid), dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((append_kernel<DT, 2>), dim3(grid), dim3(128), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((append_kernel<DT, 4>), dim3(grid), dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((append_kernel<DT, 8>), dim3(grid), dim3(512), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((append_kernel<DT, 1>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((append_kernel<DT, 2>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((append_kernel<DT, 4>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((append_kernel<DT, 8>), dim3(grid), dim3(kThreads), 0, s, p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

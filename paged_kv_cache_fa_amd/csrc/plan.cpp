@@ -85,9 +85,11 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
   if (!g.num_cu) g.num_cu = 256;
   if (!g.tiles_per_cu) g.tiles_per_cu = app ? 2 : 4;
   if (!g.min_chunk_pages) g.min_chunk_pages = 1;
-  g.qo_tile = app ? (g.qo_tile ? g.qo_tile : 32) : 1;
-  if (app && g.qo_tile != 32) {
-    set_error("append kernels are built for qo_tile 32");
+  // an append tile holds 128 query columns: the G heads x 128 / G positions
+  g.qo_tile = app ? (g.qo_tile ? g.qo_tile : 128 / G) : 1;
+  if (app && g.qo_tile > 128 / G) {
+    set_error("qo_tile %d exceeds the %d query positions of an append tile for group %d",
+              g.qo_tile, 128 / G, G);
     return FA_ERR_UNSUPPORTED;
   }
   const int64_t target = (int64_t)g.num_cu * g.tiles_per_cu;

@@ -81,7 +81,8 @@ def test_plan_default_knobs_match_the_spec_defaults():
         qo = np.arange(mb + 1, dtype=np.int32) if mode == "append" else None
         p.plan(_indptr(lens), np.asarray(lens, np.int32), qo, False)
         r = p.info().resolved
-        d = default_knobs(hkv, mb, mq, mode == "append")
+        hq = 8 * hkv if hkv < 8 else 32
+        d = default_knobs(hkv, mb, mq, mode == "append", group=hq // hkv)
         assert (r.num_cu, r.tiles_per_cu, r.min_chunk_pages, r.qo_tile, r.max_tiles,
                 r.max_partials, r.max_merge) == tuple(d[k] for k in (
                     "num_cu", "tiles_per_cu", "min_chunk_pages", "qo_tile", "max_tiles",

@@ -162,7 +162,7 @@ def test_random_geometries():
             ql = np.minimum(rng.integers(0, 70, size=B), lens)
             qo = np.concatenate([[0], np.cumsum(ql)]).astype(np.int64)
             causal = bool(rng.integers(0, 2))
-            qt = int(rng.choice([8, 16, 32]))
+            qt = min(int(rng.choice([8, 16, 32])), 128 // G)
             p = plan_spec(_indptr(lens), lens, B, G * Hkv, Hkv, 128, 16, max_batch=max(B, 1),
                           qo_indptr=qo, causal=causal, max_qo_tokens=max(int(qo[-1]), 1),
                           qo_tile=qt, **knobs)
