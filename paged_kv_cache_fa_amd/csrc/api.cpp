@@ -188,10 +188,25 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
     pl->zeroed_bytes = cbytes;
   }
   const size_t bytes = pl->lay.tiles + (size_t)pl->num_tiles * kTileInts * 4;
-  e = hipMemcpyAsync(dev_ws, host_ws, bytes, hipMemcpyHostToDevice, s);
+  // Pinned host workspaces are read by a copy kernel on the stream; pageable
+  // ones go through hipMemcpyAsync.
+  if (pl->upload_host != host_ws) {
+    pl->upload_host = host_ws;
+    pl->upload_src = nullptr;
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, host_ws) == hipSuccess && attr.type == hipMemoryTypeHost &&
+        attr.devicePointer && (reinterpret_cast<uintptr_t>(attr.devicePointer) & 15) == 0)
+      pl->upload_src = attr.devicePointer;
+    (void)hipGetLastError();  // a pageable pointer leaves an error behind; drop it
+  }
+  if (pl->upload_src)
+    e = launch_upload(static_cast<uint32_t*>(dev_ws), static_cast<const uint32_t*>(pl->upload_src),
+                      (int64_t)(bytes / 4), s);
+  else
+    e = hipMemcpyAsync(dev_ws, host_ws, bytes, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) {
     pl->planned = 0;
-    return hip_fail(e, "hipMemcpyAsync (plan upload)");
+    return hip_fail(e, "plan upload");
   }
   if (!pl->upload_event) {
     hipEvent_t ev;

@@ -26,8 +26,9 @@
 //    thread's 4 rows form 4 consecutive slots: V is stored transposed
 //    (dim-major, 4 slots per 8-byte store) without any exchange. The
 //    contraction over keys is order-free, and the mask maps slots back to
-//    keys. V^T rows are XOR-swizzled in 8-byte units so that both the
-//    transposing stores and the MFMA operand reads hit distinct banks;
+//    keys. Each lane's PV operand is one 16-byte LDS read, and V^T rows are
+//    XOR-swizzled so that both the transposing stores and the operand reads
+//    hit distinct banks;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: a lane owns one query column and 16 of
 //    every 32 slots, so the online-softmax max / sum need one exchange
@@ -83,17 +84,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p)
   return __builtin_amdgcn_make_buffer_rsrc((void*)p.part_o, 0, 0x7fffffff, 0x00020000);
 }
 
-// 8-byte unit (4 slots) swizzle of V^T row d; depends on d mod 32 only, so a
-// lane's operand reads for the 4 dim tiles differ by immediate offsets. With
-// x = d mod 32 it is 4 (x / 8) ^ (x mod 4) ^ 8 ((x / 4) mod 2): the 16 rows
-// read together (x = jq) get distinct units, and so do the 16 stores issued
-// together (4 rows 8 apart x 4 token rows).
-__device__ __forceinline__ int vswz(int d) { return ((d >> 1) & 12) ^ (d & 3) ^ ((d & 4) << 1); }
+// V^T layout. Row d holds the 64 slots of dim d as 8 units of 16 bytes. The
+// MFMA A operand of a lane of half h for slot tile kt, group kh is the 8
+// slots {32 kt + 16 kh + 4 h + e, 32 kt + 16 kh + 8 + 4 h + e : e < 4}, i.e.
+// the 4-slot groups tr and tr + 2 (tr = 8 kt + 4 kh + h): they share the
+// 16-byte unit 4 kt + 2 kh + h (first and second half). Units are XOR-swizzled
+// with vswz(d), which depends on d mod 32 only (the 4 dim tiles of a lane
+// differ by immediate offsets); the 8 rows read together (consecutive d) get
+// distinct units, and so do the 16 transposing 8-byte stores issued together.
+__device__ __forceinline__ int vswz(int d) { return (((d >> 3) & 3) << 1) ^ (d & 7); }
+// Byte offset inside row d of 4-slot group tr (slots 4 tr .. 4 tr + 3).
+__device__ __forceinline__ int vgroup_off(int tr, int d) {
+  return 16 * ((2 * (tr >> 2) + (tr & 1)) ^ vswz(d)) + 8 * ((tr >> 1) & 1);
+}
 
 // Key (0..63 within the block) held in register r of score tile kt by a lane
 // of half h: slot 32 kt + 8 (r / 4) + 4 h + r % 4, key = slot / 4 + 16 (slot % 4).
 __device__ __forceinline__ constexpr int reg_key(int kt, int r, int h) {
   return 8 * kt + 2 * (r >> 2) + h + 16 * (r & 3);
+}
+
+// Max / sum of a value over the lane pair (l, l ^ 32), in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int DT, int G>
@@ -153,7 +171,7 @@ void append_kernel(AttnParams p) {
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = kNegInf, l = 0.f;
+  float m = kNegInf, l = 0.f;  // per column: reference max (log2 units), this lane's sum
   const float scale = p.scale_log2;
 
   const int nblocks = key1 > key0 ? (key1 - key0 + kBlockKeys - 1) / kBlockKeys : 0;
@@ -206,23 +224,25 @@ void append_kernel(AttnParams p) {
       const u32x2 hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
                         __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
       const int d = 8 * dg + 2 * w;
-      *reinterpret_cast<u32x2*>(sv + d * kBlockKeys + 4 * (tr ^ vswz(d))) = lo;
-      *reinterpret_cast<u32x2*>(sv + (d + 1) * kBlockKeys + 4 * (tr ^ vswz(d + 1))) = hi;
+      char* sv8 = reinterpret_cast<char*>(sv);
+      *reinterpret_cast<u32x2*>(sv8 + d * 2 * kBlockKeys + vgroup_off(tr, d)) = lo;
+      *reinterpret_cast<u32x2*>(sv8 + (d + 1) * 2 * kBlockKeys + vgroup_off(tr, d + 1)) = hi;
     }
   };
 
   // one block of 64 keys from LDS buffer buf
+  // one block of 64 keys from LDS buffer buf, processed as two halves of 32
+  // slots: the softmax of one half overlaps the MFMAs of the other
   auto block = [&](int buf, int blk, bool need_mask) {
     const uint16_t* sk = smem + buf * kBufElems;
     const uint16_t* sv = sk + kKElems;
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
       const uint16_t* krow = sk + (32 * kt + jq) * kKStride + 8 * h;
+      s[kt] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(krow), qf[0], f32x16{});
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
+      for (int kb = 1; kb < 8; ++kb)
         s[kt] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(krow + 16 * kb), qf[kb], s[kt]);
     }
     if (need_mask) {  // wave-uniform
@@ -234,56 +254,44 @@ void append_kernel(AttnParams p) {
         for (int r = 0; r < 16; ++r)
           s[kt][r] = reg_key(kt, r, h) > lim ? kNegInf : s[kt][r];
     }
-    float mx = kNegInf;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, xor_shfl(mx, 32));
-    const float mxs = mx * scale;
-    const bool need = mxs > m + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m - mxs) : 1.f;
-      m = need ? mxs : m;
-      l *= alpha;
+      mx = pair_max(mx);
+      const float mxs = mx * scale;
+      const bool need = mxs > m + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? fast_exp2(m - mxs) : 1.f;
+        m = need ? mxs : m;
+        l *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    const float ms = m == kNegInf ? 0.f : m;
-    float rs = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(s[kt][r], scale, -ms));
-        s[kt][r] = e;
-        rs += e;
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
-    rs += xor_shfl(rs, 32);
-    l += rs;
-
-    // O^T += V^T P^T over 4 slot groups of 16
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      const float ms = m == kNegInf ? 0.f : m;
+      // O^T += V^T P^T over the half's 2 slot groups of 16 (the row sum is
+      // kept in fp32: the LSE must not carry the operand rounding)
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         u32x4 pb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pb[e] = Elt<DT>::pack(s[kt][8 * kh + 2 * e], s[kt][8 * kh + 2 * e + 1]);
-        const int u0 = 8 * kt + 4 * kh + h;
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * kh + 2 * e], scale, -ms));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * kh + 2 * e + 1], scale, -ms));
+          l += p0 + p1;
+          pb[e] = Elt<DT>::pack(p0, p1);
+        }
+        const int unit = (4 * kt + 2 * kh + h) ^ vswz(jq);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const int d = 32 * db + jq;
-          const uint16_t* vrow = sv + d * kBlockKeys;
-          const int sw = vswz(d);
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 4 * (u0 ^ sw));
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 4 * ((u0 + 2) ^ sw));
-          o[db] = Mfma<DT>::run(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[db]);
+          const uint16_t* vp = sv + (32 * db + jq) * kBlockKeys + 8 * unit;
+          o[db] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(vp), pb, o[db]);
         }
       }
+    }
   };
 
   if (nblocks > 0) {
@@ -309,7 +317,9 @@ void append_kernel(AttnParams p) {
   }
 
   // --- epilogue --------------------------------------------------------------
-  // register r of o[db] holds dim 32 db + 8 (r/4) + 4 h + r%4 of this column
+  // register r of o[db] holds dim 32 db + 8 (r/4) + 4 h + r%4 of this column;
+  // each lane summed the probabilities of its own slots
+  l = pair_sum(l);
   const bool live = l > 0.f;
   const float inv = live ? 1.f / l : 0.f;
   const float lse2 = live ? m + fast_log2(l) : kNegInf;

@@ -34,6 +34,9 @@ struct AttnParams {
 
 hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s);
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
+// Copy n_words 32-bit words from device-visible pinned host memory into device
+// memory with a small kernel (both 16-byte aligned).
+hipError_t launch_upload(uint32_t* dst, const uint32_t* src, int64_t n_words, hipStream_t s);
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
                               void* vo, float* so, int64_t n, int heads, int head_dim, int dtype,
                               hipStream_t s);

@@ -42,6 +42,8 @@ struct PlanImpl {
   void* upload_event;  // hipEvent_t recorded after the copy out of host_ws
   void* zeroed_ws;     // device workspace whose counters were cleared
   size_t zeroed_bytes;
+  void* upload_host;   // host workspace whose device mapping was looked up
+  void* upload_src;    // its device-visible address (pinned memory), or null
 };
 static_assert(sizeof(PlanImpl) <= sizeof(fa_plan_t), "plan object too large");
 
