@@ -166,8 +166,9 @@ class AppendBench(Timed):
 
 
 class CascadeBench(Timed):
-    """Prefix pass (non-causal append over the shared prefix) + suffix decode +
-    merge_state; the timed kernel is the prefix pass."""
+    """One fa_cascade call: the prefix pass (non-causal append over the shared
+    prefix, MFMA) on a side stream beside the suffix decode (HBM), then
+    merge_state; the kernel time is the whole call on the main stream."""
 
     def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30):
         import torch
@@ -191,6 +192,7 @@ class CascadeBench(Timed):
         self.op, self.lp = mk()
         self.os, self.ls = mk()
         self.out, self.lse = mk()
+        self.side = torch.cuda.Stream()  # the prefix pass runs here, beside the suffix decode
 
     def step(self, i: int, ev=None):
         wl, fa = self.wl, self.fa
@@ -200,13 +202,12 @@ class CascadeBench(Timed):
         self.splan.plan(wl.kv_indptr, wl.kv_lens)
         if ev is not None:
             ev[0].record()
-        fa.append(self.pplan, self.q, self.qo, k, v, *self.strides, self.p_indices, self.p_indptr,
-                  self.p_last, out=self.op, lse=self.lp)
+        fa.cascade(self.pplan, self.splan, self.q, k, v, *self.strides, self.qo, self.p_indices,
+                   self.p_indptr, self.p_last, self.kv_indices, self.kv_indptr, self.last,
+                   states=(self.op, self.lp, self.os, self.ls), out=self.out, lse=self.lse,
+                   side_stream=self.side)
         if ev is not None:
             ev[1].record()
-        fa.decode(self.splan, self.q, k, v, *self.strides, self.kv_indices, self.kv_indptr,
-                  self.last, out=self.os, lse=self.ls)
-        fa.merge_state(self.op, self.lp, self.os, self.ls, self.out, self.lse)
 
 
 def stored_traffic(kernel_src: str):
@@ -342,7 +343,7 @@ def main():
                            "GB/s": round(n4 / (s4 * 1e-3) / 1e9, 2),
                            "pct_of_hbm_peak": round(100 * n4 / (s4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                            "tokens_per_s": round(256 / (s4 * 1e-3), 1),
-                           "ms_per_step": round(s4, 5), "prefix_pass_ms": round(k4, 5),
+                           "ms_per_step": round(s4, 5), "kernel_ms": round(k4, 5),
                            "algorithmic_bytes": n4}
         del b4, w4
         torch.cuda.empty_cache()

@@ -153,7 +153,7 @@ fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t*
                         const int32_t** merge_h, int32_t* num_merge,
                         const int32_t** worker_ptr_h, int32_t* num_workers);
 
-/* Release the HIP event a plan keeps for reusing its host workspace. */
+/* Release the HIP events a plan keeps (host workspace reuse, cascade fork/join). */
 fa_status fa_plan_destroy(fa_plan_t* plan);
 
 /* Batched decode over the paged KV cache ([DeepDive] "Snippet One", batch
@@ -173,8 +173,9 @@ fa_status fa_plan_destroy(fa_plan_t* plan);
  *  out          device [batch, num_qo_heads, head_dim], geometry dtype.
  *  lse          device fp32 [batch, num_qo_heads] or NULL.
  * A request with no keys gets out = 0 and lse = -inf. Requests whose keys were
- * split by the plan are combined with the log-sum-exp merge in a second kernel
- * on the same stream. Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
+ * split by the plan are combined with the log-sum-exp merge inside the same
+ * kernel (the last piece to finish merges). One kernel launch on `stream`.
+ * Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
 fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
                     const void* v_pages, int64_t page_stride, int64_t token_stride,
                     int64_t head_stride, const int32_t* kv_indices_d, const int32_t* kv_indptr_d,
@@ -195,6 +196,33 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
                     int64_t token_stride, int64_t head_stride, const int32_t* kv_indices_d,
                     const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
                     void* out, float* lse, void* stream);
+
+/* Cascade attention over one shared prefix ([Guide] "Cascade attention for
+ * shared prefixes"; [DeepDive] "Why This Design Works": the shared prefix is
+ * stored once and read once): for every request b,
+ *   out[b] = merge_state(attention(q[b], prefix), attention(q[b], suffix of b)).
+ *  prefix_plan  an append plan of ONE request whose rows are the batch's
+ *               queries (qo_indptr {0, batch}), non-causal, over the prefix pages.
+ *  suffix_plan  a decode plan over the per-request suffix pages.
+ *  prefix_qo_indptr_d  device int32 {0, batch}.
+ *  prefix_indices_d / prefix_indptr_d / prefix_last_page_len_d  the prefix's
+ *               page table (one request); kv_* the suffix page tables.
+ *  prefix_out, suffix_out  device [batch, num_qo_heads, head_dim] scratch in
+ *               the q dtype; prefix_lse, suffix_lse device fp32 [batch, num_qo_heads].
+ *  out / lse    device [batch, num_qo_heads, head_dim] / fp32 (lse may be NULL).
+ * The suffix decode runs on `stream` and the prefix pass on `side_stream`
+ * concurrently (fork/join with events of the suffix plan; capturable), then
+ * merge_state on `stream`. side_stream NULL or equal to stream runs the three
+ * kernels in order on `stream`. Other arguments as fa_decode. Errors:
+ * FA_ERR_INVALID, FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
+fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan, const void* q,
+                     const void* k_pages, const void* v_pages, int64_t page_stride,
+                     int64_t token_stride, int64_t head_stride, const int32_t* prefix_qo_indptr_d,
+                     const int32_t* prefix_indices_d, const int32_t* prefix_indptr_d,
+                     const int32_t* prefix_last_page_len_d, const int32_t* kv_indices_d,
+                     const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
+                     void* prefix_out, float* prefix_lse, void* suffix_out, float* suffix_lse,
+                     void* out, float* lse, void* stream, void* side_stream);
 
 /* Merge two attention states computed over disjoint key sets ([Guide]
  * "Cascade attention for shared prefixes"):

@@ -42,9 +42,17 @@ Append — uniform chunks:
    ``(q0, kv_head, base, C)``.
 4. Tiles ``[b, kv_head, q0, q1, key0, key1, slot0, C]`` with
    ``slot0 = base + c*rows`` (-1 when ``C == 1``) are emitted in order
-   (request, q tile, kv head, chunk) and stably sorted by descending cost
-   ``(key1 - key0) * (q1 - q0)``, so in-order dispatch starts the longest
-   first.
+   (request, q tile, kv head, chunk); a tile's cost is
+   ``(key1 - key0) * (q1 - q0)``.
+5. XCD bins. A *group* is one (request, kv head): all its q tiles and
+   chunks read the same keys. Groups, in descending total cost (stable on
+   ``b * num_kv_heads + kv_head``), are dealt to ``XCD_BINS`` (8) bins, each
+   to the bin with the least total cost so far (lowest bin on ties). The
+   tile list is bin 0, bin 1, ...; inside a bin, groups in dealing order and
+   each group's tiles by descending cost (stable on emission order);
+   ``worker_ptr[0..8]`` are the bin offsets. The GPU hands workgroups to
+   its 8 XCDs round-robin and workgroup i runs bin ``i mod 8``, so a group's
+   tiles run together on one XCD and share its L2.
 
 More tiles, slots or merge entries than the capacities is an error.
 """
@@ -58,6 +66,7 @@ SUPPORTED_HEAD_DIM = (128,)
 SUPPORTED_PAGE_SIZE = (16,)
 SUPPORTED_GROUP = (1, 2, 4, 8)
 MAX_PIECE_PAGES = 128
+XCD_BINS = 8
 
 
 class PlanSpecError(Exception):
@@ -216,9 +225,25 @@ def _append_plan(kv_lens, batch, Hkv, ps, qo_indptr, causal, k):
                 t0 = c * P * ps
                 t1 = min((c + 1) * P * ps, vis)
                 tiles.append((b, h, q0, q1, t0, t1, base + c * rows if C > 1 else -1, C))
-    order = sorted(range(len(tiles)),
-                   key=lambda i: -((tiles[i][5] - tiles[i][4]) * (tiles[i][3] - tiles[i][2])))
-    return [tiles[i] for i in order], merge, slots, None, P
+    cost = [(t[5] - t[4]) * (t[3] - t[2]) for t in tiles]
+    ngroups = batch * Hkv
+    gcost = [0] * ngroups
+    for t, c in zip(tiles, cost):
+        gcost[t[0] * Hkv + t[1]] += c
+    bin_of, seq_of, bcost = [0] * ngroups, [0] * ngroups, [0] * XCD_BINS
+    for n, g in enumerate(sorted(range(ngroups), key=lambda g: -gcost[g])):
+        x = min(range(XCD_BINS), key=lambda j: bcost[j])
+        bin_of[g], seq_of[g] = x, n
+        bcost[x] += gcost[g]
+    gid = [t[0] * Hkv + t[1] for t in tiles]
+    order = sorted(range(len(tiles)), key=lambda i: (bin_of[gid[i]], seq_of[gid[i]], -cost[i]))
+    counts = [0] * XCD_BINS
+    for i in order:
+        counts[bin_of[gid[i]]] += 1
+    wptr = [0]
+    for x in range(XCD_BINS):
+        wptr.append(wptr[-1] + counts[x])
+    return [tiles[i] for i in order], merge, slots, wptr, P
 
 
 def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
@@ -226,7 +251,7 @@ def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
               max_batch: int, qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
               max_qo_tokens: int = 0, **knobs) -> dict:
     """Reference plan: tiles ``int32 [n, 8]``, merge ``int32 [m, 4]``, worker_ptr
-    ``int32 [S+1]`` (decode) and scalars."""
+    ``int32 [S+1]`` (decode: worker waves; append: the 8 XCD bins) and scalars."""
     kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     is_append = qo_indptr is not None

@@ -132,7 +132,8 @@ class Plan:
 
     def tiles(self, with_workers: bool = False):
         """Host copies of the current plan: (tiles int32 [n, 8], merge int32 [m, 4])
-        and, with ``with_workers``, worker_ptr int32 [workers+1] (None for append)."""
+        and, with ``with_workers``, worker_ptr int32 [workers+1] (decode: worker
+        waves; append: the 8 XCD bins)."""
         tp, mp, wp = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
         nt, nm, nw = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
         check(self._lib.fa_plan_tiles(ctypes.byref(self._plan), ctypes.byref(tp),
@@ -194,6 +195,31 @@ def append(p: Plan, q, qo_indptr, k_pages, v_pages, page_stride: int, token_stri
                            _ptr(v_pages), page_stride, token_stride, head_stride,
                            _ptr(kv_indices), _ptr(kv_indptr), _ptr(last_page_len),
                            float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def cascade(prefix_plan: Plan, suffix_plan: Plan, q, k_pages, v_pages, page_stride: int,
+            token_stride: int, head_stride: int, prefix_qo_indptr, prefix_indices, prefix_indptr,
+            prefix_last_page_len, kv_indices, kv_indptr, last_page_len, sm_scale: float = 0.0,
+            states=None, out=None, lse=None, stream=None, side_stream=None):
+    """Cascade attention over one shared prefix (see fa_cascade). ``states`` is
+    (prefix_out, prefix_lse, suffix_out, suffix_lse) scratch, allocated if None;
+    ``side_stream`` (a torch stream or handle) runs the prefix pass beside the
+    suffix decode. Returns (out, lse)."""
+    torch = _torch()
+    B, H = q.shape[0], q.shape[1]
+    if states is None:
+        states = (torch.empty_like(q), torch.empty(B, H, dtype=torch.float32, device=q.device),
+                  torch.empty_like(q), torch.empty(B, H, dtype=torch.float32, device=q.device))
+    out, lse = _alloc_out(q, out, lse, B, H)
+    po, pl_, so, sl = states
+    side = None if side_stream is None else _stream(side_stream)
+    check(prefix_plan._lib.fa_cascade(
+        ctypes.byref(prefix_plan._plan), ctypes.byref(suffix_plan._plan), _ptr(q), _ptr(k_pages),
+        _ptr(v_pages), page_stride, token_stride, head_stride, _ptr(prefix_qo_indptr),
+        _ptr(prefix_indices), _ptr(prefix_indptr), _ptr(prefix_last_page_len), _ptr(kv_indices),
+        _ptr(kv_indptr), _ptr(last_page_len), float(sm_scale), _ptr(po), _ptr(pl_), _ptr(so),
+        _ptr(sl), _ptr(out), _ptr(lse), _stream(stream), side))
     return out, lse
 
 

@@ -27,7 +27,7 @@ FA_MODE_DECODE, FA_MODE_APPEND = 0, 1
 # every symbol declared in include/fa.h
 EXPORTED = [
     "fa_workspace_size", "fa_plan", "fa_plan_info", "fa_plan_tiles", "fa_plan_destroy",
-    "fa_decode", "fa_append", "fa_merge_state", "fa_merge_states", "fa_status_string",
+    "fa_decode", "fa_append", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
     "fa_last_error",
 ]
 
@@ -81,6 +81,8 @@ def load(path: str = LIB_PATH):
         "fa_plan_destroy": [PP],
         "fa_decode": [PP, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
         "fa_append": [PP, P, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
+        "fa_cascade": [PP, PP, P, P, P, I64, I64, I64, P, P, P, P, P, P, P, F32, P, P, P, P, P, P,
+                       P, P],
         "fa_merge_state": [P, P, P, P, P, P, I64, I32, I32, I32, P],
         "fa_merge_states": [P, P, I64, I32, I32, I32, I32, P, P, P],
         "fa_status_string": [I32],

@@ -16,6 +16,10 @@
 #include "plan_internal.h"
 
 namespace pkfa {
+static_assert(kAppendBins == kXcdBins, "planner bins and kernel bins differ");
+}  // namespace pkfa
+
+namespace pkfa {
 const char* last_error();
 }
 
@@ -208,14 +212,15 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
     pl->planned = 0;
     return hip_fail(e, "plan upload");
   }
-  if (!pl->upload_event) {
+  for (void** slot : {&pl->upload_event, &pl->fork_event, &pl->join_event}) {
+    if (*slot) continue;
     hipEvent_t ev;
     e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
     if (e != hipSuccess) {
       pl->planned = 0;
       return hip_fail(e, "hipEventCreateWithFlags");
     }
-    pl->upload_event = ev;
+    *slot = ev;
   }
   e = hipEventRecord(static_cast<hipEvent_t>(pl->upload_event), s);
   if (e != hipSuccess) {
@@ -269,8 +274,9 @@ fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t*
 fa_status fa_plan_destroy(fa_plan_t* plan) {
   if (!plan) return FA_OK;
   PlanImpl* pl = impl(plan);
-  if (pl->magic == kPlanMagic && pl->upload_event) {
-    hipEventDestroy(static_cast<hipEvent_t>(pl->upload_event));
+  if (pl->magic == kPlanMagic) {
+    for (void* ev : {pl->upload_event, pl->fork_event, pl->join_event})
+      if (ev) hipEventDestroy(static_cast<hipEvent_t>(ev));
   }
   memset(plan, 0, sizeof(*plan));
   return FA_OK;
@@ -320,6 +326,72 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
     return FA_ERR_UNSUPPORTED;
   }
   return e == hipSuccess ? FA_OK : hip_fail(e, "append kernel launch");
+}
+
+fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan, const void* q,
+                     const void* k_pages, const void* v_pages, int64_t page_stride,
+                     int64_t token_stride, int64_t head_stride, const int32_t* prefix_qo_indptr_d,
+                     const int32_t* prefix_indices_d, const int32_t* prefix_indptr_d,
+                     const int32_t* prefix_last_page_len_d, const int32_t* kv_indices_d,
+                     const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
+                     void* prefix_out, float* prefix_lse, void* suffix_out, float* suffix_lse,
+                     void* out, float* lse, void* stream, void* side_stream) {
+  const PlanImpl* pp = prefix_plan ? impl(prefix_plan) : nullptr;
+  const PlanImpl* sp = suffix_plan ? impl(suffix_plan) : nullptr;
+  fa_status st = check_run_args(pp, FA_MODE_APPEND, q, k_pages, v_pages, page_stride, token_stride,
+                                head_stride, prefix_indices_d, prefix_indptr_d,
+                                prefix_last_page_len_d, prefix_out);
+  if (st != FA_OK) return st;
+  st = check_run_args(sp, FA_MODE_DECODE, q, k_pages, v_pages, page_stride, token_stride,
+                      head_stride, kv_indices_d, kv_indptr_d, last_page_len_d, suffix_out);
+  if (st != FA_OK) return st;
+  const fa_geometry& gp = pp->geom;
+  const fa_geometry& gs = sp->geom;
+  if (pp->causal || pp->batch != 1 || pp->num_rows != sp->batch || gp.dtype != gs.dtype ||
+      gp.num_qo_heads != gs.num_qo_heads || gp.num_kv_heads != gs.num_kv_heads) {
+    set_error("cascade: the prefix plan must be a non-causal append of one request whose rows "
+              "are the suffix plan's requests, with the same heads and dtype");
+    return FA_ERR_INVALID;
+  }
+  if (!prefix_qo_indptr_d || !prefix_lse || !suffix_lse || !out || !aligned16(out) ||
+      !aligned16(prefix_out) || !aligned16(suffix_out)) {
+    set_error("cascade: NULL or misaligned state / output buffer");
+    return FA_ERR_INVALID;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t side = static_cast<hipStream_t>(side_stream);
+  const bool fork = side && side != s;
+  hipError_t e = hipSuccess;
+  if (fork) {
+    if (!sp->fork_event || !sp->join_event) {
+      set_error("cascade: the suffix plan was not uploaded to a device workspace");
+      return FA_ERR_NOT_PLANNED;
+    }
+    e = hipEventRecord(static_cast<hipEvent_t>(sp->fork_event), s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, static_cast<hipEvent_t>(sp->fork_event), 0);
+    if (e != hipSuccess) return hip_fail(e, "cascade fork");
+  }
+  // suffix decode (HBM-bound) first on the main stream, the shared-prefix
+  // pass (MFMA-bound) beside it
+  const int G = gs.num_qo_heads / gs.num_kv_heads;
+  const AttnParams ps = make_params(sp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
+                                    kv_indices_d, kv_indptr_d, last_page_len_d, nullptr, sm_scale,
+                                    suffix_out, suffix_lse);
+  e = launch_decode(ps, gs.dtype, G, sp->num_workers, s);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  const AttnParams pa = make_params(pp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
+                                    prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
+                                    prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
+  e = launch_append(pa, gp.dtype, G, gp.max_tiles, fork ? side : s);
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  if (fork) {
+    e = hipEventRecord(static_cast<hipEvent_t>(sp->join_event), side);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(sp->join_event), 0);
+    if (e != hipSuccess) return hip_fail(e, "cascade join");
+  }
+  e = launch_merge_state(prefix_out, prefix_lse, suffix_out, suffix_lse, out, lse, sp->batch,
+                         gs.num_qo_heads, gs.head_dim, gs.dtype, s);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "merge_state kernel launch");
 }
 
 fa_status fa_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,

@@ -11,6 +11,9 @@
 // for shared prefixes").
 //
 // MI355X design (the work is a dense contraction, so it runs on MFMA):
+//  * tiles come in 8 bins, one per XCD: the planner deals each (request, kv
+//    head) group to one bin, so the q tiles that read the same keys run side
+//    by side on one XCD and share its L2;
 //  * one 256-thread workgroup (4 waves) per tile {request, kv head, up to
 //    128/G query positions, key chunk}. The tile's 128 query columns are the
 //    G heads of the kv head's group x 128/G positions (GQA packing): every
@@ -115,14 +118,9 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int DT, int G>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void append_kernel(AttnParams p) {
+__device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, uint16_t* smem,
+                                            int& s_flag) {
   constexpr int PT = 128 / G;  // query positions per tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBufElems];
-  __shared__ int s_flag;
-
-  const int tile_id = blockIdx.x;
-  if (tile_id >= p.header[0]) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -187,11 +185,14 @@ void append_kernel(AttnParams p) {
   const int64_t head_off = (int64_t)hk * p.head_stride;
   u32x4 stk[4], stv[4];
   int pid[4];
-  // page ids of a block: lanes 0..3 load them, then every lane takes them as
-  // wave-uniform values (so the buffer resources below stay scalar)
-  auto load_pids = [&](int blk) {
-    const int pg = first_page + blk * 4 + (lane & 3);
-    const int v = pg < npages_req ? p.kv_indices[pbeg + pg] : 0;
+  // page ids of a block: lanes 0..3 load them (index clamped to the request's
+  // last page: a block past the end fetches nothing, see nbytes below), and
+  // every lane takes them as wave-uniform values (scalar buffer resources)
+  auto load_pid_vec = [&](int blk) -> int {
+    const int pg = min(first_page + blk * 4 + (lane & 3), npages_req - 1);
+    return p.kv_indices[pbeg + max(pg, 0)];
+  };
+  auto take_pids = [&](int v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pid[i] = __builtin_amdgcn_readlane(v, i);
   };
@@ -294,25 +295,28 @@ void append_kernel(AttnParams p) {
     }
   };
 
+  // Software pipeline: while block blk is computed from LDS, block blk+1 is in
+  // flight into registers and the page ids of block blk+2 are loaded (issued
+  // first, so waiting for them never waits for the K/V loads). The last
+  // iteration fetches and stages one block past the end: its buffer
+  // resources have zero size, so it reads nothing and stores zeros.
   if (nblocks > 0) {
-    load_pids(0);
+    take_pids(load_pid_vec(0));
     fetch(0);
     store(0);
-    if (nblocks > 1) load_pids(1);
+    take_pids(load_pid_vec(1));
   }
   __syncthreads();
 
   for (int blk = 0; blk < nblocks; ++blk) {
     const int buf = blk & 1;
-    const bool more = blk + 1 < nblocks;
-    if (more) {
-      fetch(blk + 1);
-      if (blk + 2 < nblocks) load_pids(blk + 2);
-    }
+    const int pv = load_pid_vec(blk + 2);
+    fetch(blk + 1);
     const int kb0 = key0 + blk * kBlockKeys;
     const bool need_mask = kb0 + kBlockKeys > key1 || kb0 + kBlockKeys - 1 > qpos_min;
     block(buf, blk, need_mask);
-    if (more) store(buf ^ 1);
+    store(buf ^ 1);
+    take_pids(pv);
     __syncthreads();
   }
 
@@ -408,6 +412,19 @@ void append_kernel(AttnParams p) {
     p.lse[(int64_t)(q0 + pos) * Hq + head] = glive ? (gm + fast_log2(gl)) * kLn2 : kNegInf;
 }
 
+// Workgroup i runs tiles of bin i mod 8 (the XCD the hardware gives it), at
+// positions i / 8, i / 8 + gridDim.x / 8, ... of the bin.
+template <int DT, int G>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void append_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBufElems];
+  __shared__ int s_flag;
+  const int x = blockIdx.x % kAppendBins, stride = gridDim.x / kAppendBins;
+  const int t1 = p.worker_ptr[x + 1];
+  for (int t = p.worker_ptr[x] + (int)blockIdx.x / kAppendBins; t < t1; t += stride)
+    append_tile<DT, G>(p, t, smem, s_flag);
+}
+
 template <int DT>
 hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
   switch (group) {
@@ -424,8 +441,9 @@ hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
 
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  return dtype == FA_BF16 ? launch_dt<FA_BF16>(p, group, max_tiles, s)
-                          : launch_dt<FA_F16>(p, group, max_tiles, s);
+  const int grid = (max_tiles + kAppendBins - 1) / kAppendBins * kAppendBins;
+  return dtype == FA_BF16 ? launch_dt<FA_BF16>(p, group, grid, s)
+                          : launch_dt<FA_F16>(p, group, grid, s);
 }
 
 }  // namespace pkfa

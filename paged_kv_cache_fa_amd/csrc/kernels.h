@@ -32,6 +32,8 @@ struct AttnParams {
   int32_t causal;
 };
 
+constexpr int kAppendBins = 8;  // append tile bins = XCDs (workgroup i runs bin i % 8)
+
 hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s);
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
 // Copy n_words 32-bit words from device-visible pinned host memory into device

@@ -123,7 +123,7 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
 Layout compute_layout(const fa_geometry& g) {
   Layout L;
   const int G = g.num_qo_heads / g.num_kv_heads;
-  L.workers = g.mode == FA_MODE_DECODE ? g.num_cu * g.tiles_per_cu : 0;
+  L.workers = g.mode == FA_MODE_DECODE ? g.num_cu * g.tiles_per_cu : kXcdBins;
   L.header = 0;
   L.merge = kHeaderInts * 4;
   L.worker_ptr = L.merge + (size_t)g.max_merge * kMergeInts * 4;
@@ -137,7 +137,8 @@ Layout compute_layout(const fa_geometry& g) {
   L.host_order = L.host_unsorted + (size_t)g.max_tiles * kTileInts * 4;
   L.host_cost = align_up(L.host_order + (size_t)g.max_tiles * 4, 8);
   L.host_units = L.host_cost + (size_t)g.max_tiles * 8;
-  L.host_bytes = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 2 * 4;
+  // per (request, kv head): 2 int32 (decode) or int64 cost + 3 int32 (append)
+  L.host_bytes = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 24;
   return L;
 }
 
@@ -246,7 +247,7 @@ fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, cons
   return FA_OK;
 }
 
-// Append: uniform chunks of P pages, LPT order.
+// Append: uniform chunks of P pages; groups dealt to XCD bins, LPT inside.
 fa_status plan_append(const fa_geometry& g, const Layout& lay, uint8_t* ws, const int32_t* kv_lens,
                       int32_t batch, const int32_t* qo_indptr, int32_t causal, int64_t* ntiles_out,
                       int64_t* nmerge_out, int64_t* slots_out, int64_t* P_out) {
@@ -312,10 +313,45 @@ fa_status plan_append(const fa_geometry& g, const Layout& lay, uint8_t* ws, cons
   if (ntiles > g.max_tiles) return capacity_error("tiles", ntiles, g.max_tiles);
   if (slots > g.max_partials) return capacity_error("partial states", slots, g.max_partials);
   if (nmerge > g.max_merge) return capacity_error("merge entries", nmerge, g.max_merge);
+  // XCD bins: deal the (request, kv head) groups, largest first, to the bin
+  // with the least cost; order tiles by (bin, group dealing order, cost desc).
+  const int64_t ngroups = (int64_t)batch * Hkv;
+  int64_t* gcost = reinterpret_cast<int64_t*>(ws + lay.host_units);
+  int32_t* gorder = reinterpret_cast<int32_t*>(gcost + ngroups);
+  int32_t* gbin = gorder + ngroups;
+  int32_t* gseq = gbin + ngroups;
+  for (int64_t i = 0; i < ngroups; ++i) {
+    gcost[i] = 0;
+    gorder[i] = (int32_t)i;
+  }
+  auto group_of = [&](int64_t t) {
+    return (int64_t)unsorted[t * kTileInts] * Hkv + unsorted[t * kTileInts + 1];
+  };
+  for (int64_t t = 0; t < ntiles; ++t) gcost[group_of(t)] += cost[t];
+  std::stable_sort(gorder, gorder + ngroups, [&](int32_t a, int32_t b) { return gcost[a] > gcost[b]; });
+  int64_t bcost[kXcdBins] = {};
+  for (int64_t n = 0; n < ngroups; ++n) {
+    int x = 0;
+    for (int j = 1; j < kXcdBins; ++j)
+      if (bcost[j] < bcost[x]) x = j;
+    gbin[gorder[n]] = x;
+    gseq[gorder[n]] = (int32_t)n;
+    bcost[x] += gcost[gorder[n]];
+  }
   for (int64_t i = 0; i < ntiles; ++i) order[i] = (int32_t)i;
-  std::stable_sort(order, order + ntiles, [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
-  for (int64_t i = 0; i < ntiles; ++i)
+  std::stable_sort(order, order + ntiles, [&](int32_t a, int32_t b) {
+    const int64_t ga = group_of(a), gb = group_of(b);
+    if (gbin[ga] != gbin[gb]) return gbin[ga] < gbin[gb];
+    if (gseq[ga] != gseq[gb]) return gseq[ga] < gseq[gb];
+    return cost[a] > cost[b];
+  });
+  int32_t* wptr = reinterpret_cast<int32_t*>(ws + lay.worker_ptr);
+  for (int x = 0; x <= kXcdBins; ++x) wptr[x] = 0;
+  for (int64_t i = 0; i < ntiles; ++i) {
     memcpy(tiles + i * kTileInts, unsorted + (int64_t)order[i] * kTileInts, kTileInts * 4);
+    ++wptr[gbin[group_of(order[i])] + 1];
+  }
+  for (int x = 0; x < kXcdBins; ++x) wptr[x + 1] += wptr[x];
   *ntiles_out = ntiles;
   *nmerge_out = nmerge;
   *slots_out = slots;

@@ -16,13 +16,15 @@ constexpr int kHeaderInts = 16;  // {num_tiles, num_merge, batch, num_rows, caus
 constexpr int kSupportedHeadDim = 128;
 constexpr int kSupportedPageSize = 16;
 constexpr int kMaxPiecePages = 128;  // decode pieces: the kernel holds 128 page ids per wave
+constexpr int kXcdBins = 8;          // append tile bins, one per XCD (workgroup i runs bin i % 8)
 
 // Byte offsets of the regions inside the host and device workspaces.
 // Upload image (same offsets in host and device workspace):
 //   header | merge [max_merge][4] | worker_ptr [workers+1] | tiles [max_tiles][8]
 // Device only: arrival counters [max_partials] (zero between calls), partial
 // lse [max_partials][G] (log2 units), partial out [max_partials][G][head_dim].
-// Host only: scratch for sorting tiles and per-unit counts.
+// Host only: scratch for sorting tiles, per-unit counts and (append) per-group
+// cost / order / bin / sequence.
 struct Layout {
   size_t header, merge, worker_ptr, tiles, upload_end;
   size_t dev_counters, dev_part_lse, dev_part_o, dev_bytes;
@@ -42,6 +44,8 @@ struct PlanImpl {
   void* upload_event;  // hipEvent_t recorded after the copy out of host_ws
   void* zeroed_ws;     // device workspace whose counters were cleared
   size_t zeroed_bytes;
+  void* fork_event;    // hipEvent_t pair for the two-stream cascade call
+  void* join_event;
   void* upload_host;   // host workspace whose device mapping was looked up
   void* upload_src;    // its device-visible address (pinned memory), or null
 };

@@ -103,9 +103,12 @@ def oracle_append(wl, rows=None):
                          wl.last_page_len, wl.page_size, causal=wl.causal, rows=rows)
 
 
-def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, **knobs):
+def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, fused=False,
+                side_stream=None, **knobs):
     """Shared-prefix pass (non-causal append of every request's query over the
-    prefix) + private-suffix decode + merge_state. Returns (out, lse, plans)."""
+    prefix) + private-suffix decode + merge_state, as three calls or as one
+    fa_cascade call (optionally with the prefix pass on ``side_stream``).
+    Returns (out, lse, plans)."""
     import torch
     wl = dw.wl
     B = wl.batch
@@ -118,6 +121,12 @@ def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, **knobs):
         suffix_plan = fa.Plan(decode_geometry(wl, **knobs.get("suffix", {})), device=dw.device)
         suffix_plan.plan(wl.kv_indptr, wl.kv_lens)
     qo = torch.tensor([0, B], dtype=torch.int32, device=dw.device)
+    if fused:
+        out, lse = fa.cascade(prefix_plan, suffix_plan, dw.q, dw.k, dw.v, *dw.strides, qo,
+                              dw.prefix_indices, dw.prefix_indptr, dw.prefix_last_page_len,
+                              dw.kv_indices, dw.kv_indptr, dw.last_page_len,
+                              side_stream=side_stream)
+        return out, lse, (prefix_plan, suffix_plan)
     o_p, l_p = fa.append(prefix_plan, dw.q, qo, dw.k, dw.v, *dw.strides, dw.prefix_indices,
                          dw.prefix_indptr, dw.prefix_last_page_len)
     o_s, l_s = fa.decode(suffix_plan, dw.q, dw.k, dw.v, *dw.strides, dw.kv_indices, dw.kv_indptr,

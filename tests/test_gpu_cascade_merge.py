@@ -105,11 +105,61 @@ def test_cascade_small():
     assert_close(to_f64(out), to_f64(lse), *direct, what="cascade vs direct")
 
 
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_cascade_call_matches_three_calls(two_streams):
+    """fa_cascade (fork/join on a side stream or serial) gives the bits of the
+    three separate calls."""
+    import torch
+    wl = make_cascade(512, [5, 16, 17, 300, 1, 64, 900], 32, 8, "bf16", 22, mode="test")
+    dw = DevWorkload(wl)
+    o3, l3, plans = run_cascade(dw, prefix={"num_cu": 8}, suffix={"num_cu": 8})
+    side = torch.cuda.Stream() if two_streams else None
+    o1, l1, _ = run_cascade(dw, *plans, fused=True, side_stream=side)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    assert_close(to_f64(o1), to_f64(l1), *oracle_cascade(wl), what="fa_cascade")
+
+
+def test_cascade_graph_capture_with_side_stream():
+    """The fork/join of fa_cascade captures into one graph; replays (with eager
+    work and synchronisation between them) reproduce the eager bits."""
+    import torch
+    import paged_kv_cache_fa_amd as fa
+    wl = make_cascade(256, [40, 3, 700], 32, 8, "bf16", 23, mode="test")
+    dw = DevWorkload(wl)
+    ref_o, ref_l, plans = run_cascade(dw, prefix={"num_cu": 8}, suffix={"num_cu": 8})
+    ref_o, ref_l = ref_o.clone(), ref_l.clone()
+    B, H = wl.batch, wl.num_qo_heads
+    qo = torch.tensor([0, B], dtype=torch.int32, device="cuda")
+    states = (torch.empty_like(dw.q), torch.empty(B, H, dtype=torch.float32, device="cuda"),
+              torch.empty_like(dw.q), torch.empty(B, H, dtype=torch.float32, device="cuda"))
+    out = torch.empty_like(dw.q)
+    lse = torch.empty(B, H, dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    cap = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        fa.cascade(plans[0], plans[1], dw.q, dw.k, dw.v, *dw.strides, qo, dw.prefix_indices,
+                   dw.prefix_indptr, dw.prefix_last_page_len, dw.kv_indices, dw.kv_indptr,
+                   dw.last_page_len, states=states, out=out, lse=lse, side_stream=side)
+    for i in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+
+
 def test_config4_full_size():
+    """Config 4 in the launch configuration the benchmark times: one
+    fa_cascade call with the prefix pass on a side stream."""
+    import torch
     print("[config 4] generating", flush=True)
     wl = make_config(4, mode="test")
     dw = DevWorkload(wl)
-    out, lse, plans = run_cascade(dw)
+    out, lse, plans = run_cascade(dw, fused=True, side_stream=torch.cuda.Stream())
     print(f"[config 4] prefix tiles {plans[0].info().num_tiles} suffix tiles "
           f"{plans[1].info().num_tiles}", flush=True)
     reqs = list(range(0, 256, 5)) + [255]

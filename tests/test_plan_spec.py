@@ -50,8 +50,31 @@ def test_hand_worked_append_plan():
         [0, 0, 32, 40, 0, 32, 0, 2],
         [0, 0, 32, 40, 32, 40, 8, 2],
     ]
-    assert p["num_slots"] == 16 and p["worker_ptr"] is None
+    assert p["num_slots"] == 16
+    assert p["worker_ptr"].tolist() == [0, 4, 4, 4, 4, 4, 4, 4, 4]  # one group: all in bin 0
     assert p["merge"].tolist() == [[32, 0, 0, 2]]
+
+
+def test_hand_worked_append_xcd_bins():
+    # 2 requests x 2 kv heads (G = 1), non-causal, qo_tile 16: request 0 has 16
+    # rows over 32 keys, request 1 16 rows over 16 keys. target 64 -> P = 1 page:
+    # request 0 splits in 2 chunks (slots: head 0 base 0, head 1 base 32).
+    # Group costs (0,0) 512, (0,1) 512, (1,0) 256, (1,1) 256 are dealt to bins
+    # 0, 1, 2, 3 (each to the least-loaded bin, lowest index first).
+    p = plan_spec([0, 2, 3], [32, 16], 2, 2, 2, 128, 16, max_batch=2, qo_indptr=[0, 16, 32],
+                  causal=False, max_qo_tokens=32, num_cu=1, tiles_per_cu=64, qo_tile=16)
+    assert p["chunk_pages"] == 1
+    assert p["tiles"].tolist() == [
+        [0, 0, 0, 16, 0, 16, 0, 2],
+        [0, 0, 0, 16, 16, 32, 16, 2],
+        [0, 1, 0, 16, 0, 16, 32, 2],
+        [0, 1, 0, 16, 16, 32, 48, 2],
+        [1, 0, 16, 32, 0, 16, -1, 1],
+        [1, 1, 16, 32, 0, 16, -1, 1],
+    ]
+    assert p["worker_ptr"].tolist() == [0, 2, 4, 5, 6, 6, 6, 6, 6]
+    assert p["merge"].tolist() == [[0, 0, 0, 2], [0, 1, 32, 2]]
+    assert p["num_slots"] == 64
 
 
 def _pages(k0, k1, ps=16):
@@ -90,7 +113,26 @@ def check_decode_invariants(p, lens, Hkv, ps=16):
 def check_append_invariants(p, lens, Hkv, qo_indptr, causal, ps=16):
     tiles = p["tiles"]
     cost = (tiles[:, 5] - tiles[:, 4]).astype(np.int64) * (tiles[:, 3] - tiles[:, 2])
-    assert np.all(np.diff(cost) <= 0), "not in descending cost order"
+    # XCD bins: bin offsets, each (request, kv head) group contiguous in one
+    # bin with its tiles in descending cost, and the greedy balance bound
+    wptr = p["worker_ptr"]
+    assert len(wptr) == 9 and wptr[0] == 0 and wptr[-1] == len(tiles)
+    assert np.all(np.diff(wptr) >= 0)
+    seen, bcost, gcost = set(), [0] * 8, {}
+    for x in range(8):
+        prev = None
+        for i in range(wptr[x], wptr[x + 1]):
+            g = (int(tiles[i, 0]), int(tiles[i, 1]))
+            if g != prev:
+                assert g not in seen, "group split across runs or bins"
+                seen.add(g)
+            else:
+                assert cost[i] <= cost[i - 1], "group tiles not in descending cost"
+            prev = g
+            bcost[x] += int(cost[i])
+            gcost[g] = gcost.get(g, 0) + int(cost[i])
+    if gcost:
+        assert max(bcost) - min(bcost) <= max(gcost.values()), "bins out of balance"
     assert np.all(tiles[:, 4] % ps == 0), "chunk begin not page aligned"
     cover = {}
     for b, h, q0, q1, t0, t1, s0, C in tiles.tolist():
