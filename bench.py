@@ -166,9 +166,9 @@ class AppendBench(Timed):
 
 
 class CascadeBench(Timed):
-    """One fa_cascade call: the prefix pass (non-causal append over the shared
-    prefix, MFMA) on a side stream beside the suffix decode (HBM), then
-    merge_state; the kernel time is the whole call on the main stream."""
+    """One fa_cascade call: the suffix decode (HBM), the prefix pass
+    (non-causal append over the shared prefix, MFMA) and the combine kernel;
+    the kernel time is the whole call."""
 
     def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30):
         import torch
@@ -192,7 +192,10 @@ class CascadeBench(Timed):
         self.op, self.lp = mk()
         self.os, self.ls = mk()
         self.out, self.lse = mk()
-        self.side = torch.cuda.Stream()  # the prefix pass runs here, beside the suffix decode
+        # One stream: measured on MI355X, running the prefix pass on a side
+        # stream beside the suffix decode is slower (they compete for each
+        # CU's registers and caches) than running the two back to back.
+        self.side = None
 
     def step(self, i: int, ev=None):
         wl, fa = self.wl, self.fa

@@ -209,12 +209,16 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
  *               page table (one request); kv_* the suffix page tables.
  *  prefix_out, suffix_out  device [batch, num_qo_heads, head_dim] scratch in
  *               the q dtype; prefix_lse, suffix_lse device fp32 [batch, num_qo_heads].
+ *               (prefix_out / prefix_lse are only written when the prefix plan
+ *               does not split its keys; split prefix chunks stay as fp32
+ *               partial states in the prefix plan's workspace.)
  *  out / lse    device [batch, num_qo_heads, head_dim] / fp32 (lse may be NULL).
  * The suffix decode runs on `stream` and the prefix pass on `side_stream`
- * concurrently (fork/join with events of the suffix plan; capturable), then
- * merge_state on `stream`. side_stream NULL or equal to stream runs the three
- * kernels in order on `stream`. Other arguments as fa_decode. Errors:
- * FA_ERR_INVALID, FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
+ * concurrently (fork/join with events of the suffix plan; capturable); then
+ * one combine kernel on `stream` merges, per (request, head), the prefix
+ * chunks and the suffix state by log-sum-exp. side_stream NULL or equal to
+ * stream runs the three kernels in order on `stream`. Other arguments as
+ * fa_decode. Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
 fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan, const void* q,
                      const void* k_pages, const void* v_pages, int64_t page_stride,
                      int64_t token_stride, int64_t head_stride, const int32_t* prefix_qo_indptr_d,

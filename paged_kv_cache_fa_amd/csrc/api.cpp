@@ -101,6 +101,7 @@ AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const v
   p.num_qo_heads = pl->geom.num_qo_heads;
   p.num_kv_heads = pl->geom.num_kv_heads;
   p.causal = pl->causal;
+  p.defer_merge = 0;
   return p;
 }
 
@@ -358,6 +359,13 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
     set_error("cascade: NULL or misaligned state / output buffer");
     return FA_ERR_INVALID;
   }
+  // every prefix q tile sees the same keys, so either none or all of its
+  // (q tile, kv head) units split, with merge entries in that order
+  const int64_t units = (int64_t)(sp->batch + gp.qo_tile - 1) / gp.qo_tile * gp.num_kv_heads;
+  if (pp->num_merge != 0 && pp->num_merge != units) {
+    set_error("cascade: unexpected prefix split layout");
+    return FA_ERR_INVALID;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t side = static_cast<hipStream_t>(side_stream);
   const bool fork = side && side != s;
@@ -379,9 +387,10 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
                                     suffix_out, suffix_lse);
   e = launch_decode(ps, gs.dtype, G, sp->num_workers, s);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-  const AttnParams pa = make_params(pp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
-                                    prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
-                                    prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
+  AttnParams pa = make_params(pp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
+                              prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
+                              prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
+  pa.defer_merge = 1;  // the prefix chunks are merged together with the suffix below
   e = launch_append(pa, gp.dtype, G, gp.max_tiles, fork ? side : s);
   if (e != hipSuccess) return hip_fail(e, "append kernel launch");
   if (fork) {
@@ -389,9 +398,10 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
     if (e == hipSuccess) e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(sp->join_event), 0);
     if (e != hipSuccess) return hip_fail(e, "cascade join");
   }
-  e = launch_merge_state(prefix_out, prefix_lse, suffix_out, suffix_lse, out, lse, sp->batch,
-                         gs.num_qo_heads, gs.head_dim, gs.dtype, s);
-  return e == hipSuccess ? FA_OK : hip_fail(e, "merge_state kernel launch");
+  e = launch_cascade_merge(pa.header, pa.merge, pa.part_o, pa.part_lse, prefix_out, prefix_lse,
+                           suffix_out, suffix_lse, out, lse, sp->batch, gs.num_qo_heads, G,
+                           gs.num_kv_heads, gp.qo_tile, gs.dtype, s);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "cascade merge kernel launch");
 }
 
 fa_status fa_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,

@@ -44,7 +44,8 @@
 //    causal limit) skip the masking step;
 //  * a chunked (split) tile writes fp32 partial states; the last workgroup of
 //    the split (agent-scope counter, reset by that workgroup) merges them by
-//    log-sum-exp.
+//    log-sum-exp, unless the caller defers the merge to a later kernel (the
+//    cascade combine, which merges prefix chunks and suffix in one pass).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -360,6 +361,7 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
     if (h == 0)
       __hip_atomic_store(p.part_lse + sh, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (p.defer_merge) return;  // a later kernel combines the partial states
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);

@@ -30,6 +30,7 @@ struct AttnParams {
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t causal;
+  int32_t defer_merge;        // append: split tiles only publish their partial states
 };
 
 constexpr int kAppendBins = 8;  // append tile bins = XCDs (workgroup i runs bin i % 8)
@@ -42,6 +43,15 @@ hipError_t launch_upload(uint32_t* dst, const uint32_t* src, int64_t n_words, hi
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
                               void* vo, float* so, int64_t n, int heads, int head_dim, int dtype,
                               hipStream_t s);
+// Cascade combine: out[r, h] = merge of the shared-prefix state of (r, h)
+// (the prefix plan's deferred chunk partials, or prefix_out / prefix_lse when
+// that plan did not split) with the suffix state.
+hipError_t launch_cascade_merge(const int32_t* prefix_header, const int32_t* prefix_merge,
+                                const float* part_o, const float* part_lse, const void* prefix_out,
+                                const float* prefix_lse, const void* suffix_out,
+                                const float* suffix_lse, void* out, float* lse, int64_t n,
+                                int heads, int group, int num_kv_heads, int qo_tile, int dtype,
+                                hipStream_t s);
 hipError_t launch_merge_states(const void* v, const float* s, int64_t n, int k, int heads,
                                int head_dim, int dtype, void* vo, float* so, hipStream_t st);
 

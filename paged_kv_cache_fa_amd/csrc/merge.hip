@@ -125,6 +125,47 @@ __global__ __launch_bounds__(256) void merge_states_kernel(const void* v, const 
   }
 }
 
+// One thread per (row, head, 8 dims): the prefix state is either the merge of
+// the prefix plan's chunk partials (all prefix q tiles split alike: merge
+// entry (q tile, kv head) = qt * num_kv_heads + hk) or its direct output.
+template <int DT>
+__global__ __launch_bounds__(256) void cascade_merge_kernel(
+    const int32_t* header, const int32_t* merge, const float* part_o, const float* part_lse,
+    const void* po, const float* pls, const void* so, const float* sls, void* vo, float* lo,
+    int64_t n, int heads, int group, int num_kv_heads, int qo_tile) {
+  const int num_merge = header[1];
+  const int64_t total = n * heads * 16;
+  for (int64_t it = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; it < total;
+       it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rh = it >> 4;
+    const int64_t r = rh / heads;
+    const int h = (int)(rh % heads);
+    const int d = (int)(it & 15) * 8;
+    Online st;
+    float x[8];
+    if (num_merge > 0) {
+      const int hk = h / group, g = h % group;
+      const int32_t* e = merge + ((int64_t)(r / qo_tile) * num_kv_heads + hk) * 4;
+      const int q0 = e[0], base = e[2], C = e[3];
+      const int rows = (int)min((int64_t)qo_tile, n - q0);
+      for (int c = 0; c < C; ++c) {
+        const int64_t sh = (int64_t)(base + c * rows + (r - q0)) * group + g;
+        Vec8<FA_F32>::load(part_o, sh * 128 + d, x);
+        st.add(part_lse[sh], x);
+      }
+    } else {
+      Vec8<DT>::load(po, rh * 128 + d, x);
+      st.add(pls[rh] * kLog2e, x);
+    }
+    Vec8<DT>::load(so, rh * 128 + d, x);
+    st.add(sls[rh] * kLog2e, x);
+    float o[8], lse2;
+    st.finish(o, lse2);
+    Vec8<DT>::store(vo, rh * 128 + d, o);
+    if (lo && d == 0) lo[rh] = lse2 * kLn2;
+  }
+}
+
 int grid_for(int64_t total) {
   const int64_t blocks = (total + 255) / 256;
   return (int)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
@@ -172,6 +213,26 @@ hipError_t launch_merge_states(const void* v, const float* sv, int64_t n, int k,
       hipLaunchKernelGGL(merge_states_kernel<FA_F32>, dim3(grid), dim3(256), 0, s, v, sv, n, k,
                          heads, head_dim, vo, so);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_cascade_merge(const int32_t* prefix_header, const int32_t* prefix_merge,
+                                const float* part_o, const float* part_lse, const void* prefix_out,
+                                const float* prefix_lse, const void* suffix_out,
+                                const float* suffix_lse, void* out, float* lse, int64_t n,
+                                int heads, int group, int num_kv_heads, int qo_tile, int dtype,
+                                hipStream_t s) {
+  const int64_t total = n * heads * 16;
+  if (total <= 0) return hipSuccess;
+  const int grid = grid_for(total);
+  if (dtype == FA_BF16)
+    hipLaunchKernelGGL(cascade_merge_kernel<FA_BF16>, dim3(grid), dim3(256), 0, s, prefix_header,
+                       prefix_merge, part_o, part_lse, prefix_out, prefix_lse, suffix_out,
+                       suffix_lse, out, lse, n, heads, group, num_kv_heads, qo_tile);
+  else
+    hipLaunchKernelGGL(cascade_merge_kernel<FA_F16>, dim3(grid), dim3(256), 0, s, prefix_header,
+                       prefix_merge, part_o, part_lse, prefix_out, prefix_lse, suffix_out,
+                       suffix_lse, out, lse, n, heads, group, num_kv_heads, qo_tile);
   return hipGetLastError();
 }
 

@@ -105,18 +105,22 @@ def test_cascade_small():
     assert_close(to_f64(out), to_f64(lse), *direct, what="cascade vs direct")
 
 
-@pytest.mark.parametrize("two_streams", [False, True])
-def test_cascade_call_matches_three_calls(two_streams):
-    """fa_cascade (fork/join on a side stream or serial) gives the bits of the
-    three separate calls."""
+@pytest.mark.parametrize("prefix_len,num_cu", [(512, 8), (96, 1), (2048, 64)])
+def test_cascade_call(prefix_len, num_cu):
+    """fa_cascade matches the oracle whether the prefix pass splits its keys
+    (chunk partials merged with the suffix in the combine kernel) or not, and
+    gives the same bits serially and with the prefix pass on a side stream."""
     import torch
-    wl = make_cascade(512, [5, 16, 17, 300, 1, 64, 900], 32, 8, "bf16", 22, mode="test")
+    wl = make_cascade(prefix_len, [5, 16, 17, 300, 1, 64, 900, 0], 32, 8, "bf16", 22,
+                      mode="test")
     dw = DevWorkload(wl)
-    o3, l3, plans = run_cascade(dw, prefix={"num_cu": 8}, suffix={"num_cu": 8})
-    side = torch.cuda.Stream() if two_streams else None
-    o1, l1, _ = run_cascade(dw, *plans, fused=True, side_stream=side)
+    _, _, plans = run_cascade(dw, prefix={"num_cu": num_cu}, suffix={"num_cu": 8})
+    print(f"[cascade] prefix {prefix_len}: {plans[0].info().num_merge} split units", flush=True)
+    o1, l1, _ = run_cascade(dw, *plans, fused=True)
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2, _ = run_cascade(dw, *plans, fused=True, side_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
-    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert_close(to_f64(o1), to_f64(l1), *oracle_cascade(wl), what="fa_cascade")
 
 
@@ -127,8 +131,10 @@ def test_cascade_graph_capture_with_side_stream():
     import paged_kv_cache_fa_amd as fa
     wl = make_cascade(256, [40, 3, 700], 32, 8, "bf16", 23, mode="test")
     dw = DevWorkload(wl)
-    ref_o, ref_l, plans = run_cascade(dw, prefix={"num_cu": 8}, suffix={"num_cu": 8})
+    _, _, plans = run_cascade(dw, prefix={"num_cu": 8}, suffix={"num_cu": 8})
+    ref_o, ref_l, _ = run_cascade(dw, *plans, fused=True)  # eager fa_cascade
     ref_o, ref_l = ref_o.clone(), ref_l.clone()
+    assert plans[0].info().num_merge > 0  # the prefix chunks go through the combine kernel
     B, H = wl.batch, wl.num_qo_heads
     qo = torch.tensor([0, B], dtype=torch.int32, device="cuda")
     states = (torch.empty_like(dw.q), torch.empty(B, H, dtype=torch.float32, device="cuda"),
