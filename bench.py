@@ -314,7 +314,7 @@ def main():
                    "page_size": wl.page_size, "kv_tokens": int(wl.kv_lens.sum()),
                    "algorithmic_bytes": nbytes, "pool_copies": len(b.pools),
                    "tiles": st.num_tiles, "split_units": st.num_merge,
-                   "workers": st.num_workers, "pages_per_worker": st.chunk_pages},
+                   "workers": st.num_workers, "piece_pages": st.chunk_pages},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(wl.batch / (step_ms * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS,

@@ -76,7 +76,7 @@ typedef struct {
   /* plan knobs (0 = default) */
   int32_t num_cu;          /* compute units to spread tiles over (default 256) */
   int32_t tiles_per_cu;    /* decode: worker waves per compute unit (default 4); append: tiles per CU (default 2) */
-  int32_t min_chunk_pages; /* smallest split-KV chunk in pages (default 1) */
+  int32_t min_chunk_pages; /* smallest split-KV chunk / decode piece in pages (default 1) */
   int32_t qo_tile;         /* append: query rows per tile, 1..128/G (default 128/G,
                               G = num_qo_heads / num_kv_heads); decode: 1 */
   int32_t max_tiles;       /* capacities; default = worst case of the plan procedure */
@@ -96,7 +96,7 @@ typedef struct {
   int32_t num_tiles;       /* work tiles in the current plan */
   int32_t num_merge;       /* query rows whose state is split over several tiles */
   int32_t num_slots;       /* fp32 partial states in use */
-  int32_t chunk_pages;     /* split-KV chunk length in pages */
+  int32_t chunk_pages;     /* split-KV chunk length (append) / piece size (decode) in pages */
   int32_t batch;
   int32_t num_rows;        /* query rows (batch for decode) */
   int32_t causal;
@@ -141,11 +141,13 @@ fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats);
 
 /* Host copies of the current plan, valid until the next fa_plan on this plan.
  * tiles int32 [num_tiles][8]:
- *   decode  {request, kv_head, row, first_slot, key_begin, key_end, slot, n_pieces},
- *           listed worker by worker; worker w runs tiles worker_ptr[w] ..
- *           worker_ptr[w+1]-1 (worker_ptr int32 [num_workers+1]);
- *   append  {request, kv_head, row_begin, row_end, key_begin, key_end, slot0, n_chunks},
- *           one workgroup each, longest first; worker_ptr is NULL.
+ *   decode  {request, kv_head, kv_indptr[request], first_slot, key_begin, key_end, slot,
+ *           n_pieces};
+ *   append  {request, kv_head, row_begin, row_end, key_begin, key_end, slot0, n_chunks}.
+ * Tiles are listed in 8 bins, one per XCD: bin x is tiles worker_ptr[x] ..
+ * worker_ptr[x+1]-1 (worker_ptr int32 [9]; *num_workers receives 8). Decode
+ * waves take tiles from the queue of their XCD, then from the others; append
+ * workgroup i runs bin i mod 8.
  * A slot of -1 means the tile writes the final output. merge int32
  * [num_merge][4] = {first row, kv_head, first_slot, n_states} per split unit.
  * Any output pointer may be NULL. */

@@ -15,20 +15,30 @@ is ``vis = kv_len`` (decode, non-causal) or ``min(kv_len, kv_len - qo_len +
 i1)`` (causal; ``i1`` = request-relative end of its rows), and its cost in
 pages is ``ceil(vis / page_size)``. Units are ordered (q tile, kv head).
 
-Decode — balanced contiguous split over ``S = num_cu * tiles_per_cu``
-worker waves:
+Decode — small pieces in 8 XCD queues, taken dynamically by
+``S = num_cu * tiles_per_cu`` worker waves:
 
-1. Lay the units' pages end to end (``W`` pages in total); worker w owns
-   pages ``[floor(w W / S), floor((w+1) W / S))``.
-2. Every maximal run of one unit inside one worker's range, cut further into
-   runs of at most ``MAX_PIECE_PAGES`` (128) pages, is a piece (tile)
-   ``[b, kv_head, b, base, key0, key1, slot, C]`` where ``C`` is the unit's
-   piece count; a unit with no pages gets one empty piece in the first worker
-   whose range ends after the unit's offset (else the last).
-3. Pieces are listed in worker order; ``worker_ptr[w]`` is worker w's first.
-4. Units with ``C > 1`` get ``C`` partial slots (unit order, running count):
-   piece i of the unit writes slot ``base + i``; ``base = slot = -1`` when
-   ``C == 1``. Merge entry per split unit: ``(b, kv_head, base, C)``.
+1. ``W`` = total pages of all units; piece size
+   ``Q = min(MAX_PIECE_PAGES, max(min_chunk_pages, ceil(W / (S * PIECES_PER_WORKER))))``.
+2. A unit of ``n`` pages splits into ``C = max(1, ceil(n / Q))`` pieces;
+   piece i covers pages ``[i Q, min((i+1) Q, n))`` (full pieces, then the
+   remainder) and is the tile ``[b, kv_head, kv_indptr[b], base, key0,
+   key1, slot, C]`` (keys clipped to kv_len; a unit with no pages is one
+   empty piece). Dealt largest first (step 4), the remainders end up at the
+   tails of the queues, where small pieces even out the finish times.
+3. Units with ``C > 1`` get ``C`` partial slots (unit order, running count):
+   piece i writes slot ``base + i``; ``base = slot = -1`` when ``C == 1``.
+   Merge entry per split unit: ``(b, kv_head, base, C)``.
+4. XCD queues: the pieces of all kv heads over the same pages of a request
+   form a *piece group* (request b, piece i) of cost ``pages * num_kv_heads``.
+   Groups, in descending cost (stable on (b, i)), are dealt to ``XCD_BINS``
+   (8) queues, each to the queue with the least cost so far (lowest index on
+   ties). The tile list is queue 0, queue 1, ...; inside a queue, groups in
+   dealing order and a group's pieces by kv head; ``worker_ptr[0..8]`` are
+   the queue offsets. At run time the waves of XCD x take tiles from queue x
+   with an atomic counter and then from the other queues, so faster XCDs do
+   more; neighbouring waves read the kv heads of the same pages, i.e. whole
+   token rows, at about the same time.
 
 Append — uniform chunks:
 
@@ -67,6 +77,7 @@ SUPPORTED_PAGE_SIZE = (16,)
 SUPPORTED_GROUP = (1, 2, 4, 8)
 MAX_PIECE_PAGES = 128
 XCD_BINS = 8
+PIECES_PER_WORKER = 1
 
 
 class PlanSpecError(Exception):
@@ -103,8 +114,8 @@ def default_knobs(num_kv_heads: int, max_batch: int, max_qo_tokens: int, is_appe
         max_merge = max_merge or target
     else:
         units = max_batch * num_kv_heads
-        max_tiles = max_tiles or (2 * target + units)
-        max_partials = max_partials or (2 * target + units)
+        max_tiles = max_tiles or (PIECES_PER_WORKER * target + units)
+        max_partials = max_partials or (PIECES_PER_WORKER * target + units)
         max_merge = max_merge or units
     return dict(num_cu=num_cu, tiles_per_cu=tiles_per_cu, min_chunk_pages=min_chunk_pages,
                 qo_tile=qo_tile, max_tiles=max_tiles, max_partials=max_partials,
@@ -146,56 +157,55 @@ def validate(kv_indptr, kv_lens, batch, num_qo_heads, num_kv_heads, head_dim, pa
             raise PlanSpecError("INVALID", "too many query rows for max_qo_tokens")
 
 
-def _decode_plan(kv_lens, batch, Hkv, ps, k):
+def _deal(costs):
+    """Deal items (in descending cost, stable) to XCD_BINS bins, each to the
+    bin with the least total cost (lowest index on ties). Returns the item
+    order (bin-major, dealing order inside a bin) and the bin offsets."""
+    bin_of, bcost = [0] * len(costs), [0] * XCD_BINS
+    dealt = sorted(range(len(costs)), key=lambda i: -costs[i])
+    for i in dealt:
+        x = min(range(XCD_BINS), key=lambda j: bcost[j])
+        bin_of[i] = x
+        bcost[x] += costs[i]
+    order = sorted(dealt, key=lambda i: bin_of[i])      # stable: keeps dealing order
+    ptr = [0]
+    for x in range(XCD_BINS):
+        ptr.append(ptr[-1] + sum(1 for i in order if bin_of[i] == x))
+    return order, ptr
+
+
+def _decode_plan(kv_indptr, kv_lens, batch, Hkv, ps, k):
     S = k["num_cu"] * k["tiles_per_cu"]
     units = [(b, h, int(kv_lens[b])) for b in range(batch) for h in range(Hkv)]
-    cost = [_cdiv(L, ps) for (_, _, L) in units]
-    W = sum(cost)
-    pieces = []                          # (worker, unit, page0, page1)
-    w, E, O = 0, W // S, 0
-    for u, c in enumerate(cost):
-        if c == 0:
-            while E <= O and w < S - 1:
-                w += 1
-                E = (w + 1) * W // S
-            pieces.append((w, u, 0, 0))
-            continue
-        pos = O
-        while pos < O + c:
-            while E <= pos:
-                w += 1
-                E = (w + 1) * W // S
-            end = min(E, O + c)
-            q = pos
-            while q < end:
-                e2 = min(end, q + MAX_PIECE_PAGES)
-                pieces.append((w, u, q - O, e2 - O))
-                q = e2
-            pos = end
-        O += c
-    npieces = [0] * len(units)
-    for (_, u, _, _) in pieces:
-        npieces[u] += 1
-    base, slots, merge = [-1] * len(units), 0, []
-    for u, n in enumerate(npieces):
-        if n > 1:
-            base[u] = slots
-            slots += n
-            merge.append((units[u][0], units[u][1], base[u], n))
-    seen = [0] * len(units)
-    tiles = []
-    for (w, u, p0, p1) in pieces:
-        b, h, L = units[u]
-        C = npieces[u]
-        slot = base[u] + seen[u] if C > 1 else -1
-        seen[u] += 1
-        tiles.append((b, h, b, base[u], p0 * ps, min(p1 * ps, L), slot, C))
-    wptr = [0] * (S + 1)
-    for (w, _, _, _) in pieces:
-        wptr[w + 1] += 1
-    for i in range(S):
-        wptr[i + 1] += wptr[i]
-    return tiles, merge, slots, wptr, _cdiv(W, S)
+    npg = [_cdiv(L, ps) for (_, _, L) in units]
+    W = sum(npg)
+    Q = min(MAX_PIECE_PAGES, max(k["min_chunk_pages"], _cdiv(W, S * PIECES_PER_WORKER)))
+    bases, merge, slots = {}, [], 0
+    for (b, h, L), n in zip(units, npg):
+        C = max(1, _cdiv(n, Q))
+        bases[(b, h)] = -1
+        if C > 1:
+            bases[(b, h)] = slots
+            slots += C
+            merge.append((b, h, slots - C, C))
+    groups, gcost = [], []                   # piece groups (b, i): tiles of heads 0..Hkv-1
+    for b in range(batch):
+        L = int(kv_lens[b])
+        n = _cdiv(L, ps)
+        C = max(1, _cdiv(n, Q))
+        for i in range(C):
+            p0, p1 = i * Q, min((i + 1) * Q, n)
+            grp = []
+            for h in range(Hkv):
+                base = bases[(b, h)]
+                grp.append((b, h, int(kv_indptr[b]), base, p0 * ps, min(p1 * ps, L),
+                            base + i if C > 1 else -1, C))
+            groups.append(grp)
+            gcost.append((p1 - p0) * Hkv)
+    order, gptr = _deal(gcost)
+    tiles = [t for g in order for t in groups[g]]
+    wptr = [x * Hkv for x in gptr]
+    return tiles, merge, slots, wptr, Q
 
 
 def _append_plan(kv_lens, batch, Hkv, ps, qo_indptr, causal, k):
@@ -264,7 +274,8 @@ def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
         tiles, merge, slots, wptr, P = _append_plan(kv_lens, batch, num_kv_heads, page_size,
                                                     np.asarray(qo_indptr, np.int64), causal, k)
     else:
-        tiles, merge, slots, wptr, P = _decode_plan(kv_lens, batch, num_kv_heads, page_size, k)
+        tiles, merge, slots, wptr, P = _decode_plan(kv_indptr, kv_lens, batch, num_kv_heads,
+                                                    page_size, k)
     if len(tiles) > k["max_tiles"]:
         raise PlanSpecError("CAPACITY", "too many tiles")
     if slots > k["max_partials"]:

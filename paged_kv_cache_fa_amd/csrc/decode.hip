@@ -11,9 +11,11 @@
 // prefixes").
 //
 // MI355X design (decode is HBM-bound, so no MFMA):
-//  * one wave64 per worker; the planner gives every worker a contiguous,
-//    equal share of all (request, kv head) pages, as pieces {request, kv head,
-//    key range}; 4 independent waves per 256-thread workgroup, no barriers;
+//  * one wave64 per worker, 4 independent waves per 256-thread workgroup, no
+//    barriers; the planner cuts every (request, kv head) into pieces of about
+//    the same number of pages and deals them to 8 queues, one per XCD; waves
+//    take pieces with atomic counters (own XCD's queue first), so the load
+//    follows the speed each XCD actually gets from memory;
 //  * all G = Hq/Hkv query heads of the kv head are packed in the wave (GQA),
 //    so each K/V byte is read from HBM once for all of them;
 //  * lane = 8 x row-group + segment: row group r (0..7) owns tokens r and r+8
@@ -35,9 +37,10 @@
 //    than 2^8 above it, so most pages skip the rescale;
 //  * a (request, kv head) cut into several pieces: each piece writes an fp32
 //    partial state, then the last wave to arrive (an agent-scope counter per
-//    split unit) merges all pieces and writes the final output, so one launch
-//    does the whole decode. The counter is reset by that wave, so the kernel
-//    can be replayed from a graph.
+//    split unit, counted one piece later so the wait for the stores is free)
+//    merges all pieces and writes the final output, so one launch does the
+//    whole decode. Counters and queue heads are reset by the kernel itself,
+//    so it can be replayed from a graph.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -141,21 +144,17 @@ __device__ __forceinline__ void merge_row_groups(float (&m)[G], float (&l)[G],
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float M = m[g];
-    M = fmaxf(M, xor_shfl(M, 8));
-    M = fmaxf(M, xor_shfl(M, 16));
-    M = fmaxf(M, xor_shfl(M, 32));
+    M = fmaxf(M, xor8(M));
+    M = pair32_max(pair16_max(M));
     const float f = fast_exp2(m[g] - (M == kNegInf ? 0.f : M));
     float L = l[g] * f;
-    L += xor_shfl(L, 8);
-    L += xor_shfl(L, 16);
-    L += xor_shfl(L, 32);
+    L += xor8(L);
+    L = pair32_sum(pair16_sum(L));
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float a = acc[g][e] * f;
-      a += xor_shfl(a, 8);
-      a += xor_shfl(a, 16);
-      a += xor_shfl(a, 32);
-      acc[g][e] = a;
+      a += xor8(a);
+      acc[g][e] = pair32_sum(pair16_sum(a));
     }
     m[g] = M;
     l[g] = L;
@@ -268,24 +267,33 @@ __device__ __forceinline__ void write_partial(const AttnParams& p, int64_t slot,
   }
 }
 
+// Identity of a piece, wave-uniform.
+struct PieceId {
+  int row, hk, base, slot, npieces;
+};
+
 // One piece: keys [key0, key1) of kv head hk of request b, for its G q heads.
+// Leaves the piece's state per row group in (m, l, acc).
 template <int DT, int G, int NBUF>
-__device__ __forceinline__ void decode_piece(const AttnParams& p, const int32_t* t, int lane) {
+__device__ __forceinline__ void piece_state(const AttnParams& p, const int32_t* t, int lane,
+                                            PieceId& id, float (&m)[G], float (&l)[G],
+                                            float (&acc)[G][16]) {
   // Everything that addresses memory is made wave-uniform explicitly (loaded
   // once per piece by a few lanes, then v_readlane into scalar registers):
   // the compiler cannot prove these loads uniform across the pieces' stores,
   // and a per-lane buffer resource would turn every page load into a loop.
   const int tv = t[lane & 7];
   const int b = __builtin_amdgcn_readlane(tv, 0), hk = __builtin_amdgcn_readlane(tv, 1);
-  const int row = __builtin_amdgcn_readlane(tv, 2), base = __builtin_amdgcn_readlane(tv, 3);
-  const int key0 = __builtin_amdgcn_readlane(tv, 4);
+  const int pbeg = __builtin_amdgcn_readlane(tv, 2), base = __builtin_amdgcn_readlane(tv, 3);
+  const int key0 = __builtin_amdgcn_readlane(tv, 4), key1_plan = __builtin_amdgcn_readlane(tv, 5);
   const int slot = __builtin_amdgcn_readlane(tv, 6), npieces = __builtin_amdgcn_readlane(tv, 7);
-  const int pv3 = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
-  const int pbeg = __builtin_amdgcn_readlane(pv3, 0);
-  const int npages_req = __builtin_amdgcn_readlane(pv3, 1) - pbeg;
-  const int kv_len = npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(pv3, 2) : 0;
-  const int key1 = min(__builtin_amdgcn_readlane(tv, 5), kv_len);
+  const int row = b;
   const int Hq = p.num_qo_heads;
+  // The tile carries the request's page offset, so the page ids, q and the
+  // page-table check below are all requested together. The check: the
+  // device page table must agree with the plan (offset, and the key range
+  // within the request's valid tokens); a piece that disagrees reads nothing.
+  const int pv3 = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
 
   const int r = lane >> 3;
   const int s = lane & 7;
@@ -293,6 +301,11 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, const int32_t*
   const uint32_t off[4] = {r * ts2 + s * 16u, r * ts2 + 128u + s * 16u, (r + 8) * ts2 + s * 16u,
                            (r + 8) * ts2 + 128u + s * 16u};
 
+  id.row = row;
+  id.hk = hk;
+  id.base = base;
+  id.slot = slot;
+  id.npieces = npieces;
   u32x4 qlo[G], qhi[G];
   const uint16_t* qp = p.q + ((int64_t)row * Hq + hk * G) * 128;
 #pragma unroll
@@ -300,7 +313,6 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, const int32_t*
     qlo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + s * 8);
     qhi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + 64 + s * 8);
   }
-  float m[G], l[G], acc[G][16];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = kNegInf;
@@ -310,15 +322,20 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, const int32_t*
   }
 
   const int first_page = key0 >> 4;
-  const int npg = key1 > key0 ? ((key1 + 15) >> 4) - first_page : 0;
+  const int npg_plan = key1_plan > key0 ? ((key1_plan + 15) >> 4) - first_page : 0;
   // Page ids of the piece (at most 128 pages, a planner guarantee) are fetched
   // once, before any K/V load is in flight (lane i holds pages i and i+64),
   // and handed to the scalar unit with v_readlane: waiting on a load later
   // would drain the in-order load counter.
   const int32_t* ids_base = p.kv_indices + pbeg + first_page;
-  const int ids0 = lane < npg ? ids_base[lane] : 0;
-  const int ids1 = lane + 64 < npg ? ids_base[lane + 64] : 0;
-  asm volatile("" ::"v"(ids0), "v"(ids1));  // both arrive before the page loop starts
+  const int ids0 = lane < npg_plan ? ids_base[lane] : 0;
+  const int ids1 = lane + 64 < npg_plan ? ids_base[lane + 64] : 0;
+  asm volatile("" ::"v"(ids0), "v"(ids1), "v"(pv3));  // all arrive before the page loop starts
+  const int npages_req = __builtin_amdgcn_readlane(pv3, 1) - __builtin_amdgcn_readlane(pv3, 0);
+  const int kv_len = npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(pv3, 2) : 0;
+  const bool agrees = __builtin_amdgcn_readlane(pv3, 0) == pbeg && key1_plan <= kv_len;
+  const int key1 = agrees ? key1_plan : key0;
+  const int npg = agrees ? npg_plan : 0;
   auto page_id = [&](int j) -> int {
     return j < 64 ? __builtin_amdgcn_readlane(ids0, j & 63)
                   : __builtin_amdgcn_readlane(ids1, j & 63);
@@ -371,39 +388,91 @@ __device__ __forceinline__ void decode_piece(const AttnParams& p, const int32_t*
       consume_page<DT, G>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1, tb + r + 8 < key1);
     }
   }
-  merge_row_groups<G>(m, l, acc);
-
-  if (slot < 0) {
-    write_final<DT, G>(p, row, hk, r, s, m, l, acc);
-    return;
-  }
-  // split unit: publish this piece; the last piece to arrive merges them all
-  write_partial<G>(p, slot, r, s, m, l, acc);
-  int32_t* counter = p.counters + base;
-  // the coherent stores above must have completed before the arrival is counted
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  int prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0, 64);
-  if (prev != npieces - 1) return;
-  if (lane == 0) *counter = 0;
-  gather_partials<G>(p, base, npieces, r, s, m, l, acc);
-  merge_row_groups<G>(m, l, acc);
-  write_final<DT, G>(p, row, hk, r, s, m, l, acc);
 }
 
-// One wave per worker: its pieces are tiles worker_ptr[w] .. worker_ptr[w+1]-1,
-// a contiguous, equal share of all pages (4 independent waves per workgroup).
+// Worker waves take pieces from 8 queues (one per XCD; bin offsets in
+// worker_ptr) with agent-scope atomic counters: first the queue of their own
+// XCD (workgroup i runs on XCD i mod 8), then the others, so waves that run
+// faster take more pieces. A split unit's pieces publish fp32 partial states;
+// a wave reports a piece's arrival only after its next piece (the partial's
+// stores have long completed by then, so the wait is free), and the last
+// arriving piece merges the unit. The last wave to finish resets the queue
+// heads, so the kernel can be replayed from a graph.
 template <int DT, int G, int NBUF>
 __global__ __launch_bounds__(256, (G <= 4 ? 2 : 1)) void decode_kernel(AttnParams p) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + wave;
-  if (w >= p.header[6]) return;
-  const int t1 = p.worker_ptr[w + 1];
-  for (int t = p.worker_ptr[w]; t < t1; ++t) decode_piece<DT, G, NBUF>(p, p.tiles + t * 8, lane);
+  const int r = lane >> 3, s = lane & 7;
+  const int x = blockIdx.x % 8;
+  // queue heads and the finished-wave count, each on its own 256-byte line
+  // (atomics to one line serialise)
+  int32_t* heads = p.queue;
+  auto head = [&](int q) { return heads + q * kQueueStride; };
+  const int bv = lane <= 8 ? p.worker_ptr[lane] : 0;
+  auto bin_lo = [&](int q) { return __builtin_amdgcn_readlane(bv, q); };
+  auto fetch_add = [&](int32_t* ptr) -> int {  // lane 0 only; result read by readlane
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(ptr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  };
+  // own-queue take: issued early, resolved (with stealing) later
+  auto resolve = [&](int issued) -> int {
+    const int idx = __builtin_amdgcn_readlane(issued, 0);
+    if (bin_lo(x) + idx < bin_lo(x + 1)) return bin_lo(x) + idx;
+    for (int k = 1; k < 8; ++k) {
+      const int q = (x + k) & 7;
+      const int lo = bin_lo(q), n = bin_lo(q + 1) - lo;
+      if (n <= 0) continue;
+      int cur = 0;
+      if (lane == 0) cur = __hip_atomic_load(head(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_readlane(cur, 0) >= n) continue;  // exhausted: no update
+      const int got = __builtin_amdgcn_readlane(fetch_add(head(q)), 0);
+      if (got < n) return lo + got;
+    }
+    return -1;
+  };
+  // arrival of a split piece whose partial was published earlier; the last
+  // arrival of the unit merges all its pieces and writes the output
+  float m[G], l[G], acc[G][16];
+  auto finish_arrival = [&](const PieceId& pd, int arr) {
+    if (__builtin_amdgcn_readlane(arr, 0) != pd.npieces - 1) return;
+    if (lane == 0) p.counters[pd.base] = 0;
+    gather_partials<G>(p, pd.base, pd.npieces, r, s, m, l, acc);
+    merge_row_groups<G>(m, l, acc);
+    write_final<DT, G>(p, pd.row, pd.hk, r, s, m, l, acc);
+  };
+  auto arrive = [&](const PieceId& pd) -> int {
+    // the partial's coherent stores must be complete before the count
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return fetch_add(p.counters + pd.base);
+  };
+
+  PieceId pd = {0, 0, -1, -1, 0};  // pending arrival (slot < 0: none)
+  int t = resolve(fetch_add(head(x)));
+  while (t >= 0) {
+    PieceId id;
+    piece_state<DT, G, NBUF>(p, p.tiles + t * 8, lane, id, m, l, acc);
+    // the arrival and the next take are requested first; their round trips
+    // overlap the reduction and the stores below
+    const int arr = pd.slot >= 0 ? arrive(pd) : 0;
+    const int next = fetch_add(head(x));
+    merge_row_groups<G>(m, l, acc);
+    if (id.slot < 0)
+      write_final<DT, G>(p, id.row, id.hk, r, s, m, l, acc);
+    else
+      write_partial<G>(p, id.slot, r, s, m, l, acc);
+    if (pd.slot >= 0) finish_arrival(pd, arr);
+    pd = id;
+    t = resolve(next);
+  }
+  if (pd.slot >= 0) finish_arrival(pd, arrive(pd));
+  const int done = __builtin_amdgcn_readlane(fetch_add(head(8)), 0);
+  if (done == (int)gridDim.x * 4 - 1 && lane == 0) {
+#pragma unroll
+    for (int q = 0; q <= 8; ++q)
+      __hip_atomic_store(head(q), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int DT>

@@ -77,4 +77,27 @@ __device__ __forceinline__ float octet_sum(float x) {
 
 __device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Exchanges across lane bits 3, 4 and 5 without LDS: a row rotate by 8 (DPP)
+// pairs lanes l and l^8 inside each row of 16; v_permlane16_swap /
+// v_permlane32_swap on (x, x) return x of lanes l and l^16 (l^32) in some
+// order, which is all a symmetric reduction needs.
+constexpr int kDppRowRor8 = 0x128;
+__device__ __forceinline__ float xor8(float x) { return dpp<kDppRowRor8>(x); }
+__device__ __forceinline__ float pair16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 }  // namespace pkfa

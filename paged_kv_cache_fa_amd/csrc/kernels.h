@@ -26,6 +26,8 @@ struct AttnParams {
   float* part_o;              // [slots, G, 128] fp32 partial outputs (normalised)
   float* part_lse;            // [slots, G] partial lse in log2 units
   int32_t* counters;          // [slots] arrivals per split unit, indexed by its first slot
+  int32_t* queue;             // decode: queue heads q = 0..7 and the finished-wave count (q = 8)
+                              // at queue[q * kQueueStride]; zero between calls
   float scale_log2;           // sm_scale * log2(e)
   int32_t num_qo_heads;
   int32_t num_kv_heads;
@@ -33,6 +35,7 @@ struct AttnParams {
   int32_t defer_merge;        // append: split tiles only publish their partial states
 };
 
+constexpr int kQueueStride = 64;  // int32s between decode queue counters (one 256-byte line each)
 constexpr int kAppendBins = 8;  // append tile bins = XCDs (workgroup i runs bin i % 8)
 
 hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s);

@@ -101,8 +101,8 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
     mm = g.max_merge ? g.max_merge : target;
   } else {
     const int64_t units = (int64_t)g.max_batch * g.num_kv_heads;
-    mt = g.max_tiles ? g.max_tiles : 2 * target + units;
-    mp = g.max_partials ? g.max_partials : 2 * target + units;
+    mt = g.max_tiles ? g.max_tiles : kPiecesPerWorker * target + units;
+    mp = g.max_partials ? g.max_partials : kPiecesPerWorker * target + units;
     mm = g.max_merge ? g.max_merge : units;
   }
   if (target > (1 << 22)) {
@@ -123,20 +123,22 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
 Layout compute_layout(const fa_geometry& g) {
   Layout L;
   const int G = g.num_qo_heads / g.num_kv_heads;
-  L.workers = g.mode == FA_MODE_DECODE ? g.num_cu * g.tiles_per_cu : kXcdBins;
+  L.workers = g.mode == FA_MODE_DECODE ? g.num_cu * g.tiles_per_cu : 0;
   L.header = 0;
   L.merge = kHeaderInts * 4;
   L.worker_ptr = L.merge + (size_t)g.max_merge * kMergeInts * 4;
-  L.tiles = align_up(L.worker_ptr + (size_t)(L.workers + 1) * 4, 64);
+  L.tiles = align_up(L.worker_ptr + (size_t)(kXcdBins + 1) * 4, 64);
   L.upload_end = L.tiles + (size_t)g.max_tiles * kTileInts * 4;
-  L.dev_counters = align_up(L.upload_end, 256);
+  L.dev_queue = align_up(L.upload_end, 256);
+  L.dev_counters = L.dev_queue + (size_t)(kXcdBins + 1) * 256;  // queue counters, one line each
   L.dev_part_lse = align_up(L.dev_counters + (size_t)g.max_partials * 4, 256);
   L.dev_part_o = align_up(L.dev_part_lse + (size_t)g.max_partials * G * 4, 256);
   L.dev_bytes = align_up(L.dev_part_o + (size_t)g.max_partials * G * g.head_dim * 4, 256);
   L.host_unsorted = align_up(L.upload_end, 64);
   L.host_order = L.host_unsorted + (size_t)g.max_tiles * kTileInts * 4;
   L.host_cost = align_up(L.host_order + (size_t)g.max_tiles * 4, 8);
-  L.host_units = L.host_cost + (size_t)g.max_tiles * 8;
+  L.host_bin = L.host_cost + (size_t)g.max_tiles * 8;
+  L.host_units = align_up(L.host_bin + (size_t)g.max_tiles * 4, 8);
   // per (request, kv head): 2 int32 (decode) or int64 cost + 3 int32 (append)
   L.host_bytes = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 24;
   return L;
@@ -149,101 +151,113 @@ fa_status capacity_error(const char* what, int64_t n, int32_t cap) {
   return FA_ERR_CAPACITY;
 }
 
-// Decode: balanced contiguous split of the units' pages over the workers.
-fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, const int32_t* kv_lens,
-                      int32_t batch, int64_t* ntiles_out, int64_t* nmerge_out, int64_t* slots_out,
-                      int64_t* per_worker_out) {
+// Decode: units cut into pieces of Q pages (and a remainder); the pieces of all kv heads
+// over the same pages of a request form a group, and groups are dealt to the
+// XCD queues (largest first, each to the least-loaded queue). Group costs
+// are small integers (pages * Hkv, pages <= Q), so both orderings are
+// counting sorts: linear in the number of pieces.
+fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, const int32_t* kv_indptr,
+                      const int32_t* kv_lens, int32_t batch, int64_t* ntiles_out,
+                      int64_t* nmerge_out, int64_t* slots_out, int64_t* piece_pages_out) {
   const int ps = g.page_size, Hkv = g.num_kv_heads;
   const int64_t S = lay.workers;
-  const int64_t nunits = (int64_t)batch * Hkv;
   int32_t* merge = reinterpret_cast<int32_t*>(ws + lay.merge);
   int32_t* wptr = reinterpret_cast<int32_t*>(ws + lay.worker_ptr);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
-  int32_t* npieces = reinterpret_cast<int32_t*>(ws + lay.host_units);
-  int32_t* base = npieces + (size_t)g.max_batch * Hkv;
+  int32_t* grp = reinterpret_cast<int32_t*>(ws + lay.host_unsorted);  // [ngroups][5] b, p0, p1, C, i
+  int32_t* order = reinterpret_cast<int32_t*>(ws + lay.host_order);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + lay.host_bin);
+  int32_t* bases = reinterpret_cast<int32_t*>(ws + lay.host_units);     // [batch * Hkv]
   int64_t W = 0;
   for (int b = 0; b < batch; ++b) W += cdiv(kv_lens[b], ps) * Hkv;
-
-  // Walk the cut points once; emit(worker, unit, page0, page1) per piece.
-  auto walk = [&](auto&& emit) {
-    int64_t w = 0, E = W / S, O = 0;
-    for (int64_t u = 0; u < nunits; ++u) {
-      const int64_t c = cdiv(kv_lens[u / Hkv], ps);
-      if (c == 0) {
-        while (E <= O && w < S - 1) {
-          ++w;
-          E = (w + 1) * W / S;
+  const int64_t Q = std::min<int64_t>(
+      kMaxPiecePages, std::max<int64_t>(g.min_chunk_pages, cdiv(W, S * kPiecesPerWorker)));
+  // pieces, slots and merge entries in unit order
+  int64_t ngroups = 0, nmerge = 0, slots = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t C = std::max<int64_t>(1, cdiv(cdiv(kv_lens[b], ps), Q));
+    ngroups += C;
+    for (int h = 0; h < Hkv; ++h) {
+      bases[(int64_t)b * Hkv + h] = -1;
+      if (C > 1) {
+        bases[(int64_t)b * Hkv + h] = (int32_t)slots;
+        if (nmerge < g.max_merge) {
+          int32_t* m = merge + nmerge * kMergeInts;
+          m[0] = b;
+          m[1] = h;
+          m[2] = (int32_t)slots;
+          m[3] = (int32_t)C;
         }
-        emit(w, u, (int64_t)0, (int64_t)0);
-        continue;
+        slots += C;
+        ++nmerge;
       }
-      for (int64_t pos = O; pos < O + c;) {
-        while (E <= pos) {
-          ++w;
-          E = (w + 1) * W / S;
-        }
-        const int64_t end = std::min(E, O + c);
-        for (int64_t q = pos; q < end; q += kMaxPiecePages)
-          emit(w, u, q - O, std::min(end, q + kMaxPiecePages) - O);
-        pos = end;
-      }
-      O += c;
-    }
-  };
-  int64_t ntiles = 0;
-  for (int64_t u = 0; u < nunits; ++u) npieces[u] = 0;
-  walk([&](int64_t, int64_t u, int64_t, int64_t) {
-    ++npieces[u];
-    ++ntiles;
-  });
-  if (ntiles > g.max_tiles) return capacity_error("tiles", ntiles, g.max_tiles);
-  int64_t slots = 0, nmerge = 0;
-  for (int64_t u = 0; u < nunits; ++u) {
-    base[u] = -1;
-    if (npieces[u] > 1) {
-      base[u] = (int32_t)slots;
-      slots += npieces[u];
-      if (nmerge < g.max_merge) {
-        int32_t* m = merge + nmerge * kMergeInts;
-        m[0] = (int32_t)(u / Hkv);
-        m[1] = (int32_t)(u % Hkv);
-        m[2] = base[u];
-        m[3] = npieces[u];
-      }
-      ++nmerge;
     }
   }
+  const int64_t ntiles = ngroups * Hkv;
+  if (ntiles > g.max_tiles) return capacity_error("tiles", ntiles, g.max_tiles);
   if (slots > g.max_partials) return capacity_error("partial states", slots, g.max_partials);
   if (nmerge > g.max_merge) return capacity_error("merge entries", nmerge, g.max_merge);
-  for (int64_t w = 0; w <= S; ++w) wptr[w] = 0;
-  int64_t i = 0;
-  for (int64_t u = 0; u < nunits; ++u) npieces[u] = 0;  // reused: pieces seen so far
-  walk([&](int64_t w, int64_t u, int64_t p0, int64_t p1) {
-    const int b = (int)(u / Hkv);
-    const int64_t L = kv_lens[b];
-    int32_t* t = tiles + i * kTileInts;
-    const bool split = base[u] >= 0;
-    t[0] = b;
-    t[1] = (int32_t)(u % Hkv);
-    t[2] = b;
-    t[3] = base[u];
-    t[4] = (int32_t)(p0 * ps);
-    t[5] = (int32_t)std::min(p1 * ps, L);
-    t[6] = split ? base[u] + npieces[u] : -1;
-    ++npieces[u];
-    ++wptr[w + 1];
-    ++i;
-  });
-  // piece counts are complete now: fill C
-  for (int64_t k = 0; k < ntiles; ++k) {
-    int32_t* t = tiles + k * kTileInts;
-    t[7] = npieces[(int64_t)t[0] * Hkv + t[1]];
+  // groups in emission order, bucketed by pages (0..Q)
+  int64_t cnt[kMaxPiecePages + 2] = {};
+  for (int b = 0, k = 0; b < batch; ++b) {
+    const int64_t n = cdiv(kv_lens[b], ps);
+    const int64_t C = std::max<int64_t>(1, cdiv(n, Q));
+    for (int64_t i = 0; i < C; ++i, ++k) {
+      int32_t* r = grp + (int64_t)k * 5;
+      r[0] = b;
+      r[1] = (int32_t)(i * Q);
+      r[2] = (int32_t)std::min((i + 1) * Q, n);
+      r[3] = (int32_t)C;
+      r[4] = (int32_t)i;
+      ++cnt[r[2] - r[1]];
+    }
   }
-  for (int64_t w = 0; w < S; ++w) wptr[w + 1] += wptr[w];
+  // dealing order: descending pages, stable (counting sort)
+  int64_t start[kMaxPiecePages + 2];
+  for (int64_t pg = Q, acc = 0; pg >= 0; --pg) {
+    start[pg] = acc;
+    acc += cnt[pg];
+  }
+  for (int64_t k = 0; k < ngroups; ++k) {
+    const int32_t* r = grp + k * 5;
+    order[start[r[2] - r[1]]++] = (int32_t)k;
+  }
+  // deal; then stable by queue (counting sort by queue)
+  int64_t qcost[kXcdBins] = {}, qcnt[kXcdBins + 1] = {};
+  for (int64_t n = 0; n < ngroups; ++n) {
+    int x = 0;
+    for (int j = 1; j < kXcdBins; ++j)
+      if (qcost[j] < qcost[x]) x = j;
+    const int32_t* r = grp + (int64_t)order[n] * 5;
+    qcost[x] += (int64_t)(r[2] - r[1]) * Hkv;
+    ++qcnt[x + 1];
+    sorted[n] = x;  // queue of the n-th dealt group
+  }
+  for (int x = 0; x < kXcdBins; ++x) qcnt[x + 1] += qcnt[x];
+  for (int x = 0; x <= kXcdBins; ++x) wptr[x] = (int32_t)(qcnt[x] * Hkv);
+  int64_t qpos[kXcdBins];
+  for (int x = 0; x < kXcdBins; ++x) qpos[x] = qcnt[x];
+  for (int64_t n = 0; n < ngroups; ++n) {
+    const int32_t* r = grp + (int64_t)order[n] * 5;
+    const int b = r[0];
+    const int64_t k = qpos[sorted[n]]++;
+    for (int h = 0; h < Hkv; ++h) {
+      int32_t* t = tiles + (k * Hkv + h) * kTileInts;
+      const int32_t base = bases[(int64_t)b * Hkv + h];
+      t[0] = b;
+      t[1] = h;
+      t[2] = kv_indptr[b];
+      t[3] = base;
+      t[4] = r[1] * ps;
+      t[5] = (int32_t)std::min<int64_t>((int64_t)r[2] * ps, kv_lens[b]);
+      t[6] = base >= 0 ? base + r[4] : -1;
+      t[7] = r[3];
+    }
+  }
   *ntiles_out = ntiles;
   *nmerge_out = nmerge;
   *slots_out = slots;
-  *per_worker_out = S > 0 ? cdiv(W, S) : 0;
+  *piece_pages_out = Q;
   return FA_OK;
 }
 
@@ -426,7 +440,8 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
   int64_t ntiles = 0, nmerge = 0, slots = 0, P = 0;
   fa_status st = app ? plan_append(g, lay, ws, kv_lens, batch, qo_indptr, causal, &ntiles, &nmerge,
                                    &slots, &P)
-                     : plan_decode(g, lay, ws, kv_lens, batch, &ntiles, &nmerge, &slots, &P);
+                     : plan_decode(g, lay, ws, kv_indptr, kv_lens, batch, &ntiles, &nmerge, &slots,
+                                   &P);
   if (st != FA_OK) return st;
   memset(header, 0, kHeaderInts * 4);
   header[0] = (int32_t)ntiles;

@@ -13,28 +13,30 @@ def _indptr(lens, ps=16):
 
 def test_hand_worked_decode_plan():
     # Three requests of 4, 2, 5 full pages (the page lists of the worked CSR
-    # example), 2 kv heads -> units of 4,4,2,2,5,5 pages (W = 22) laid end to
-    # end; 4 workers own pages [0,5) [5,11) [11,16) [16,22).
+    # example), 2 kv heads -> units of 4,4,2,2,5,5 pages, W = 22. 8 workers:
+    # Q = ceil(22 / 8) = 3 pages; units split into full pieces of 3
+    # pages and a remainder: 4 -> [0,3) [3,4), 2 -> [0,2), 5 -> [0,3) [3,5).
+    # Piece groups (request, piece) hold both heads: costs (0,0) 6, (0,1) 2,
+    # (1,0) 4, (2,0) 6, (2,1) 4 pages, dealt largest first to queues 0..4.
+    # Field 2 is the request's first page in kv_indices (0, 4, 6).
     lens = [64, 32, 80]
-    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=4)
+    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=2, tiles_per_cu=4)
     assert p["tiles"].tolist() == [
-        [0, 0, 0, -1, 0, 64, -1, 1],                                   # worker 0
-        [0, 1, 0, 0, 0, 16, 0, 2],
-        [0, 1, 0, 0, 16, 64, 1, 2],                                    # worker 1
-        [1, 0, 1, -1, 0, 32, -1, 1],
-        [1, 1, 1, 2, 0, 16, 2, 2],
-        [1, 1, 1, 2, 16, 32, 3, 2],                                    # worker 2
-        [2, 0, 2, 4, 0, 64, 4, 2],
-        [2, 0, 2, 4, 64, 80, 5, 2],                                    # worker 3
-        [2, 1, 2, -1, 0, 80, -1, 1],
+        [0, 0, 0, 0, 0, 48, 0, 2], [0, 1, 0, 2, 0, 48, 2, 2],       # queue 0
+        [2, 0, 6, 4, 0, 48, 4, 2], [2, 1, 6, 6, 0, 48, 6, 2],       # queue 1
+        [1, 0, 4, -1, 0, 32, -1, 1], [1, 1, 4, -1, 0, 32, -1, 1],   # queue 2
+        [2, 0, 6, 4, 48, 80, 5, 2], [2, 1, 6, 6, 48, 80, 7, 2],     # queue 3
+        [0, 0, 0, 0, 48, 64, 1, 2], [0, 1, 0, 2, 48, 64, 3, 2],     # queue 4
     ]
-    assert p["worker_ptr"].tolist() == [0, 2, 5, 7, 9]
-    assert p["merge"].tolist() == [[0, 1, 0, 2], [1, 1, 2, 2], [2, 0, 4, 2]]
-    assert p["num_slots"] == 6 and p["chunk_pages"] == 6
-    # one worker: every unit is one piece, nothing to merge
+    assert p["worker_ptr"].tolist() == [0, 2, 4, 6, 8, 10, 10, 10, 10]
+    assert p["merge"].tolist() == [[0, 0, 0, 2], [0, 1, 2, 2], [2, 0, 4, 2], [2, 1, 6, 2]]
+    assert p["num_slots"] == 8 and p["chunk_pages"] == 3
+    # one worker: Q = 22, every unit is one piece, nothing to merge; groups of
+    # 10, 8, 4 pages go to queues 0, 1, 2
     p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=1)
     assert p["num_slots"] == 0 and p["merge"].shape == (0, 4)
-    assert p["worker_ptr"].tolist() == [0, 6]
+    assert p["tiles"][:, :2].tolist() == [[2, 0], [2, 1], [0, 0], [0, 1], [1, 0], [1, 1]]
+    assert p["worker_ptr"].tolist() == [0, 2, 4, 6, 6, 6, 6, 6, 6]
 
 
 def test_hand_worked_append_plan():
@@ -82,26 +84,40 @@ def _pages(k0, k1, ps=16):
 
 
 def check_decode_invariants(p, lens, Hkv, ps=16):
-    tiles, wptr = p["tiles"], p["worker_ptr"]
-    S = len(wptr) - 1
-    assert wptr[0] == 0 and wptr[-1] == len(tiles) and np.all(np.diff(wptr) >= 0)
-    W = sum(-(-int(L) // ps) for L in lens) * Hkv
-    for w in range(S):
-        load = sum(_pages(t[4], t[5], ps) for t in tiles[wptr[w]:wptr[w + 1]].tolist())
-        assert load == (w + 1) * W // S - w * W // S, "worker load must be its exact share"
+    tiles, wptr, Q = p["tiles"], p["worker_ptr"], p["chunk_pages"]
+    assert len(wptr) == 9 and wptr[0] == 0 and wptr[-1] == len(tiles)
+    assert np.all(np.diff(wptr) >= 0)
+    pages = [_pages(t[4], t[5], ps) for t in tiles.tolist()]
+    qload = []
+    for x in range(8):
+        seg = pages[wptr[x]:wptr[x + 1]]
+        assert all(a >= b for a, b in zip(seg, seg[1:])), "queue not in descending pages"
+        assert (wptr[x + 1] - wptr[x]) % Hkv == 0
+        for g0 in range(wptr[x], wptr[x + 1], Hkv):   # a piece group: same pages, heads in order
+            grp = tiles[g0:g0 + Hkv]
+            assert grp[:, 1].tolist() == list(range(Hkv))
+            assert (grp[:, [0, 4, 5]] == grp[0, [0, 4, 5]]).all()
+        qload.append(sum(seg))
+    if pages:
+        assert max(qload) - min(qload) <= max(pages) * Hkv, "queues out of balance"
     by_unit = {}
     for t in tiles.tolist():
         by_unit.setdefault((t[0], t[1]), []).append(t)
     assert sorted(by_unit) == [(b, h) for b in range(len(lens)) for h in range(Hkv)]
     slots = set()
     for (b, h), parts in by_unit.items():
+        parts.sort(key=lambda t: t[4] if t[6] < 0 else t[6])
         L = int(lens[b])
+        n = -(-L // ps)
         C = len(parts)
+        assert C == max(1, -(-n // Q)), "piece count"
         assert parts[0][4] == 0 and parts[-1][5] == L
         for a, c in zip(parts[:-1], parts[1:]):
             assert a[5] == c[4] and c[4] % ps == 0
+        sizes = [_pages(t[4], t[5], ps) for t in parts]
+        assert all(x == Q for x in sizes[:-1]) and sizes[-1] <= Q  # full pieces, then the rest
         for i, t in enumerate(parts):
-            assert t[2] == b and t[7] == C
+            assert t[2] == sum(-(-int(x) // ps) for x in lens[:b]) and t[7] == C
             if C == 1:
                 assert t[3] == -1 and t[6] == -1
             else:
