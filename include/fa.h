@@ -82,7 +82,8 @@ typedef struct {
   int32_t max_tiles;       /* capacities; default = worst case of the plan procedure */
   int32_t max_partials;
   int32_t max_merge;
-  int32_t reserved[9];
+  int32_t pieces_per_worker; /* decode: pieces per worker wave the piece size aims at (default 1) */
+  int32_t reserved[8];
 } fa_geometry;
 
 /* Caller-allocated plan object. Zero it before first use; release the HIP

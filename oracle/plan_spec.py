@@ -19,7 +19,8 @@ Decode — small pieces in 8 XCD queues, taken dynamically by
 ``S = num_cu * tiles_per_cu`` worker waves:
 
 1. ``W`` = total pages of all units; piece size
-   ``Q = min(MAX_PIECE_PAGES, max(min_chunk_pages, ceil(W / (S * PIECES_PER_WORKER))))``.
+   ``Q = min(MAX_PIECE_PAGES, max(min_chunk_pages, ceil(W / (S * pieces_per_worker))))``
+   (``pieces_per_worker`` defaults to ``PIECES_PER_WORKER``).
 2. A unit of ``n`` pages splits into ``C = max(1, ceil(n / Q))`` pieces;
    piece i covers pages ``[i Q, min((i+1) Q, n))`` (full pieces, then the
    remainder) and is the tile ``[b, kv_head, kv_indptr[b], base, key0,
@@ -95,12 +96,13 @@ def _cdiv(a: int, b: int) -> int:
 def default_knobs(num_kv_heads: int, max_batch: int, max_qo_tokens: int, is_append: bool,
                   num_cu: int = 0, tiles_per_cu: int = 0, min_chunk_pages: int = 0,
                   qo_tile: int = 0, max_tiles: int = 0, max_partials: int = 0,
-                  max_merge: int = 0, group: int = 1) -> dict:
+                  max_merge: int = 0, pieces_per_worker: int = 0, group: int = 1) -> dict:
     """Fill zero knobs with defaults; capacities are the worst case of the procedure.
 
     An append q tile holds at most ``128 / group`` rows (the library's tiles
     have 128 query columns = group heads x rows); that is also the default."""
     num_cu = num_cu or 256
+    pieces_per_worker = 0 if is_append else (pieces_per_worker or PIECES_PER_WORKER)
     tiles_per_cu = tiles_per_cu or (2 if is_append else 4)
     min_chunk_pages = min_chunk_pages or 1
     qo_tile = (qo_tile or 128 // group) if is_append else 1
@@ -114,12 +116,12 @@ def default_knobs(num_kv_heads: int, max_batch: int, max_qo_tokens: int, is_appe
         max_merge = max_merge or target
     else:
         units = max_batch * num_kv_heads
-        max_tiles = max_tiles or (PIECES_PER_WORKER * target + units)
-        max_partials = max_partials or (PIECES_PER_WORKER * target + units)
+        max_tiles = max_tiles or (pieces_per_worker * target + units)
+        max_partials = max_partials or (pieces_per_worker * target + units)
         max_merge = max_merge or units
     return dict(num_cu=num_cu, tiles_per_cu=tiles_per_cu, min_chunk_pages=min_chunk_pages,
                 qo_tile=qo_tile, max_tiles=max_tiles, max_partials=max_partials,
-                max_merge=max_merge)
+                max_merge=max_merge, pieces_per_worker=pieces_per_worker)
 
 
 def validate(kv_indptr, kv_lens, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
@@ -179,7 +181,7 @@ def _decode_plan(kv_indptr, kv_lens, batch, Hkv, ps, k):
     units = [(b, h, int(kv_lens[b])) for b in range(batch) for h in range(Hkv)]
     npg = [_cdiv(L, ps) for (_, _, L) in units]
     W = sum(npg)
-    Q = min(MAX_PIECE_PAGES, max(k["min_chunk_pages"], _cdiv(W, S * PIECES_PER_WORKER)))
+    Q = min(MAX_PIECE_PAGES, max(k["min_chunk_pages"], _cdiv(W, S * k["pieces_per_worker"])))
     bases, merge, slots = {}, [], 0
     for (b, h, L), n in zip(units, npg):
         C = max(1, _cdiv(n, Q))

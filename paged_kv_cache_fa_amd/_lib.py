@@ -36,7 +36,8 @@ class Geometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "dtype", "max_batch", "max_qo_tokens", "num_qo_heads", "num_kv_heads",
         "head_dim", "page_size", "num_cu", "tiles_per_cu", "min_chunk_pages", "qo_tile",
-        "max_tiles", "max_partials", "max_merge")] + [("reserved", ctypes.c_int32 * 9)]
+        "max_tiles", "max_partials", "max_merge", "pieces_per_worker")] + [
+            ("reserved", ctypes.c_int32 * 8)]
 
 
 class PlanT(ctypes.Structure):

@@ -272,40 +272,60 @@ struct PieceId {
   int row, hk, base, slot, npieces;
 };
 
-// One piece: keys [key0, key1) of kv head hk of request b, for its G q heads.
-// Leaves the piece's state per row group in (m, l, acc).
-template <int DT, int G, int NBUF>
-__device__ __forceinline__ void piece_state(const AttnParams& p, const int32_t* t, int lane,
-                                            PieceId& id, float (&m)[G], float (&l)[G],
-                                            float (&acc)[G][16]) {
-  // Everything that addresses memory is made wave-uniform explicitly (loaded
-  // once per piece by a few lanes, then v_readlane into scalar registers):
-  // the compiler cannot prove these loads uniform across the pieces' stores,
-  // and a per-lane buffer resource would turn every page load into a loop.
-  const int tv = t[lane & 7];
-  const int b = __builtin_amdgcn_readlane(tv, 0), hk = __builtin_amdgcn_readlane(tv, 1);
-  const int pbeg = __builtin_amdgcn_readlane(tv, 2), base = __builtin_amdgcn_readlane(tv, 3);
-  const int key0 = __builtin_amdgcn_readlane(tv, 4), key1_plan = __builtin_amdgcn_readlane(tv, 5);
-  const int slot = __builtin_amdgcn_readlane(tv, 6), npieces = __builtin_amdgcn_readlane(tv, 7);
-  const int row = b;
-  const int Hq = p.num_qo_heads;
-  // The tile carries the request's page offset, so the page ids, q and the
-  // page-table check below are all requested together. The check: the
-  // device page table must agree with the plan (offset, and the key range
-  // within the request's valid tokens); a piece that disagrees reads nothing.
-  const int pv3 = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
+// A piece being set up: tile fields (wave-uniform after v_readlane), its page
+// ids (lane i holds pages i and i+64; at most 128 pages, a planner guarantee)
+// and the device page-table check (kv_indptr[b], kv_indptr[b+1],
+// last_page_len[b] in lanes 0..2).
+struct PieceCtx {
+  PieceId id;
+  int pbeg, key0, key1_plan, first_page, npg_plan;
+  int ids0, ids1, chk;
+};
 
+// Request the tile of piece t (one VGPR, lanes 0..7).
+__device__ __forceinline__ int load_tile(const AttnParams& p, int t, int lane) {
+  return p.tiles[t * 8 + (lane & 7)];
+}
+
+// Take the tile fields and request the page ids and the page-table check.
+__device__ __forceinline__ void open_piece(const AttnParams& p, int tv, int lane, PieceCtx& c) {
+  const int b = __builtin_amdgcn_readlane(tv, 0);
+  c.id.row = b;
+  c.id.hk = __builtin_amdgcn_readlane(tv, 1);
+  c.pbeg = __builtin_amdgcn_readlane(tv, 2);
+  c.id.base = __builtin_amdgcn_readlane(tv, 3);
+  c.key0 = __builtin_amdgcn_readlane(tv, 4);
+  c.key1_plan = __builtin_amdgcn_readlane(tv, 5);
+  c.id.slot = __builtin_amdgcn_readlane(tv, 6);
+  c.id.npieces = __builtin_amdgcn_readlane(tv, 7);
+  c.first_page = c.key0 >> 4;
+  c.npg_plan = c.key1_plan > c.key0 ? ((c.key1_plan + 15) >> 4) - c.first_page : 0;
+  const int32_t* ids_base = p.kv_indices + c.pbeg + c.first_page;
+  c.ids0 = lane < c.npg_plan ? ids_base[lane] : 0;
+  c.ids1 = lane + 64 < c.npg_plan ? ids_base[lane + 64] : 0;
+  c.chk = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
+}
+
+// Stream one piece: keys [key0, key1) of kv head hk of request row, for its G
+// q heads; leaves the state per row group in (m, l, acc). hook(k) runs at
+// the start of steady ring pass k counted from the end (k = 2, 1, 0 for the
+// last three passes; all three run after the loop if the piece has fewer),
+// where the caller overlaps the set-up of its next piece with the loads.
+template <int DT, int G, int NBUF, typename Hook>
+__device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx& c, int lane,
+                                             float (&m)[G], float (&l)[G], float (&acc)[G][16],
+                                             Hook&& hook) {
+  // The context's fields are wave-uniform; readfirstlane says so to the
+  // compiler (it loses track across the loop that hands pieces over), so the
+  // page buffer resources stay scalar.
+  const int hk = __builtin_amdgcn_readfirstlane(c.id.hk);
+  const int row = __builtin_amdgcn_readfirstlane(c.id.row);
+  const int Hq = p.num_qo_heads;
   const int r = lane >> 3;
   const int s = lane & 7;
   const uint32_t ts2 = (uint32_t)p.token_stride * 2u;
   const uint32_t off[4] = {r * ts2 + s * 16u, r * ts2 + 128u + s * 16u, (r + 8) * ts2 + s * 16u,
                            (r + 8) * ts2 + 128u + s * 16u};
-
-  id.row = row;
-  id.hk = hk;
-  id.base = base;
-  id.slot = slot;
-  id.npieces = npieces;
   u32x4 qlo[G], qhi[G];
   const uint16_t* qp = p.q + ((int64_t)row * Hq + hk * G) * 128;
 #pragma unroll
@@ -320,34 +340,33 @@ __device__ __forceinline__ void piece_state(const AttnParams& p, const int32_t* 
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
   }
-
-  const int first_page = key0 >> 4;
-  const int npg_plan = key1_plan > key0 ? ((key1_plan + 15) >> 4) - first_page : 0;
-  // Page ids of the piece (at most 128 pages, a planner guarantee) are fetched
-  // once, before any K/V load is in flight (lane i holds pages i and i+64),
-  // and handed to the scalar unit with v_readlane: waiting on a load later
-  // would drain the in-order load counter.
-  const int32_t* ids_base = p.kv_indices + pbeg + first_page;
-  const int ids0 = lane < npg_plan ? ids_base[lane] : 0;
-  const int ids1 = lane + 64 < npg_plan ? ids_base[lane + 64] : 0;
-  asm volatile("" ::"v"(ids0), "v"(ids1), "v"(pv3));  // all arrive before the page loop starts
-  const int npages_req = __builtin_amdgcn_readlane(pv3, 1) - __builtin_amdgcn_readlane(pv3, 0);
-  const int kv_len = npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(pv3, 2) : 0;
-  const bool agrees = __builtin_amdgcn_readlane(pv3, 0) == pbeg && key1_plan <= kv_len;
+  // The device page table must agree with the plan (offset, and the key
+  // range inside the request's valid tokens); a piece that disagrees reads
+  // nothing.
+  const int npages_req = __builtin_amdgcn_readlane(c.chk, 1) - __builtin_amdgcn_readlane(c.chk, 0);
+  const int kv_len =
+      npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(c.chk, 2) : 0;
+  const int key0 = __builtin_amdgcn_readfirstlane(c.key0);
+  const int first_page = __builtin_amdgcn_readfirstlane(c.first_page);
+  const int key1_plan = __builtin_amdgcn_readfirstlane(c.key1_plan);
+  const bool agrees = __builtin_amdgcn_readlane(c.chk, 0) == __builtin_amdgcn_readfirstlane(c.pbeg) &&
+                      key1_plan <= kv_len;
   const int key1 = agrees ? key1_plan : key0;
-  const int npg = agrees ? npg_plan : 0;
+  const int npg = agrees ? __builtin_amdgcn_readfirstlane(c.npg_plan) : 0;
   auto page_id = [&](int j) -> int {
-    return j < 64 ? __builtin_amdgcn_readlane(ids0, j & 63)
-                  : __builtin_amdgcn_readlane(ids1, j & 63);
+    return j < 64 ? __builtin_amdgcn_readlane(c.ids0, j & 63)
+                  : __builtin_amdgcn_readlane(c.ids1, j & 63);
   };
-  // bytes of the page that hold valid tokens (a buffer load past them returns 0)
+  // bytes of the page that hold valid tokens (a buffer load past them returns
+  // 0); kept scalar so the buffer resource needs no per-lane loop
   auto page_bytes = [&](int j) -> uint32_t {
-    return (uint32_t)min(16, key1 - (first_page + j) * 16) * ts2;
+    return (uint32_t)__builtin_amdgcn_readfirstlane(min(16, key1 - (first_page + j) * 16) * (int)ts2);
   };
   const float scale = p.scale_log2;
 
   PageRegs buf[NBUF];
   int j = 0;
+  int hooks_left = 3;
   if (npg >= 2 * NBUF) {
     // Steady state: every page touched here is full and has a successor, so
     // all loads (prologue included) are unconditional and the next page id is
@@ -366,11 +385,18 @@ __device__ __forceinline__ void piece_state(const AttnParams& p, const int32_t* 
         consume_page<DT, G>(buf[u], qlo, qhi, m, l, acc, scale, true, true);
       }
     };
+    // passes: the peeled first one, then while j + 2 NBUF - 1 < npg
+    const int passes = 1 + (npg - NBUF) / NBUF - ((npg - NBUF) % NBUF == 0 ? 1 : 0);
     // The first pass is peeled so that the q loads are waited for there; in
     // the loop only K/V page loads are then outstanding at the loop header
     // and the compiler's wait counts keep NBUF-1 pages in flight.
+    if (passes - 1 < 3) hook(--hooks_left);
     ring_pass(0);
-    for (j = NBUF; j + 2 * NBUF - 1 < npg; j += NBUF) ring_pass(j);
+    int k = 1;
+    for (j = NBUF; j + 2 * NBUF - 1 < npg; j += NBUF, ++k) {
+      if (passes - 1 - k < hooks_left) hook(--hooks_left);
+      ring_pass(j);
+    }
   } else {
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u)
@@ -388,18 +414,22 @@ __device__ __forceinline__ void piece_state(const AttnParams& p, const int32_t* 
       consume_page<DT, G>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1, tb + r + 8 < key1);
     }
   }
+  while (hooks_left > 0) hook(--hooks_left);
 }
 
 // Worker waves take pieces from 8 queues (one per XCD; bin offsets in
 // worker_ptr) with agent-scope atomic counters: first the queue of their own
 // XCD (workgroup i runs on XCD i mod 8), then the others, so waves that run
-// faster take more pieces. A split unit's pieces publish fp32 partial states;
-// a wave reports a piece's arrival only after its next piece (the partial's
-// stores have long completed by then, so the wait is free), and the last
-// arriving piece merges the unit. The last wave to finish resets the queue
-// heads, so the kernel can be replayed from a graph.
+// faster take more pieces. The next piece is taken near the end of the
+// current one, and its tile and page ids are requested while the current
+// piece's last pages stream, so a new piece starts without a dependent round
+// trip. A split unit's pieces publish fp32 partial states; a wave reports a
+// piece's arrival only after its next piece (the partial's stores have long
+// completed by then, so the wait is free), and the last arriving piece
+// merges the unit. The last wave to finish resets the queue heads, so the
+// kernel can be replayed from a graph.
 template <int DT, int G, int NBUF>
-__global__ __launch_bounds__(256, (G <= 4 ? 2 : 1)) void decode_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int r = lane >> 3, s = lane & 7;
   const int x = blockIdx.x % 8;
@@ -430,9 +460,9 @@ __global__ __launch_bounds__(256, (G <= 4 ? 2 : 1)) void decode_kernel(AttnParam
     }
     return -1;
   };
+  float m[G], l[G], acc[G][16];
   // arrival of a split piece whose partial was published earlier; the last
   // arrival of the unit merges all its pieces and writes the output
-  float m[G], l[G], acc[G][16];
   auto finish_arrival = [&](const PieceId& pd, int arr) {
     if (__builtin_amdgcn_readlane(arr, 0) != pd.npieces - 1) return;
     if (lane == 0) p.counters[pd.base] = 0;
@@ -449,22 +479,32 @@ __global__ __launch_bounds__(256, (G <= 4 ? 2 : 1)) void decode_kernel(AttnParam
   };
 
   PieceId pd = {0, 0, -1, -1, 0};  // pending arrival (slot < 0: none)
+  PieceCtx cur, nxt;
   int t = resolve(fetch_add(head(x)));
+  if (t >= 0) open_piece(p, load_tile(p, t, lane), lane, cur);
   while (t >= 0) {
-    PieceId id;
-    piece_state<DT, G, NBUF>(p, p.tiles + t * 8, lane, id, m, l, acc);
-    // the arrival and the next take are requested first; their round trips
-    // overlap the reduction and the stores below
+    // overlapped set-up of the next piece: take it (pass 2 from the end),
+    // request its tile (pass 1), open it (pass 0)
+    int issued = 0, tn = -1, tvn = 0;
+    auto hook = [&](int k) {
+      if (k == 2) issued = fetch_add(head(x));
+      if (k == 1) {
+        tn = resolve(issued);
+        if (tn >= 0) tvn = load_tile(p, tn, lane);
+      }
+      if (k == 0 && tn >= 0) open_piece(p, tvn, lane, nxt);
+    };
+    stream_piece<DT, G, NBUF>(p, cur, lane, m, l, acc, hook);
     const int arr = pd.slot >= 0 ? arrive(pd) : 0;
-    const int next = fetch_add(head(x));
     merge_row_groups<G>(m, l, acc);
-    if (id.slot < 0)
-      write_final<DT, G>(p, id.row, id.hk, r, s, m, l, acc);
+    if (cur.id.slot < 0)
+      write_final<DT, G>(p, cur.id.row, cur.id.hk, r, s, m, l, acc);
     else
-      write_partial<G>(p, id.slot, r, s, m, l, acc);
+      write_partial<G>(p, cur.id.slot, r, s, m, l, acc);
     if (pd.slot >= 0) finish_arrival(pd, arr);
-    pd = id;
-    t = resolve(next);
+    pd = cur.id;
+    t = tn;
+    cur = nxt;
   }
   if (pd.slot >= 0) finish_arrival(pd, arrive(pd));
   const int done = __builtin_amdgcn_readlane(fetch_add(head(8)), 0);

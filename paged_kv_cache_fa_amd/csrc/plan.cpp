@@ -69,7 +69,7 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
     return FA_ERR_INVALID;
   }
   if (g.num_cu < 0 || g.tiles_per_cu < 0 || g.min_chunk_pages < 0 || g.qo_tile < 0 ||
-      g.max_tiles < 0 || g.max_partials < 0 || g.max_merge < 0) {
+      g.max_tiles < 0 || g.max_partials < 0 || g.max_merge < 0 || g.pieces_per_worker < 0) {
     set_error("negative plan knob");
     return FA_ERR_INVALID;
   }
@@ -85,6 +85,7 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
   if (!g.num_cu) g.num_cu = 256;
   if (!g.tiles_per_cu) g.tiles_per_cu = app ? 2 : 4;
   if (!g.min_chunk_pages) g.min_chunk_pages = 1;
+  g.pieces_per_worker = app ? 0 : (g.pieces_per_worker ? g.pieces_per_worker : kPiecesPerWorker);
   // an append tile holds 128 query columns: the G heads x 128 / G positions
   g.qo_tile = app ? (g.qo_tile ? g.qo_tile : 128 / G) : 1;
   if (app && g.qo_tile > 128 / G) {
@@ -101,8 +102,8 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
     mm = g.max_merge ? g.max_merge : target;
   } else {
     const int64_t units = (int64_t)g.max_batch * g.num_kv_heads;
-    mt = g.max_tiles ? g.max_tiles : kPiecesPerWorker * target + units;
-    mp = g.max_partials ? g.max_partials : kPiecesPerWorker * target + units;
+    mt = g.max_tiles ? g.max_tiles : (int64_t)g.pieces_per_worker * target + units;
+    mp = g.max_partials ? g.max_partials : (int64_t)g.pieces_per_worker * target + units;
     mm = g.max_merge ? g.max_merge : units;
   }
   if (target > (1 << 22)) {
@@ -171,7 +172,7 @@ fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, cons
   int64_t W = 0;
   for (int b = 0; b < batch; ++b) W += cdiv(kv_lens[b], ps) * Hkv;
   const int64_t Q = std::min<int64_t>(
-      kMaxPiecePages, std::max<int64_t>(g.min_chunk_pages, cdiv(W, S * kPiecesPerWorker)));
+      kMaxPiecePages, std::max<int64_t>(g.min_chunk_pages, cdiv(W, S * g.pieces_per_worker)));
   // pieces, slots and merge entries in unit order
   int64_t ngroups = 0, nmerge = 0, slots = 0;
   for (int b = 0; b < batch; ++b) {

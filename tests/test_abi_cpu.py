@@ -50,7 +50,7 @@ def _compare(g, lens, qo_indptr=None, causal=False, **spec_knobs):
     r = st.resolved
     knobs = dict(num_cu=r.num_cu, tiles_per_cu=r.tiles_per_cu, min_chunk_pages=r.min_chunk_pages,
                  qo_tile=r.qo_tile, max_tiles=r.max_tiles, max_partials=r.max_partials,
-                 max_merge=r.max_merge)
+                 max_merge=r.max_merge, pieces_per_worker=r.pieces_per_worker)
     spec = plan_spec(_indptr(lens), lens, len(lens), g.num_qo_heads, g.num_kv_heads, 128, 16,
                      max_batch=g.max_batch, qo_indptr=qo_indptr, causal=causal,
                      max_qo_tokens=g.max_qo_tokens, **knobs)
@@ -84,9 +84,9 @@ def test_plan_default_knobs_match_the_spec_defaults():
         hq = 8 * hkv if hkv < 8 else 32
         d = default_knobs(hkv, mb, mq, mode == "append", group=hq // hkv)
         assert (r.num_cu, r.tiles_per_cu, r.min_chunk_pages, r.qo_tile, r.max_tiles,
-                r.max_partials, r.max_merge) == tuple(d[k] for k in (
+                r.max_partials, r.max_merge, r.pieces_per_worker) == tuple(d[k] for k in (
                     "num_cu", "tiles_per_cu", "min_chunk_pages", "qo_tile", "max_tiles",
-                    "max_partials", "max_merge"))
+                    "max_partials", "max_merge", "pieces_per_worker"))
 
 
 def test_plan_bit_exact_append_and_cascade_prefix():
@@ -106,6 +106,7 @@ def test_plan_bit_exact_random():
         knobs = dict(num_cu=int(rng.integers(1, 40)), tiles_per_cu=int(rng.integers(1, 9)),
                      min_chunk_pages=int(rng.integers(1, 5)))
         if it % 2:
+            knobs["pieces_per_worker"] = int(rng.integers(1, 5))
             _compare(_geom("decode", max(B, 1) + int(rng.integers(0, 3)), G * Hkv, Hkv, **knobs),
                      lens)
         else:

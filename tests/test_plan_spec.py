@@ -214,7 +214,7 @@ def test_random_geometries():
                      min_chunk_pages=int(rng.integers(1, 4)))
         if it % 2:
             p = plan_spec(_indptr(lens), lens, B, G * Hkv, Hkv, 128, 16, max_batch=max(B, 1),
-                          **knobs)
+                          pieces_per_worker=int(rng.integers(1, 5)), **knobs)
             check_decode_invariants(p, lens, Hkv)
         else:
             ql = np.minimum(rng.integers(0, 70, size=B), lens)
