@@ -216,12 +216,15 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
  *               does not split its keys; split prefix chunks stay as fp32
  *               partial states in the prefix plan's workspace.)
  *  out / lse    device [batch, num_qo_heads, head_dim] / fp32 (lse may be NULL).
- * The suffix decode runs on `stream` and the prefix pass on `side_stream`
- * concurrently (fork/join with events of the suffix plan; capturable); then
- * one combine kernel on `stream` merges, per (request, head), the prefix
- * chunks and the suffix state by log-sum-exp. side_stream NULL or equal to
- * stream runs the three kernels in order on `stream`. Other arguments as
- * fa_decode. Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
+ * The suffix decode runs on `suffix_stream` and the prefix pass on
+ * `prefix_stream` (each NULL or equal to `stream` = run on `stream`); streams
+ * other than `stream` are forked from it and joined back with events of the
+ * suffix plan (capturable). Then one combine kernel on `stream` merges, per
+ * (request, head), the prefix chunks and the suffix state by log-sum-exp.
+ * (Measured on MI355X at batch 256 / 16k prefix: running the two passes
+ * concurrently, on shared or on disjoint compute units, was slower than in
+ * order on one stream.) Other arguments as fa_decode. Errors: FA_ERR_INVALID,
+ * FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
 fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan, const void* q,
                      const void* k_pages, const void* v_pages, int64_t page_stride,
                      int64_t token_stride, int64_t head_stride, const int32_t* prefix_qo_indptr_d,
@@ -229,7 +232,8 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
                      const int32_t* prefix_last_page_len_d, const int32_t* kv_indices_d,
                      const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
                      void* prefix_out, float* prefix_lse, void* suffix_out, float* suffix_lse,
-                     void* out, float* lse, void* stream, void* side_stream);
+                     void* out, float* lse, void* stream, void* prefix_stream,
+                     void* suffix_stream);
 
 /* Merge two attention states computed over disjoint key sets ([Guide]
  * "Cascade attention for shared prefixes"):

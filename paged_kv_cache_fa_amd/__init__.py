@@ -201,11 +201,12 @@ def append(p: Plan, q, qo_indptr, k_pages, v_pages, page_stride: int, token_stri
 def cascade(prefix_plan: Plan, suffix_plan: Plan, q, k_pages, v_pages, page_stride: int,
             token_stride: int, head_stride: int, prefix_qo_indptr, prefix_indices, prefix_indptr,
             prefix_last_page_len, kv_indices, kv_indptr, last_page_len, sm_scale: float = 0.0,
-            states=None, out=None, lse=None, stream=None, side_stream=None):
+            states=None, out=None, lse=None, stream=None, side_stream=None, suffix_stream=None):
     """Cascade attention over one shared prefix (see fa_cascade). ``states`` is
     (prefix_out, prefix_lse, suffix_out, suffix_lse) scratch, allocated if None;
-    ``side_stream`` (a torch stream or handle) runs the prefix pass beside the
-    suffix decode. Returns (out, lse)."""
+    ``side_stream`` / ``suffix_stream`` (torch streams or handles) run the
+    prefix pass / the suffix decode, forked from and joined back to ``stream``.
+    Returns (out, lse)."""
     torch = _torch()
     B, H = q.shape[0], q.shape[1]
     if states is None:
@@ -214,12 +215,13 @@ def cascade(prefix_plan: Plan, suffix_plan: Plan, q, k_pages, v_pages, page_stri
     out, lse = _alloc_out(q, out, lse, B, H)
     po, pl_, so, sl = states
     side = None if side_stream is None else _stream(side_stream)
+    suf = None if suffix_stream is None else _stream(suffix_stream)
     check(prefix_plan._lib.fa_cascade(
         ctypes.byref(prefix_plan._plan), ctypes.byref(suffix_plan._plan), _ptr(q), _ptr(k_pages),
         _ptr(v_pages), page_stride, token_stride, head_stride, _ptr(prefix_qo_indptr),
         _ptr(prefix_indices), _ptr(prefix_indptr), _ptr(prefix_last_page_len), _ptr(kv_indices),
         _ptr(kv_indptr), _ptr(last_page_len), float(sm_scale), _ptr(po), _ptr(pl_), _ptr(so),
-        _ptr(sl), _ptr(out), _ptr(lse), _stream(stream), side))
+        _ptr(sl), _ptr(out), _ptr(lse), _stream(stream), side, suf))
     return out, lse
 
 

@@ -83,7 +83,7 @@ def load(path: str = LIB_PATH):
         "fa_decode": [PP, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
         "fa_append": [PP, P, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
         "fa_cascade": [PP, PP, P, P, P, I64, I64, I64, P, P, P, P, P, P, P, F32, P, P, P, P, P, P,
-                       P, P],
+                       P, P, P],
         "fa_merge_state": [P, P, P, P, P, P, I64, I32, I32, I32, P],
         "fa_merge_states": [P, P, I64, I32, I32, I32, I32, P, P, P],
         "fa_status_string": [I32],

@@ -215,7 +215,7 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
     pl->planned = 0;
     return hip_fail(e, "plan upload");
   }
-  for (void** slot : {&pl->upload_event, &pl->fork_event, &pl->join_event}) {
+  for (void** slot : {&pl->upload_event, &pl->fork_event, &pl->join_event, &pl->join2_event}) {
     if (*slot) continue;
     hipEvent_t ev;
     e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
@@ -277,7 +277,7 @@ fa_status fa_plan_destroy(fa_plan_t* plan) {
   if (!plan) return FA_OK;
   PlanImpl* pl = impl(plan);
   if (pl->magic == kPlanMagic) {
-    for (void* ev : {pl->upload_event, pl->fork_event, pl->join_event})
+    for (void* ev : {pl->upload_event, pl->fork_event, pl->join_event, pl->join2_event})
       if (ev) hipEventDestroy(static_cast<hipEvent_t>(ev));
   }
   memset(plan, 0, sizeof(*plan));
@@ -337,7 +337,8 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
                      const int32_t* prefix_last_page_len_d, const int32_t* kv_indices_d,
                      const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
                      void* prefix_out, float* prefix_lse, void* suffix_out, float* suffix_lse,
-                     void* out, float* lse, void* stream, void* side_stream) {
+                     void* out, float* lse, void* stream, void* prefix_stream,
+                     void* suffix_stream) {
   const PlanImpl* pp = prefix_plan ? impl(prefix_plan) : nullptr;
   const PlanImpl* sp = suffix_plan ? impl(suffix_plan) : nullptr;
   fa_status st = check_run_args(pp, FA_MODE_APPEND, q, k_pages, v_pages, page_stride, token_stride,
@@ -368,35 +369,43 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
     return FA_ERR_INVALID;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipStream_t side = static_cast<hipStream_t>(side_stream);
-  const bool fork = side && side != s;
+  hipStream_t s_pre = prefix_stream ? static_cast<hipStream_t>(prefix_stream) : s;
+  hipStream_t s_suf = suffix_stream ? static_cast<hipStream_t>(suffix_stream) : s;
+  const bool fork_pre = s_pre != s, fork_suf = s_suf != s;
   hipError_t e = hipSuccess;
-  if (fork) {
-    if (!sp->fork_event || !sp->join_event) {
+  if (fork_pre || fork_suf) {
+    if (!sp->fork_event || !sp->join_event || !sp->join2_event) {
       set_error("cascade: the suffix plan was not uploaded to a device workspace");
       return FA_ERR_NOT_PLANNED;
     }
     e = hipEventRecord(static_cast<hipEvent_t>(sp->fork_event), s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side, static_cast<hipEvent_t>(sp->fork_event), 0);
+    if (e == hipSuccess && fork_pre)
+      e = hipStreamWaitEvent(s_pre, static_cast<hipEvent_t>(sp->fork_event), 0);
+    if (e == hipSuccess && fork_suf)
+      e = hipStreamWaitEvent(s_suf, static_cast<hipEvent_t>(sp->fork_event), 0);
     if (e != hipSuccess) return hip_fail(e, "cascade fork");
   }
-  // suffix decode (HBM-bound) first on the main stream, the shared-prefix
-  // pass (MFMA-bound) beside it
+  // suffix decode (HBM-bound) and the shared-prefix pass (MFMA-bound)
   const int G = gs.num_qo_heads / gs.num_kv_heads;
   const AttnParams ps = make_params(sp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
                                     kv_indices_d, kv_indptr_d, last_page_len_d, nullptr, sm_scale,
                                     suffix_out, suffix_lse);
-  e = launch_decode(ps, gs.dtype, G, sp->num_workers, s);
+  e = launch_decode(ps, gs.dtype, G, sp->num_workers, s_suf);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   AttnParams pa = make_params(pp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
                               prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
                               prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
   pa.defer_merge = 1;  // the prefix chunks are merged together with the suffix below
-  e = launch_append(pa, gp.dtype, G, gp.max_tiles, fork ? side : s);
+  e = launch_append(pa, gp.dtype, G, gp.max_tiles, s_pre);
   if (e != hipSuccess) return hip_fail(e, "append kernel launch");
-  if (fork) {
-    e = hipEventRecord(static_cast<hipEvent_t>(sp->join_event), side);
+  if (fork_pre) {
+    e = hipEventRecord(static_cast<hipEvent_t>(sp->join_event), s_pre);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(sp->join_event), 0);
+    if (e != hipSuccess) return hip_fail(e, "cascade join");
+  }
+  if (fork_suf) {
+    e = hipEventRecord(static_cast<hipEvent_t>(sp->join2_event), s_suf);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(sp->join2_event), 0);
     if (e != hipSuccess) return hip_fail(e, "cascade join");
   }
   e = launch_cascade_merge(pa.header, pa.merge, pa.part_o, pa.part_lse, prefix_out, prefix_lse,

@@ -46,8 +46,9 @@ struct PlanImpl {
   void* upload_event;  // hipEvent_t recorded after the copy out of host_ws
   void* zeroed_ws;     // device workspace whose counters were cleared
   size_t zeroed_bytes;
-  void* fork_event;    // hipEvent_t pair for the two-stream cascade call
+  void* fork_event;    // hipEvent_t fork / join events for the cascade call's streams
   void* join_event;
+  void* join2_event;
   void* upload_host;   // host workspace whose device mapping was looked up
   void* upload_src;    // its device-visible address (pinned memory), or null
 };

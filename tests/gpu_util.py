@@ -104,7 +104,7 @@ def oracle_append(wl, rows=None):
 
 
 def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, fused=False,
-                side_stream=None, **knobs):
+                side_stream=None, suffix_stream=None, **knobs):
     """Shared-prefix pass (non-causal append of every request's query over the
     prefix) + private-suffix decode + merge_state, as three calls or as one
     fa_cascade call (optionally with the prefix pass on ``side_stream``).
@@ -125,7 +125,7 @@ def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, fused=False
         out, lse = fa.cascade(prefix_plan, suffix_plan, dw.q, dw.k, dw.v, *dw.strides, qo,
                               dw.prefix_indices, dw.prefix_indptr, dw.prefix_last_page_len,
                               dw.kv_indices, dw.kv_indptr, dw.last_page_len,
-                              side_stream=side_stream)
+                              side_stream=side_stream, suffix_stream=suffix_stream)
         return out, lse, (prefix_plan, suffix_plan)
     o_p, l_p = fa.append(prefix_plan, dw.q, qo, dw.k, dw.v, *dw.strides, dw.prefix_indices,
                          dw.prefix_indptr, dw.prefix_last_page_len)

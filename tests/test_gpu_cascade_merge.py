@@ -109,7 +109,7 @@ def test_cascade_small():
 def test_cascade_call(prefix_len, num_cu):
     """fa_cascade matches the oracle whether the prefix pass splits its keys
     (chunk partials merged with the suffix in the combine kernel) or not, and
-    gives the same bits serially and with the prefix pass on a side stream."""
+    gives the same bits serially and with the passes forked onto other streams."""
     import torch
     wl = make_cascade(prefix_len, [5, 16, 17, 300, 1, 64, 900, 0], 32, 8, "bf16", 22,
                       mode="test")
@@ -119,8 +119,12 @@ def test_cascade_call(prefix_len, num_cu):
     o1, l1, _ = run_cascade(dw, *plans, fused=True)
     o1, l1 = o1.clone(), l1.clone()
     o2, l2, _ = run_cascade(dw, *plans, fused=True, side_stream=torch.cuda.Stream())
+    o2, l2 = o2.clone(), l2.clone()
+    o3, l3, _ = run_cascade(dw, *plans, fused=True, side_stream=torch.cuda.Stream(),
+                            suffix_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
     assert_close(to_f64(o1), to_f64(l1), *oracle_cascade(wl), what="fa_cascade")
 
 
