@@ -14,6 +14,8 @@ Reported alongside in the same JSON line:
     suffix decode + merge_state), as HBM GB/s with the prefix counted once;
   * ``append``: causal append of 16 x 512 rows onto 4096 cached tokens, as
     MFMA utilisation (584.2 GFLOP of unmasked work per step);
+  * ``fp8``: the batch-64 decode with an E4M3 page pool (per-tensor scales,
+    bf16 q / out), as HBM GB/s with one byte per K/V element;
   * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
     from HIP events on its stream), with HBM traffic from rocprofv3 counters
     when the stored counter summary matches the current kernel source;
@@ -54,7 +56,8 @@ def io_bytes(rows, hq, d=128, elt=2) -> int:
 
 def algorithmic_bytes(wl) -> int:
     """Valid K/V bytes of every request (a shared prefix once) plus q, out, lse."""
-    b = kv_bytes(wl.kv_lens, wl.num_kv_heads) + io_bytes(wl.rows, wl.num_qo_heads)
+    elt = 1 if wl.kv_dtype == "e4m3" else 2
+    b = kv_bytes(wl.kv_lens, wl.num_kv_heads, elt=elt) + io_bytes(wl.rows, wl.num_qo_heads)
     if wl.prefix_len:
         b += kv_bytes([wl.prefix_len], wl.num_kv_heads)
     return b
@@ -76,8 +79,11 @@ def append_flops(wl) -> float:
 def _dev(wl, device, min_rotation_bytes):
     import torch
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
-    pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
-    copies = max(1, math.ceil(min_rotation_bytes / max(1, pool.numel() * 2)))
+    if wl.kv_dtype == "e4m3":
+        pool = torch.from_numpy(wl.pool).to(device)
+    else:
+        pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
+    copies = max(1, math.ceil(min_rotation_bytes / max(1, pool.numel() * pool.element_size())))
     pools = [pool] + [pool.clone() for _ in range(copies - 1)]
     q = torch.from_numpy(wl.q.view(np.int16)).to(device).view(dt)
     _, _, ps, hkv, d = wl.pool.shape
@@ -119,7 +125,8 @@ class DecodeBench(Timed):
         self.kv_indptr = _i32(wl.kv_indptr, device)
         self.kv_indices = _i32(wl.kv_indices, device)
         self.last = _i32(wl.last_page_len, device)
-        geom = fa.geometry("decode", wl.dtype, wl.batch, wl.num_qo_heads, wl.num_kv_heads, **knobs)
+        geom = fa.geometry("decode", wl.dtype, wl.batch, wl.num_qo_heads, wl.num_kv_heads,
+                           kv_dtype=wl.kv_dtype, **knobs)
         self.plan = fa.Plan(geom, device=device)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(wl.rows, wl.num_qo_heads, dtype=torch.float32, device=device)
@@ -131,8 +138,13 @@ class DecodeBench(Timed):
         self.plan.plan(self.indptr_h, self.lens_h)
         if ev is not None:
             ev[0].record()
-        self.fa.decode(self.plan, self.q, pool[:, 0], pool[:, 1], *self.strides, self.kv_indices,
-                       self.kv_indptr, self.last, out=self.out, lse=self.lse)
+        args = (self.plan, self.q, pool[:, 0], pool[:, 1], *self.strides, self.kv_indices,
+                self.kv_indptr, self.last)
+        if self.wl.kv_dtype is None:
+            self.fa.decode(*args, out=self.out, lse=self.lse)
+        else:
+            self.fa.decode_scaled(*args, k_scale=self.wl.k_scale, v_scale=self.wl.v_scale,
+                                  out=self.out, lse=self.lse)
         if ev is not None:
             ev[1].record()
 
@@ -266,7 +278,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="decode workload for the headline (1-3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip batch128/cascade/append")
-    ap.add_argument("--parts", default="batch128,cascade,append",
+    ap.add_argument("--parts", default="batch128,cascade,append,fp8",
                     help="comma list of the secondary workloads to run after the headline")
     ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
     ap.add_argument("--copy-probe", action="store_true",
@@ -361,6 +373,22 @@ def main():
                           "flops": f5, "kernel_ms": round(k5, 5), "ms_per_step": round(s5, 5),
                           "tokens_per_s": round(w5.rows / (s5 * 1e-3), 1)}
         del b5, w5
+        torch.cuda.empty_cache()
+    if "fp8" in parts:
+        w8 = make_config(2, kv_dtype="e4m3")
+        b8 = DecodeBench(w8, **knobs)
+        s8, k8 = b8.run(args.steps, args.warmup)
+        n8 = algorithmic_bytes(w8)
+        line["fp8"] = {"workload": f"config2 with an E4M3 page pool: {CONFIG_NAMES[2]}",
+                       "kv_dtype": "e4m3", "k_scale": w8.k_scale, "v_scale": w8.v_scale,
+                       "GB/s": round(n8 / (s8 * 1e-3) / 1e9, 2),
+                       "pct_of_hbm_peak": round(100 * n8 / (s8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                       "kernel_GB/s": round(n8 / (k8 * 1e-3) / 1e9, 2),
+                       "kernel_frac": round(n8 / (k8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "tokens_per_s": round(w8.batch / (s8 * 1e-3), 1),
+                       "ms_per_step": round(s8, 5), "kernel_ms": round(k8, 5),
+                       "algorithmic_bytes": n8}
+        del b8, w8
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

@@ -36,7 +36,8 @@
  *    `s_j = sm_scale * <q, k_j>`; `sm_scale <= 0` selects 1/sqrt(head_dim).
  *  - Query head h reads kv head h / (num_qo_heads / num_kv_heads).
  *  - Supported: head_dim 128, page_size 16, num_qo_heads / num_kv_heads in
- *    {1, 2, 4, 8}, fp16 or bf16 q / K / V / out with fp32 accumulation. Other
+ *    {1, 2, 4, 8}, fp16 or bf16 q / K / V / out with fp32 accumulation, and
+ *    for decode also FP8 (E4M3) K/V pages under fp16 or bf16 q / out. Other
  *    shapes return FA_ERR_UNSUPPORTED.
  */
 #ifndef PAGED_KV_FA_H_
@@ -59,7 +60,10 @@ typedef int32_t fa_status;
 #define FA_ERR_CAPTURING (-6)   /* fa_plan called on a stream that is capturing a graph */
 #define FA_ERR_NOT_PLANNED (-7) /* run call with a plan that has no device upload */
 
-typedef enum { FA_F16 = 0, FA_BF16 = 1, FA_F32 = 2 } fa_dtype;
+/* FA_E4M3: OCP 8-bit floating point E4M3 (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, subnormals, no infinities, NaN = S.1111.111, max 448), one
+ * byte per element; a K/V page-pool type only (fa_geometry.kv_dtype). */
+typedef enum { FA_F16 = 0, FA_BF16 = 1, FA_F32 = 2, FA_E4M3 = 3 } fa_dtype;
 typedef enum { FA_MODE_DECODE = 0, FA_MODE_APPEND = 1 } fa_mode;
 
 /* Static geometry: fixed for the life of a captured graph. Zero knobs take
@@ -83,7 +87,10 @@ typedef struct {
   int32_t max_partials;
   int32_t max_merge;
   int32_t pieces_per_worker; /* decode: pieces per worker wave the piece size aims at (default 1) */
-  int32_t reserved[8];
+  int32_t kv_dtype;        /* K/V page-pool type: 0 or `dtype` = the same as q; FA_E4M3 = FP8
+                              pages with per-tensor scales (decode only, see fa_decode_scaled).
+                              Resolved to `dtype` when the same. */
+  int32_t reserved[7];
 } fa_geometry;
 
 /* Caller-allocated plan object. Zero it before first use; release the HIP
@@ -184,6 +191,27 @@ fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
                     int64_t head_stride, const int32_t* kv_indices_d, const int32_t* kv_indptr_d,
                     const int32_t* last_page_len_d, float sm_scale, void* out, float* lse,
                     void* stream);
+
+/* Decode over a paged KV cache whose stored values carry one scale per tensor
+ * ([Tool] "FlashInfer", "What it does": FP8 compute for attention; [Guide]
+ * "Features (from the repository README)": FP8 with per-tensor scaling).
+ * The stored element e of K stands for k_scale * e, of V for v_scale * e:
+ * s_j = sm_scale * k_scale * <q, k_j> and out = v_scale * sum_j p_j v_j, with
+ * lse over those s_j. The pages' element type is the plan's kv_dtype: with
+ * FA_E4M3 every page element is one byte, so page_stride, token_stride and
+ * head_stride count bytes and must be multiples of 16; with 16-bit pages the
+ * call is fa_decode with the two scales. K/V codes are widened exactly and
+ * the products accumulate in fp32, as in fa_decode.
+ *  k_scale, v_scale  finite and > 0.
+ * Other arguments as fa_decode. Errors: FA_ERR_INVALID (also for a bad
+ * scale), FA_ERR_NOT_PLANNED, FA_ERR_HIP. fa_decode on an FA_E4M3 plan is
+ * this call with both scales 1. */
+fa_status fa_decode_scaled(const fa_plan_t* plan, const void* q, const void* k_pages,
+                           const void* v_pages, int64_t page_stride, int64_t token_stride,
+                           int64_t head_stride, const int32_t* kv_indices_d,
+                           const int32_t* kv_indptr_d, const int32_t* last_page_len_d,
+                           float sm_scale, float k_scale, float v_scale, void* out, float* lse,
+                           void* stream);
 
 /* Append / prefill over the paged KV cache, causal or not as planned ([Guide]
  * "Features (from the repository README)": prefill and append kernels). The

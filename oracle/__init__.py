@@ -36,5 +36,6 @@ from .attention import (  # noqa: F401
     cascade,
     cascade_direct,
 )
+from .fp8 import e4m3_value  # noqa: F401
 from .merge import merge_state, merge_states  # noqa: F401
 from .plan_spec import plan_spec, PlanSpecError  # noqa: F401

@@ -33,11 +33,15 @@ from typing import Optional, Sequence
 
 import numpy as np
 
+from .fp8 import e4m3_value
 from .merge import merge_state
 
 
 def upcast(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact widening of stored bf16/fp16 bit patterns to float64."""
+    """Exact widening of stored bf16/fp16 bit patterns (or E4M3 byte codes,
+    unscaled) to float64."""
+    if dtype == "e4m3":
+        return e4m3_value(bits)
     bits = np.asarray(bits, dtype=np.uint16)
     if dtype == "bf16":
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
@@ -61,19 +65,21 @@ def request_kv_len(kv_indptr: np.ndarray, last_page_len: np.ndarray, page_size: 
 
 
 def gather_request_kv(pool: np.ndarray, dtype: str, kv_indptr, kv_indices, last_page_len,
-                      page_size: int, b: int):
+                      page_size: int, b: int, k_scale: float = 1.0, v_scale: float = 1.0):
     """K and V of request b as float64 ``[kv_len, kv_heads, head_dim]``.
 
     Token t is read from page ``pages[t // page_size]`` at slot
-    ``t % page_size``; slots past ``last_page_len`` are never touched.
+    ``t % page_size``; slots past ``last_page_len`` are never touched. The
+    stored values are multiplied by the per-tensor scales (1 for 16-bit
+    pools; see ``oracle.fp8`` for the FP8 reading).
     """
     pages = request_pages(kv_indptr, kv_indices, b)
     L = request_kv_len(kv_indptr, last_page_len, page_size, b)
     t = np.arange(L)
     page_of_token = pages[t // page_size]
     slot_of_token = t % page_size
-    K = upcast(pool[page_of_token, 0, slot_of_token], dtype)
-    V = upcast(pool[page_of_token, 1, slot_of_token], dtype)
+    K = k_scale * upcast(pool[page_of_token, 0, slot_of_token], dtype)
+    V = v_scale * upcast(pool[page_of_token, 1, slot_of_token], dtype)
     return K, V
 
 
@@ -119,18 +125,23 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
 
 def decode(q_bits: np.ndarray, pool: np.ndarray, dtype: str, kv_indptr, kv_indices,
            last_page_len, page_size: int, scale: Optional[float] = None,
-           requests: Optional[Sequence[int]] = None):
+           requests: Optional[Sequence[int]] = None, kv_dtype: Optional[str] = None,
+           k_scale: float = 1.0, v_scale: float = 1.0):
     """Decode: one query row per request over its paged KV.
 
-    Returns ``out [n, Hq, D]``, ``lse [n, Hq]`` for the requested rows (all
-    requests by default, in order).
+    ``dtype`` is the query type; the pool holds ``kv_dtype`` (default: the
+    same), scaled by ``k_scale`` / ``v_scale``. Returns ``out [n, Hq, D]``,
+    ``lse [n, Hq]`` for the requested rows (all requests by default, in
+    order).
     """
     D = q_bits.shape[-1]
     scale = default_scale(D) if scale is None else scale
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
     reqs = range(q_bits.shape[0]) if requests is None else list(requests)
     outs, lses = [], []
     for b in reqs:
-        K, V = gather_request_kv(pool, dtype, kv_indptr, kv_indices, last_page_len, page_size, b)
+        K, V = gather_request_kv(pool, kv_dtype, kv_indptr, kv_indices, last_page_len, page_size,
+                                 b, k_scale, v_scale)
         o, s = attend(upcast(q_bits[b: b + 1], dtype), K, V, scale)
         outs.append(o[0])
         lses.append(s[0])

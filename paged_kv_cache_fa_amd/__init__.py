@@ -7,7 +7,8 @@ tensors (used for memory and streams only); there is no CPU fallback — if the
 library is missing, the import of any entry point raises.
 
 Entry points (same names as the C ABI): ``workspace_size``, ``plan`` (returns a
-``Plan``), ``decode``, ``append``, ``merge_state``, ``merge_states``.
+``Plan``), ``decode``, ``decode_scaled``, ``append``, ``cascade``,
+``merge_state``, ``merge_states``.
 """
 from __future__ import annotations
 
@@ -17,10 +18,10 @@ from typing import Optional
 import numpy as np
 
 from . import _lib
-from ._lib import (FA_BF16, FA_F16, FA_F32, FA_MODE_APPEND, FA_MODE_DECODE, FAError,  # noqa: F401
-                   Geometry, PlanStats, PlanT, check, load)
+from ._lib import (FA_BF16, FA_E4M3, FA_F16, FA_F32, FA_MODE_APPEND, FA_MODE_DECODE,  # noqa: F401
+                   FAError, Geometry, PlanStats, PlanT, check, load)
 
-_DTYPE_CODES = {"bf16": FA_BF16, "fp16": FA_F16, "fp32": FA_F32}
+_DTYPE_CODES = {"bf16": FA_BF16, "fp16": FA_F16, "fp32": FA_F32, "e4m3": FA_E4M3}
 
 
 def _torch():
@@ -29,11 +30,12 @@ def _torch():
 
 
 def dtype_code(dt) -> int:
-    """Map "bf16"/"fp16"/"fp32" or a torch dtype to the ABI dtype code."""
+    """Map "bf16"/"fp16"/"fp32"/"e4m3" or a torch dtype to the ABI dtype code."""
     if isinstance(dt, str):
         return _DTYPE_CODES[dt]
     torch = _torch()
-    return {torch.bfloat16: FA_BF16, torch.float16: FA_F16, torch.float32: FA_F32}[dt]
+    return {torch.bfloat16: FA_BF16, torch.float16: FA_F16, torch.float32: FA_F32,
+            torch.float8_e4m3fn: FA_E4M3}[dt]
 
 
 def geometry(mode: str, dtype, max_batch: int, num_qo_heads: int, num_kv_heads: int,
@@ -49,6 +51,8 @@ def geometry(mode: str, dtype, max_batch: int, num_qo_heads: int, num_kv_heads: 
     g.head_dim = head_dim
     g.page_size = page_size
     for k, v in knobs.items():
+        if k == "kv_dtype":
+            v = 0 if v is None else dtype_code(v)
         setattr(g, k, int(v))
     return g
 
@@ -183,6 +187,21 @@ def decode(p: Plan, q, k_pages, v_pages, page_stride: int, token_stride: int, he
                            page_stride, token_stride, head_stride, _ptr(kv_indices),
                            _ptr(kv_indptr), _ptr(last_page_len), float(sm_scale), _ptr(out),
                            _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def decode_scaled(p: Plan, q, k_pages, v_pages, page_stride: int, token_stride: int,
+                  head_stride: int, kv_indices, kv_indptr, last_page_len, sm_scale: float = 0.0,
+                  k_scale: float = 1.0, v_scale: float = 1.0, out=None, lse=None, stream=None):
+    """Paged decode with per-tensor K/V scales, e.g. over an E4M3 page pool
+    (see fa_decode_scaled; strides count pool elements, bytes for E4M3).
+    Returns (out, lse)."""
+    out, lse = _alloc_out(q, out, lse, q.shape[0], q.shape[1])
+    check(p._lib.fa_decode_scaled(ctypes.byref(p._plan), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                  page_stride, token_stride, head_stride, _ptr(kv_indices),
+                                  _ptr(kv_indptr), _ptr(last_page_len), float(sm_scale),
+                                  float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
+                                  _stream(stream)))
     return out, lse
 
 

@@ -21,13 +21,13 @@ STATUS_NAMES = {
     FA_ERR_CAPTURING: "CAPTURING", FA_ERR_NOT_PLANNED: "NOT_PLANNED",
 }
 
-FA_F16, FA_BF16, FA_F32 = 0, 1, 2
+FA_F16, FA_BF16, FA_F32, FA_E4M3 = 0, 1, 2, 3
 FA_MODE_DECODE, FA_MODE_APPEND = 0, 1
 
 # every symbol declared in include/fa.h
 EXPORTED = [
     "fa_workspace_size", "fa_plan", "fa_plan_info", "fa_plan_tiles", "fa_plan_destroy",
-    "fa_decode", "fa_append", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
+    "fa_decode", "fa_decode_scaled", "fa_append", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
     "fa_last_error",
 ]
 
@@ -36,8 +36,8 @@ class Geometry(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "mode", "dtype", "max_batch", "max_qo_tokens", "num_qo_heads", "num_kv_heads",
         "head_dim", "page_size", "num_cu", "tiles_per_cu", "min_chunk_pages", "qo_tile",
-        "max_tiles", "max_partials", "max_merge", "pieces_per_worker")] + [
-            ("reserved", ctypes.c_int32 * 8)]
+        "max_tiles", "max_partials", "max_merge", "pieces_per_worker", "kv_dtype")] + [
+            ("reserved", ctypes.c_int32 * 7)]
 
 
 class PlanT(ctypes.Structure):
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH):
                           ctypes.POINTER(I32), ctypes.POINTER(P), ctypes.POINTER(I32)],
         "fa_plan_destroy": [PP],
         "fa_decode": [PP, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
+        "fa_decode_scaled": [PP, P, P, P, I64, I64, I64, P, P, P, F32, F32, F32, P, P, P],
         "fa_append": [PP, P, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
         "fa_cascade": [PP, PP, P, P, P, I64, I64, I64, P, P, P, P, P, P, P, F32, P, P, P, P, P, P,
                        P, P, P],

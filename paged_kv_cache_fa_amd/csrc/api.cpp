@@ -61,11 +61,14 @@ fa_status check_run_args(const PlanImpl* pl, int want_mode, const void* q, const
     return FA_ERR_INVALID;
   }
   const int D = pl->geom.head_dim;
-  if (page_stride <= 0 || token_stride < D || head_stride < D || (page_stride & 7) ||
-      (token_stride & 7) || (head_stride & 7) ||
-      (int64_t)token_stride * 2 * pl->geom.page_size > 0x7fffffffLL) {
-    set_error("strides must be positive multiples of 8 elements with token/head stride >= "
-              "head_dim");
+  // 16 bytes per stride step: 8 elements of a 16-bit pool, 16 of an E4M3 pool
+  const int64_t eb = pl->geom.kv_dtype == FA_E4M3 ? 1 : 2;
+  const int64_t step = 16 / eb;
+  if (page_stride <= 0 || token_stride < D || head_stride < D || page_stride % step ||
+      token_stride % step || head_stride % step ||
+      (int64_t)token_stride * eb * pl->geom.page_size > 0x7fffffffLL) {
+    set_error("strides must be positive multiples of %d elements with token/head stride >= "
+              "head_dim", (int)step);
     return FA_ERR_INVALID;
   }
   return FA_OK;
@@ -100,6 +103,7 @@ AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const v
   p.queue = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + pl->lay.dev_queue);
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)pl->geom.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.v_scale = 1.0f;
   p.num_qo_heads = pl->geom.num_qo_heads;
   p.num_kv_heads = pl->geom.num_kv_heads;
   p.causal = pl->causal;
@@ -278,10 +282,37 @@ fa_status fa_plan_destroy(fa_plan_t* plan) {
   PlanImpl* pl = impl(plan);
   if (pl->magic == kPlanMagic) {
     for (void* ev : {pl->upload_event, pl->fork_event, pl->join_event, pl->join2_event})
-      if (ev) hipEventDestroy(static_cast<hipEvent_t>(ev));
+      if (ev) (void)hipEventDestroy(static_cast<hipEvent_t>(ev));
   }
   memset(plan, 0, sizeof(*plan));
   return FA_OK;
+}
+
+fa_status fa_decode_scaled(const fa_plan_t* plan, const void* q, const void* k_pages,
+                           const void* v_pages, int64_t page_stride, int64_t token_stride,
+                           int64_t head_stride, const int32_t* kv_indices_d,
+                           const int32_t* kv_indptr_d, const int32_t* last_page_len_d,
+                           float sm_scale, float k_scale, float v_scale, void* out, float* lse,
+                           void* stream) {
+  const PlanImpl* pl = plan ? impl(plan) : nullptr;
+  fa_status st = check_run_args(pl, FA_MODE_DECODE, q, k_pages, v_pages, page_stride,
+                                token_stride, head_stride, kv_indices_d, kv_indptr_d,
+                                last_page_len_d, out);
+  if (st != FA_OK) return st;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale)) {
+    set_error("k_scale and v_scale must be finite and positive");
+    return FA_ERR_INVALID;
+  }
+  AttnParams p = make_params(pl, q, k_pages, v_pages, page_stride, token_stride, head_stride,
+                             kv_indices_d, kv_indptr_d, last_page_len_d, nullptr, sm_scale, out,
+                             lse);
+  p.scale_log2 *= k_scale;
+  p.v_scale = v_scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
+  const hipError_t e = launch_decode(p, pl->geom.dtype, pl->geom.kv_dtype == FA_E4M3, G,
+                                     pl->num_workers, s);
+  return e == hipSuccess ? FA_OK : hip_fail(e, "decode kernel launch");
 }
 
 fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
@@ -289,18 +320,9 @@ fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
                     int64_t head_stride, const int32_t* kv_indices_d, const int32_t* kv_indptr_d,
                     const int32_t* last_page_len_d, float sm_scale, void* out, float* lse,
                     void* stream) {
-  const PlanImpl* pl = plan ? impl(plan) : nullptr;
-  fa_status st = check_run_args(pl, FA_MODE_DECODE, q, k_pages, v_pages, page_stride,
-                                token_stride, head_stride, kv_indices_d, kv_indptr_d,
-                                last_page_len_d, out);
-  if (st != FA_OK) return st;
-  const AttnParams p = make_params(pl, q, k_pages, v_pages, page_stride, token_stride,
-                                   head_stride, kv_indices_d, kv_indptr_d, last_page_len_d,
-                                   nullptr, sm_scale, out, lse);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
-  const hipError_t e = launch_decode(p, pl->geom.dtype, G, pl->num_workers, s);
-  return e == hipSuccess ? FA_OK : hip_fail(e, "decode kernel launch");
+  return fa_decode_scaled(plan, q, k_pages, v_pages, page_stride, token_stride, head_stride,
+                          kv_indices_d, kv_indptr_d, last_page_len_d, sm_scale, 1.0f, 1.0f, out,
+                          lse, stream);
 }
 
 fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indptr_d,
@@ -351,9 +373,11 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
   const fa_geometry& gp = pp->geom;
   const fa_geometry& gs = sp->geom;
   if (pp->causal || pp->batch != 1 || pp->num_rows != sp->batch || gp.dtype != gs.dtype ||
+      gs.kv_dtype != gs.dtype ||
       gp.num_qo_heads != gs.num_qo_heads || gp.num_kv_heads != gs.num_kv_heads) {
     set_error("cascade: the prefix plan must be a non-causal append of one request whose rows "
-              "are the suffix plan's requests, with the same heads and dtype");
+              "are the suffix plan's requests, with the same heads and dtype and 16-bit K/V "
+              "pages");
     return FA_ERR_INVALID;
   }
   if (!prefix_qo_indptr_d || !prefix_lse || !suffix_lse || !out || !aligned16(out) ||
@@ -390,7 +414,7 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
   const AttnParams ps = make_params(sp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
                                     kv_indices_d, kv_indptr_d, last_page_len_d, nullptr, sm_scale,
                                     suffix_out, suffix_lse);
-  e = launch_decode(ps, gs.dtype, G, sp->num_workers, s_suf);
+  e = launch_decode(ps, gs.dtype, false, G, sp->num_workers, s_suf);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   AttnParams pa = make_params(pp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
                               prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,

@@ -52,10 +52,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
 constexpr int kCoherent = 16;          // cache policy sc1: device-coherent access
 
+// One page of the lane's two tokens (r and r+8). 16-bit pools: k[0], k[1]
+// = token r dims [8s, 8s+8) and [64+8s, 64+8s+8), k[2], k[3] the same for
+// token r+8. E4M3 pools (KV8): k[0] = token r dims [16s, 16s+16), k[1] =
+// token r+8 (one 16-byte load per 128-byte row).
+template <bool KV8>
 struct PageRegs {
-  u32x4 k[4];  // token r lo/hi, token r+8 lo/hi
-  u32x4 v[4];
+  static constexpr int N = KV8 ? 2 : 4;
+  u32x4 k[N];
+  u32x4 v[N];
 };
+
+// Dims of the lane's 16 accumulators: float4 group i (i = 0..3) of segment s
+// starts at dim acc_dim(s, i).
+template <bool KV8>
+__device__ __forceinline__ int acc_dim(int s, int i) {
+  return KV8 ? 16 * s + 4 * i : (i < 2 ? 8 * s + 4 * i : 64 + 8 * s + 4 * (i - 2));
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
@@ -67,35 +80,60 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p)
   return __builtin_amdgcn_make_buffer_rsrc((void*)p.part_o, 0, 0x7fffffff, 0x00020000);
 }
 
-__device__ __forceinline__ void load_page(PageRegs& pr, const AttnParams& p, int pid, int hk,
+template <bool KV8>
+__device__ __forceinline__ void load_page(PageRegs<KV8>& pr, const AttnParams& p, int pid, int hk,
                                           uint32_t bytes, const uint32_t (&off)[4]) {
-  const int64_t base = (int64_t)pid * p.page_stride + (int64_t)hk * p.head_stride;
-  const __amdgpu_buffer_rsrc_t rk = page_rsrc(p.k + base, bytes);
-  const __amdgpu_buffer_rsrc_t rv = page_rsrc(p.v + base, bytes);
+  constexpr int N = PageRegs<KV8>::N;
+  const int64_t base = ((int64_t)pid * p.page_stride + (int64_t)hk * p.head_stride) * (KV8 ? 1 : 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      page_rsrc(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.k) + base), bytes);
+  const __amdgpu_buffer_rsrc_t rv =
+      page_rsrc(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.v) + base), bytes);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, 0);
+  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, 0);
+  for (int i = 0; i < N; ++i) pr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, 0);
 }
 
-template <int DT, int G>
-__device__ __forceinline__ void consume_page(const PageRegs& pr, const u32x4 (&qlo)[G],
+template <int DT, int G, bool KV8>
+__device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const u32x4 (&qlo)[G],
                                              const u32x4 (&qhi)[G], float (&m)[G], float (&l)[G],
                                              float (&acc)[G][16], float scale, bool va, bool vb) {
   using E = Elt<DT>;
+  // key pairs of tokens r (ka) and r+8 (kb) in the q layout: pair i < 4 meets
+  // qlo[g][i], pair 4 + i meets qhi[g][i]
+  uint32_t ka[8], kb[8];
+  if constexpr (KV8) {
+    // E4M3 codes widened to the q type; dword i holds dims 16s+4i .. 16s+4i+3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ka[2 * i] = E::template from_e4m3<false>(pr.k[0][i]);
+      ka[2 * i + 1] = E::template from_e4m3<true>(pr.k[0][i]);
+      kb[2 * i] = E::template from_e4m3<false>(pr.k[1][i]);
+      kb[2 * i + 1] = E::template from_e4m3<true>(pr.k[1][i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ka[i] = pr.k[0][i];
+      ka[4 + i] = pr.k[1][i];
+      kb[i] = pr.k[2][i];
+      kb[4 + i] = pr.k[3][i];
+    }
+  }
   float sa[G], sb[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float x = 0.f, y = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x = E::dot2(qlo[g][i], pr.k[0][i], x);
-      y = E::dot2(qlo[g][i], pr.k[2][i], y);
+      x = E::dot2(qlo[g][i], ka[i], x);
+      y = E::dot2(qlo[g][i], kb[i], y);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x = E::dot2(qhi[g][i], pr.k[1][i], x);
-      y = E::dot2(qhi[g][i], pr.k[3][i], y);
+      x = E::dot2(qhi[g][i], ka[4 + i], x);
+      y = E::dot2(qhi[g][i], kb[4 + i], y);
     }
     const float xs = octet_sum(x) * scale;
     const float ys = octet_sum(y) * scale;
@@ -118,12 +156,26 @@ __device__ __forceinline__ void consume_page(const PageRegs& pr, const u32x4 (&q
   }
   // element e of tokens r and r+8 side by side: (A_e, B_e)
   uint32_t pv[16];
+  if constexpr (KV8) {
+    // interleave the codes of the two tokens byte by byte (A0 B0 A1 B1 and
+    // A2 B2 A3 B3), then widen each code pair
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    pv[2 * i] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x05040100u);
-    pv[2 * i + 1] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x07060302u);
-    pv[8 + 2 * i] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x05040100u);
-    pv[8 + 2 * i + 1] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x07060302u);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t p01 = __builtin_amdgcn_perm(pr.v[1][i], pr.v[0][i], 0x05010400u);
+      const uint32_t p23 = __builtin_amdgcn_perm(pr.v[1][i], pr.v[0][i], 0x07030602u);
+      pv[4 * i] = E::template from_e4m3<false>(p01);
+      pv[4 * i + 1] = E::template from_e4m3<true>(p01);
+      pv[4 * i + 2] = E::template from_e4m3<false>(p23);
+      pv[4 * i + 3] = E::template from_e4m3<true>(p23);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[2 * i] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x05040100u);
+      pv[2 * i + 1] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x07060302u);
+      pv[8 + 2 * i] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x05040100u);
+      pv[8 + 2 * i + 1] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x07060302u);
+    }
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -165,7 +217,7 @@ __device__ __forceinline__ void merge_row_groups(float (&m)[G], float (&l)[G],
 // layout [slot][G][128], piece c taken by row group c % 8). The partials were
 // published by other waves with device-coherent stores; they are read back
 // with device-coherent loads (sc1).
-template <int G>
+template <int G, bool KV8>
 __device__ __forceinline__ void gather_partials(const AttnParams& p, int64_t base, int C, int r,
                                                 int s, float (&m)[G], float (&l)[G],
                                                 float (&acc)[G][16]) {
@@ -184,8 +236,8 @@ __device__ __forceinline__ void gather_partials(const AttnParams& p, int64_t bas
     const uint32_t o = (uint32_t)sh * 512u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4 raw = __builtin_amdgcn_raw_buffer_load_b128(
-          rs, o + (i < 2 ? 32 * s : 256 + 32 * s) + 16 * (i & 1), 0, kCoherent);
+      const u32x4 raw =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, o + 4 * acc_dim<KV8>(s, i), 0, kCoherent);
 #pragma unroll
       for (int k = 0; k < 4; ++k) v[4 * i + k] = __uint_as_float(raw[k]);
     }
@@ -214,7 +266,7 @@ __device__ __forceinline__ void gather_partials(const AttnParams& p, int64_t bas
   }
 }
 
-template <int DT, int G>
+template <int DT, int G, bool KV8>
 __device__ __forceinline__ void write_final(const AttnParams& p, int row, int hk, int r, int s,
                                             const float (&m)[G], const float (&l)[G],
                                             const float (&acc)[G][16]) {
@@ -224,7 +276,8 @@ __device__ __forceinline__ void write_final(const AttnParams& p, int row, int hk
     if (r != g) continue;  // row group g writes head g of the group
     const int h = hk * G + g;
     const bool live = l[g] > 0.f;
-    const float inv = live ? 1.f / l[g] : 0.f;
+    // the V scale (1 for unscaled pools) joins the normalisation
+    const float inv = live ? p.v_scale / l[g] : 0.f;
     uint16_t* op = p.out + ((int64_t)row * Hq + h) * 128;
     u32x4 lo, hi;
 #pragma unroll
@@ -232,8 +285,8 @@ __device__ __forceinline__ void write_final(const AttnParams& p, int row, int hk
       lo[i] = Elt<DT>::pack(acc[g][2 * i] * inv, acc[g][2 * i + 1] * inv);
       hi[i] = Elt<DT>::pack(acc[g][8 + 2 * i] * inv, acc[g][8 + 2 * i + 1] * inv);
     }
-    *reinterpret_cast<u32x4*>(op + s * 8) = lo;
-    *reinterpret_cast<u32x4*>(op + 64 + s * 8) = hi;
+    *reinterpret_cast<u32x4*>(op + acc_dim<KV8>(s, 0)) = lo;
+    *reinterpret_cast<u32x4*>(op + acc_dim<KV8>(s, 2)) = hi;
     if (s == 0 && p.lse)
       p.lse[(int64_t)row * Hq + h] = live ? (m[g] + fast_log2(l[g])) * kLn2 : kNegInf;
   }
@@ -241,7 +294,7 @@ __device__ __forceinline__ void write_final(const AttnParams& p, int row, int hk
 
 // Publish a chunk's normalised state with device-coherent stores (sc1), so a
 // wave on any XCD can read it after the arrival counter says it is complete.
-template <int G>
+template <int G, bool KV8>
 __device__ __forceinline__ void write_partial(const AttnParams& p, int64_t slot, int r, int s,
                                               const float (&m)[G], const float (&l)[G],
                                               const float (&acc)[G][16]) {
@@ -258,8 +311,7 @@ __device__ __forceinline__ void write_partial(const AttnParams& p, int64_t slot,
       u32x4 u;
 #pragma unroll
       for (int k = 0; k < 4; ++k) u[k] = __float_as_uint(acc[g][4 * i + k] * inv);
-      __builtin_amdgcn_raw_buffer_store_b128(u, rs, o + (i < 2 ? 32 * s : 256 + 32 * s) + 16 * (i & 1),
-                                             0, kCoherent);
+      __builtin_amdgcn_raw_buffer_store_b128(u, rs, o + 4 * acc_dim<KV8>(s, i), 0, kCoherent);
     }
     if (s == 0)
       __hip_atomic_store(p.part_lse + sh, live ? m[g] + fast_log2(l[g]) : kNegInf, __ATOMIC_RELAXED,
@@ -311,7 +363,7 @@ __device__ __forceinline__ void open_piece(const AttnParams& p, int tv, int lane
 // the start of steady ring pass k counted from the end (k = 2, 1, 0 for the
 // last three passes; all three run after the loop if the piece has fewer),
 // where the caller overlaps the set-up of its next piece with the loads.
-template <int DT, int G, int NBUF, typename Hook>
+template <int DT, int G, int NBUF, bool KV8, typename Hook>
 __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx& c, int lane,
                                              float (&m)[G], float (&l)[G], float (&acc)[G][16],
                                              Hook&& hook) {
@@ -323,15 +375,25 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
   const int Hq = p.num_qo_heads;
   const int r = lane >> 3;
   const int s = lane & 7;
-  const uint32_t ts2 = (uint32_t)p.token_stride * 2u;
-  const uint32_t off[4] = {r * ts2 + s * 16u, r * ts2 + 128u + s * 16u, (r + 8) * ts2 + s * 16u,
-                           (r + 8) * ts2 + 128u + s * 16u};
+  // bytes per token row of the pool, and the lane's load offsets in a page
+  const uint32_t ts2 = (uint32_t)p.token_stride * (KV8 ? 1u : 2u);
+  uint32_t off[4];
+  if constexpr (KV8) {
+    off[0] = r * ts2 + s * 16u;
+    off[1] = (r + 8) * ts2 + s * 16u;
+    off[2] = off[3] = 0u;  // unused
+  } else {
+    off[0] = r * ts2 + s * 16u;
+    off[1] = r * ts2 + 128u + s * 16u;
+    off[2] = (r + 8) * ts2 + s * 16u;
+    off[3] = (r + 8) * ts2 + 128u + s * 16u;
+  }
   u32x4 qlo[G], qhi[G];
   const uint16_t* qp = p.q + ((int64_t)row * Hq + hk * G) * 128;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    qlo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + s * 8);
-    qhi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + 64 + s * 8);
+    qlo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 0));
+    qhi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 2));
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -364,7 +426,7 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
   };
   const float scale = p.scale_log2;
 
-  PageRegs buf[NBUF];
+  PageRegs<KV8> buf[NBUF];
   int j = 0;
   int hooks_left = 3;
   if (npg >= 2 * NBUF) {
@@ -382,7 +444,7 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
         const int pid = nid;
         nid = page_id(jn + 1);
         load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, off);
-        consume_page<DT, G>(buf[u], qlo, qhi, m, l, acc, scale, true, true);
+        consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, true, true);
       }
     };
     // passes: the peeled first one, then while j + 2 NBUF - 1 < npg
@@ -411,7 +473,8 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
       const int jn = jj + NBUF - 1;
       if (jn < npg) load_page(buf[(u + NBUF - 1) % NBUF], p, page_id(jn), hk, page_bytes(jn), off);
       const int tb = (first_page + jj) * 16;
-      consume_page<DT, G>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1, tb + r + 8 < key1);
+      consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1,
+                               tb + r + 8 < key1);
     }
   }
   while (hooks_left > 0) hook(--hooks_left);
@@ -428,7 +491,7 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
 // completed by then, so the wait is free), and the last arriving piece
 // merges the unit. The last wave to finish resets the queue heads, so the
 // kernel can be replayed from a graph.
-template <int DT, int G, int NBUF>
+template <int DT, int G, int NBUF, bool KV8>
 __global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int r = lane >> 3, s = lane & 7;
@@ -466,9 +529,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
   auto finish_arrival = [&](const PieceId& pd, int arr) {
     if (__builtin_amdgcn_readlane(arr, 0) != pd.npieces - 1) return;
     if (lane == 0) p.counters[pd.base] = 0;
-    gather_partials<G>(p, pd.base, pd.npieces, r, s, m, l, acc);
+    gather_partials<G, KV8>(p, pd.base, pd.npieces, r, s, m, l, acc);
     merge_row_groups<G>(m, l, acc);
-    write_final<DT, G>(p, pd.row, pd.hk, r, s, m, l, acc);
+    write_final<DT, G, KV8>(p, pd.row, pd.hk, r, s, m, l, acc);
   };
   auto arrive = [&](const PieceId& pd) -> int {
     // the partial's coherent stores must be complete before the count
@@ -494,13 +557,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
       }
       if (k == 0 && tn >= 0) open_piece(p, tvn, lane, nxt);
     };
-    stream_piece<DT, G, NBUF>(p, cur, lane, m, l, acc, hook);
+    stream_piece<DT, G, NBUF, KV8>(p, cur, lane, m, l, acc, hook);
     const int arr = pd.slot >= 0 ? arrive(pd) : 0;
     merge_row_groups<G>(m, l, acc);
     if (cur.id.slot < 0)
-      write_final<DT, G>(p, cur.id.row, cur.id.hk, r, s, m, l, acc);
+      write_final<DT, G, KV8>(p, cur.id.row, cur.id.hk, r, s, m, l, acc);
     else
-      write_partial<G>(p, cur.id.slot, r, s, m, l, acc);
+      write_partial<G, KV8>(p, cur.id.slot, r, s, m, l, acc);
     if (pd.slot >= 0) finish_arrival(pd, arr);
     pd = cur.id;
     t = tn;
@@ -515,13 +578,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
   }
 }
 
-template <int DT>
+// Ring depth per group size: 16-bit pages keep 2 pages (16 KB per wave) in
+// flight for G <= 4 (1 for G = 8, whose 8 heads of accumulators fill the
+// registers); E4M3 pages are half the size, so the ring is deeper.
+template <int DT, bool KV8>
 hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
+  constexpr int R = KV8 ? 5 : 3;
   switch (group) {
-    case 1: hipLaunchKernelGGL((decode_kernel<DT, 1, 3>), dim3(grid), dim3(256), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<DT, 2, 3>), dim3(grid), dim3(256), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<DT, 4, 3>), dim3(grid), dim3(256), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((decode_kernel<DT, 8, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((decode_kernel<DT, 1, R, KV8>), dim3(grid), dim3(256), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<DT, 2, R, KV8>), dim3(grid), dim3(256), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<DT, 4, R, KV8>), dim3(grid), dim3(256), 0, s, p); break;
+    case 8:
+      hipLaunchKernelGGL((decode_kernel<DT, 8, KV8 ? 3 : 2, KV8>), dim3(grid), dim3(256), 0, s, p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -529,11 +598,15 @@ hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s) {
+hipError_t launch_decode(const AttnParams& p, int dtype, bool kv_e4m3, int group, int workers,
+                         hipStream_t s) {
   const int grid = (workers + 3) / 4;
   if (grid <= 0) return hipSuccess;
-  return dtype == FA_BF16 ? launch_dt<FA_BF16>(p, group, grid, s)
-                          : launch_dt<FA_F16>(p, group, grid, s);
+  if (kv_e4m3)
+    return dtype == FA_BF16 ? launch_dt<FA_BF16, true>(p, group, grid, s)
+                            : launch_dt<FA_F16, true>(p, group, grid, s);
+  return dtype == FA_BF16 ? launch_dt<FA_BF16, false>(p, group, grid, s)
+                          : launch_dt<FA_F16, false>(p, group, grid, s);
 }
 
 }  // namespace pkfa

@@ -36,6 +36,12 @@ struct Elt<FA_BF16> {
     bf16x2_t v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // Two E4M3 codes (bytes 2W, 2W+1 of x) widened to a bf16 pair, exactly
+  // (every E4M3 value is a bf16 value; scale operand 1).
+  template <bool W>
+  __device__ __forceinline__ static uint32_t from_e4m3(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, W));
+  }
 };
 
 template <>
@@ -53,6 +59,12 @@ struct Elt<FA_F16> {
   __device__ __forceinline__ static uint32_t pack(float a, float b) {
     f16x2_t v = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(uint32_t, v);
+  }
+  // Two E4M3 codes widened to an fp16 pair, exactly (E4M3's range and
+  // 3-bit mantissa fit fp16).
+  template <bool W>
+  __device__ __forceinline__ static uint32_t from_e4m3(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, W));
   }
 };
 

@@ -14,9 +14,9 @@ struct AttnParams {
   const int32_t* worker_ptr;  // decode: [workers+1] tile ranges per worker wave
   const int32_t* merge;
   const uint16_t* q;          // [rows, Hq, 128]
-  const uint16_t* k;          // page pools (16-bit elements)
+  const uint16_t* k;          // page pools (16-bit elements, or E4M3 bytes)
   const uint16_t* v;
-  int64_t page_stride, token_stride, head_stride;  // elements
+  int64_t page_stride, token_stride, head_stride;  // elements of the pool type
   const int32_t* kv_indices;
   const int32_t* kv_indptr;
   const int32_t* last_page_len;
@@ -28,7 +28,8 @@ struct AttnParams {
   int32_t* counters;          // [slots] arrivals per split unit, indexed by its first slot
   int32_t* queue;             // decode: queue heads q = 0..7 and the finished-wave count (q = 8)
                               // at queue[q * kQueueStride]; zero between calls
-  float scale_log2;           // sm_scale * log2(e)
+  float scale_log2;           // sm_scale * k_scale * log2(e)
+  float v_scale;              // per-tensor V scale, applied to the final output
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t causal;
@@ -38,7 +39,9 @@ struct AttnParams {
 constexpr int kQueueStride = 64;  // int32s between decode queue counters (one 256-byte line each)
 constexpr int kAppendBins = 8;  // append tile bins = XCDs (workgroup i runs bin i % 8)
 
-hipError_t launch_decode(const AttnParams& p, int dtype, int group, int workers, hipStream_t s);
+// kv_e4m3: the K/V pools hold E4M3 codes (strides in bytes) instead of dtype.
+hipError_t launch_decode(const AttnParams& p, int dtype, bool kv_e4m3, int group, int workers,
+                         hipStream_t s);
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
 // Copy n_words 32-bit words from device-visible pinned host memory into device
 // memory with a small kernel (both 16-byte aligned).

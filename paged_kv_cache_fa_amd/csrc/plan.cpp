@@ -81,6 +81,12 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
     return FA_ERR_UNSUPPORTED;
   }
   const bool app = g.mode == FA_MODE_APPEND;
+  if (g.kv_dtype == 0) g.kv_dtype = g.dtype;
+  if (g.kv_dtype != g.dtype && !(g.kv_dtype == FA_E4M3 && !app)) {
+    set_error("unsupported: kv_dtype %d with dtype %d in %s (built: the q dtype, or E4M3 for "
+              "decode)", g.kv_dtype, g.dtype, app ? "append" : "decode");
+    return FA_ERR_UNSUPPORTED;
+  }
   if (!app) g.max_qo_tokens = 0;
   if (!g.num_cu) g.num_cu = 256;
   if (!g.tiles_per_cu) g.tiles_per_cu = app ? 2 : 4;

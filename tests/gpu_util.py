@@ -23,7 +23,10 @@ class DevWorkload:
         self.wl = wl
         dt = torch_dtype(wl.dtype)
         self.device = device
-        self.pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
+        if wl.kv_dtype == "e4m3":  # E4M3 codes, one byte per element
+            self.pool = torch.from_numpy(wl.pool).to(device)
+        else:
+            self.pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
         self.q = torch.from_numpy(wl.q.view(np.int16)).to(device).view(dt)
         self.kv_indptr = torch.from_numpy(wl.kv_indptr).to(device)
         self.kv_indices = torch.from_numpy(wl.kv_indices).to(device)
@@ -47,17 +50,24 @@ class DevWorkload:
 
 
 def decode_geometry(wl, **knobs):
+    if wl.kv_dtype is not None:
+        knobs.setdefault("kv_dtype", wl.kv_dtype)
     return fa.geometry("decode", wl.dtype, max(wl.batch, 1), wl.num_qo_heads, wl.num_kv_heads,
                        **knobs)
 
 
 def run_decode(dw: DevWorkload, plan=None, out=None, lse=None, **knobs):
+    """fa_decode, or fa_decode_scaled with the workload's scales for an FP8 pool."""
     wl = dw.wl
     if plan is None:
         plan = fa.Plan(decode_geometry(wl, **knobs), device=dw.device)
         plan.plan(wl.kv_indptr, wl.kv_lens)
-    out, lse = fa.decode(plan, dw.q, dw.k, dw.v, *dw.strides, dw.kv_indices, dw.kv_indptr,
-                         dw.last_page_len, out=out, lse=lse)
+    args = (plan, dw.q, dw.k, dw.v, *dw.strides, dw.kv_indices, dw.kv_indptr, dw.last_page_len)
+    if wl.kv_dtype is not None:
+        out, lse = fa.decode_scaled(*args, k_scale=wl.k_scale, v_scale=wl.v_scale, out=out,
+                                    lse=lse)
+    else:
+        out, lse = fa.decode(*args, out=out, lse=lse)
     return plan, out, lse
 
 
@@ -67,7 +77,8 @@ def to_f64(t):
 
 def oracle_decode(wl, requests=None):
     return oracle.decode(wl.q, wl.pool, wl.dtype, wl.kv_indptr, wl.kv_indices, wl.last_page_len,
-                         wl.page_size, requests=requests)
+                         wl.page_size, requests=requests, kv_dtype=wl.kv_dtype,
+                         k_scale=wl.k_scale, v_scale=wl.v_scale)
 
 
 def assert_close(out, lse, ref_out, ref_lse, out_tol=OUT_TOL, lse_tol=LSE_TOL, what=""):

@@ -335,9 +335,91 @@ def check_cascade(dtype="bf16", seed=12):
     _close(a[0], b[0]); _close(a[1], b[1])
 
 
+# ---------------------------------------------------------------- FP8 (E4M3) KV
+# Values fixed by the OCP 8-bit floating-point definition of E4M3 (bias 7,
+# 3 mantissa bits, subnormals at exponent field 0, no infinities, NaN at
+# S.1111.111), worked out by hand.
+E4M3_SPOT = {
+    0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5, 0x38: 1.0,
+    0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0,
+}
+
+
+def _torch_e4m3(codes):
+    """Codes -> float64 through torch's float8_e4m3fn (not the oracle's code)."""
+    import torch
+
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def check_e4m3_definition():
+    codes = np.arange(256, dtype=np.uint8)
+    v = OA.upcast(codes, "e4m3")
+    for c, want in E4M3_SPOT.items():
+        assert v[c] == want, f"code {c:#04x}: {v[c]} != {want}"
+    assert math.copysign(1.0, v[0x80]) < 0 and v[0x80] == 0.0, "0x80 must be -0"
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]), "S.1111.111 must be NaN"
+    assert np.all(np.diff(v[:127]) > 0), "codes 0..126 must increase"
+    assert np.array_equal(v[128:255], -v[:127]), "sign bit must negate"
+    ref = _torch_e4m3(codes)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(v[fin], ref[fin]), "differs from torch float8_e4m3fn"
+
+
+def _fp8_tiny(seed):
+    from workloads import make_workload
+
+    return make_workload([0, 1, 15, 16, 17, 40], 4, 2, "bf16", seed, head_dim=16, page_size=4,
+                         mode="test", extra_pages=2, kv_dtype="e4m3")
+
+
+def check_fp8_scale_placement(seed=41):
+    """s_j is linear in k (k_scale joins sm_scale); out is linear in v and the
+    lse does not see v_scale."""
+    wl = _fp8_tiny(seed)
+    args = (wl.q, wl.pool, "bf16", wl.kv_indptr, wl.kv_indices, wl.last_page_len, wl.page_size)
+    sm, a, b = 0.3, 0.05, 0.07
+    o1, s1 = OA.decode(*args, scale=sm, kv_dtype="e4m3", k_scale=a, v_scale=b)
+    o0, s0 = OA.decode(*args, scale=sm * a, kv_dtype="e4m3")
+    _close(o1, b * o0)
+    _close(s1, s0)
+
+
+def check_brute_decode_fp8(seed=42):
+    """Uniform random codes (subnormals to +-448, NaN codes excluded) decoded by
+    torch, scaled, and attended by the pure-Python brute force."""
+    rng = np.random.default_rng(seed)
+    lens = [0, 1, 3, 4, 5, 9]
+    Hq, Hkv, D, ps = 4, 2, 6, 4
+    n = [-(-L // ps) for L in lens]
+    P = sum(n) + 1
+    perm = rng.permutation(P)
+    lists, off = [], 0
+    for k in n:
+        lists.append(list(perm[off: off + k]))
+        off += k
+    indptr, indices = csr_from_page_lists(lists)
+    last = np.array([0 if k == 0 else L - (k - 1) * ps for L, k in zip(lens, n)], np.int32)
+    pool = rng.integers(0, 256, size=(P, 2, ps, Hkv, D)).astype(np.uint8)
+    pool[(pool & 0x7F) == 0x7F] = 0x3A  # no NaN codes
+    q = to_storage_bits(rng.standard_normal((len(lens), Hq, D)).astype(np.float32), "bf16")
+    ks, vs, sm = 1.0 / 56.0, 3.0 / 224.0, 1 / math.sqrt(D)
+    out, lse = OA.decode(q, pool, "bf16", indptr, indices, last, ps, kv_dtype="e4m3",
+                         k_scale=ks, v_scale=vs)
+    vals = _torch_e4m3(pool)
+    vals[:, 0] *= ks
+    vals[:, 1] *= vs
+    bo, bl = brute_paged(OA.upcast(q, "bf16").tolist(), vals.tolist(), indptr.tolist(),
+                         indices.tolist(), last.tolist(), ps, list(range(len(lens))),
+                         [10 ** 9] * len(lens), Hq, Hkv, sm)
+    _close(out, np.array(bo))
+    _close(lse, np.array(bl))
+
+
 ALL_CHECKS = [
     check_single_token, check_identical_keys, check_q_zero_and_v_ones, check_scale_default,
     check_gqa_map, check_identity_gather, check_count, check_brute_decode, check_brute_append,
     check_causal_prefill, check_permutation_invariance, check_merge_split, check_merge_algebra,
-    check_cascade,
+    check_cascade, check_e4m3_definition, check_fp8_scale_placement, check_brute_decode_fp8,
 ]

@@ -154,6 +154,28 @@ def test_geometry_errors():
     assert st == fa._lib.FA_ERR_WORKSPACE
 
 
+def test_kv_dtype_geometry():
+    """E4M3 pages are a decode-only pool type; 0 resolves to the q dtype."""
+    g = fa.geometry("decode", "bf16", 4, 32, 8, kv_dtype="e4m3")
+    p = fa.Plan(g).plan(_indptr([40, 7]), np.array([40, 7], np.int32))
+    st = p.info()
+    assert st.resolved.kv_dtype == fa.FA_E4M3 and st.resolved.dtype == fa.FA_BF16
+    st = fa.Plan(fa.geometry("decode", "fp16", 4, 32, 8)).plan(
+        _indptr([40]), np.array([40], np.int32)).info()
+    assert st.resolved.kv_dtype == fa.FA_F16
+    # same plan as the 16-bit pool: the work split does not depend on the pool type
+    t8, m8 = p.tiles()
+    t16, m16 = fa.Plan(fa.geometry("decode", "bf16", 4, 32, 8)).plan(
+        _indptr([40, 7]), np.array([40, 7], np.int32)).tiles()
+    assert np.array_equal(t8, t16) and np.array_equal(m8, m16)
+    for bad in (fa.geometry("append", "bf16", 4, 32, 8, max_qo_tokens=64, kv_dtype="e4m3"),
+                fa.geometry("decode", "fp16", 4, 32, 8, kv_dtype="bf16"),
+                fa.geometry("decode", "bf16", 4, 32, 8, kv_dtype="fp32")):
+        with pytest.raises(fa.FAError) as e:
+            fa.workspace_size(bad)
+        assert e.value.code == "UNSUPPORTED"
+
+
 def test_capacity_error():
     g = _geom("decode", 4, 8, 8, max_tiles=16, num_cu=64)
     with pytest.raises(fa.FAError) as e:
@@ -172,4 +194,7 @@ def test_run_calls_reject_host_only_plans():
     assert st == fa._lib.FA_ERR_NOT_PLANNED
     st = lib.fa_append(ctypes.byref(p._plan), ptr, ptr, ptr, ptr, 2048, 256, 128, ptr, ptr, ptr,
                        0.0, ptr, None, None)
+    assert st == fa._lib.FA_ERR_NOT_PLANNED
+    st = lib.fa_decode_scaled(ctypes.byref(p._plan), ptr, ptr, ptr, 2048, 256, 128, ptr, ptr, ptr,
+                              0.0, 1.0, 1.0, ptr, None, None)
     assert st == fa._lib.FA_ERR_NOT_PLANNED

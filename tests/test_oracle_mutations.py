@@ -74,6 +74,43 @@ def _merge_no_norm(v, s):
     return (w[..., None] * v).sum(axis=-2), m + np.log(w.sum(axis=-1))
 
 
+import oracle.fp8 as OF  # noqa: E402
+
+_e4m3 = OF.e4m3_value
+
+
+def _e4m3_bias8(codes):
+    """Mistake: exponent bias 8 (the E5M2-style or off-by-one bias)."""
+    return _e4m3(codes) / 2.0
+
+
+def _e4m3_no_subnormals(codes):
+    """Mistake: exponent field 0 read as a normal number."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    v = _e4m3(codes)
+    sub = ((c >> 3) & 0xF) == 0
+    m = (c & 7).astype(np.float64)
+    return np.where(sub, np.where(c >> 7, -1.0, 1.0) * (1 + m / 8) * 2.0 ** -7, v)
+
+
+def _e4m3_fnuz_nan(codes):
+    """Mistake: the FNUZ variant's NaN at 0x80 and no NaN at S.1111.111."""
+    c = np.asarray(codes, dtype=np.uint8)
+    v = _e4m3(np.where((c & 0x7F) == 0x7F, c & 0xFE, c))
+    v = np.where((c & 0x7F) == 0x7F, np.where(c >> 7, -480.0, 480.0), v)
+    return np.where(c == 0x80, np.nan, v)
+
+
+_gather = OA.gather_request_kv
+
+
+def _gather_swapped_scales(pool, dtype, kv_indptr, kv_indices, last_page_len, page_size, b,
+                           k_scale=1.0, v_scale=1.0):
+    """Mistake: K multiplied by v_scale and V by k_scale."""
+    return _gather(pool, dtype, kv_indptr, kv_indices, last_page_len, page_size, b, v_scale,
+                   k_scale)
+
+
 def _run_all():
     for chk in P.ALL_CHECKS:
         chk()
@@ -88,6 +125,10 @@ MUTATIONS = [
     ("kv_len_ignores_last_page_len", OA, "request_kv_len", _kv_len_full_pages),
     ("merge_wrong_sign", OM, "merge_states", _merge_wrong_sign),
     ("merge_no_normalisation", OM, "merge_states", _merge_no_norm),
+    ("e4m3_bias_8", OA, "e4m3_value", _e4m3_bias8),
+    ("e4m3_no_subnormals", OA, "e4m3_value", _e4m3_no_subnormals),
+    ("e4m3_fnuz_nan", OA, "e4m3_value", _e4m3_fnuz_nan),
+    ("fp8_scales_swapped", OA, "gather_request_kv", _gather_swapped_scales),
 ]
 
 

@@ -13,5 +13,8 @@ from .gen import (  # noqa: F401
     make_cascade,
     csr_from_page_lists,
     to_storage_bits,
+    to_e4m3_codes,
     CONFIG_NAMES,
+    FP8_K_SCALE,
+    FP8_V_SCALE,
 )

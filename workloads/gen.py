@@ -2,8 +2,9 @@
 
 Everything here is input preparation: lengths, a page table in CSR form
 (``kv_indptr`` / ``kv_indices`` / ``last_page_len``), a page pool and the
-queries, all stored as 16-bit floating-point bit patterns. There is no
-attention arithmetic in this module.
+queries, stored as 16-bit floating-point bit patterns (or, for an FP8 pool,
+E4M3 byte codes with one scale per tensor). There is no attention
+arithmetic in this module.
 
 Layout of the pool (the combined K/V pool shown in the page "FlashInfer: The
 Attention Kernel Library That Proves the Bottleneck ...", section "Snippet
@@ -33,8 +34,16 @@ CONFIG_NAMES = {
     5: "causal append, batch 16 x 512 new tokens onto 4096 cached, 32/8 heads, bf16",
 }
 
-_NAN_BITS = {"bf16": 0x7FC0, "fp16": 0x7E00}
+_NAN_BITS = {"bf16": 0x7FC0, "fp16": 0x7E00, "e4m3": 0x7F}
 _PAGE_CHUNK = 1024
+
+# Per-tensor scales of FP8 (E4M3) pools: stored code c stands for
+# scale * e4m3(c). With these, N(0,1) draws up to 8 (K) and 6 (V) standard
+# deviations map inside the format's finite range (|code value| <= 448);
+# the rare draw beyond saturates there.
+FP8_K_SCALE = 8.0 / 448.0
+FP8_V_SCALE = 6.0 / 448.0
+_E4M3_MAX = 448.0
 
 
 def to_storage_bits(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -51,6 +60,16 @@ def to_storage_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     if nan.any():
         r[nan] = np.uint16(_NAN_BITS["bf16"])
     return r
+
+
+def to_e4m3_codes(x: np.ndarray, scale: float) -> np.ndarray:
+    """Quantise float32 values to E4M3 byte codes of ``x / scale``
+    (round to nearest even, saturating at +-448), via torch's float8 cast."""
+    import torch
+
+    y = np.clip(np.asarray(x, dtype=np.float32) / np.float32(scale), -_E4M3_MAX, _E4M3_MAX)
+    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
 
 
 def csr_from_page_lists(page_lists: Sequence[Sequence[int]]):
@@ -88,10 +107,13 @@ class Workload:
     last_page_len: np.ndarray      # int32 [B]
     qo_indptr: Optional[np.ndarray]  # int32 [B+1]; None = decode (one row per request)
     causal: bool
-    pool: np.ndarray               # uint16 [P, 2, ps, Hkv, D]
+    pool: np.ndarray               # uint16 [P, 2, ps, Hkv, D] (uint8 codes for e4m3)
     q: np.ndarray                  # uint16 [rows, Hq, D]
     seed: int
     mode: str = "bench"
+    kv_dtype: Optional[str] = None  # pool storage type when it differs from dtype ("e4m3")
+    k_scale: float = 1.0            # per-tensor scales of an e4m3 pool
+    v_scale: float = 1.0
     # shared prefix (cascade); one extra "request" whose pages every request shares
     prefix_len: int = 0
     prefix_indptr: Optional[np.ndarray] = None
@@ -137,12 +159,15 @@ def _fill_normal_pool(rng, pool: np.ndarray, which: int, dtype: str) -> None:
     for p0 in range(0, P, _PAGE_CHUNK):
         p1 = min(P, p0 + _PAGE_CHUNK)
         x = rng.standard_normal((p1 - p0, ps, hkv, d), dtype=np.float32)
-        pool[p0:p1, which] = to_storage_bits(x, dtype)
+        if dtype == "e4m3":
+            pool[p0:p1, which] = to_e4m3_codes(x, FP8_K_SCALE if which == 0 else FP8_V_SCALE)
+        else:
+            pool[p0:p1, which] = to_storage_bits(x, dtype)
 
 
 def _poison_tails(pool, page_tables, page_size, dtype):
     """Test mode: slots past last_page_len of each last page hold NaN."""
-    nan = np.uint16(_NAN_BITS[dtype])
+    nan = pool.dtype.type(_NAN_BITS[dtype])
     for indptr, indices, last in page_tables:
         for b in range(len(indptr) - 1):
             n = indptr[b + 1] - indptr[b]
@@ -167,14 +192,18 @@ def make_workload(
     mode: str = "bench",
     extra_pages: int = 0,
     name: str = "custom",
+    kv_dtype: Optional[str] = None,
 ) -> Workload:
     """Lay out a paged KV cache for the given lengths and draw Q, K, V.
 
     ``rng`` continues a generator that already drew the lengths; if None a
     fresh ``default_rng(seed)`` is used. ``qo_lens=None`` means decode (one
     query row per request). With ``mode="test"`` unused tail slots and the
-    ``extra_pages`` unreferenced pool pages hold NaN.
+    ``extra_pages`` unreferenced pool pages hold NaN. ``kv_dtype="e4m3"``
+    stores the pool as E4M3 codes with the scales FP8_K_SCALE / FP8_V_SCALE
+    (the same normal draws, quantised); q stays in ``dtype``.
     """
+    kvt = dtype if kv_dtype is None else kv_dtype
     if rng is None:
         rng = np.random.default_rng(seed)
     kv_lens = np.asarray(kv_lens, dtype=np.int32)
@@ -203,19 +232,22 @@ def make_workload(
 
     qf = rng.standard_normal((rows, num_qo_heads, head_dim), dtype=np.float32)
     q = to_storage_bits(qf, dtype)
-    pool = np.empty((P, 2, page_size, num_kv_heads, head_dim), dtype=np.uint16)
-    _fill_normal_pool(rng, pool, 0, dtype)
-    _fill_normal_pool(rng, pool, 1, dtype)
+    pool = np.empty((P, 2, page_size, num_kv_heads, head_dim),
+                    dtype=np.uint8 if kvt == "e4m3" else np.uint16)
+    _fill_normal_pool(rng, pool, 0, kvt)
+    _fill_normal_pool(rng, pool, 1, kvt)
     if mode == "test":
-        _poison_tails(pool, [(kv_indptr, kv_indices, last)], page_size, dtype)
+        _poison_tails(pool, [(kv_indptr, kv_indices, last)], page_size, kvt)
         if extra_pages:
             unref = perm[total:]
-            pool[unref] = np.uint16(_NAN_BITS[dtype])
+            pool[unref] = pool.dtype.type(_NAN_BITS[kvt])
+    fp8 = kvt == "e4m3"
     return Workload(
         name=name, dtype=dtype, num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
         head_dim=head_dim, page_size=page_size, kv_lens=kv_lens, kv_indptr=kv_indptr,
         kv_indices=kv_indices, last_page_len=last, qo_indptr=qo_indptr, causal=causal,
-        pool=pool, q=q, seed=seed, mode=mode,
+        pool=pool, q=q, seed=seed, mode=mode, kv_dtype=kv_dtype if fp8 else None,
+        k_scale=FP8_K_SCALE if fp8 else 1.0, v_scale=FP8_V_SCALE if fp8 else 1.0,
     )
 
 
@@ -292,17 +324,24 @@ def config_lengths(k: int, rng: np.random.Generator) -> dict:
     raise ValueError(f"no config {k}")
 
 
-def make_config(k: int, seed: Optional[int] = None, mode: str = "bench") -> Workload:
-    """The five benchmark workloads (seed defaults to the config number)."""
+def make_config(k: int, seed: Optional[int] = None, mode: str = "bench",
+                kv_dtype: Optional[str] = None) -> Workload:
+    """The five benchmark workloads (seed defaults to the config number).
+
+    ``kv_dtype="e4m3"`` gives the decode configs 2 and 3 with an FP8 pool
+    (same lengths, page table and draws; q stays bf16)."""
     if seed is None:
         seed = k
+    if kv_dtype is not None and k not in (2, 3):
+        raise ValueError("an FP8 pool is defined for the decode configs 2 and 3 only")
     rng = np.random.default_rng(seed)
-    name = f"config{k}"
+    name = f"config{k}" + ("" if kv_dtype is None else f"_{kv_dtype}")
     ln = config_lengths(k, rng)
     if k == 1:
         return make_workload(ln["kv_lens"], 32, 32, "fp16", seed, rng=rng, mode=mode, name=name)
     if k in (2, 3):
-        return make_workload(ln["kv_lens"], 32, 8, "bf16", seed, rng=rng, mode=mode, name=name)
+        return make_workload(ln["kv_lens"], 32, 8, "bf16", seed, rng=rng, mode=mode, name=name,
+                             kv_dtype=kv_dtype)
     if k == 4:
         return make_cascade(ln["prefix_len"], ln["suffix_lens"], 32, 8, "bf16", seed, rng=rng,
                             mode=mode, name=name)
