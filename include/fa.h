@@ -80,13 +80,13 @@ typedef struct {
   /* plan knobs (0 = default) */
   int32_t num_cu;          /* compute units to spread tiles over (default 256) */
   int32_t tiles_per_cu;    /* decode: worker waves per compute unit (default 4); append: tiles per CU (default 2) */
-  int32_t min_chunk_pages; /* smallest split-KV chunk / decode piece in pages (default 1) */
+  int32_t min_chunk_pages; /* smallest split-KV chunk / decode piece size in pages (default 1) */
   int32_t qo_tile;         /* append: query rows per tile, 1..128/G (default 128/G,
                               G = num_qo_heads / num_kv_heads); decode: 1 */
   int32_t max_tiles;       /* capacities; default = worst case of the plan procedure */
   int32_t max_partials;
   int32_t max_merge;
-  int32_t pieces_per_worker; /* decode: pieces per worker wave the piece size aims at (default 1) */
+  int32_t pieces_per_worker; /* decode: work lists per worker wave (default 1) */
   int32_t kv_dtype;        /* K/V page-pool type: 0 or `dtype` = the same as q; FA_E4M3 = FP8
                               pages with per-tensor scales (decode only, see fa_decode_scaled).
                               Resolved to `dtype` when the same. */
@@ -152,10 +152,11 @@ fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats);
  *   decode  {request, kv_head, kv_indptr[request], first_slot, key_begin, key_end, slot,
  *           n_pieces};
  *   append  {request, kv_head, row_begin, row_end, key_begin, key_end, slot0, n_chunks}.
- * Tiles are listed in 8 bins, one per XCD: bin x is tiles worker_ptr[x] ..
- * worker_ptr[x+1]-1 (worker_ptr int32 [9]; *num_workers receives 8). Decode
- * waves take tiles from the queue of their XCD, then from the others; append
- * workgroup i runs bin i mod 8.
+ * Decode: worker wave w runs tiles worker_ptr[w] .. worker_ptr[w+1]-1 in
+ * order (worker_ptr int32 [num_workers+1]; *num_workers receives num_cu *
+ * tiles_per_cu). Append: tiles are listed in 8 bins, one per XCD: bin x is
+ * tiles worker_ptr[x] .. worker_ptr[x+1]-1 (worker_ptr int32 [9];
+ * *num_workers receives 8), and workgroup i runs bin i mod 8.
  * A slot of -1 means the tile writes the final output. merge int32
  * [num_merge][4] = {first row, kv_head, first_slot, n_states} per split unit.
  * Any output pointer may be NULL. */

@@ -15,31 +15,34 @@ is ``vis = kv_len`` (decode, non-causal) or ``min(kv_len, kv_len - qo_len +
 i1)`` (causal; ``i1`` = request-relative end of its rows), and its cost in
 pages is ``ceil(vis / page_size)``. Units are ordered (q tile, kv head).
 
-Decode — small pieces in 8 XCD queues, taken dynamically by
-``S = num_cu * tiles_per_cu`` worker waves:
+Decode — static work lists, balanced by dealing pieces largest first:
 
-1. ``W`` = total pages of all units; piece size
-   ``Q = min(MAX_PIECE_PAGES, max(min_chunk_pages, ceil(W / (S * pieces_per_worker))))``
-   (``pieces_per_worker`` defaults to ``PIECES_PER_WORKER``).
-2. A unit of ``n`` pages splits into ``C = max(1, ceil(n / Q))`` pieces;
-   piece i covers pages ``[i Q, min((i+1) Q, n))`` (full pieces, then the
-   remainder) and is the tile ``[b, kv_head, kv_indptr[b], base, key0,
-   key1, slot, C]`` (keys clipped to kv_len; a unit with no pages is one
-   empty piece). Dealt largest first (step 4), the remainders end up at the
-   tails of the queues, where small pieces even out the finish times.
-3. Units with ``C > 1`` get ``C`` partial slots (unit order, running count):
-   piece i writes slot ``base + i``; ``base = slot = -1`` when ``C == 1``.
-   Merge entry per split unit: ``(b, kv_head, base, C)``.
-4. XCD queues: the pieces of all kv heads over the same pages of a request
-   form a *piece group* (request b, piece i) of cost ``pages * num_kv_heads``.
-   Groups, in descending cost (stable on (b, i)), are dealt to ``XCD_BINS``
-   (8) queues, each to the queue with the least cost so far (lowest index on
-   ties). The tile list is queue 0, queue 1, ...; inside a queue, groups in
-   dealing order and a group's pieces by kv head; ``worker_ptr[0..8]`` are
-   the queue offsets. At run time the waves of XCD x take tiles from queue x
-   with an atomic counter and then from the other queues, so faster XCDs do
-   more; neighbouring waves read the kv heads of the same pages, i.e. whole
-   token rows, at about the same time.
+1. ``S = num_cu * tiles_per_cu`` worker waves; ``NS = max(1, S *
+   pieces_per_worker // num_kv_heads)`` bins (``pieces_per_worker`` defaults
+   to ``PIECES_PER_WORKER``). A piece costs its pages plus ``c0`` =
+   ``PIECE_COST_PAGES`` (8 for an E4M3 pool, else 4): the set-up and
+   epilogue of a piece, in pages of streaming time.
+2. ``N`` = total pages of the requests (``n_b = ceil(kv_len_b / ps)``);
+   piece size ``Q = min(MAX_PIECE_PAGES, max(1, min_chunk_pages,
+   ceil((N + c0 * batch) / NS)))``, the bins' mean cost.
+3. Request b splits into ``C_b = max(1, ceil(n_b / Q))`` pieces; piece i
+   covers pages ``[i Q, min((i+1) Q, n_b))`` (a request with no pages is one
+   empty piece).
+4. Pieces, in descending pages (stable on (b, i)), are dealt to the NS bins,
+   each to the bin with the least cost so far (lowest index on ties); a bin
+   keeps its pieces in dealing order.
+5. Requests with ``C_b > 1`` get ``C_b`` partial slots per kv head (request
+   order, running count ``base_b``; kv head h owns ``base_b + h C_b ..``);
+   piece i of unit (b, h) writes slot ``base_b + h C_b + i``; ``base = slot
+   = -1`` when ``C_b == 1``. Merge entry per split unit: ``(b, kv_head,
+   base_b + h C_b, C_b)``, in (request, kv head) order.
+6. Work list ``j = bin * num_kv_heads + h`` is bin ``bin``'s pieces for kv
+   head h, as tiles ``[b, h, kv_indptr[b], unit base, key0, key1, slot,
+   C_b]`` (keys clipped to kv_len); it runs on wave ``j mod S``. The tile
+   list is wave-major (a wave's lists in increasing j) and ``worker_ptr[w]
+   .. worker_ptr[w+1]-1`` are wave w's tiles. The num_kv_heads waves of a bin
+   read the kv heads of the same pages, i.e. whole token rows, at about the
+   same time.
 
 Append — uniform chunks:
 
@@ -79,6 +82,7 @@ SUPPORTED_GROUP = (1, 2, 4, 8)
 MAX_PIECE_PAGES = 128
 XCD_BINS = 8
 PIECES_PER_WORKER = 1
+PIECE_COST_PAGES = {"16-bit": 4, "e4m3": 8}
 
 
 class PlanSpecError(Exception):
@@ -176,37 +180,40 @@ def _deal(costs):
     return order, ptr
 
 
-def _decode_plan(kv_indptr, kv_lens, batch, Hkv, ps, k):
+def _decode_plan(kv_indptr, kv_lens, batch, Hkv, ps, k, c0):
     S = k["num_cu"] * k["tiles_per_cu"]
-    units = [(b, h, int(kv_lens[b])) for b in range(batch) for h in range(Hkv)]
-    npg = [_cdiv(L, ps) for (_, _, L) in units]
-    W = sum(npg)
-    Q = min(MAX_PIECE_PAGES, max(k["min_chunk_pages"], _cdiv(W, S * k["pieces_per_worker"])))
-    bases, merge, slots = {}, [], 0
-    for (b, h, L), n in zip(units, npg):
-        C = max(1, _cdiv(n, Q))
-        bases[(b, h)] = -1
-        if C > 1:
-            bases[(b, h)] = slots
-            slots += C
-            merge.append((b, h, slots - C, C))
-    groups, gcost = [], []                   # piece groups (b, i): tiles of heads 0..Hkv-1
+    NS = max(1, S * k["pieces_per_worker"] // Hkv)
+    n = [_cdiv(int(kv_lens[b]), ps) for b in range(batch)]
+    Q = min(MAX_PIECE_PAGES, max(1, k["min_chunk_pages"], _cdiv(sum(n) + c0 * batch, NS)))
+    pieces, C = [], []                      # (b, first page, end page, i)
     for b in range(batch):
-        L = int(kv_lens[b])
-        n = _cdiv(L, ps)
-        C = max(1, _cdiv(n, Q))
-        for i in range(C):
-            p0, p1 = i * Q, min((i + 1) * Q, n)
-            grp = []
-            for h in range(Hkv):
-                base = bases[(b, h)]
-                grp.append((b, h, int(kv_indptr[b]), base, p0 * ps, min(p1 * ps, L),
-                            base + i if C > 1 else -1, C))
-            groups.append(grp)
-            gcost.append((p1 - p0) * Hkv)
-    order, gptr = _deal(gcost)
-    tiles = [t for g in order for t in groups[g]]
-    wptr = [x * Hkv for x in gptr]
+        C.append(max(1, _cdiv(n[b], Q)))
+        for i in range(C[b]):
+            pieces.append((b, i * Q, min((i + 1) * Q, n[b]), i))
+    dealt = sorted(range(len(pieces)), key=lambda x: -(pieces[x][2] - pieces[x][1]))
+    cost, bins = [0] * NS, [[] for _ in range(NS)]
+    for x in dealt:
+        j = min(range(NS), key=lambda y: (cost[y], y))
+        bins[j].append(x)
+        cost[j] += pieces[x][2] - pieces[x][1] + c0
+    base, merge, slots = {}, [], 0
+    for b in range(batch):
+        base[b] = -1
+        if C[b] > 1:
+            base[b] = slots
+            merge += [(b, h, slots + h * C[b], C[b]) for h in range(Hkv)]
+            slots += C[b] * Hkv
+    tiles, wptr = [], []
+    for w in range(S):
+        wptr.append(len(tiles))
+        for j in range(w, NS * Hkv, S):
+            sg, h = divmod(j, Hkv)
+            for x in bins[sg]:
+                b, p0, p1, i = pieces[x]
+                ub = base[b] + h * C[b] if base[b] >= 0 else -1
+                tiles.append((b, h, int(kv_indptr[b]), ub, p0 * ps, min(p1 * ps, int(kv_lens[b])),
+                              ub + i if ub >= 0 else -1, C[b]))
+    wptr.append(len(tiles))
     return tiles, merge, slots, wptr, Q
 
 
@@ -261,9 +268,10 @@ def _append_plan(kv_lens, batch, Hkv, ps, qo_indptr, causal, k):
 def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
               num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
               max_batch: int, qo_indptr: Optional[Sequence[int]] = None, causal: bool = False,
-              max_qo_tokens: int = 0, **knobs) -> dict:
+              max_qo_tokens: int = 0, kv_dtype: Optional[str] = None, **knobs) -> dict:
     """Reference plan: tiles ``int32 [n, 8]``, merge ``int32 [m, 4]``, worker_ptr
-    ``int32 [S+1]`` (decode: worker waves; append: the 8 XCD bins) and scalars."""
+    ``int32 [S+1]`` (decode: worker waves; append: the 8 XCD bins) and scalars.
+    ``kv_dtype="e4m3"`` plans a decode over an FP8 pool (another piece cost)."""
     kv_indptr = np.asarray(kv_indptr, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     is_append = qo_indptr is not None
@@ -276,8 +284,9 @@ def plan_spec(kv_indptr: Sequence[int], kv_lens: Sequence[int], batch: int,
         tiles, merge, slots, wptr, P = _append_plan(kv_lens, batch, num_kv_heads, page_size,
                                                     np.asarray(qo_indptr, np.int64), causal, k)
     else:
+        c0 = PIECE_COST_PAGES["e4m3" if kv_dtype == "e4m3" else "16-bit"]
         tiles, merge, slots, wptr, P = _decode_plan(kv_indptr, kv_lens, batch, num_kv_heads,
-                                                    page_size, k)
+                                                    page_size, k, c0)
     if len(tiles) > k["max_tiles"]:
         raise PlanSpecError("CAPACITY", "too many tiles")
     if slots > k["max_partials"]:

@@ -17,7 +17,6 @@
 
 namespace pkfa {
 static_assert(kAppendBins == kXcdBins, "planner bins and kernel bins differ");
-static_assert(kQueueStride * 4 == 256, "decode queue counters are laid out one per 256 bytes");
 }  // namespace pkfa
 
 namespace pkfa {
@@ -100,7 +99,6 @@ AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const v
   p.part_o = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl->lay.dev_part_o);
   p.part_lse = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + pl->lay.dev_part_lse);
   p.counters = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + pl->lay.dev_counters);
-  p.queue = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + pl->lay.dev_queue);
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)pl->geom.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.v_scale = 1.0f;
@@ -187,10 +185,10 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
   }
   // Queue heads and arrival counters return to zero at the end of every run
   // call; clear them once per device workspace (fresh memory holds garbage).
-  const size_t cbytes = pl->lay.dev_part_lse - pl->lay.dev_queue;
+  const size_t cbytes = pl->lay.dev_part_lse - pl->lay.dev_counters;
   hipError_t e = hipSuccess;
   if (pl->zeroed_ws != dev_ws || pl->zeroed_bytes < cbytes) {
-    e = hipMemsetAsync(static_cast<uint8_t*>(dev_ws) + pl->lay.dev_queue, 0, cbytes, s);
+    e = hipMemsetAsync(static_cast<uint8_t*>(dev_ws) + pl->lay.dev_counters, 0, cbytes, s);
     if (e != hipSuccess) {
       pl->planned = 0;
       return hip_fail(e, "hipMemsetAsync (arrival counters)");
@@ -273,7 +271,7 @@ fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t*
   if (num_merge) *num_merge = pl->num_merge;
   if (worker_ptr_h)
     *worker_ptr_h = reinterpret_cast<const int32_t*>(ws + pl->lay.worker_ptr);
-  if (num_workers) *num_workers = kXcdBins;
+  if (num_workers) *num_workers = pl->geom.mode == FA_MODE_DECODE ? pl->num_workers : kXcdBins;
   return FA_OK;
 }
 

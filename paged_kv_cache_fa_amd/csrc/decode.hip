@@ -12,10 +12,10 @@
 //
 // MI355X design (decode is HBM-bound, so no MFMA):
 //  * one wave64 per worker, 4 independent waves per 256-thread workgroup, no
-//    barriers; the planner cuts every (request, kv head) into pieces of about
-//    the same number of pages and deals them to 8 queues, one per XCD; waves
-//    take pieces with atomic counters (own XCD's queue first), so the load
-//    follows the speed each XCD actually gets from memory;
+//    barriers; the planner cuts requests into pieces and deals them, largest
+//    first, to static per-wave work lists of the same cost (pages plus a
+//    per-piece overhead), the kv heads of a piece to neighbouring waves, so
+//    they read whole token rows of the same pages at about the same time;
 //  * all G = Hq/Hkv query heads of the kv head are packed in the wave (GQA),
 //    so each K/V byte is read from HBM once for all of them;
 //  * lane = 8 x row-group + segment: row group r (0..7) owns tokens r and r+8
@@ -31,6 +31,11 @@
 //    8-lane DPP sum; P*V: the two tokens a lane holds are paired per element
 //    (v_perm) and multiplied with the packed probabilities by the same dot2,
 //    accumulating in fp32;
+//  * E4M3 pages (one byte per element, one scale per tensor): a 128-byte K/V
+//    row is one 16-byte load per lane (segment s owns dims [16s, 16s+16));
+//    codes are widened exactly to the q type in registers (v_cvt_scalef32_pk
+//    with scale 1) and take the same dot2 path; the K scale joins the score
+//    scale and the V scale the final normalisation;
 //  * each row group keeps its own online-softmax state (reference max in log2
 //    units, sum, 16 fp32 accumulators per head); the reference is only moved
 //    (and the accumulators rescaled) when a wave-wide vote finds a score more
@@ -358,26 +363,17 @@ __device__ __forceinline__ void open_piece(const AttnParams& p, int tv, int lane
   c.chk = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
 }
 
-// Stream one piece: keys [key0, key1) of kv head hk of request row, for its G
-// q heads; leaves the state per row group in (m, l, acc). hook(k) runs at
-// the start of steady ring pass k counted from the end (k = 2, 1, 0 for the
-// last three passes; all three run after the loop if the piece has fewer),
-// where the caller overlaps the set-up of its next piece with the loads.
-template <int DT, int G, int NBUF, bool KV8, typename Hook>
-__device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx& c, int lane,
-                                             float (&m)[G], float (&l)[G], float (&acc)[G][16],
-                                             Hook&& hook) {
-  // The context's fields are wave-uniform; readfirstlane says so to the
-  // compiler (it loses track across the loop that hands pieces over), so the
-  // page buffer resources stay scalar.
-  const int hk = __builtin_amdgcn_readfirstlane(c.id.hk);
-  const int row = __builtin_amdgcn_readfirstlane(c.id.row);
-  const int Hq = p.num_qo_heads;
-  const int r = lane >> 3;
-  const int s = lane & 7;
-  // bytes per token row of the pool, and the lane's load offsets in a page
+// Wave-uniform bounds of a piece, taken from its context once its loads have
+// arrived.
+struct PieceRun {
+  int hk, row, key1, first_page, npg;
+};
+
+// Bytes per token row of the pool, and the lane's load offsets in a page.
+template <bool KV8>
+__device__ __forceinline__ uint32_t page_offsets(const AttnParams& p, int lane, uint32_t (&off)[4]) {
+  const uint32_t r = lane >> 3, s = lane & 7;
   const uint32_t ts2 = (uint32_t)p.token_stride * (KV8 ? 1u : 2u);
-  uint32_t off[4];
   if constexpr (KV8) {
     off[0] = r * ts2 + s * 16u;
     off[1] = (r + 8) * ts2 + s * 16u;
@@ -388,20 +384,32 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
     off[2] = (r + 8) * ts2 + s * 16u;
     off[3] = (r + 8) * ts2 + 128u + s * 16u;
   }
-  u32x4 qlo[G], qhi[G];
-  const uint16_t* qp = p.q + ((int64_t)row * Hq + hk * G) * 128;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    qlo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 0));
-    qhi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 2));
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
-  }
+  return ts2;
+}
+
+__device__ __forceinline__ int page_id_of(const PieceCtx& c, int j) {
+  return j < 64 ? __builtin_amdgcn_readlane(c.ids0, j & 63) : __builtin_amdgcn_readlane(c.ids1, j & 63);
+}
+
+// Bytes of page j of a piece that hold valid tokens (a buffer load past them
+// returns 0); kept scalar so the buffer resource needs no per-lane loop.
+__device__ __forceinline__ uint32_t page_bytes_of(const PieceRun& run, int j, uint32_t ts2) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(min(16, run.key1 - (run.first_page + j) * 16) *
+                                                  (int)ts2);
+}
+
+// Start a piece: check it against the device page table, request its q rows
+// and its first NBUF-1 pages into the ring. The caller runs this before the
+// previous piece's epilogue, which then overlaps the first loads' latency.
+template <int G, int NBUF, bool KV8>
+__device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx& c, int lane,
+                                            PieceRun& run, PageRegs<KV8> (&buf)[NBUF],
+                                            u32x4 (&qlo)[G], u32x4 (&qhi)[G]) {
+  // The context's fields are wave-uniform; readfirstlane says so to the
+  // compiler (it loses track across the loop that hands pieces over), so the
+  // page buffer resources stay scalar.
+  run.hk = __builtin_amdgcn_readfirstlane(c.id.hk);
+  run.row = __builtin_amdgcn_readfirstlane(c.id.row);
   // The device page table must agree with the plan (offset, and the key
   // range inside the request's valid tokens); a piece that disagrees reads
   // nothing.
@@ -409,40 +417,69 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
   const int kv_len =
       npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(c.chk, 2) : 0;
   const int key0 = __builtin_amdgcn_readfirstlane(c.key0);
-  const int first_page = __builtin_amdgcn_readfirstlane(c.first_page);
   const int key1_plan = __builtin_amdgcn_readfirstlane(c.key1_plan);
   const bool agrees = __builtin_amdgcn_readlane(c.chk, 0) == __builtin_amdgcn_readfirstlane(c.pbeg) &&
                       key1_plan <= kv_len;
-  const int key1 = agrees ? key1_plan : key0;
-  const int npg = agrees ? __builtin_amdgcn_readfirstlane(c.npg_plan) : 0;
-  auto page_id = [&](int j) -> int {
-    return j < 64 ? __builtin_amdgcn_readlane(c.ids0, j & 63)
-                  : __builtin_amdgcn_readlane(c.ids1, j & 63);
-  };
-  // bytes of the page that hold valid tokens (a buffer load past them returns
-  // 0); kept scalar so the buffer resource needs no per-lane loop
-  auto page_bytes = [&](int j) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_readfirstlane(min(16, key1 - (first_page + j) * 16) * (int)ts2);
-  };
-  const float scale = p.scale_log2;
+  run.first_page = __builtin_amdgcn_readfirstlane(c.first_page);
+  run.key1 = agrees ? key1_plan : key0;
+  run.npg = agrees ? __builtin_amdgcn_readfirstlane(c.npg_plan) : 0;
+  const int s = lane & 7;
+  const uint16_t* qp = p.q + ((int64_t)run.row * p.num_qo_heads + run.hk * G) * 128;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qlo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 0));
+    qhi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 2));
+  }
+  uint32_t off[4];
+  const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
+  if (run.npg >= 2 * NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u) load_page(buf[u], p, page_id_of(c, u), run.hk, 16u * ts2, off);
+  } else {
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u)
+      if (u < run.npg) load_page(buf[u], p, page_id_of(c, u), run.hk, page_bytes_of(run, u, ts2), off);
+  }
+}
 
-  PageRegs<KV8> buf[NBUF];
+// Stream one piece begun by begin_piece: keys [key0, key1) of kv head hk of
+// request row, for its G q heads; leaves the state per row group in (m, l,
+// acc). hook(k) runs at the start of steady ring pass k counted from the end
+// (k = 2, 1, 0 for the last three passes; all three run after the loop if
+// the piece has fewer), where the caller overlaps the set-up of its next
+// piece with the loads.
+template <int DT, int G, int NBUF, bool KV8, typename Hook>
+__device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx& c,
+                                             const PieceRun& run, int lane,
+                                             PageRegs<KV8> (&buf)[NBUF], const u32x4 (&qlo)[G],
+                                             const u32x4 (&qhi)[G], float (&m)[G], float (&l)[G],
+                                             float (&acc)[G][16], Hook&& hook) {
+  const int r = lane >> 3;
+  const int hk = run.hk, npg = run.npg, key1 = run.key1;
+  uint32_t off[4];
+  const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
+  }
+  const float scale = p.scale_log2;
   int j = 0;
   int hooks_left = 3;
   if (npg >= 2 * NBUF) {
     // Steady state: every page touched here is full and has a successor, so
-    // all loads (prologue included) are unconditional and the next page id is
-    // fetched one page ahead; the compiler then keeps NBUF-1 pages in flight.
+    // all loads are unconditional and the next page id is fetched one page
+    // ahead; the compiler then keeps NBUF-1 pages in flight.
     const uint32_t full = 16u * ts2;
-#pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u) load_page(buf[u], p, page_id(u), hk, full, off);
-    int nid = page_id(NBUF - 1);
+    int nid = page_id_of(c, NBUF - 1);
     auto ring_pass = [&](int j0) {
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         const int jn = j0 + u + NBUF - 1;
         const int pid = nid;
-        nid = page_id(jn + 1);
+        nid = page_id_of(c, jn + 1);
         load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, off);
         consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, true, true);
       }
@@ -459,10 +496,6 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
       if (passes - 1 - k < hooks_left) hook(--hooks_left);
       ring_pass(j);
     }
-  } else {
-#pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u)
-      if (u < npg) load_page(buf[u], p, page_id(u), hk, page_bytes(u), off);
   }
   // Tail: at most 2*NBUF-1 pages, the last one possibly partial.
   for (; j < npg; j += NBUF) {
@@ -471,8 +504,10 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
       const int jj = j + u;
       if (jj >= npg) break;
       const int jn = jj + NBUF - 1;
-      if (jn < npg) load_page(buf[(u + NBUF - 1) % NBUF], p, page_id(jn), hk, page_bytes(jn), off);
-      const int tb = (first_page + jj) * 16;
+      if (jn < npg)
+        load_page(buf[(u + NBUF - 1) % NBUF], p, page_id_of(c, jn), hk, page_bytes_of(run, jn, ts2),
+                  off);
+      const int tb = (run.first_page + jj) * 16;
       consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1,
                                tb + r + 8 < key1);
     }
@@ -480,48 +515,27 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
   while (hooks_left > 0) hook(--hooks_left);
 }
 
-// Worker waves take pieces from 8 queues (one per XCD; bin offsets in
-// worker_ptr) with agent-scope atomic counters: first the queue of their own
-// XCD (workgroup i runs on XCD i mod 8), then the others, so waves that run
-// faster take more pieces. The next piece is taken near the end of the
-// current one, and its tile and page ids are requested while the current
-// piece's last pages stream, so a new piece starts without a dependent round
-// trip. A split unit's pieces publish fp32 partial states; a wave reports a
-// piece's arrival only after its next piece (the partial's stores have long
+// Worker wave w runs the pieces worker_ptr[w] .. worker_ptr[w+1]-1 in order
+// (the planner gives every wave the same number of pages). The next piece's
+// tile and page ids are requested while the current piece's last pages
+// stream, so a new piece starts without a dependent round trip. A split
+// unit's pieces publish fp32 partial states; a wave reports a piece's
+// arrival only after its next piece (the partial's stores have long
 // completed by then, so the wait is free), and the last arriving piece
-// merges the unit. The last wave to finish resets the queue heads, so the
-// kernel can be replayed from a graph.
+// merges the unit and clears its counter, so the kernel can be replayed from
+// a graph.
 template <int DT, int G, int NBUF, bool KV8>
 __global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int r = lane >> 3, s = lane & 7;
-  const int x = blockIdx.x % 8;
-  // queue heads and the finished-wave count, each on its own 256-byte line
-  // (atomics to one line serialise)
-  int32_t* heads = p.queue;
-  auto head = [&](int q) { return heads + q * kQueueStride; };
-  const int bv = lane <= 8 ? p.worker_ptr[lane] : 0;
-  auto bin_lo = [&](int q) { return __builtin_amdgcn_readlane(bv, q); };
+  const int w = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (w >= p.header[6]) return;  // the grid rounds the worker count up to whole workgroups
+  const int t_end = __builtin_amdgcn_readfirstlane(p.worker_ptr[w + 1]);
+  int t = __builtin_amdgcn_readfirstlane(p.worker_ptr[w]);
   auto fetch_add = [&](int32_t* ptr) -> int {  // lane 0 only; result read by readlane
     int v = 0;
     if (lane == 0) v = __hip_atomic_fetch_add(ptr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return v;
-  };
-  // own-queue take: issued early, resolved (with stealing) later
-  auto resolve = [&](int issued) -> int {
-    const int idx = __builtin_amdgcn_readlane(issued, 0);
-    if (bin_lo(x) + idx < bin_lo(x + 1)) return bin_lo(x) + idx;
-    for (int k = 1; k < 8; ++k) {
-      const int q = (x + k) & 7;
-      const int lo = bin_lo(q), n = bin_lo(q + 1) - lo;
-      if (n <= 0) continue;
-      int cur = 0;
-      if (lane == 0) cur = __hip_atomic_load(head(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__builtin_amdgcn_readlane(cur, 0) >= n) continue;  // exhausted: no update
-      const int got = __builtin_amdgcn_readlane(fetch_add(head(q)), 0);
-      if (got < n) return lo + got;
-    }
-    return -1;
   };
   float m[G], l[G], acc[G][16];
   // arrival of a split piece whose partial was published earlier; the last
@@ -543,22 +557,26 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
 
   PieceId pd = {0, 0, -1, -1, 0};  // pending arrival (slot < 0: none)
   PieceCtx cur, nxt;
-  int t = resolve(fetch_add(head(x)));
-  if (t >= 0) open_piece(p, load_tile(p, t, lane), lane, cur);
-  while (t >= 0) {
-    // overlapped set-up of the next piece: take it (pass 2 from the end),
-    // request its tile (pass 1), open it (pass 0)
-    int issued = 0, tn = -1, tvn = 0;
+  PieceRun run, nrun;
+  PageRegs<KV8> buf[NBUF];
+  u32x4 qlo[G], qhi[G];
+  if (t < t_end) {
+    open_piece(p, load_tile(p, t, lane), lane, cur);
+    begin_piece<G, NBUF, KV8>(p, cur, lane, run, buf, qlo, qhi);
+  }
+  while (t < t_end) {
+    // overlapped set-up of the next piece: request its tile (pass 2 from the
+    // end) and its page ids (pass 1); it begins (q and first pages requested)
+    // before this piece's epilogue
+    const int tn = t + 1;
+    int tvn = 0;
     auto hook = [&](int k) {
-      if (k == 2) issued = fetch_add(head(x));
-      if (k == 1) {
-        tn = resolve(issued);
-        if (tn >= 0) tvn = load_tile(p, tn, lane);
-      }
-      if (k == 0 && tn >= 0) open_piece(p, tvn, lane, nxt);
+      if (k == 2 && tn < t_end) tvn = load_tile(p, tn, lane);
+      if (k == 1 && tn < t_end) open_piece(p, tvn, lane, nxt);
     };
-    stream_piece<DT, G, NBUF, KV8>(p, cur, lane, m, l, acc, hook);
+    stream_piece<DT, G, NBUF, KV8>(p, cur, run, lane, buf, qlo, qhi, m, l, acc, hook);
     const int arr = pd.slot >= 0 ? arrive(pd) : 0;
+    if (tn < t_end) begin_piece<G, NBUF, KV8>(p, nxt, lane, nrun, buf, qlo, qhi);
     merge_row_groups<G>(m, l, acc);
     if (cur.id.slot < 0)
       write_final<DT, G, KV8>(p, cur.id.row, cur.id.hk, r, s, m, l, acc);
@@ -568,14 +586,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(AttnParams p) {
     pd = cur.id;
     t = tn;
     cur = nxt;
+    run = nrun;
   }
   if (pd.slot >= 0) finish_arrival(pd, arrive(pd));
-  const int done = __builtin_amdgcn_readlane(fetch_add(head(8)), 0);
-  if (done == (int)gridDim.x * 4 - 1 && lane == 0) {
-#pragma unroll
-    for (int q = 0; q <= 8; ++q)
-      __hip_atomic_store(head(q), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
 }
 
 // Ring depth per group size: 16-bit pages keep 2 pages (16 KB per wave) in

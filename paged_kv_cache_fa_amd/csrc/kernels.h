@@ -11,7 +11,7 @@ namespace pkfa {
 struct AttnParams {
   const int32_t* header;      // {num_tiles, num_merge, ...}
   const int32_t* tiles;
-  const int32_t* worker_ptr;  // decode: [workers+1] tile ranges per worker wave
+  const int32_t* worker_ptr;  // decode: [workers+1] tile range of each worker wave
   const int32_t* merge;
   const uint16_t* q;          // [rows, Hq, 128]
   const uint16_t* k;          // page pools (16-bit elements, or E4M3 bytes)
@@ -26,8 +26,6 @@ struct AttnParams {
   float* part_o;              // [slots, G, 128] fp32 partial outputs (normalised)
   float* part_lse;            // [slots, G] partial lse in log2 units
   int32_t* counters;          // [slots] arrivals per split unit, indexed by its first slot
-  int32_t* queue;             // decode: queue heads q = 0..7 and the finished-wave count (q = 8)
-                              // at queue[q * kQueueStride]; zero between calls
   float scale_log2;           // sm_scale * k_scale * log2(e)
   float v_scale;              // per-tensor V scale, applied to the final output
   int32_t num_qo_heads;
@@ -36,7 +34,6 @@ struct AttnParams {
   int32_t defer_merge;        // append: split tiles only publish their partial states
 };
 
-constexpr int kQueueStride = 64;  // int32s between decode queue counters (one 256-byte line each)
 constexpr int kAppendBins = 8;  // append tile bins = XCDs (workgroup i runs bin i % 8)
 
 // kv_e4m3: the K/V pools hold E4M3 codes (strides in bytes) instead of dtype.

@@ -9,12 +9,12 @@
 // algorithm; this planner fixes one per mode. A *unit* is one kv head of one
 // q tile (a request in decode, up to qo_tile query rows in append).
 //
-// Decode (HBM-bound, one wave per worker): the units' pages are laid end to
-// end and cut into num_cu * tiles_per_cu equal contiguous shares, one per
-// worker wave, so every wave streams the same number of pages (+-1) in a
-// single round; runs longer than 128 pages are cut further (a wave keeps the
-// ids of one piece in two registers). A unit cut into C > 1 pieces gets C fp32
-// partial states, combined by log-sum-exp by the last piece to finish.
+// Decode (HBM-bound, one wave per worker): requests are cut into pieces of
+// about the mean load of a wave (at most 128 pages: a wave keeps the ids of
+// one piece in two registers) and the pieces are dealt largest first to
+// static work lists, one per worker wave, the kv heads of a piece to
+// neighbouring waves. A unit cut into C > 1 pieces gets C fp32 partial
+// states, combined by log-sum-exp by the last piece to finish.
 //
 // Append (MFMA-bound, one workgroup per tile): every q tile is cut into
 // chunks of P = max(min_chunk_pages, ceil(units / target)) pages, so tiles
@@ -112,8 +112,8 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
     mp = g.max_partials ? g.max_partials : (int64_t)g.pieces_per_worker * target + units;
     mm = g.max_merge ? g.max_merge : units;
   }
-  if (target > (1 << 22)) {
-    set_error("num_cu * tiles_per_cu too large");
+  if (target * std::max(1, g.pieces_per_worker) > (1 << 22)) {
+    set_error("num_cu * tiles_per_cu (* pieces_per_worker) too large");
     return FA_ERR_INVALID;
   }
   if (mt > (1 << 26) || mp > (1 << 26) || mm > (1 << 26)) {
@@ -134,18 +134,22 @@ Layout compute_layout(const fa_geometry& g) {
   L.header = 0;
   L.merge = kHeaderInts * 4;
   L.worker_ptr = L.merge + (size_t)g.max_merge * kMergeInts * 4;
-  L.tiles = align_up(L.worker_ptr + (size_t)(kXcdBins + 1) * 4, 64);
+  L.tiles = align_up(L.worker_ptr + (size_t)(std::max<int32_t>(L.workers, kXcdBins) + 1) * 4, 64);
   L.upload_end = L.tiles + (size_t)g.max_tiles * kTileInts * 4;
-  L.dev_queue = align_up(L.upload_end, 256);
-  L.dev_counters = L.dev_queue + (size_t)(kXcdBins + 1) * 256;  // queue counters, one line each
+  L.dev_counters = align_up(L.upload_end, 256);
   L.dev_part_lse = align_up(L.dev_counters + (size_t)g.max_partials * 4, 256);
   L.dev_part_o = align_up(L.dev_part_lse + (size_t)g.max_partials * G * 4, 256);
   L.dev_bytes = align_up(L.dev_part_o + (size_t)g.max_partials * G * g.head_dim * 4, 256);
   L.host_unsorted = align_up(L.upload_end, 64);
   L.host_order = L.host_unsorted + (size_t)g.max_tiles * kTileInts * 4;
-  L.host_cost = align_up(L.host_order + (size_t)g.max_tiles * 4, 8);
-  L.host_bin = L.host_cost + (size_t)g.max_tiles * 8;
-  L.host_units = align_up(L.host_bin + (size_t)g.max_tiles * 4, 8);
+  // tile order (append) / first piece of each decode segment (at most workers + 1)
+  // decode bins: at most workers * pieces_per_worker
+  const int64_t bins = (int64_t)L.workers * std::max(1, g.pieces_per_worker) + 2;
+  const size_t nlist = (size_t)std::max<int64_t>(g.max_tiles, bins);
+  L.host_cost = align_up(L.host_order + nlist * 4, 8);
+  L.host_bin = L.host_cost + nlist * 8;
+  L.host_seg = align_up(L.host_bin + nlist * 4, 8);
+  L.host_units = align_up(L.host_seg + (size_t)bins * 4, 8);
   // per (request, kv head): 2 int32 (decode) or int64 cost + 3 int32 (append)
   L.host_bytes = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 24;
   return L;
@@ -158,11 +162,15 @@ fa_status capacity_error(const char* what, int64_t n, int32_t cap) {
   return FA_ERR_CAPACITY;
 }
 
-// Decode: units cut into pieces of Q pages (and a remainder); the pieces of all kv heads
-// over the same pages of a request form a group, and groups are dealt to the
-// XCD queues (largest first, each to the least-loaded queue). Group costs
-// are small integers (pages * Hkv, pages <= Q), so both orderings are
-// counting sorts: linear in the number of pieces.
+// Decode: NS = S * pieces_per_worker / Hkv bins; bin s and kv head h form the
+// work list of wave s * Hkv + h (lists beyond S wrap round), so the Hkv waves
+// of a bin read the same pages at the same time. Each request is cut into
+// pieces of Q pages (the last one shorter; a request with no pages is one
+// empty piece), with Q the bins' mean cost, and a piece costs its pages plus
+// c0 pages' worth of set-up and epilogue. Pieces are dealt largest first
+// (stable), each to the bin of least cost (lowest index on ties), and keep
+// the dealing order inside their bin. Tiles are stored wave-major:
+// worker_ptr[w] .. worker_ptr[w+1]-1 are wave w's.
 fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, const int32_t* kv_indptr,
                       const int32_t* kv_lens, int32_t batch, int64_t* ntiles_out,
                       int64_t* nmerge_out, int64_t* slots_out, int64_t* piece_pages_out) {
@@ -171,51 +179,34 @@ fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, cons
   int32_t* merge = reinterpret_cast<int32_t*>(ws + lay.merge);
   int32_t* wptr = reinterpret_cast<int32_t*>(ws + lay.worker_ptr);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + lay.tiles);
-  int32_t* grp = reinterpret_cast<int32_t*>(ws + lay.host_unsorted);  // [ngroups][5] b, p0, p1, C, i
-  int32_t* order = reinterpret_cast<int32_t*>(ws + lay.host_order);
-  int32_t* sorted = reinterpret_cast<int32_t*>(ws + lay.host_bin);
-  int32_t* bases = reinterpret_cast<int32_t*>(ws + lay.host_units);     // [batch * Hkv]
-  int64_t W = 0;
-  for (int b = 0; b < batch; ++b) W += cdiv(kv_lens[b], ps) * Hkv;
+  int32_t* items = reinterpret_cast<int32_t*>(ws + lay.host_unsorted);  // [np][4] b, p0, p1, i
+  int32_t* order = reinterpret_cast<int32_t*>(ws + lay.host_order);     // dealing order
+  int64_t* heap = reinterpret_cast<int64_t*>(ws + lay.host_cost);       // [NS] cost << 23 | bin
+  int32_t* bin_of = reinterpret_cast<int32_t*>(ws + lay.host_bin);      // bin of the n-th dealt
+  int32_t* first = reinterpret_cast<int32_t*>(ws + lay.host_seg);       // [NS+1]
+  int32_t* npc = reinterpret_cast<int32_t*>(ws + lay.host_units);       // [batch] pieces
+  int32_t* base = npc + batch;                                           // [batch] first slot
+  const int64_t NS = std::max<int64_t>(1, S * g.pieces_per_worker / Hkv);
+  const int64_t c0 = g.kv_dtype == FA_E4M3 ? kPieceCostPagesE4M3 : kPieceCostPages16;
+  int64_t N = 0;
+  for (int b = 0; b < batch; ++b) N += cdiv(kv_lens[b], ps);
   const int64_t Q = std::min<int64_t>(
-      kMaxPiecePages, std::max<int64_t>(g.min_chunk_pages, cdiv(W, S * g.pieces_per_worker)));
-  // pieces, slots and merge entries in unit order
-  int64_t ngroups = 0, nmerge = 0, slots = 0;
-  for (int b = 0; b < batch; ++b) {
-    const int64_t C = std::max<int64_t>(1, cdiv(cdiv(kv_lens[b], ps), Q));
-    ngroups += C;
-    for (int h = 0; h < Hkv; ++h) {
-      bases[(int64_t)b * Hkv + h] = -1;
-      if (C > 1) {
-        bases[(int64_t)b * Hkv + h] = (int32_t)slots;
-        if (nmerge < g.max_merge) {
-          int32_t* m = merge + nmerge * kMergeInts;
-          m[0] = b;
-          m[1] = h;
-          m[2] = (int32_t)slots;
-          m[3] = (int32_t)C;
-        }
-        slots += C;
-        ++nmerge;
-      }
-    }
-  }
-  const int64_t ntiles = ngroups * Hkv;
-  if (ntiles > g.max_tiles) return capacity_error("tiles", ntiles, g.max_tiles);
-  if (slots > g.max_partials) return capacity_error("partial states", slots, g.max_partials);
-  if (nmerge > g.max_merge) return capacity_error("merge entries", nmerge, g.max_merge);
-  // groups in emission order, bucketed by pages (0..Q)
+      kMaxPiecePages,
+      std::max<int64_t>({1, (int64_t)g.min_chunk_pages, cdiv(N + c0 * batch, NS)}));
+  // pieces in request order
+  int64_t np = 0;
+  for (int b = 0; b < batch; ++b) np += std::max<int64_t>(1, cdiv(cdiv(kv_lens[b], ps), Q));
+  if (np * Hkv > g.max_tiles) return capacity_error("tiles", np * Hkv, g.max_tiles);
   int64_t cnt[kMaxPiecePages + 2] = {};
   for (int b = 0, k = 0; b < batch; ++b) {
     const int64_t n = cdiv(kv_lens[b], ps);
-    const int64_t C = std::max<int64_t>(1, cdiv(n, Q));
-    for (int64_t i = 0; i < C; ++i, ++k) {
-      int32_t* r = grp + (int64_t)k * 5;
+    npc[b] = (int32_t)std::max<int64_t>(1, cdiv(n, Q));
+    for (int32_t i = 0; i < npc[b]; ++i, ++k) {
+      int32_t* r = items + (int64_t)k * 4;
       r[0] = b;
       r[1] = (int32_t)(i * Q);
-      r[2] = (int32_t)std::min((i + 1) * Q, n);
-      r[3] = (int32_t)C;
-      r[4] = (int32_t)i;
+      r[2] = (int32_t)std::min<int64_t>((i + 1) * Q, n);
+      r[3] = i;
       ++cnt[r[2] - r[1]];
     }
   }
@@ -225,42 +216,83 @@ fa_status plan_decode(const fa_geometry& g, const Layout& lay, uint8_t* ws, cons
     start[pg] = acc;
     acc += cnt[pg];
   }
-  for (int64_t k = 0; k < ngroups; ++k) {
-    const int32_t* r = grp + k * 5;
+  for (int64_t k = 0; k < np; ++k) {
+    const int32_t* r = items + k * 4;
     order[start[r[2] - r[1]]++] = (int32_t)k;
   }
-  // deal; then stable by queue (counting sort by queue)
-  int64_t qcost[kXcdBins] = {}, qcnt[kXcdBins + 1] = {};
-  for (int64_t n = 0; n < ngroups; ++n) {
-    int x = 0;
-    for (int j = 1; j < kXcdBins; ++j)
-      if (qcost[j] < qcost[x]) x = j;
-    const int32_t* r = grp + (int64_t)order[n] * 5;
-    qcost[x] += (int64_t)(r[2] - r[1]) * Hkv;
-    ++qcnt[x + 1];
-    sorted[n] = x;  // queue of the n-th dealt group
+  // deal: a binary min-heap of (cost, bin) keys; ascending keys form a heap
+  constexpr int kBinBits = 23;
+  for (int64_t x = 0; x < NS; ++x) heap[x] = x;
+  for (int64_t n = 0; n < np; ++n) {
+    const int32_t* r = items + (int64_t)order[n] * 4;
+    const int64_t top = heap[0];
+    bin_of[n] = (int32_t)(top & ((1 << kBinBits) - 1));
+    const int64_t key = top + ((int64_t)(r[2] - r[1] + c0) << kBinBits);
+    // sift the raised key down from the root
+    int64_t i = 0;
+    for (;;) {
+      const int64_t c = 2 * i + 1;
+      if (c >= NS) break;
+      const int64_t m = (c + 1 < NS && heap[c + 1] < heap[c]) ? c + 1 : c;
+      if (heap[m] >= key) break;
+      heap[i] = heap[m];
+      i = m;
+    }
+    heap[i] = key;
   }
-  for (int x = 0; x < kXcdBins; ++x) qcnt[x + 1] += qcnt[x];
-  for (int x = 0; x <= kXcdBins; ++x) wptr[x] = (int32_t)(qcnt[x] * Hkv);
-  int64_t qpos[kXcdBins];
-  for (int x = 0; x < kXcdBins; ++x) qpos[x] = qcnt[x];
-  for (int64_t n = 0; n < ngroups; ++n) {
-    const int32_t* r = grp + (int64_t)order[n] * 5;
-    const int b = r[0];
-    const int64_t k = qpos[sorted[n]]++;
-    for (int h = 0; h < Hkv; ++h) {
-      int32_t* t = tiles + (k * Hkv + h) * kTileInts;
-      const int32_t base = bases[(int64_t)b * Hkv + h];
-      t[0] = b;
-      t[1] = h;
-      t[2] = kv_indptr[b];
-      t[3] = base;
-      t[4] = r[1] * ps;
-      t[5] = (int32_t)std::min<int64_t>((int64_t)r[2] * ps, kv_lens[b]);
-      t[6] = base >= 0 ? base + r[4] : -1;
-      t[7] = r[3];
+  // bins' pieces in dealing order
+  for (int64_t x = 0; x <= NS; ++x) first[x] = 0;
+  for (int64_t n = 0; n < np; ++n) ++first[bin_of[n] + 1];
+  for (int64_t x = 0; x < NS; ++x) first[x + 1] += first[x];
+  int32_t* binned = items + np * 4;  // [np] item per bin position
+  for (int64_t n = 0; n < np; ++n) binned[first[bin_of[n]]++] = order[n];
+  for (int64_t x = NS; x > 0; --x) first[x] = first[x - 1];
+  first[0] = 0;
+  // slots: unit (b, h) of a request cut into C > 1 pieces owns base[b] + h*C .. + C-1
+  int64_t nmerge = 0, slots = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t C = npc[b];
+    base[b] = -1;
+    if (C <= 1) continue;
+    base[b] = (int32_t)slots;
+    for (int h = 0; h < Hkv; ++h, ++nmerge) {
+      if (nmerge >= g.max_merge) continue;
+      int32_t* m = merge + nmerge * kMergeInts;
+      m[0] = b;
+      m[1] = h;
+      m[2] = (int32_t)(slots + (int64_t)h * C);
+      m[3] = C;
+    }
+    slots += (int64_t)C * Hkv;
+  }
+  const int64_t ntiles = np * Hkv;
+  if (slots > g.max_partials) return capacity_error("partial states", slots, g.max_partials);
+  if (nmerge > g.max_merge) return capacity_error("merge entries", nmerge, g.max_merge);
+  // wave-major tiles: list j = bin * Hkv + head runs on wave j % S
+  int64_t k = 0;
+  for (int64_t w = 0; w < S; ++w) {
+    wptr[w] = (int32_t)k;
+    for (int64_t j = w; j < NS * Hkv; j += S) {
+      const int64_t sgm = j / Hkv;
+      const int h = (int)(j % Hkv);
+      for (int64_t q = first[sgm]; q < first[sgm + 1]; ++q, ++k) {
+        const int32_t* r = items + (int64_t)binned[q] * 4;
+        const int b = r[0];
+        const int32_t C = npc[b];
+        const int32_t ub = base[b] >= 0 ? base[b] + h * C : -1;
+        int32_t* t = tiles + k * kTileInts;
+        t[0] = b;
+        t[1] = h;
+        t[2] = kv_indptr[b];
+        t[3] = ub;
+        t[4] = r[1] * ps;
+        t[5] = (int32_t)std::min<int64_t>((int64_t)r[2] * ps, kv_lens[b]);
+        t[6] = ub >= 0 ? ub + r[3] : -1;
+        t[7] = C;
+      }
     }
   }
+  wptr[S] = (int32_t)k;
   *ntiles_out = ntiles;
   *nmerge_out = nmerge;
   *slots_out = slots;

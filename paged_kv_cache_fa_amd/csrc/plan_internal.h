@@ -16,21 +16,25 @@ constexpr int kHeaderInts = 16;  // {num_tiles, num_merge, batch, num_rows, caus
 constexpr int kSupportedHeadDim = 128;
 constexpr int kSupportedPageSize = 16;
 constexpr int kMaxPiecePages = 128;  // decode pieces: the kernel holds 128 page ids per wave
-constexpr int kXcdBins = 8;          // tile bins / queues, one per XCD (workgroup i runs on XCD i % 8)
-constexpr int kPiecesPerWorker = 1;  // decode: pieces per worker wave the piece size aims at
+constexpr int kXcdBins = 8;          // append tile bins, one per XCD (workgroup i runs on XCD i % 8)
+constexpr int kPiecesPerWorker = 1;  // decode: work lists per worker wave
+// decode: set-up and epilogue of one piece, in pages of streaming time
+constexpr int kPieceCostPages16 = 4;
+constexpr int kPieceCostPagesE4M3 = 8;
 
 // Byte offsets of the regions inside the host and device workspaces.
 // Upload image (same offsets in host and device workspace):
-//   header | merge [max_merge][4] | bin offsets [9] | tiles [max_tiles][8]
-// Device only: decode queue heads [8] + finished-wave count (zero between
-// calls), arrival counters [max_partials] (zero between calls), partial
+//   header | merge [max_merge][4] | tile offsets (decode: [workers+1] per
+//   worker wave; append: [9] per XCD bin) | tiles [max_tiles][8]
+// Device only: arrival counters [max_partials] (zero between calls), partial
 // lse [max_partials][G] (log2 units), partial out [max_partials][G][head_dim].
-// Host only: scratch for sorting tiles, per-unit counts and (append) per-group
-// cost / order / bin / sequence.
+// Host only: scratch for sorting and dealing tiles (decode: pieces, dealing
+// order, bin heap, bin of each dealt piece, bin offsets; append: per-group
+// cost / order / bin / sequence) and per-request / per-unit counts.
 struct Layout {
   size_t header, merge, worker_ptr, tiles, upload_end;
-  size_t dev_queue, dev_counters, dev_part_lse, dev_part_o, dev_bytes;
-  size_t host_unsorted, host_order, host_cost, host_bin, host_units, host_bytes;
+  size_t dev_counters, dev_part_lse, dev_part_o, dev_bytes;
+  size_t host_unsorted, host_order, host_cost, host_bin, host_seg, host_units, host_bytes;
   int32_t workers;
 };
 

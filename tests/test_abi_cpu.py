@@ -53,7 +53,8 @@ def _compare(g, lens, qo_indptr=None, causal=False, **spec_knobs):
                  max_merge=r.max_merge, pieces_per_worker=r.pieces_per_worker)
     spec = plan_spec(_indptr(lens), lens, len(lens), g.num_qo_heads, g.num_kv_heads, 128, 16,
                      max_batch=g.max_batch, qo_indptr=qo_indptr, causal=causal,
-                     max_qo_tokens=g.max_qo_tokens, **knobs)
+                     max_qo_tokens=g.max_qo_tokens,
+                     kv_dtype="e4m3" if r.kv_dtype == fa.FA_E4M3 else None, **knobs)
     tiles, merge, wptr = p.tiles(with_workers=True)
     assert np.array_equal(tiles, spec["tiles"])
     assert np.array_equal(merge, spec["merge"])
@@ -71,6 +72,8 @@ def test_plan_bit_exact_decode_configs(k):
     lens = config_lengths(k, np.random.default_rng(k))["kv_lens"]
     Hkv = 32 if k == 1 else 8
     _compare(_geom("decode", len(lens), 32, Hkv), lens)
+    if k != 1:  # E4M3 pools plan with their own piece cost
+        _compare(_geom("decode", len(lens), 32, Hkv, kv_dtype="e4m3"), lens)
 
 
 def test_plan_default_knobs_match_the_spec_defaults():
@@ -107,6 +110,7 @@ def test_plan_bit_exact_random():
                      min_chunk_pages=int(rng.integers(1, 5)))
         if it % 2:
             knobs["pieces_per_worker"] = int(rng.integers(1, 5))
+            knobs["kv_dtype"] = "e4m3" if it % 4 == 1 else None
             _compare(_geom("decode", max(B, 1) + int(rng.integers(0, 3)), G * Hkv, Hkv, **knobs),
                      lens)
         else:
@@ -163,11 +167,6 @@ def test_kv_dtype_geometry():
     st = fa.Plan(fa.geometry("decode", "fp16", 4, 32, 8)).plan(
         _indptr([40]), np.array([40], np.int32)).info()
     assert st.resolved.kv_dtype == fa.FA_F16
-    # same plan as the 16-bit pool: the work split does not depend on the pool type
-    t8, m8 = p.tiles()
-    t16, m16 = fa.Plan(fa.geometry("decode", "bf16", 4, 32, 8)).plan(
-        _indptr([40, 7]), np.array([40, 7], np.int32)).tiles()
-    assert np.array_equal(t8, t16) and np.array_equal(m8, m16)
     for bad in (fa.geometry("append", "bf16", 4, 32, 8, max_qo_tokens=64, kv_dtype="e4m3"),
                 fa.geometry("decode", "fp16", 4, 32, 8, kv_dtype="bf16"),
                 fa.geometry("decode", "bf16", 4, 32, 8, kv_dtype="fp32")):

@@ -13,30 +13,43 @@ def _indptr(lens, ps=16):
 
 def test_hand_worked_decode_plan():
     # Three requests of 4, 2, 5 full pages (the page lists of the worked CSR
-    # example), 2 kv heads -> units of 4,4,2,2,5,5 pages, W = 22. 8 workers:
-    # Q = ceil(22 / 8) = 3 pages; units split into full pieces of 3
-    # pages and a remainder: 4 -> [0,3) [3,4), 2 -> [0,2), 5 -> [0,3) [3,5).
-    # Piece groups (request, piece) hold both heads: costs (0,0) 6, (0,1) 2,
-    # (1,0) 4, (2,0) 6, (2,1) 4 pages, dealt largest first to queues 0..4.
-    # Field 2 is the request's first page in kv_indices (0, 4, 6).
+    # example), 2 kv heads; piece cost c0 = 4 pages. 16 workers -> NS = 8 bins;
+    # N = 11 pages, Q = ceil((11 + 4*3) / 8) = 3: request 0 -> [0,3) [3,4),
+    # request 1 -> [0,2), request 2 -> [0,3) [3,5). Dealt largest first
+    # (stable): (0,[0,3)) bin 0, (2,[0,3)) bin 1, (1,[0,2)) bin 2, (2,[3,5))
+    # bin 3, (0,[3,4)) bin 4. List j = bin*2 + head runs on wave j. Requests 0
+    # and 2 are split: head h of request 0 owns slots 2h, 2h+1; of request 2,
+    # 4+2h, 5+2h. Field 2 is the request's first page in kv_indices (0, 4, 6).
     lens = [64, 32, 80]
-    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=2, tiles_per_cu=4)
+    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=4, tiles_per_cu=4)
     assert p["tiles"].tolist() == [
-        [0, 0, 0, 0, 0, 48, 0, 2], [0, 1, 0, 2, 0, 48, 2, 2],       # queue 0
-        [2, 0, 6, 4, 0, 48, 4, 2], [2, 1, 6, 6, 0, 48, 6, 2],       # queue 1
-        [1, 0, 4, -1, 0, 32, -1, 1], [1, 1, 4, -1, 0, 32, -1, 1],   # queue 2
-        [2, 0, 6, 4, 48, 80, 5, 2], [2, 1, 6, 6, 48, 80, 7, 2],     # queue 3
-        [0, 0, 0, 0, 48, 64, 1, 2], [0, 1, 0, 2, 48, 64, 3, 2],     # queue 4
+        [0, 0, 0, 0, 0, 48, 0, 2], [0, 1, 0, 2, 0, 48, 2, 2],       # bin 0
+        [2, 0, 6, 4, 0, 48, 4, 2], [2, 1, 6, 6, 0, 48, 6, 2],       # bin 1
+        [1, 0, 4, -1, 0, 32, -1, 1], [1, 1, 4, -1, 0, 32, -1, 1],   # bin 2
+        [2, 0, 6, 4, 48, 80, 5, 2], [2, 1, 6, 6, 48, 80, 7, 2],     # bin 3
+        [0, 0, 0, 0, 48, 64, 1, 2], [0, 1, 0, 2, 48, 64, 3, 2],     # bin 4
     ]
-    assert p["worker_ptr"].tolist() == [0, 2, 4, 6, 8, 10, 10, 10, 10]
+    assert p["worker_ptr"].tolist() == list(range(11)) + [10] * 6
     assert p["merge"].tolist() == [[0, 0, 0, 2], [0, 1, 2, 2], [2, 0, 4, 2], [2, 1, 6, 2]]
     assert p["num_slots"] == 8 and p["chunk_pages"] == 3
-    # one worker: Q = 22, every unit is one piece, nothing to merge; groups of
-    # 10, 8, 4 pages go to queues 0, 1, 2
+    # 8 workers -> 4 bins, Q = ceil(23 / 4) = 6: no request is split; dealt
+    # 5, 4, 2 pages to bins 0, 1, 2 (waves 0-1, 2-3, 4-5)
+    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=2, tiles_per_cu=4)
+    assert p["num_slots"] == 0 and p["merge"].shape == (0, 4) and p["chunk_pages"] == 6
+    assert p["tiles"].tolist() == [
+        [2, 0, 6, -1, 0, 80, -1, 1], [2, 1, 6, -1, 0, 80, -1, 1],
+        [0, 0, 0, -1, 0, 64, -1, 1], [0, 1, 0, -1, 0, 64, -1, 1],
+        [1, 0, 4, -1, 0, 32, -1, 1], [1, 1, 4, -1, 0, 32, -1, 1],
+    ]
+    assert p["worker_ptr"].tolist() == [0, 1, 2, 3, 4, 5, 6, 6, 6]
+    # one worker: one bin; the wave runs list 0 (head 0) then list 1 (head 1)
     p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=1, tiles_per_cu=1)
-    assert p["num_slots"] == 0 and p["merge"].shape == (0, 4)
-    assert p["tiles"][:, :2].tolist() == [[2, 0], [2, 1], [0, 0], [0, 1], [1, 0], [1, 1]]
-    assert p["worker_ptr"].tolist() == [0, 2, 4, 6, 6, 6, 6, 6, 6]
+    assert p["tiles"][:, :2].tolist() == [[2, 0], [0, 0], [1, 0], [2, 1], [0, 1], [1, 1]]
+    assert p["worker_ptr"].tolist() == [0, 6]
+    # an E4M3 pool: c0 = 8 -> Q = ceil((11 + 24) / 8) = 5, no split
+    p = plan_spec(_indptr(lens), lens, 3, 2, 2, 128, 16, max_batch=3, num_cu=4, tiles_per_cu=4,
+                  kv_dtype="e4m3")
+    assert p["chunk_pages"] == 5 and p["num_slots"] == 0
 
 
 def test_hand_worked_append_plan():
@@ -83,23 +96,28 @@ def _pages(k0, k1, ps=16):
     return -(-k1 // ps) - k0 // ps
 
 
-def check_decode_invariants(p, lens, Hkv, ps=16):
+def check_decode_invariants(p, lens, Hkv, ps=16, c0=4):
     tiles, wptr, Q = p["tiles"], p["worker_ptr"], p["chunk_pages"]
-    assert len(wptr) == 9 and wptr[0] == 0 and wptr[-1] == len(tiles)
+    S = p["target"]
+    assert len(wptr) == S + 1 and wptr[0] == 0 and wptr[-1] == len(tiles)
     assert np.all(np.diff(wptr) >= 0)
-    pages = [_pages(t[4], t[5], ps) for t in tiles.tolist()]
-    qload = []
-    for x in range(8):
-        seg = pages[wptr[x]:wptr[x + 1]]
-        assert all(a >= b for a, b in zip(seg, seg[1:])), "queue not in descending pages"
-        assert (wptr[x + 1] - wptr[x]) % Hkv == 0
-        for g0 in range(wptr[x], wptr[x + 1], Hkv):   # a piece group: same pages, heads in order
-            grp = tiles[g0:g0 + Hkv]
-            assert grp[:, 1].tolist() == list(range(Hkv))
-            assert (grp[:, [0, 4, 5]] == grp[0, [0, 4, 5]]).all()
-        qload.append(sum(seg))
-    if pages:
-        assert max(qload) - min(qload) <= max(pages) * Hkv, "queues out of balance"
+    NS = max(1, S * p["knobs"]["pieces_per_worker"] // Hkv)
+    if NS * Hkv <= S:
+        # wave s*Hkv + h runs bin s for head h: the Hkv waves of a bin run the
+        # same pieces; the pieces of a bin come in non-increasing pages; the
+        # bins' costs (pages + c0 per piece) are within one piece of each other
+        bcost = []
+        for sg in range(NS):
+            lists = [tiles[wptr[sg * Hkv + h]:wptr[sg * Hkv + h + 1]] for h in range(Hkv)]
+            for h, lst in enumerate(lists):
+                assert (lst[:, 1] == h).all()
+                assert (lst[:, [0, 4, 5]] == lists[0][:, [0, 4, 5]]).all()
+            pg = [_pages(t[4], t[5], ps) for t in lists[0].tolist()]
+            assert all(x >= y for x, y in zip(pg, pg[1:])), "bin not in dealing order"
+            bcost.append(sum(pg) + c0 * len(pg))
+        assert wptr[NS * Hkv] == len(tiles), "waves past the bins hold tiles"
+        if len(tiles):
+            assert max(bcost) - min(bcost) <= Q + c0, "bins out of balance"
     by_unit = {}
     for t in tiles.tolist():
         by_unit.setdefault((t[0], t[1]), []).append(t)
