@@ -83,7 +83,11 @@ typedef struct {
   int32_t min_chunk_pages; /* smallest split-KV chunk / decode piece size in pages (default 1) */
   int32_t qo_tile;         /* append: query rows per tile, 1..128/G (default 128/G,
                               G = num_qo_heads / num_kv_heads); decode: 1 */
-  int32_t max_tiles;       /* capacities; default = worst case of the plan procedure */
+  int32_t max_tiles;       /* capacities; the defaults cover every plan whose total pages
+                              (plus 4 or 8 per request) stay within 128 pages per bin (decode:
+                              bins = num_cu * tiles_per_cu * pieces_per_worker / num_kv_heads),
+                              and append plans up to max_qo_tokens rows; larger plans return
+                              FA_ERR_CAPACITY */
   int32_t max_partials;
   int32_t max_merge;
   int32_t pieces_per_worker; /* decode: work lists per worker wave (default 1) */
@@ -143,6 +147,24 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
                   const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
                   int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
                   size_t dev_ws_bytes, void* stream);
+
+/* Plan over a ragged (contiguous) KV cache instead of a paged one ([Guide]
+ * "What FlashInfer is", idea 1: one block-sparse format describes a ragged
+ * tensor as well as a page table; [DeepDive] "Snippet One": single-request
+ * decode over a contiguous KV cache). Request b's keys are rows
+ * kv_offsets_h[b] .. kv_offsets_h[b+1]-1 of K / V tensors [total_rows,
+ * num_kv_heads, head_dim]; a single request over a contiguous K / V is the
+ * batch-1 case (kv_offsets {0, kv_len}).
+ *  kv_offsets_h  host int32 [batch+1], starting at 0 and non-decreasing.
+ * The offsets are also copied into the device workspace, where run calls read
+ * them when given no device copy. The work plan is the one fa_plan makes for
+ * the same lengths (page_size rows standing for a page). Other arguments and
+ * errors as fa_plan. Run the plan with fa_decode_ragged / fa_append_ragged
+ * only; the paged run calls refuse it (and these refuse fa_plan's plans). */
+fa_status fa_plan_ragged(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_offsets_h,
+                         int32_t batch, const int32_t* qo_indptr_h, int32_t causal,
+                         void* host_ws, size_t host_ws_bytes, void* dev_ws, size_t dev_ws_bytes,
+                         void* stream);
 
 /* Summary of the current plan. */
 fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats);
@@ -213,6 +235,28 @@ fa_status fa_decode_scaled(const fa_plan_t* plan, const void* q, const void* k_p
                            const int32_t* kv_indptr_d, const int32_t* last_page_len_d,
                            float sm_scale, float k_scale, float v_scale, void* out, float* lse,
                            void* stream);
+
+/* Decode over a ragged KV cache planned by fa_plan_ragged.
+ *  k, v          device [total_rows, num_kv_heads, head_dim] (element (row, h, d) at
+ *                row*token_stride + h*head_stride + d; 16-byte aligned; strides as in
+ *                fa_decode, in bytes for an FA_E4M3 plan).
+ *  kv_offsets_d  device int32 [batch+1], the same content as given to fa_plan_ragged,
+ *                or NULL to use the copy in the plan's workspace.
+ *  k_scale, v_scale  as in fa_decode_scaled (1 for unscaled 16-bit K / V).
+ * Other arguments, results and errors as fa_decode_scaled. */
+fa_status fa_decode_ragged(const fa_plan_t* plan, const void* q, const void* k, const void* v,
+                           int64_t token_stride, int64_t head_stride, const int32_t* kv_offsets_d,
+                           float sm_scale, float k_scale, float v_scale, void* out, float* lse,
+                           void* stream);
+
+/* Append / prefill over a ragged KV cache planned by fa_plan_ragged with
+ * qo_indptr (the new rows' K / V are the last qo_len rows of each request).
+ * k, v, strides and kv_offsets_d as in fa_decode_ragged; other arguments,
+ * results and errors as fa_append. */
+fa_status fa_append_ragged(const fa_plan_t* plan, const void* q, const int32_t* qo_indptr_d,
+                           const void* k, const void* v, int64_t token_stride,
+                           int64_t head_stride, const int32_t* kv_offsets_d, float sm_scale,
+                           void* out, float* lse, void* stream);
 
 /* Append / prefill over the paged KV cache, causal or not as planned ([Guide]
  * "Features (from the repository README)": prefill and append kernels). The

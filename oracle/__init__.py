@@ -33,6 +33,9 @@ from .attention import (  # noqa: F401
     attend,
     decode,
     append,
+    ragged_request_kv,
+    decode_ragged,
+    append_ragged,
     cascade,
     cascade_direct,
 )

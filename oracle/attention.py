@@ -158,6 +158,52 @@ def append(q_bits: np.ndarray, qo_indptr, pool: np.ndarray, dtype: str, kv_indpt
     keys. Returns ``out``/``lse`` for the listed rows of the packed q (all
     rows by default, in order).
     """
+    return _append_rows(q_bits, qo_indptr, dtype, lambda b: gather_request_kv(
+        pool, dtype, kv_indptr, kv_indices, last_page_len, page_size, b), causal, scale, rows)
+
+
+def ragged_request_kv(k_bits: np.ndarray, v_bits: np.ndarray, dtype: str, kv_offsets, b: int,
+                      k_scale: float = 1.0, v_scale: float = 1.0):
+    """K and V of request b of a ragged cache as float64 ``[kv_len, kv_heads, head_dim]``.
+
+    [Guide, "What FlashInfer is", idea 1]: a ragged tensor holds each
+    request's keys as consecutive rows; request b owns rows
+    ``kv_offsets[b] .. kv_offsets[b+1]-1`` of ``[rows, kv_heads, head_dim]``.
+    """
+    r0, r1 = int(kv_offsets[b]), int(kv_offsets[b + 1])
+    return k_scale * upcast(k_bits[r0:r1], dtype), v_scale * upcast(v_bits[r0:r1], dtype)
+
+
+def decode_ragged(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dtype: str,
+                  kv_offsets, scale: Optional[float] = None,
+                  requests: Optional[Sequence[int]] = None, kv_dtype: Optional[str] = None,
+                  k_scale: float = 1.0, v_scale: float = 1.0):
+    """Decode over a ragged cache (one query row per request); a single
+    request over one contiguous K / V ([DeepDive, "Snippet One"]: the
+    single-sequence decode) is ``kv_offsets = [0, kv_len]``."""
+    D = q_bits.shape[-1]
+    scale = default_scale(D) if scale is None else scale
+    kv_dtype = dtype if kv_dtype is None else kv_dtype
+    reqs = range(q_bits.shape[0]) if requests is None else list(requests)
+    outs, lses = [], []
+    for b in reqs:
+        K, V = ragged_request_kv(k_bits, v_bits, kv_dtype, kv_offsets, b, k_scale, v_scale)
+        o, s = attend(upcast(q_bits[b: b + 1], dtype), K, V, scale)
+        outs.append(o[0])
+        lses.append(s[0])
+    return np.stack(outs), np.stack(lses)
+
+
+def append_ragged(q_bits: np.ndarray, qo_indptr, k_bits: np.ndarray, v_bits: np.ndarray,
+                  dtype: str, kv_offsets, causal: bool = True, scale: Optional[float] = None,
+                  rows: Optional[Sequence[int]] = None):
+    """Append/prefill over a ragged cache; rows and masking as ``append``."""
+    return _append_rows(q_bits, qo_indptr, dtype, lambda b: ragged_request_kv(
+        k_bits, v_bits, dtype, kv_offsets, b), causal, scale, rows)
+
+
+def _append_rows(q_bits, qo_indptr, dtype, kv_of, causal, scale, rows):
+    """Rows of ``append`` / ``append_ragged``; ``kv_of(b)`` gives request b's K, V."""
     D = q_bits.shape[-1]
     scale = default_scale(D) if scale is None else scale
     qo_indptr = np.asarray(qo_indptr)
@@ -171,7 +217,7 @@ def append(q_bits: np.ndarray, qo_indptr, pool: np.ndarray, dtype: str, kv_indpt
     for b in range(B):
         if b not in by_req:
             continue
-        K, V = gather_request_kv(pool, dtype, kv_indptr, kv_indices, last_page_len, page_size, b)
+        K, V = kv_of(b)
         L = K.shape[0]
         qo_len = int(qo_indptr[b + 1] - qo_indptr[b])
         rs = by_req[b]

@@ -6,9 +6,11 @@ computation runs in the library's HIP kernels. Device buffers are torch
 tensors (used for memory and streams only); there is no CPU fallback — if the
 library is missing, the import of any entry point raises.
 
-Entry points (same names as the C ABI): ``workspace_size``, ``plan`` (returns a
-``Plan``), ``decode``, ``decode_scaled``, ``append``, ``cascade``,
-``merge_state``, ``merge_states``.
+Entry points (same names as the C ABI): ``workspace_size``, ``plan`` /
+``plan_ragged`` (return a ``Plan``), ``decode``, ``decode_scaled``,
+``decode_ragged``, ``append``, ``append_ragged``, ``cascade``, ``merge_state``,
+``merge_states``; and ``single_decode_with_kv_cache``, which plans and runs a
+one-request decode over a contiguous K / V.
 """
 from __future__ import annotations
 
@@ -129,6 +131,21 @@ class Plan:
                                 _stream(stream) if self.dev_ws is not None else None))
         return self
 
+    def plan_ragged(self, kv_offsets, qo_indptr=None, causal: bool = False, stream=None):
+        """Plan over a ragged KV cache: request b's keys are rows kv_offsets[b] ..
+        kv_offsets[b+1]-1 (see fa_plan_ragged)."""
+        kv_offsets, qo_indptr = _i32(kv_offsets), _i32(qo_indptr)
+        self._keep = (kv_offsets, qo_indptr)
+        batch = int(kv_offsets.shape[0]) - 1
+        check(self._lib.fa_plan_ragged(ctypes.byref(self._plan), ctypes.byref(self.geom),
+                                       _ptr(kv_offsets), batch,
+                                       _ptr(qo_indptr) if qo_indptr is not None else None,
+                                       int(causal), _ptr(self.host_ws), self.host_bytes,
+                                       _ptr(self.dev_ws) if self.dev_ws is not None else None,
+                                       self.dev_bytes if self.dev_ws is not None else 0,
+                                       _stream(stream) if self.dev_ws is not None else None))
+        return self
+
     def info(self) -> PlanStats:
         st = PlanStats()
         check(self._lib.fa_plan_info(ctypes.byref(self._plan), ctypes.byref(st)))
@@ -169,6 +186,12 @@ def plan(geom: Geometry, kv_indptr, kv_lens, qo_indptr=None, causal: bool = Fals
     return Plan(geom, device).plan(kv_indptr, kv_lens, qo_indptr, causal, stream)
 
 
+def plan_ragged(geom: Geometry, kv_offsets, qo_indptr=None, causal: bool = False, device=None,
+                stream=None) -> Plan:
+    """Build a ragged-KV plan (and upload it when ``device`` is given)."""
+    return Plan(geom, device).plan_ragged(kv_offsets, qo_indptr, causal, stream)
+
+
 def _alloc_out(q, out, lse, rows, heads):
     torch = _torch()
     if out is None:
@@ -203,6 +226,47 @@ def decode_scaled(p: Plan, q, k_pages, v_pages, page_stride: int, token_stride: 
                                   float(k_scale), float(v_scale), _ptr(out), _ptr(lse),
                                   _stream(stream)))
     return out, lse
+
+
+def decode_ragged(p: Plan, q, k, v, token_stride: int, head_stride: int, kv_offsets=None,
+                  sm_scale: float = 0.0, k_scale: float = 1.0, v_scale: float = 1.0, out=None,
+                  lse=None, stream=None):
+    """Decode over a ragged KV cache (see fa_decode_ragged); ``kv_offsets`` is a
+    device int32 tensor or None for the plan's copy. Returns (out, lse)."""
+    out, lse = _alloc_out(q, out, lse, q.shape[0], q.shape[1])
+    check(p._lib.fa_decode_ragged(ctypes.byref(p._plan), _ptr(q), _ptr(k), _ptr(v), token_stride,
+                                  head_stride, _ptr(kv_offsets), float(sm_scale), float(k_scale),
+                                  float(v_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def append_ragged(p: Plan, q, qo_indptr, k, v, token_stride: int, head_stride: int,
+                  kv_offsets=None, sm_scale: float = 0.0, out=None, lse=None, stream=None):
+    """Append / prefill over a ragged KV cache (see fa_append_ragged). Returns (out, lse)."""
+    out, lse = _alloc_out(q, out, lse, q.shape[0], q.shape[1])
+    check(p._lib.fa_append_ragged(ctypes.byref(p._plan), _ptr(q), _ptr(qo_indptr), _ptr(k),
+                                  _ptr(v), token_stride, head_stride, _ptr(kv_offsets),
+                                  float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def single_decode_with_kv_cache(q, k, v, sm_scale: float = 0.0, k_scale: float = 1.0,
+                                v_scale: float = 1.0, return_lse: bool = False, **knobs):
+    """One query row per q head against a contiguous K / V of one request.
+
+    q [num_qo_heads, head_dim], k / v [kv_len, num_kv_heads, head_dim] (16-bit,
+    or uint8 E4M3 codes with their scales). Plans a batch-1 ragged decode
+    (workspaces allocated here, as torch tensors) and runs it: every step is
+    the library's. Returns out [num_qo_heads, head_dim] (and lse [num_qo_heads])."""
+    torch = _torch()
+    L, hkv, d = k.shape
+    kvd = "e4m3" if k.dtype in (torch.uint8, torch.float8_e4m3fn) else None
+    g = geometry("decode", q.dtype, 1, q.shape[0], hkv, head_dim=d, kv_dtype=kvd, **knobs)
+    p = Plan(g, device=q.device).plan_ragged(np.array([0, L], dtype=np.int32))
+    out, lse = decode_ragged(p, q.reshape(1, *q.shape), k, v, k.stride(0), k.stride(1),
+                             sm_scale=sm_scale, k_scale=k_scale, v_scale=v_scale)
+    out = out.reshape(q.shape)
+    return (out, lse.reshape(-1)) if return_lse else out
 
 
 def append(p: Plan, q, qo_indptr, k_pages, v_pages, page_stride: int, token_stride: int,

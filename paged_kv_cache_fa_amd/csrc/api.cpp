@@ -37,7 +37,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 fa_status check_run_args(const PlanImpl* pl, int want_mode, const void* q, const void* k,
                           const void* v, int64_t page_stride, int64_t token_stride,
                           int64_t head_stride, const int32_t* kv_indices, const int32_t* kv_indptr,
-                          const int32_t* last_page_len, const void* out) {
+                          const int32_t* last_page_len, const void* out, bool ragged = false) {
   if (!pl || pl->magic != kPlanMagic || !pl->planned) {
     set_error("plan object was not filled by fa_plan");
     return FA_ERR_INVALID;
@@ -51,7 +51,12 @@ fa_status check_run_args(const PlanImpl* pl, int want_mode, const void* q, const
                                           : "plan was made for decode, not append");
     return FA_ERR_INVALID;
   }
-  if (!q || !k || !v || !kv_indices || !kv_indptr || !last_page_len || !out) {
+  if ((pl->ragged != 0) != ragged) {
+    set_error(ragged ? "plan was made by fa_plan (paged KV), not fa_plan_ragged"
+                     : "plan was made by fa_plan_ragged (ragged KV), not fa_plan");
+    return FA_ERR_INVALID;
+  }
+  if (!q || !k || !v || (!ragged && (!kv_indices || !kv_indptr || !last_page_len)) || !out) {
     set_error("NULL tensor argument");
     return FA_ERR_INVALID;
   }
@@ -102,6 +107,7 @@ AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const v
   const float scale = sm_scale > 0.f ? sm_scale : 1.0f / sqrtf((float)pl->geom.head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.v_scale = 1.0f;
+  p.kv_offsets = nullptr;
   p.num_qo_heads = pl->geom.num_qo_heads;
   p.num_kv_heads = pl->geom.num_kv_heads;
   p.causal = pl->causal;
@@ -139,10 +145,13 @@ fa_status fa_workspace_size(const fa_geometry* geom, size_t* host_bytes, size_t*
   return FA_OK;
 }
 
-fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
-                  const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
-                  int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
-                  size_t dev_ws_bytes, void* stream) {
+namespace {
+
+// fa_plan and fa_plan_ragged: build on the host, upload into dev_ws.
+fa_status plan_and_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
+                          const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
+                          int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
+                          size_t dev_ws_bytes, void* stream, bool ragged) {
   if (!plan) {
     set_error("plan is NULL");
     return FA_ERR_INVALID;
@@ -173,7 +182,7 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
   fa_status st = resolve_geometry(geom, &g);
   if (st != FA_OK) return st;
   st = build_plan(pl, g, kv_indptr_h, kv_lens_h, batch, qo_indptr_h, causal, host_ws,
-                  host_ws_bytes);
+                  host_ws_bytes, ragged);
   if (st != FA_OK) return st;
   pl->planned = 1;
   pl->dev_ws = dev_ws;
@@ -234,6 +243,47 @@ fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_in
   }
   pl->uploaded = 1;
   return FA_OK;
+}
+
+}  // namespace
+
+fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
+                  const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
+                  int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
+                  size_t dev_ws_bytes, void* stream) {
+  return plan_and_upload(plan, geom, kv_indptr_h, kv_lens_h, batch, qo_indptr_h, causal, host_ws,
+                         host_ws_bytes, dev_ws, dev_ws_bytes, stream, false);
+}
+
+fa_status fa_plan_ragged(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_offsets_h,
+                         int32_t batch, const int32_t* qo_indptr_h, int32_t causal,
+                         void* host_ws, size_t host_ws_bytes, void* dev_ws, size_t dev_ws_bytes,
+                         void* stream) {
+  fa_geometry g;
+  fa_status st = resolve_geometry(geom, &g);
+  if (st != FA_OK) return st;
+  if (batch < 0 || batch > g.max_batch || (batch > 0 && !kv_offsets_h)) {
+    set_error("batch %d outside [0, %d] or kv_offsets NULL", batch, g.max_batch);
+    return FA_ERR_INVALID;
+  }
+  const Layout lay = compute_layout(g);
+  if (!host_ws || host_ws_bytes < lay.host_bytes) {
+    set_error("host workspace needs %zu bytes", lay.host_bytes);
+    return FA_ERR_WORKSPACE;
+  }
+  // request lengths into the host-only tail of the workspace (never part of
+  // an upload that may still be reading the image)
+  int32_t* lens = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(host_ws) + lay.host_lens);
+  for (int b = 0; b < batch; ++b) {
+    const int64_t L = (int64_t)kv_offsets_h[b + 1] - kv_offsets_h[b];
+    if (L < 0) {
+      set_error("kv_offsets decrease at request %d", b);
+      return FA_ERR_INVALID;
+    }
+    lens[b] = (int32_t)L;
+  }
+  return plan_and_upload(plan, geom, kv_offsets_h, lens, batch, qo_indptr_h, causal, host_ws,
+                         host_ws_bytes, dev_ws, dev_ws_bytes, stream, true);
 }
 
 fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats) {
@@ -321,6 +371,71 @@ fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
   return fa_decode_scaled(plan, q, k_pages, v_pages, page_stride, token_stride, head_stride,
                           kv_indices_d, kv_indptr_d, last_page_len_d, sm_scale, 1.0f, 1.0f, out,
                           lse, stream);
+}
+
+namespace {
+
+// Ragged KV: request b's keys are rows kv_offsets[b] .. kv_offsets[b+1]-1 of
+// k / v. The kernels address them as pages of 16 rows that start at row
+// kv_offsets[b] + 16 p, i.e. a page id is a row index and the page stride is
+// the token stride.
+AttnParams ragged_params(const PlanImpl* pl, const void* q, const void* k, const void* v,
+                         int64_t token_stride, int64_t head_stride, const int32_t* kv_offsets_d,
+                         const int32_t* qo_indptr, float sm_scale, void* out, float* lse) {
+  AttnParams p = make_params(pl, q, k, v, token_stride, token_stride, head_stride, nullptr,
+                             nullptr, nullptr, qo_indptr, sm_scale, out, lse);
+  p.kv_offsets = kv_offsets_d ? kv_offsets_d
+                              : reinterpret_cast<const int32_t*>(
+                                    static_cast<const uint8_t*>(pl->dev_ws) + pl->lay.offsets);
+  return p;
+}
+
+}  // namespace
+
+fa_status fa_decode_ragged(const fa_plan_t* plan, const void* q, const void* k, const void* v,
+                           int64_t token_stride, int64_t head_stride, const int32_t* kv_offsets_d,
+                           float sm_scale, float k_scale, float v_scale, void* out, float* lse,
+                           void* stream) {
+  const PlanImpl* pl = plan ? impl(plan) : nullptr;
+  fa_status st = check_run_args(pl, FA_MODE_DECODE, q, k, v, token_stride, token_stride,
+                                head_stride, nullptr, nullptr, nullptr, out, true);
+  if (st != FA_OK) return st;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !isfinite(k_scale) || !isfinite(v_scale)) {
+    set_error("k_scale and v_scale must be finite and positive");
+    return FA_ERR_INVALID;
+  }
+  AttnParams p = ragged_params(pl, q, k, v, token_stride, head_stride, kv_offsets_d, nullptr,
+                               sm_scale, out, lse);
+  p.scale_log2 *= k_scale;
+  p.v_scale = v_scale;
+  const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
+  const hipError_t e = launch_decode(p, pl->geom.dtype, pl->geom.kv_dtype == FA_E4M3, G,
+                                     pl->num_workers, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e, "decode kernel launch");
+}
+
+fa_status fa_append_ragged(const fa_plan_t* plan, const void* q, const int32_t* qo_indptr_d,
+                           const void* k, const void* v, int64_t token_stride,
+                           int64_t head_stride, const int32_t* kv_offsets_d, float sm_scale,
+                           void* out, float* lse, void* stream) {
+  const PlanImpl* pl = plan ? impl(plan) : nullptr;
+  fa_status st = check_run_args(pl, FA_MODE_APPEND, q, k, v, token_stride, token_stride,
+                                head_stride, nullptr, nullptr, nullptr, out, true);
+  if (st != FA_OK) return st;
+  if (!qo_indptr_d) {
+    set_error("qo_indptr is NULL");
+    return FA_ERR_INVALID;
+  }
+  const AttnParams p = ragged_params(pl, q, k, v, token_stride, head_stride, kv_offsets_d,
+                                     qo_indptr_d, sm_scale, out, lse);
+  const int G = pl->geom.num_qo_heads / pl->geom.num_kv_heads;
+  const hipError_t e = launch_append(p, pl->geom.dtype, G, pl->geom.max_tiles,
+                                     static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) {
+    set_error("append kernel not built for this group size");
+    return FA_ERR_UNSUPPORTED;
+  }
+  return e == hipSuccess ? FA_OK : hip_fail(e, "append kernel launch");
 }
 
 fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indptr_d,

@@ -134,14 +134,20 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
   const int q0 = __builtin_amdgcn_readlane(tv, 2), q1 = __builtin_amdgcn_readlane(tv, 3);
   const int key0 = __builtin_amdgcn_readlane(tv, 4);
   const int slot0 = __builtin_amdgcn_readlane(tv, 6), nchunk = __builtin_amdgcn_readlane(tv, 7);
-  const int pv = lane == 0   ? p.kv_indptr[b]
-                 : lane == 1 ? p.kv_indptr[b + 1]
-                 : lane == 2 ? p.last_page_len[b]
+  // paged: page offsets and last_page_len; ragged KV: the request's first and
+  // end rows (a page is 16 rows from row kv_offsets[b] + 16 p)
+  const bool ragged = p.kv_offsets != nullptr;
+  const int32_t* kvp = ragged ? p.kv_offsets : p.kv_indptr;
+  const int pv = lane == 0   ? kvp[b]
+                 : lane == 1 ? kvp[b + 1]
+                 : lane == 2 ? (ragged ? 0 : p.last_page_len[b])
                  : lane == 3 ? p.qo_indptr[b]
                              : p.qo_indptr[b + 1];
   const int pbeg = __builtin_amdgcn_readlane(pv, 0);
-  const int npages_req = __builtin_amdgcn_readlane(pv, 1) - pbeg;
-  const int kv_len = npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(pv, 2) : 0;
+  const int span = __builtin_amdgcn_readlane(pv, 1) - pbeg;
+  const int kv_len =
+      ragged ? span : (span > 0 ? (span - 1) * 16 + __builtin_amdgcn_readlane(pv, 2) : 0);
+  const int npages_req = ragged ? (span + 15) >> 4 : span;
   const int qo_beg = __builtin_amdgcn_readlane(pv, 3);
   const int qo_len = __builtin_amdgcn_readlane(pv, 4) - qo_beg;
   const int key1 = min(__builtin_amdgcn_readlane(tv, 5), kv_len);
@@ -190,8 +196,8 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
   // last page: a block past the end fetches nothing, see nbytes below), and
   // every lane takes them as wave-uniform values (scalar buffer resources)
   auto load_pid_vec = [&](int blk) -> int {
-    const int pg = min(first_page + blk * 4 + (lane & 3), npages_req - 1);
-    return p.kv_indices[pbeg + max(pg, 0)];
+    const int pg = max(min(first_page + blk * 4 + (lane & 3), npages_req - 1), 0);
+    return ragged ? pbeg + 16 * pg : p.kv_indices[pbeg + pg];
   };
   auto take_pids = [&](int v) {
 #pragma unroll

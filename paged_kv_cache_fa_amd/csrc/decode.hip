@@ -357,10 +357,19 @@ __device__ __forceinline__ void open_piece(const AttnParams& p, int tv, int lane
   c.id.npieces = __builtin_amdgcn_readlane(tv, 7);
   c.first_page = c.key0 >> 4;
   c.npg_plan = c.key1_plan > c.key0 ? ((c.key1_plan + 15) >> 4) - c.first_page : 0;
-  const int32_t* ids_base = p.kv_indices + c.pbeg + c.first_page;
-  c.ids0 = lane < c.npg_plan ? ids_base[lane] : 0;
-  c.ids1 = lane + 64 < c.npg_plan ? ids_base[lane + 64] : 0;
-  c.chk = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
+  if (p.kv_offsets) {
+    // ragged KV: page j of the piece starts at row pbeg + 16 (first_page + j)
+    // (the tile carries kv_offsets[b]); the check reads the row offsets
+    const int row0 = c.pbeg + 16 * c.first_page;
+    c.ids0 = lane < c.npg_plan ? row0 + 16 * lane : 0;
+    c.ids1 = lane + 64 < c.npg_plan ? row0 + 16 * (lane + 64) : 0;
+    c.chk = lane == 0 ? p.kv_offsets[b] : lane == 1 ? p.kv_offsets[b + 1] : 0;
+  } else {
+    const int32_t* ids_base = p.kv_indices + c.pbeg + c.first_page;
+    c.ids0 = lane < c.npg_plan ? ids_base[lane] : 0;
+    c.ids1 = lane + 64 < c.npg_plan ? ids_base[lane + 64] : 0;
+    c.chk = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
+  }
 }
 
 // Wave-uniform bounds of a piece, taken from its context once its loads have
@@ -413,9 +422,9 @@ __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx&
   // The device page table must agree with the plan (offset, and the key
   // range inside the request's valid tokens); a piece that disagrees reads
   // nothing.
-  const int npages_req = __builtin_amdgcn_readlane(c.chk, 1) - __builtin_amdgcn_readlane(c.chk, 0);
-  const int kv_len =
-      npages_req > 0 ? (npages_req - 1) * 16 + __builtin_amdgcn_readlane(c.chk, 2) : 0;
+  const int span = __builtin_amdgcn_readlane(c.chk, 1) - __builtin_amdgcn_readlane(c.chk, 0);
+  const int kv_len = p.kv_offsets ? span  // ragged: rows
+                                  : (span > 0 ? (span - 1) * 16 + __builtin_amdgcn_readlane(c.chk, 2) : 0);
   const int key0 = __builtin_amdgcn_readfirstlane(c.key0);
   const int key1_plan = __builtin_amdgcn_readfirstlane(c.key1_plan);
   const bool agrees = __builtin_amdgcn_readlane(c.chk, 0) == __builtin_amdgcn_readfirstlane(c.pbeg) &&

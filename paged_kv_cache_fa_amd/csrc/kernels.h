@@ -21,6 +21,8 @@ struct AttnParams {
   const int32_t* kv_indptr;
   const int32_t* last_page_len;
   const int32_t* qo_indptr;   // append only
+  const int32_t* kv_offsets;  // ragged KV: request b's keys are rows kv_offsets[b] ..
+                              // kv_offsets[b+1]-1, a page id is a row index; null: paged
   uint16_t* out;              // [rows, Hq, 128]
   float* lse;                 // [rows, Hq] natural log, may be null
   float* part_o;              // [slots, G, 128] fp32 partial outputs (normalised)

@@ -134,7 +134,8 @@ Layout compute_layout(const fa_geometry& g) {
   L.header = 0;
   L.merge = kHeaderInts * 4;
   L.worker_ptr = L.merge + (size_t)g.max_merge * kMergeInts * 4;
-  L.tiles = align_up(L.worker_ptr + (size_t)(std::max<int32_t>(L.workers, kXcdBins) + 1) * 4, 64);
+  L.offsets = L.worker_ptr + (size_t)(std::max<int32_t>(L.workers, kXcdBins) + 1) * 4;
+  L.tiles = align_up(L.offsets + ((size_t)g.max_batch + 1) * 4, 64);
   L.upload_end = L.tiles + (size_t)g.max_tiles * kTileInts * 4;
   L.dev_counters = align_up(L.upload_end, 256);
   L.dev_part_lse = align_up(L.dev_counters + (size_t)g.max_partials * 4, 256);
@@ -151,7 +152,8 @@ Layout compute_layout(const fa_geometry& g) {
   L.host_seg = align_up(L.host_bin + nlist * 4, 8);
   L.host_units = align_up(L.host_seg + (size_t)bins * 4, 8);
   // per (request, kv head): 2 int32 (decode) or int64 cost + 3 int32 (append)
-  L.host_bytes = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 24;
+  L.host_lens = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 24;
+  L.host_bytes = L.host_lens + ((size_t)g.max_batch + 1) * 4;
   return L;
 }
 
@@ -416,7 +418,7 @@ fa_status plan_append(const fa_geometry& g, const Layout& lay, uint8_t* ws, cons
 
 fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr,
                      const int32_t* kv_lens, int32_t batch, const int32_t* qo_indptr,
-                     int32_t causal, void* host_ws, size_t host_ws_bytes) {
+                     int32_t causal, void* host_ws, size_t host_ws_bytes, bool ragged) {
   const bool app = g.mode == FA_MODE_APPEND;
   const int ps = g.page_size;
   if (batch < 0 || batch > g.max_batch) {
@@ -442,7 +444,7 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
       set_error("kv_indptr decreases at request %d", b);
       return FA_ERR_INVALID;
     }
-    if (n == 0 ? L != 0 : !((n - 1) * ps < L && L <= n * ps)) {
+    if (ragged ? n != L : (n == 0 ? L != 0 : !((n - 1) * ps < L && L <= n * ps))) {
       set_error("request %d: kv_len %lld inconsistent with %lld pages", b, (long long)L,
                 (long long)n);
       return FA_ERR_INVALID;
@@ -490,6 +492,11 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
   header[4] = app ? causal : 0;
   header[5] = (int32_t)P;
   header[6] = lay.workers;
+  header[7] = ragged ? 1 : 0;
+  if (ragged) {
+    int32_t* offs = reinterpret_cast<int32_t*>(ws + lay.offsets);
+    for (int b = 0; b <= batch; ++b) offs[b] = kv_indptr ? kv_indptr[b] : 0;
+  }
 
   p->num_tiles = (int32_t)ntiles;
   p->num_merge = (int32_t)nmerge;
@@ -499,6 +506,7 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
   p->num_rows = header[3];
   p->causal = header[4];
   p->num_workers = lay.workers;
+  p->ragged = ragged ? 1 : 0;
   p->geom = g;
   p->lay = lay;
   p->host_ws = host_ws;

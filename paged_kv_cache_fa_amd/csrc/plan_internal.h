@@ -12,7 +12,7 @@ namespace pkfa {
 constexpr uint32_t kPlanMagic = 0x70666131u;  // "pfa1"
 constexpr int kTileInts = 8;                   // {b, h, row0, row1, key0, key1, slot0, nchunk}
 constexpr int kMergeInts = 4;                  // {row0, kv_head, base slot, n_chunks}
-constexpr int kHeaderInts = 16;  // {num_tiles, num_merge, batch, num_rows, causal, chunk_pages, num_workers, ...}
+constexpr int kHeaderInts = 16;  // {num_tiles, num_merge, batch, num_rows, causal, chunk_pages, num_workers, ragged, ...}
 constexpr int kSupportedHeadDim = 128;
 constexpr int kSupportedPageSize = 16;
 constexpr int kMaxPiecePages = 128;  // decode pieces: the kernel holds 128 page ids per wave
@@ -25,16 +25,18 @@ constexpr int kPieceCostPagesE4M3 = 8;
 // Byte offsets of the regions inside the host and device workspaces.
 // Upload image (same offsets in host and device workspace):
 //   header | merge [max_merge][4] | tile offsets (decode: [workers+1] per
-//   worker wave; append: [9] per XCD bin) | tiles [max_tiles][8]
+//   worker wave; append: [9] per XCD bin) | ragged KV row offsets
+//   [max_batch+1] | tiles [max_tiles][8]
 // Device only: arrival counters [max_partials] (zero between calls), partial
 // lse [max_partials][G] (log2 units), partial out [max_partials][G][head_dim].
 // Host only: scratch for sorting and dealing tiles (decode: pieces, dealing
 // order, bin heap, bin of each dealt piece, bin offsets; append: per-group
-// cost / order / bin / sequence) and per-request / per-unit counts.
+// cost / order / bin / sequence), per-request / per-unit counts, and the
+// request lengths of a ragged plan.
 struct Layout {
-  size_t header, merge, worker_ptr, tiles, upload_end;
+  size_t header, merge, worker_ptr, offsets, tiles, upload_end;
   size_t dev_counters, dev_part_lse, dev_part_o, dev_bytes;
-  size_t host_unsorted, host_order, host_cost, host_bin, host_seg, host_units, host_bytes;
+  size_t host_unsorted, host_order, host_cost, host_bin, host_seg, host_units, host_lens, host_bytes;
   int32_t workers;
 };
 
@@ -43,6 +45,7 @@ struct PlanImpl {
   int32_t planned;    // 1 after a successful fa_plan
   int32_t uploaded;   // 1 if the plan was copied into a device workspace
   int32_t num_tiles, num_merge, num_slots, chunk_pages, batch, num_rows, causal, num_workers;
+  int32_t ragged;     // 1: planned by fa_plan_ragged (contiguous KV rows, no page table)
   fa_geometry geom;   // resolved
   Layout lay;
   void* host_ws;
@@ -66,9 +69,11 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out);
 Layout compute_layout(const fa_geometry& g);
 
 // Build the plan into the host workspace (upload image + scratch). Host only.
+// With ragged, kv_indptr holds the requests' first KV rows (batch+1 offsets,
+// copied into the image) instead of page offsets.
 fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr,
                      const int32_t* kv_lens, int32_t batch, const int32_t* qo_indptr,
-                     int32_t causal, void* host_ws, size_t host_ws_bytes);
+                     int32_t causal, void* host_ws, size_t host_ws_bytes, bool ragged);
 
 void set_error(const char* fmt, ...);
 

@@ -417,9 +417,50 @@ def check_brute_decode_fp8(seed=42):
     _close(lse, np.array(bl))
 
 
+# ---------------------------------------------------------------- ragged KV
+def check_brute_ragged(seed=43):
+    """Ragged decode and causal / non-causal append against the pure-Python
+    brute force over explicit row slices (q heads 4, kv heads 2)."""
+    from oracle.brute import brute_attention_row
+    from workloads import make_ragged
+    lens, qo = [0, 1, 3, 5, 9], [0, 1, 2, 5, 3]
+    Hq, Hkv, D = 4, 2, 6
+    for causal in (True, False):
+        rw = make_ragged(lens, Hq, Hkv, "bf16", seed, qo_lens=qo, causal=causal, head_dim=D)
+        sc = 1 / math.sqrt(D)
+        K, V = OA.upcast(rw.k, "bf16").tolist(), OA.upcast(rw.v, "bf16").tolist()
+        Q = OA.upcast(rw.q, "bf16").tolist()
+        out, lse = OA.append_ragged(rw.q, rw.qo_indptr, rw.k, rw.v, "bf16", rw.kv_offsets,
+                                    causal=causal)
+        r = 0
+        for b, L in enumerate(lens):
+            o0 = int(rw.kv_offsets[b])
+            for i in range(qo[b]):
+                vis = L - qo[b] + i + 1 if causal else L
+                for h in range(Hq):
+                    keys = [K[o0 + t][h // 2] for t in range(vis)]
+                    vals = [V[o0 + t][h // 2] for t in range(vis)]
+                    bo, bl = brute_attention_row(Q[r][h], keys, vals, sc)
+                    _close(out[r, h], np.array(bo))
+                    _close([lse[r, h]], [bl])
+                r += 1
+    dw = make_ragged(lens, Hq, Hkv, "bf16", seed + 1, head_dim=D)
+    out, lse = OA.decode_ragged(dw.q, dw.k, dw.v, "bf16", dw.kv_offsets)
+    K, V = OA.upcast(dw.k, "bf16").tolist(), OA.upcast(dw.v, "bf16").tolist()
+    Q = OA.upcast(dw.q, "bf16").tolist()
+    for b, L in enumerate(lens):
+        o0 = int(dw.kv_offsets[b])
+        for h in range(Hq):
+            bo, bl = brute_attention_row(Q[b][h], [K[o0 + t][h // 2] for t in range(L)],
+                                         [V[o0 + t][h // 2] for t in range(L)], 1 / math.sqrt(D))
+            _close(out[b, h], np.array(bo))
+            _close([lse[b, h]], [bl])
+
+
 ALL_CHECKS = [
     check_single_token, check_identical_keys, check_q_zero_and_v_ones, check_scale_default,
     check_gqa_map, check_identity_gather, check_count, check_brute_decode, check_brute_append,
     check_causal_prefill, check_permutation_invariance, check_merge_split, check_merge_algebra,
     check_cascade, check_e4m3_definition, check_fp8_scale_placement, check_brute_decode_fp8,
+    check_brute_ragged,
 ]

@@ -111,6 +111,17 @@ def _gather_swapped_scales(pool, dtype, kv_indptr, kv_indices, last_page_len, pa
                    k_scale)
 
 
+_ragged_kv = OA.ragged_request_kv
+
+
+def _ragged_shifted(k_bits, v_bits, dtype, kv_offsets, b, k_scale=1.0, v_scale=1.0):
+    """Mistake: request b's rows taken one row late."""
+    off = np.asarray(kv_offsets).copy()
+    off[b] += 1
+    off[b + 1] += 1
+    return _ragged_kv(k_bits, v_bits, dtype, off, b, k_scale, v_scale)
+
+
 def _run_all():
     for chk in P.ALL_CHECKS:
         chk()
@@ -129,6 +140,7 @@ MUTATIONS = [
     ("e4m3_no_subnormals", OA, "e4m3_value", _e4m3_no_subnormals),
     ("e4m3_fnuz_nan", OA, "e4m3_value", _e4m3_fnuz_nan),
     ("fp8_scales_swapped", OA, "gather_request_kv", _gather_swapped_scales),
+    ("ragged_rows_shifted", OA, "ragged_request_kv", _ragged_shifted),
 ]
 
 

@@ -11,6 +11,8 @@ from .gen import (  # noqa: F401
     config_lengths,
     make_workload,
     make_cascade,
+    make_ragged,
+    RaggedWorkload,
     csr_from_page_lists,
     to_storage_bits,
     to_e4m3_codes,

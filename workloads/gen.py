@@ -305,6 +305,81 @@ def make_cascade(
     )
 
 
+@dataclass
+class RaggedWorkload:
+    """A ragged KV cache: request b's keys are rows kv_offsets[b] ..
+    kv_offsets[b+1]-1 of k / v ``[rows, num_kv_heads, head_dim]`` (stored bits;
+    E4M3 codes with ``kv_dtype="e4m3"``). Test mode appends ``pad_rows`` NaN
+    rows after the last request."""
+    dtype: str
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    kv_lens: np.ndarray            # int32 [B]
+    kv_offsets: np.ndarray         # int32 [B+1]
+    qo_indptr: Optional[np.ndarray]
+    causal: bool
+    k: np.ndarray                  # [rows + pad_rows, Hkv, D]
+    v: np.ndarray
+    q: np.ndarray                  # uint16 [rows_q, Hq, D]
+    seed: int
+    kv_dtype: Optional[str] = None
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_lens.shape[0])
+
+    @property
+    def rows(self) -> int:
+        return int(self.q.shape[0])
+
+
+def make_ragged(kv_lens: Sequence[int], num_qo_heads: int, num_kv_heads: int, dtype: str,
+                seed: int, qo_lens: Optional[Sequence[int]] = None, causal: bool = True,
+                head_dim: int = 128, mode: str = "bench", pad_rows: int = 0,
+                kv_dtype: Optional[str] = None) -> RaggedWorkload:
+    """Draw a ragged KV cache for the given lengths: Q, then K rows, then V
+    rows, N(0,1) as float32 rounded to the storage type (E4M3 with the FP8
+    scales when ``kv_dtype="e4m3"``). ``qo_lens=None`` means decode."""
+    rng = np.random.default_rng(seed)
+    kv_lens = np.asarray(kv_lens, dtype=np.int32)
+    B = kv_lens.shape[0]
+    kv_offsets = np.zeros(B + 1, dtype=np.int32)
+    kv_offsets[1:] = np.cumsum(kv_lens)
+    total = int(kv_offsets[-1])
+    if qo_lens is None:
+        qo_indptr, rows = None, B
+    else:
+        qo_lens = np.asarray(qo_lens, dtype=np.int32)
+        if qo_lens.shape[0] != B or np.any(qo_lens > kv_lens) or np.any(qo_lens < 0):
+            raise ValueError("qo_lens must be per-request and not exceed kv_lens")
+        qo_indptr = np.zeros(B + 1, dtype=np.int32)
+        qo_indptr[1:] = np.cumsum(qo_lens)
+        rows = int(qo_indptr[-1])
+    q = to_storage_bits(rng.standard_normal((rows, num_qo_heads, head_dim), dtype=np.float32),
+                        dtype)
+    kvt = dtype if kv_dtype is None else kv_dtype
+    fp8 = kvt == "e4m3"
+    shape = (total + pad_rows, num_kv_heads, head_dim)
+    kv = []
+    for which in range(2):
+        x = rng.standard_normal((total, num_kv_heads, head_dim), dtype=np.float32)
+        arr = np.empty(shape, dtype=np.uint8 if fp8 else np.uint16)
+        if fp8:
+            arr[:total] = to_e4m3_codes(x, FP8_K_SCALE if which == 0 else FP8_V_SCALE)
+        else:
+            arr[:total] = to_storage_bits(x, kvt)
+        arr[total:] = _NAN_BITS[kvt] if mode == "test" else 0
+        kv.append(arr)
+    return RaggedWorkload(
+        dtype=dtype, num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        kv_lens=kv_lens, kv_offsets=kv_offsets, qo_indptr=qo_indptr, causal=causal, k=kv[0],
+        v=kv[1], q=q, seed=seed, kv_dtype=kv_dtype if fp8 else None,
+        k_scale=FP8_K_SCALE if fp8 else 1.0, v_scale=FP8_V_SCALE if fp8 else 1.0)
+
+
 def config_lengths(k: int, rng: np.random.Generator) -> dict:
     """Draw the lengths of config k (the first draws of its generator)."""
     if k == 1:
