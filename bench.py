@@ -16,6 +16,9 @@ Reported alongside in the same JSON line:
     MFMA utilisation (584.2 GFLOP of unmasked work per step);
   * ``fp8``: the batch-64 decode with an E4M3 page pool (per-tensor scales,
     bf16 q / out), as HBM GB/s with one byte per K/V element;
+  * ``ragged``: the batch-64 decode over a ragged (contiguous-row) KV cache;
+  * ``single``: the single-request decode (32 heads, kv_len 2048, fp16) over a
+    contiguous K / V;
   * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
     from HIP events on its stream), with HBM traffic from rocprofv3 counters
     when the stored counter summary matches the current kernel source;
@@ -149,6 +152,41 @@ class DecodeBench(Timed):
             ev[1].record()
 
 
+class RaggedDecodeBench(Timed):
+    """Decode over a ragged KV cache (rows of K / V in request order)."""
+
+    def __init__(self, rw, device="cuda", min_rotation_bytes=1 << 30, **knobs):
+        import torch
+        import paged_kv_cache_fa_amd as fa
+        self.fa, self.rw = fa, rw
+        dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[rw.dtype]
+        k = torch.from_numpy(rw.k.view(np.int16)).to(device).view(dt)
+        v = torch.from_numpy(rw.v.view(np.int16)).to(device).view(dt)
+        copies = max(1, math.ceil(min_rotation_bytes / (2 * k.numel() * 2)))
+        self.kv = [(k, v)] + [(k.clone(), v.clone()) for _ in range(copies - 1)]
+        self.q = torch.from_numpy(rw.q.view(np.int16)).to(device).view(dt)
+        self.offs = _i32(rw.kv_offsets, device)
+        self.offs_h = np.ascontiguousarray(rw.kv_offsets, dtype=np.int32)
+        geom = fa.geometry("decode", rw.dtype, rw.batch, rw.num_qo_heads, rw.num_kv_heads, **knobs)
+        self.plan = fa.Plan(geom, device=device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(rw.rows, rw.num_qo_heads, dtype=torch.float32, device=device)
+
+    def step(self, i: int, ev=None):
+        k, v = self.kv[i % len(self.kv)]
+        self.plan.plan_ragged(self.offs_h)
+        if ev is not None:
+            ev[0].record()
+        self.fa.decode_ragged(self.plan, self.q, k, v, k.stride(0), k.stride(1), self.offs,
+                              out=self.out, lse=self.lse)
+        if ev is not None:
+            ev[1].record()
+
+
+def ragged_bytes(rw) -> int:
+    return kv_bytes(rw.kv_lens, rw.num_kv_heads) + io_bytes(rw.rows, rw.num_qo_heads)
+
+
 class AppendBench(Timed):
     def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, **knobs):
         import torch
@@ -278,7 +316,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="decode workload for the headline (1-3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip batch128/cascade/append")
-    ap.add_argument("--parts", default="batch128,cascade,append,fp8",
+    ap.add_argument("--parts", default="batch128,cascade,append,fp8,ragged,single",
                     help="comma list of the secondary workloads to run after the headline")
     ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
     ap.add_argument("--copy-probe", action="store_true",
@@ -389,6 +427,26 @@ def main():
                        "ms_per_step": round(s8, 5), "kernel_ms": round(k8, 5),
                        "algorithmic_bytes": n8}
         del b8, w8
+        torch.cuda.empty_cache()
+    from workloads import make_ragged
+    for part, k in (("ragged", 2), ("single", 1)):
+        if part not in parts:
+            continue
+        wk = make_config(k)
+        rw = make_ragged(wk.kv_lens, wk.num_qo_heads, wk.num_kv_heads, wk.dtype, seed=k)
+        br = RaggedDecodeBench(rw, **knobs)
+        sr, kr = br.run(args.steps, args.warmup)
+        nr = ragged_bytes(rw)
+        line[part] = {"workload": f"config{k} lengths as a ragged (contiguous) KV cache: "
+                                  f"{CONFIG_NAMES[k]}",
+                      "GB/s": round(nr / (sr * 1e-3) / 1e9, 2),
+                      "pct_of_hbm_peak": round(100 * nr / (sr * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                      "kernel_GB/s": round(nr / (kr * 1e-3) / 1e9, 2),
+                      "tokens_per_s": round(rw.batch / (sr * 1e-3), 1),
+                      "ms_per_step": round(sr, 5), "kernel_ms": round(kr, 5),
+                      "algorithmic_bytes": nr, "kv_copies": len(br.kv)}
+        del br, rw, wk
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)
