@@ -220,7 +220,8 @@ class CascadeBench(Timed):
     (non-causal append over the shared prefix, MFMA) and the combine kernel;
     the kernel time is the whole call."""
 
-    def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30):
+    def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, prefix_knobs=None,
+                 suffix_knobs=None):
         import torch
         import paged_kv_cache_fa_amd as fa
         self.fa, self.wl = fa, wl
@@ -233,8 +234,10 @@ class CascadeBench(Timed):
         self.p_indices = _i32(wl.prefix_indices, device)
         self.p_last = _i32(wl.prefix_last_page_len, device)
         self.qo = _i32([0, B], device)
-        gp = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads, max_qo_tokens=B)
-        gs = fa.geometry("decode", wl.dtype, B, wl.num_qo_heads, wl.num_kv_heads)
+        gp = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads, max_qo_tokens=B,
+                         **(prefix_knobs or {}))
+        gs = fa.geometry("decode", wl.dtype, B, wl.num_qo_heads, wl.num_kv_heads,
+                         **(suffix_knobs or {}))
         self.pplan = fa.Plan(gp, device=device)
         self.splan = fa.Plan(gs, device=device)
         mk = lambda: (torch.empty_like(self.q),

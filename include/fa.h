@@ -289,15 +289,20 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
  *               does not split its keys; split prefix chunks stay as fp32
  *               partial states in the prefix plan's workspace.)
  *  out / lse    device [batch, num_qo_heads, head_dim] / fp32 (lse may be NULL).
- * The suffix decode runs on `suffix_stream` and the prefix pass on
+ * With both extra streams NULL (or equal to `stream`) and num_qo_heads /
+ * num_kv_heads <= 4, one kernel on `stream` runs both passes side by side in
+ * the same compute units (decode workgroups next to append workgroups: the
+ * matrix work of the prefix overlaps the suffix streaming). Otherwise the
+ * suffix decode runs on `suffix_stream` and the prefix pass on
  * `prefix_stream` (each NULL or equal to `stream` = run on `stream`); streams
  * other than `stream` are forked from it and joined back with events of the
  * suffix plan (capturable). Then one combine kernel on `stream` merges, per
  * (request, head), the prefix chunks and the suffix state by log-sum-exp.
- * (Measured on MI355X at batch 256 / 16k prefix: running the two passes
- * concurrently, on shared or on disjoint compute units, was slower than in
- * order on one stream.) Other arguments as fa_decode. Errors: FA_ERR_INVALID,
- * FA_ERR_NOT_PLANNED, FA_ERR_HIP. */
+ * (Measured on MI355X at batch 256 / 16k prefix: the one-kernel form is about
+ * 7% faster than the two passes in order; the passes on separate streams,
+ * sharing or splitting the compute units, were slower than in order.) Other
+ * arguments as fa_decode. Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED,
+ * FA_ERR_HIP. */
 fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan, const void* q,
                      const void* k_pages, const void* v_pages, int64_t page_stride,
                      int64_t token_stride, int64_t head_stride, const int32_t* prefix_qo_indptr_d,

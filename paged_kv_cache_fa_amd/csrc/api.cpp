@@ -17,6 +17,8 @@
 
 namespace pkfa {
 static_assert(kAppendBins == kXcdBins, "planner bins and kernel bins differ");
+// fa_cascade on one stream: both passes in one kernel (true) or two launches
+constexpr bool kCascadeOneLaunch = true;
 }  // namespace pkfa
 
 namespace pkfa {
@@ -527,14 +529,20 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
   const AttnParams ps = make_params(sp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
                                     kv_indices_d, kv_indptr_d, last_page_len_d, nullptr, sm_scale,
                                     suffix_out, suffix_lse);
-  e = launch_decode(ps, gs.dtype, false, G, sp->num_workers, s_suf);
-  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   AttnParams pa = make_params(pp, q, k_pages, v_pages, page_stride, token_stride, head_stride,
                               prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
                               prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
   pa.defer_merge = 1;  // the prefix chunks are merged together with the suffix below
-  e = launch_append(pa, gp.dtype, G, gp.max_tiles, s_pre);
-  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  if (!fork_pre && !fork_suf && kCascadeOneLaunch && G <= 4) {
+    // both passes in one launch, sharing the CUs
+    e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, s);
+    if (e != hipSuccess) return hip_fail(e, "cascade kernel launch");
+  } else {
+    e = launch_decode(ps, gs.dtype, false, G, sp->num_workers, s_suf);
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    e = launch_append(pa, gp.dtype, G, gp.max_tiles, s_pre);
+    if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  }
   if (fork_pre) {
     e = hipEventRecord(static_cast<hipEvent_t>(sp->join_event), s_pre);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(sp->join_event), 0);

@@ -1,0 +1,439 @@
+// Paged-KV append / prefill kernel for gfx950 (MFMA).
+//
+// What it computes ([Guide] "FlashInfer: GPU Kernels for LLM Inference (2026
+// Guide)", section "Features (from the repository README)": prefill and
+// append over paged and ragged caches; [DeepDive] "FlashInfer: The Attention
+// Kernel Library That Proves the Bottleneck ...", section "Snippet One"):
+// request b has qo_len new query rows whose K/V are already in its pages;
+// with the causal mask, row i (position kv_len - qo_len + i) attends to keys
+// 0 .. kv_len - qo_len + i. Without it, every row sees all kv_len keys (the
+// shared-prefix pass of cascade attention, [Guide] section "Cascade attention
+// for shared prefixes").
+//
+// MI355X design (the work is a dense contraction, so it runs on MFMA):
+//  * tiles come in 8 bins, one per XCD: the planner deals each (request, kv
+//    head) group to one bin, so the q tiles that read the same keys run side
+//    by side on one XCD and share its L2;
+//  * one 256-thread workgroup (4 waves) per tile {request, kv head, up to
+//    128/G query positions, key chunk}. The tile's 128 query columns are the
+//    G heads of the kv head's group x 128/G positions (GQA packing): every
+//    K/V block staged in LDS feeds all of them. Wave w owns columns
+//    32w .. 32w+31;
+//  * blocks of 64 keys: each thread fetches 16 bytes of 4 token rows of K and
+//    of V (one row from each of the block's 4 pages, so every load's page is
+//    uniform across the workgroup) through a per-page buffer resource that
+//    ends at the last valid token: keys past the end read as zero. The
+//    registers are written to a double-buffered LDS after the current block's
+//    math, one barrier per block;
+//  * inside a block, key k sits in LDS slot 4 (k mod 16) + k / 16, so one
+//    thread's 4 rows form 4 consecutive slots: V is stored transposed
+//    (dim-major, 4 slots per 8-byte store) without any exchange. The
+//    contraction over keys is order-free, and the mask maps slots back to
+//    keys. Each lane's PV operand is one 16-byte LDS read, and V^T rows are
+//    XOR-swizzled so that both the transposing stores and the operand reads
+//    hit distinct banks;
+//  * scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_{bf16,f16}: a lane owns one query column and 16 of
+//    every 32 slots, so the online-softmax max / sum need one exchange
+//    (lanes l and l^32) and the output rescale is lane-local. The reference
+//    max only moves (with a rescale) when a wave-wide vote sees a score more
+//    than 2^8 above it, so most blocks skip the rescale;
+//  * O^T += V^T P^T reuses the score registers (rounded to the input type) as
+//    the B operand;
+//  * blocks that need no mask (all keys valid and below the first row's
+//    causal limit) skip the masking step;
+//  * a chunked (split) tile writes fp32 partial states; the last workgroup of
+//    the split (agent-scope counter, reset by that workgroup) merges them by
+//    log-sum-exp, unless the caller defers the merge to a later kernel (the
+//    cascade combine, which merges prefix chunks and suffix in one pass).
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkfa {
+namespace app {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kBlockKeys = 64;
+constexpr int kKStride = 136;  // 16-bit elements per K slot row in LDS (128 dims + 8 pad)
+constexpr int kKElems = kBlockKeys * kKStride;
+constexpr int kVElems = 128 * kBlockKeys;  // V^T: 128 dim rows x 64 slots (swizzled)
+constexpr int kBufElems = kKElems + kVElems;
+constexpr int kCoherent = 16;          // cache policy sc1: device-coherent access
+constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
+
+template <int DT>
+struct Mfma;
+template <>
+struct Mfma<FA_BF16> {
+  __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<FA_F16> {
+  __device__ __forceinline__ static f32x16 run(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p.part_o, 0, 0x7fffffff, 0x00020000);
+}
+
+// V^T layout. Row d holds the 64 slots of dim d as 8 units of 16 bytes. The
+// MFMA A operand of a lane of half h for slot tile kt, group kh is the 8
+// slots {32 kt + 16 kh + 4 h + e, 32 kt + 16 kh + 8 + 4 h + e : e < 4}, i.e.
+// the 4-slot groups tr and tr + 2 (tr = 8 kt + 4 kh + h): they share the
+// 16-byte unit 4 kt + 2 kh + h (first and second half). Units are XOR-swizzled
+// with vswz(d), which depends on d mod 32 only (the 4 dim tiles of a lane
+// differ by immediate offsets); the 8 rows read together (consecutive d) get
+// distinct units, and so do the 16 transposing 8-byte stores issued together.
+__device__ __forceinline__ int vswz(int d) { return (((d >> 3) & 3) << 1) ^ (d & 7); }
+// Byte offset inside row d of 4-slot group tr (slots 4 tr .. 4 tr + 3).
+__device__ __forceinline__ int vgroup_off(int tr, int d) {
+  return 16 * ((2 * (tr >> 2) + (tr & 1)) ^ vswz(d)) + 8 * ((tr >> 1) & 1);
+}
+
+// Key (0..63 within the block) held in register r of score tile kt by a lane
+// of half h: slot 32 kt + 8 (r / 4) + 4 h + r % 4, key = slot / 4 + 16 (slot % 4).
+__device__ __forceinline__ constexpr int reg_key(int kt, int r, int h) {
+  return 8 * kt + 2 * (r >> 2) + h + 16 * (r & 3);
+}
+
+// Max / sum of a value over the lane pair (l, l ^ 32), in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int DT, int G>
+__device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, uint16_t* smem,
+                                            int& s_flag) {
+  constexpr int PT = 128 / G;  // query positions per tile
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int jq = lane & 31, h = lane >> 5;
+
+  // tile fields, made wave-uniform
+  const int32_t* t = p.tiles + tile_id * 8;
+  const int tv = t[lane & 7];
+  const int b = __builtin_amdgcn_readlane(tv, 0), hk = __builtin_amdgcn_readlane(tv, 1);
+  const int q0 = __builtin_amdgcn_readlane(tv, 2), q1 = __builtin_amdgcn_readlane(tv, 3);
+  const int key0 = __builtin_amdgcn_readlane(tv, 4);
+  const int slot0 = __builtin_amdgcn_readlane(tv, 6), nchunk = __builtin_amdgcn_readlane(tv, 7);
+  // paged: page offsets and last_page_len; ragged KV: the request's first and
+  // end rows (a page is 16 rows from row kv_offsets[b] + 16 p)
+  const bool ragged = p.kv_offsets != nullptr;
+  const int32_t* kvp = ragged ? p.kv_offsets : p.kv_indptr;
+  const int pv = lane == 0   ? kvp[b]
+                 : lane == 1 ? kvp[b + 1]
+                 : lane == 2 ? (ragged ? 0 : p.last_page_len[b])
+                 : lane == 3 ? p.qo_indptr[b]
+                             : p.qo_indptr[b + 1];
+  const int pbeg = __builtin_amdgcn_readlane(pv, 0);
+  const int span = __builtin_amdgcn_readlane(pv, 1) - pbeg;
+  const int kv_len =
+      ragged ? span : (span > 0 ? (span - 1) * 16 + __builtin_amdgcn_readlane(pv, 2) : 0);
+  const int npages_req = ragged ? (span + 15) >> 4 : span;
+  const int qo_beg = __builtin_amdgcn_readlane(pv, 3);
+  const int qo_len = __builtin_amdgcn_readlane(pv, 4) - qo_beg;
+  const int key1 = min(__builtin_amdgcn_readlane(tv, 5), kv_len);
+  const int rows = q1 - q0;
+  const int Hq = p.num_qo_heads;
+
+  // this lane's query column: head hk*G + g, row q0 + pos
+  const int col = 32 * wave + jq;
+  const int g = col / PT, pos = col % PT;
+  const int head = hk * G + g;
+  const bool qvalid = pos < rows;
+  const int qpos_min = p.causal ? kv_len - qo_len + (q0 - qo_beg) : 0x7fffffff;
+  const int qpos = p.causal ? qpos_min + pos : 0x7fffffff;
+
+  // Q^T operand: 8 blocks of 16 dims, this lane supplies dims 16 kb + 8 h .. +8
+  u32x4 qf[8];
+  {
+    const uint16_t* qp = p.q + ((int64_t)(q0 + pos) * Hq + head) * 128 + 8 * h;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+      qf[kb] = qvalid ? *reinterpret_cast<const u32x4*>(qp + 16 * kb) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = kNegInf, l = 0.f;  // per column: reference max (log2 units), this lane's sum
+  const float scale = p.scale_log2;
+
+  const int nblocks = key1 > key0 ? (key1 - key0 + kBlockKeys - 1) / kBlockKeys : 0;
+  const int first_page = key0 >> 4;  // chunks start on a page boundary
+
+  // --- K/V staging: thread = (token row tr of each of the 4 pages, dims 8 dg..) --
+  // tid bits [1:0] and [5:4] give dg, bits [3:2] and [7:6] give tr: a wave
+  // reads 4 whole token rows per load, and 16 lanes that store together cover
+  // 4 dg x 4 tr (conflict-free V^T stores under vswz).
+  const int dg = (tid & 3) | ((tid >> 2) & 12), tr = ((tid >> 2) & 3) | ((tid >> 4) & 12);
+  const uint32_t row_bytes = (uint32_t)p.token_stride * 2u;
+  const uint32_t ld_off = (uint32_t)tr * row_bytes + 16u * dg;
+  const int64_t head_off = (int64_t)hk * p.head_stride;
+  u32x4 stk[4], stv[4];
+  int pid[4];
+  // page ids of a block: lanes 0..3 load them (index clamped to the request's
+  // last page: a block past the end fetches nothing, see nbytes below), and
+  // every lane takes them as wave-uniform values (scalar buffer resources)
+  auto load_pid_vec = [&](int blk) -> int {
+    const int pg = max(min(first_page + blk * 4 + (lane & 3), npages_req - 1), 0);
+    return ragged ? pbeg + 16 * pg : p.kv_indices[pbeg + pg];
+  };
+  auto take_pids = [&](int v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pid[i] = __builtin_amdgcn_readlane(v, i);
+  };
+  auto fetch = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kstart = key0 + blk * kBlockKeys + 16 * i;
+      const int nbytes =
+          __builtin_amdgcn_readfirstlane(min(max(key1 - kstart, 0), 16) * (int)row_bytes);
+      const int64_t base = (int64_t)pid[i] * p.page_stride + head_off;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + base), 0, nbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + base), 0, nbytes, 0x00020000);
+      stk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ld_off, 0, 0);
+      stv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ld_off, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+    uint16_t* sk = smem + buf * kBufElems;
+    uint16_t* sv = sk + kKElems;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(sk + (4 * tr + i) * kKStride + 8 * dg) = stk[i];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = stv[0][w], a1 = stv[1][w], a2 = stv[2][w], a3 = stv[3][w];
+      const u32x2 lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                        __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+      const u32x2 hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                        __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+      const int d = 8 * dg + 2 * w;
+      char* sv8 = reinterpret_cast<char*>(sv);
+      *reinterpret_cast<u32x2*>(sv8 + d * 2 * kBlockKeys + vgroup_off(tr, d)) = lo;
+      *reinterpret_cast<u32x2*>(sv8 + (d + 1) * 2 * kBlockKeys + vgroup_off(tr, d + 1)) = hi;
+    }
+  };
+
+  // one block of 64 keys from LDS buffer buf
+  // one block of 64 keys from LDS buffer buf, processed as two halves of 32
+  // slots: the softmax of one half overlaps the MFMAs of the other
+  auto block = [&](int buf, int blk, bool need_mask) {
+    const uint16_t* sk = smem + buf * kBufElems;
+    const uint16_t* sv = sk + kKElems;
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint16_t* krow = sk + (32 * kt + jq) * kKStride + 8 * h;
+      s[kt] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(krow), qf[0], f32x16{});
+#pragma unroll
+      for (int kb = 1; kb < 8; ++kb)
+        s[kt] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(krow + 16 * kb), qf[kb], s[kt]);
+    }
+    if (need_mask) {  // wave-uniform
+      const int kb0 = key0 + blk * kBlockKeys;
+      const int lim = min(key1 - 1, qpos) - kb0;  // last visible key of this column, in-block
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[kt][r] = reg_key(kt, r, h) > lim ? kNegInf : s[kt][r];
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      mx = pair_max(mx);
+      const float mxs = mx * scale;
+      const bool need = mxs > m + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? fast_exp2(m - mxs) : 1.f;
+        m = need ? mxs : m;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      const float ms = m == kNegInf ? 0.f : m;
+      // O^T += V^T P^T over the half's 2 slot groups of 16 (the row sum is
+      // kept in fp32: the LSE must not carry the operand rounding)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        u32x4 pb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * kh + 2 * e], scale, -ms));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * kh + 2 * e + 1], scale, -ms));
+          l += p0 + p1;
+          pb[e] = Elt<DT>::pack(p0, p1);
+        }
+        const int unit = (4 * kt + 2 * kh + h) ^ vswz(jq);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint16_t* vp = sv + (32 * db + jq) * kBlockKeys + 8 * unit;
+          o[db] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(vp), pb, o[db]);
+        }
+      }
+    }
+  };
+
+  // Software pipeline: while block blk is computed from LDS, block blk+1 is in
+  // flight into registers and the page ids of block blk+2 are loaded (issued
+  // first, so waiting for them never waits for the K/V loads). The last
+  // iteration fetches and stages one block past the end: its buffer
+  // resources have zero size, so it reads nothing and stores zeros.
+  if (nblocks > 0) {
+    take_pids(load_pid_vec(0));
+    fetch(0);
+    store(0);
+    take_pids(load_pid_vec(1));
+  }
+  __syncthreads();
+
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const int buf = blk & 1;
+    const int pv = load_pid_vec(blk + 2);
+    fetch(blk + 1);
+    const int kb0 = key0 + blk * kBlockKeys;
+    const bool need_mask = kb0 + kBlockKeys > key1 || kb0 + kBlockKeys - 1 > qpos_min;
+    block(buf, blk, need_mask);
+    store(buf ^ 1);
+    take_pids(pv);
+    __syncthreads();
+  }
+
+  // --- epilogue --------------------------------------------------------------
+  // register r of o[db] holds dim 32 db + 8 (r/4) + 4 h + r%4 of this column;
+  // each lane summed the probabilities of its own slots
+  l = pair_sum(l);
+  const bool live = l > 0.f;
+  const float inv = live ? 1.f / l : 0.f;
+  const float lse2 = live ? m + fast_log2(l) : kNegInf;
+  if (slot0 < 0) {
+    if (qvalid) {
+      uint16_t* op = p.out + ((int64_t)(q0 + pos) * Hq + head) * 128;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const u32x2 w = {Elt<DT>::pack(o[db][4 * rg] * inv, o[db][4 * rg + 1] * inv),
+                           Elt<DT>::pack(o[db][4 * rg + 2] * inv, o[db][4 * rg + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + 32 * db + 8 * rg + 4 * h) = w;
+        }
+      if (h == 0 && p.lse) p.lse[(int64_t)(q0 + pos) * Hq + head] = lse2 * kLn2;
+    }
+    return;
+  }
+
+  // split tile: publish the partial state of every column with device-coherent stores
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
+  if (qvalid) {
+    const int64_t sh = (int64_t)(slot0 + pos) * G + g;
+    const uint32_t ob = (uint32_t)sh * 512u;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const u32x4 w = {__float_as_uint(o[db][4 * rg] * inv), __float_as_uint(o[db][4 * rg + 1] * inv),
+                         __float_as_uint(o[db][4 * rg + 2] * inv),
+                         __float_as_uint(o[db][4 * rg + 3] * inv)};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rs, ob + 4u * (32 * db + 8 * rg + 4 * h), 0, kCoherent);
+      }
+    if (h == 0)
+      __hip_atomic_store(p.part_lse + sh, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (p.defer_merge) return;  // a later kernel combines the partial states
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  const int chunk = key0 / (p.header[5] * 16);
+  const int base = slot0 - chunk * rows;
+  if (tid == 0) {
+    const int prev =
+        __hip_atomic_fetch_add(p.counters + base, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == nchunk - 1;
+    if (last) p.counters[base] = 0;
+    s_flag = last;
+  }
+  __syncthreads();
+  if (!s_flag || !qvalid) return;
+
+  // last workgroup of the split: merge the chunks of every column; lane (h, jq)
+  // owns dims 64 h .. 64 h + 63 of its column
+  float acc[64];
+#pragma unroll
+  for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+  float gm = kNegInf, gl = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const int64_t sh = (int64_t)(base + c * rows + pos) * G + g;
+    const float s2 = __hip_atomic_load(p.part_lse + sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t ob = (uint32_t)sh * 512u + 256u * h;
+    u32x4 raw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ob + 16 * i, 0, kCoherent);
+    const float mn = fmaxf(gm, s2);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float f = fast_exp2(gm - ms);
+    const float w = fast_exp2(s2 - ms);
+    gl = gl * f + w;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) acc[i] = acc[i] * f + w * __uint_as_float(raw[i >> 2][i & 3]);
+    gm = mn;
+  }
+  const bool glive = gl > 0.f;
+  const float ginv = glive ? 1.f / gl : 0.f;
+  uint16_t* op = p.out + ((int64_t)(q0 + pos) * Hq + head) * 128 + 64 * h;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = Elt<DT>::pack(acc[8 * i + 2 * e] * ginv, acc[8 * i + 2 * e + 1] * ginv);
+    *reinterpret_cast<u32x4*>(op + 8 * i) = w;
+  }
+  if (h == 0 && p.lse)
+    p.lse[(int64_t)(q0 + pos) * Hq + head] = glive ? (gm + fast_log2(gl)) * kLn2 : kNegInf;
+}
+
+// Workgroup i runs tiles of bin i mod 8 (the XCD the hardware gives it), at
+// positions i / 8, i / 8 + gridDim.x / 8, ... of the bin.
+// Workgroup `block` of `nblocks` runs the tiles of bin block mod 8, strided
+// by nblocks / 8 (nblocks a multiple of 8).
+template <int DT, int G>
+__device__ __forceinline__ void append_worker(const AttnParams& p, int block, int nblocks,
+                                              uint16_t* smem, int& s_flag) {
+  const int x = block % kAppendBins, stride = nblocks / kAppendBins;
+  const int t1 = p.worker_ptr[x + 1];
+  for (int t = p.worker_ptr[x] + block / kAppendBins; t < t1; t += stride)
+    append_tile<DT, G>(p, t, smem, s_flag);
+}
+
+}  // namespace app
+}  // namespace pkfa

@@ -1,0 +1,605 @@
+// Paged-KV decode kernel for gfx950.
+//
+// What it computes: for each request b and query head h, scaled-dot-product
+// attention of q[b, h] over the request's keys gathered through its page
+// table ([DeepDive] "FlashInfer: The Attention Kernel Library That Proves the
+// Bottleneck ...", section "Snippet One: Paged KV-Cache Attention and MLA":
+// page pool, CSR page list, last_page_len), split into key chunks by the
+// planner ([Guide] "FlashInfer: GPU Kernels for LLM Inference (2026 Guide)",
+// section "What FlashInfer is", idea 3). Chunks of one request are combined by
+// the log-sum-exp merge ([Guide] section "Cascade attention for shared
+// prefixes").
+//
+// MI355X design (decode is HBM-bound, so no MFMA):
+//  * one wave64 per worker, 4 independent waves per 256-thread workgroup, no
+//    barriers; the planner cuts requests into pieces and deals them, largest
+//    first, to static per-wave work lists of the same cost (pages plus a
+//    per-piece overhead), the kv heads of a piece to neighbouring waves, so
+//    they read whole token rows of the same pages at about the same time;
+//  * all G = Hq/Hkv query heads of the kv head are packed in the wave (GQA),
+//    so each K/V byte is read from HBM once for all of them;
+//  * lane = 8 x row-group + segment: row group r (0..7) owns tokens r and r+8
+//    of every 16-token page, segment s (0..7) owns dims [8s, 8s+8) and
+//    [64+8s, 64+8s+8); each K/V row (256 B) is two fully coalesced 128-byte
+//    halves, 16 bytes per lane (buffer_load_dwordx4);
+//  * loads go through a per-page buffer resource whose size stops at the
+//    last valid token, so slots past last_page_len read as zero without any
+//    memory access and without branches;
+//  * a ring of NBUF pages in registers: page j+NBUF-1 is requested while page
+//    j is consumed;
+//  * scores: packed 2-element dot products (v_dot2_f32_bf16 / _f16) and an
+//    8-lane DPP sum; P*V: the two tokens a lane holds are paired per element
+//    (v_perm) and multiplied with the packed probabilities by the same dot2,
+//    accumulating in fp32;
+//  * E4M3 pages (one byte per element, one scale per tensor): a 128-byte K/V
+//    row is one 16-byte load per lane (segment s owns dims [16s, 16s+16));
+//    codes are widened exactly to the q type in registers (v_cvt_scalef32_pk
+//    with scale 1) and take the same dot2 path; the K scale joins the score
+//    scale and the V scale the final normalisation;
+//  * each row group keeps its own online-softmax state (reference max in log2
+//    units, sum, 16 fp32 accumulators per head); the reference is only moved
+//    (and the accumulators rescaled) when a wave-wide vote finds a score more
+//    than 2^8 above it, so most pages skip the rescale;
+//  * a (request, kv head) cut into several pieces: each piece writes an fp32
+//    partial state, then the last wave to arrive (an agent-scope counter per
+//    split unit, counted one piece later so the wait for the stores is free)
+//    merges all pieces and writes the final output, so one launch does the
+//    whole decode. Counters and queue heads are reset by the kernel itself,
+//    so it can be replayed from a graph.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkfa {
+namespace dec {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
+constexpr int kCoherent = 16;          // cache policy sc1: device-coherent access
+
+// One page of the lane's two tokens (r and r+8). 16-bit pools: k[0], k[1]
+// = token r dims [8s, 8s+8) and [64+8s, 64+8s+8), k[2], k[3] the same for
+// token r+8. E4M3 pools (KV8): k[0] = token r dims [16s, 16s+16), k[1] =
+// token r+8 (one 16-byte load per 128-byte row).
+template <bool KV8>
+struct PageRegs {
+  static constexpr int N = KV8 ? 2 : 4;
+  u32x4 k[N];
+  u32x4 v[N];
+};
+
+// Dims of the lane's 16 accumulators: float4 group i (i = 0..3) of segment s
+// starts at dim acc_dim(s, i).
+template <bool KV8>
+__device__ __forceinline__ int acc_dim(int s, int i) {
+  return KV8 ? 16 * s + 4 * i : (i < 2 ? 8 * s + 4 * i : 64 + 8 * s + 4 * (i - 2));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+}
+
+// The fp32 partial outputs [slots][G][128] as one buffer (byte offsets < 2^31:
+// the planner's capacities keep slots * G * 512 below that).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p.part_o, 0, 0x7fffffff, 0x00020000);
+}
+
+template <bool KV8>
+__device__ __forceinline__ void load_page(PageRegs<KV8>& pr, const AttnParams& p, int pid, int hk,
+                                          uint32_t bytes, const uint32_t (&off)[4]) {
+  constexpr int N = PageRegs<KV8>::N;
+  const int64_t base = ((int64_t)pid * p.page_stride + (int64_t)hk * p.head_stride) * (KV8 ? 1 : 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      page_rsrc(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.k) + base), bytes);
+  const __amdgpu_buffer_rsrc_t rv =
+      page_rsrc(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.v) + base), bytes);
+#pragma unroll
+  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) pr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, 0);
+}
+
+template <int DT, int G, bool KV8>
+__device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const u32x4 (&qlo)[G],
+                                             const u32x4 (&qhi)[G], float (&m)[G], float (&l)[G],
+                                             float (&acc)[G][16], float scale, bool va, bool vb) {
+  using E = Elt<DT>;
+  // key pairs of tokens r (ka) and r+8 (kb) in the q layout: pair i < 4 meets
+  // qlo[g][i], pair 4 + i meets qhi[g][i]
+  uint32_t ka[8], kb[8];
+  if constexpr (KV8) {
+    // E4M3 codes widened to the q type; dword i holds dims 16s+4i .. 16s+4i+3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ka[2 * i] = E::template from_e4m3<false>(pr.k[0][i]);
+      ka[2 * i + 1] = E::template from_e4m3<true>(pr.k[0][i]);
+      kb[2 * i] = E::template from_e4m3<false>(pr.k[1][i]);
+      kb[2 * i + 1] = E::template from_e4m3<true>(pr.k[1][i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ka[i] = pr.k[0][i];
+      ka[4 + i] = pr.k[1][i];
+      kb[i] = pr.k[2][i];
+      kb[4 + i] = pr.k[3][i];
+    }
+  }
+  float sa[G], sb[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float x = 0.f, y = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x = E::dot2(qlo[g][i], ka[i], x);
+      y = E::dot2(qlo[g][i], kb[i], y);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x = E::dot2(qhi[g][i], ka[4 + i], x);
+      y = E::dot2(qhi[g][i], kb[4 + i], y);
+    }
+    const float xs = octet_sum(x) * scale;
+    const float ys = octet_sum(y) * scale;
+    sa[g] = va ? xs : kNegInf;
+    sb[g] = vb ? ys : kNegInf;
+  }
+  bool need = false;
+#pragma unroll
+  for (int g = 0; g < G; ++g) need |= fmaxf(sa[g], sb[g]) > m[g] + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(m[g], fmaxf(sa[g], sb[g]));
+      const float alpha = fast_exp2(m[g] - (mn == kNegInf ? 0.f : mn));
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[g][e] *= alpha;
+      m[g] = mn;
+    }
+  }
+  // element e of tokens r and r+8 side by side: (A_e, B_e)
+  uint32_t pv[16];
+  if constexpr (KV8) {
+    // interleave the codes of the two tokens byte by byte (A0 B0 A1 B1 and
+    // A2 B2 A3 B3), then widen each code pair
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t p01 = __builtin_amdgcn_perm(pr.v[1][i], pr.v[0][i], 0x05010400u);
+      const uint32_t p23 = __builtin_amdgcn_perm(pr.v[1][i], pr.v[0][i], 0x07030602u);
+      pv[4 * i] = E::template from_e4m3<false>(p01);
+      pv[4 * i + 1] = E::template from_e4m3<true>(p01);
+      pv[4 * i + 2] = E::template from_e4m3<false>(p23);
+      pv[4 * i + 3] = E::template from_e4m3<true>(p23);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[2 * i] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x05040100u);
+      pv[2 * i + 1] = __builtin_amdgcn_perm(pr.v[2][i], pr.v[0][i], 0x07060302u);
+      pv[8 + 2 * i] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x05040100u);
+      pv[8 + 2 * i + 1] = __builtin_amdgcn_perm(pr.v[3][i], pr.v[1][i], 0x07060302u);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float ms = m[g] == kNegInf ? 0.f : m[g];
+    const float pa = fast_exp2(sa[g] - ms);
+    const float pb = fast_exp2(sb[g] - ms);
+    l[g] += pa + pb;
+    const uint32_t pp = E::pack(pa, pb);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = E::dot2(pp, pv[e], acc[g][e]);
+  }
+}
+
+// Merge the 8 row-group states of the wave (lanes that differ in bits 3..5).
+template <int G>
+__device__ __forceinline__ void merge_row_groups(float (&m)[G], float (&l)[G],
+                                                 float (&acc)[G][16]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float M = m[g];
+    M = fmaxf(M, xor8(M));
+    M = pair32_max(pair16_max(M));
+    const float f = fast_exp2(m[g] - (M == kNegInf ? 0.f : M));
+    float L = l[g] * f;
+    L += xor8(L);
+    L = pair32_sum(pair16_sum(L));
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float a = acc[g][e] * f;
+      a += xor8(a);
+      acc[g][e] = pair32_sum(pair16_sum(a));
+    }
+    m[g] = M;
+    l[g] = L;
+  }
+}
+
+// Online merge of the fp32 partial states in slots base .. base+C-1 (slot
+// layout [slot][G][128], piece c taken by row group c % 8). The partials were
+// published by other waves with device-coherent stores; they are read back
+// with device-coherent loads (sc1).
+template <int G, bool KV8>
+__device__ __forceinline__ void gather_partials(const AttnParams& p, int64_t base, int C, int r,
+                                                int s, float (&m)[G], float (&l)[G],
+                                                float (&acc)[G][16]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
+  }
+  // one resource over the whole partial array: row groups read different slots
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
+  auto load_state = [&](int c, int g, float& s2, float (&v)[16]) {
+    const int64_t sh = (base + c) * G + g;
+    s2 = __hip_atomic_load(p.part_lse + sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t o = (uint32_t)sh * 512u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 raw =
+          __builtin_amdgcn_raw_buffer_load_b128(rs, o + 4 * acc_dim<KV8>(s, i), 0, kCoherent);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[4 * i + k] = __uint_as_float(raw[k]);
+    }
+  };
+  auto add_state = [&](int g, float s2, const float (&v)[16]) {
+    const float mn = fmaxf(m[g], s2);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float f = fast_exp2(m[g] - ms);
+    const float w = fast_exp2(s2 - ms);
+    l[g] = l[g] * f + w;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = acc[g][e] * f + w * v[e];
+    m[g] = mn;
+  };
+  // two chunks per row group per round, both requested before either is used
+  for (int c = r; c < C; c += 16) {
+    const bool two = c + 8 < C;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float sa2, sb2 = kNegInf, va[16], vb[16];
+      load_state(c, g, sa2, va);
+      if (two) load_state(c + 8, g, sb2, vb);
+      add_state(g, sa2, va);
+      if (two) add_state(g, sb2, vb);
+    }
+  }
+}
+
+template <int DT, int G, bool KV8>
+__device__ __forceinline__ void write_final(const AttnParams& p, int row, int hk, int r, int s,
+                                            const float (&m)[G], const float (&l)[G],
+                                            const float (&acc)[G][16]) {
+  const int Hq = p.num_qo_heads;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (r != g) continue;  // row group g writes head g of the group
+    const int h = hk * G + g;
+    const bool live = l[g] > 0.f;
+    // the V scale (1 for unscaled pools) joins the normalisation
+    const float inv = live ? p.v_scale / l[g] : 0.f;
+    uint16_t* op = p.out + ((int64_t)row * Hq + h) * 128;
+    u32x4 lo, hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = Elt<DT>::pack(acc[g][2 * i] * inv, acc[g][2 * i + 1] * inv);
+      hi[i] = Elt<DT>::pack(acc[g][8 + 2 * i] * inv, acc[g][8 + 2 * i + 1] * inv);
+    }
+    *reinterpret_cast<u32x4*>(op + acc_dim<KV8>(s, 0)) = lo;
+    *reinterpret_cast<u32x4*>(op + acc_dim<KV8>(s, 2)) = hi;
+    if (s == 0 && p.lse)
+      p.lse[(int64_t)row * Hq + h] = live ? (m[g] + fast_log2(l[g])) * kLn2 : kNegInf;
+  }
+}
+
+// Publish a chunk's normalised state with device-coherent stores (sc1), so a
+// wave on any XCD can read it after the arrival counter says it is complete.
+template <int G, bool KV8>
+__device__ __forceinline__ void write_partial(const AttnParams& p, int64_t slot, int r, int s,
+                                              const float (&m)[G], const float (&l)[G],
+                                              const float (&acc)[G][16]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (r != g) continue;
+    const int64_t sh = slot * G + g;
+    const bool live = l[g] > 0.f;
+    const float inv = live ? 1.f / l[g] : 0.f;
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
+    const uint32_t o = (uint32_t)sh * 512u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[k] = __float_as_uint(acc[g][4 * i + k] * inv);
+      __builtin_amdgcn_raw_buffer_store_b128(u, rs, o + 4 * acc_dim<KV8>(s, i), 0, kCoherent);
+    }
+    if (s == 0)
+      __hip_atomic_store(p.part_lse + sh, live ? m[g] + fast_log2(l[g]) : kNegInf, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Identity of a piece, wave-uniform.
+struct PieceId {
+  int row, hk, base, slot, npieces;
+};
+
+// A piece being set up: tile fields (wave-uniform after v_readlane), its page
+// ids (lane i holds pages i and i+64; at most 128 pages, a planner guarantee)
+// and the device page-table check (kv_indptr[b], kv_indptr[b+1],
+// last_page_len[b] in lanes 0..2).
+struct PieceCtx {
+  PieceId id;
+  int pbeg, key0, key1_plan, first_page, npg_plan;
+  int ids0, ids1, chk;
+};
+
+// Request the tile of piece t (one VGPR, lanes 0..7).
+__device__ __forceinline__ int load_tile(const AttnParams& p, int t, int lane) {
+  return p.tiles[t * 8 + (lane & 7)];
+}
+
+// Take the tile fields and request the page ids and the page-table check.
+__device__ __forceinline__ void open_piece(const AttnParams& p, int tv, int lane, PieceCtx& c) {
+  const int b = __builtin_amdgcn_readlane(tv, 0);
+  c.id.row = b;
+  c.id.hk = __builtin_amdgcn_readlane(tv, 1);
+  c.pbeg = __builtin_amdgcn_readlane(tv, 2);
+  c.id.base = __builtin_amdgcn_readlane(tv, 3);
+  c.key0 = __builtin_amdgcn_readlane(tv, 4);
+  c.key1_plan = __builtin_amdgcn_readlane(tv, 5);
+  c.id.slot = __builtin_amdgcn_readlane(tv, 6);
+  c.id.npieces = __builtin_amdgcn_readlane(tv, 7);
+  c.first_page = c.key0 >> 4;
+  c.npg_plan = c.key1_plan > c.key0 ? ((c.key1_plan + 15) >> 4) - c.first_page : 0;
+  if (p.kv_offsets) {
+    // ragged KV: page j of the piece starts at row pbeg + 16 (first_page + j)
+    // (the tile carries kv_offsets[b]); the check reads the row offsets
+    const int row0 = c.pbeg + 16 * c.first_page;
+    c.ids0 = lane < c.npg_plan ? row0 + 16 * lane : 0;
+    c.ids1 = lane + 64 < c.npg_plan ? row0 + 16 * (lane + 64) : 0;
+    c.chk = lane == 0 ? p.kv_offsets[b] : lane == 1 ? p.kv_offsets[b + 1] : 0;
+  } else {
+    const int32_t* ids_base = p.kv_indices + c.pbeg + c.first_page;
+    c.ids0 = lane < c.npg_plan ? ids_base[lane] : 0;
+    c.ids1 = lane + 64 < c.npg_plan ? ids_base[lane + 64] : 0;
+    c.chk = lane == 0 ? p.kv_indptr[b] : lane == 1 ? p.kv_indptr[b + 1] : p.last_page_len[b];
+  }
+}
+
+// Wave-uniform bounds of a piece, taken from its context once its loads have
+// arrived.
+struct PieceRun {
+  int hk, row, key1, first_page, npg;
+};
+
+// Bytes per token row of the pool, and the lane's load offsets in a page.
+template <bool KV8>
+__device__ __forceinline__ uint32_t page_offsets(const AttnParams& p, int lane, uint32_t (&off)[4]) {
+  const uint32_t r = lane >> 3, s = lane & 7;
+  const uint32_t ts2 = (uint32_t)p.token_stride * (KV8 ? 1u : 2u);
+  if constexpr (KV8) {
+    off[0] = r * ts2 + s * 16u;
+    off[1] = (r + 8) * ts2 + s * 16u;
+    off[2] = off[3] = 0u;  // unused
+  } else {
+    off[0] = r * ts2 + s * 16u;
+    off[1] = r * ts2 + 128u + s * 16u;
+    off[2] = (r + 8) * ts2 + s * 16u;
+    off[3] = (r + 8) * ts2 + 128u + s * 16u;
+  }
+  return ts2;
+}
+
+__device__ __forceinline__ int page_id_of(const PieceCtx& c, int j) {
+  return j < 64 ? __builtin_amdgcn_readlane(c.ids0, j & 63) : __builtin_amdgcn_readlane(c.ids1, j & 63);
+}
+
+// Bytes of page j of a piece that hold valid tokens (a buffer load past them
+// returns 0); kept scalar so the buffer resource needs no per-lane loop.
+__device__ __forceinline__ uint32_t page_bytes_of(const PieceRun& run, int j, uint32_t ts2) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane(min(16, run.key1 - (run.first_page + j) * 16) *
+                                                  (int)ts2);
+}
+
+// Start a piece: check it against the device page table, request its q rows
+// and its first NBUF-1 pages into the ring. The caller runs this before the
+// previous piece's epilogue, which then overlaps the first loads' latency.
+template <int G, int NBUF, bool KV8>
+__device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx& c, int lane,
+                                            PieceRun& run, PageRegs<KV8> (&buf)[NBUF],
+                                            u32x4 (&qlo)[G], u32x4 (&qhi)[G]) {
+  // The context's fields are wave-uniform; readfirstlane says so to the
+  // compiler (it loses track across the loop that hands pieces over), so the
+  // page buffer resources stay scalar.
+  run.hk = __builtin_amdgcn_readfirstlane(c.id.hk);
+  run.row = __builtin_amdgcn_readfirstlane(c.id.row);
+  // The device page table must agree with the plan (offset, and the key
+  // range inside the request's valid tokens); a piece that disagrees reads
+  // nothing.
+  const int span = __builtin_amdgcn_readlane(c.chk, 1) - __builtin_amdgcn_readlane(c.chk, 0);
+  const int kv_len = p.kv_offsets ? span  // ragged: rows
+                                  : (span > 0 ? (span - 1) * 16 + __builtin_amdgcn_readlane(c.chk, 2) : 0);
+  const int key0 = __builtin_amdgcn_readfirstlane(c.key0);
+  const int key1_plan = __builtin_amdgcn_readfirstlane(c.key1_plan);
+  const bool agrees = __builtin_amdgcn_readlane(c.chk, 0) == __builtin_amdgcn_readfirstlane(c.pbeg) &&
+                      key1_plan <= kv_len;
+  run.first_page = __builtin_amdgcn_readfirstlane(c.first_page);
+  run.key1 = agrees ? key1_plan : key0;
+  run.npg = agrees ? __builtin_amdgcn_readfirstlane(c.npg_plan) : 0;
+  const int s = lane & 7;
+  const uint16_t* qp = p.q + ((int64_t)run.row * p.num_qo_heads + run.hk * G) * 128;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    qlo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 0));
+    qhi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 2));
+  }
+  uint32_t off[4];
+  const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
+  if (run.npg >= 2 * NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u) load_page(buf[u], p, page_id_of(c, u), run.hk, 16u * ts2, off);
+  } else {
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u)
+      if (u < run.npg) load_page(buf[u], p, page_id_of(c, u), run.hk, page_bytes_of(run, u, ts2), off);
+  }
+}
+
+// Stream one piece begun by begin_piece: keys [key0, key1) of kv head hk of
+// request row, for its G q heads; leaves the state per row group in (m, l,
+// acc). hook(k) runs at the start of steady ring pass k counted from the end
+// (k = 2, 1, 0 for the last three passes; all three run after the loop if
+// the piece has fewer), where the caller overlaps the set-up of its next
+// piece with the loads.
+template <int DT, int G, int NBUF, bool KV8, typename Hook>
+__device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx& c,
+                                             const PieceRun& run, int lane,
+                                             PageRegs<KV8> (&buf)[NBUF], const u32x4 (&qlo)[G],
+                                             const u32x4 (&qhi)[G], float (&m)[G], float (&l)[G],
+                                             float (&acc)[G][16], Hook&& hook) {
+  const int r = lane >> 3;
+  const int hk = run.hk, npg = run.npg, key1 = run.key1;
+  uint32_t off[4];
+  const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
+  }
+  const float scale = p.scale_log2;
+  int j = 0;
+  int hooks_left = 3;
+  if (npg >= 2 * NBUF) {
+    // Steady state: every page touched here is full and has a successor, so
+    // all loads are unconditional and the next page id is fetched one page
+    // ahead; the compiler then keeps NBUF-1 pages in flight.
+    const uint32_t full = 16u * ts2;
+    int nid = page_id_of(c, NBUF - 1);
+    auto ring_pass = [&](int j0) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int jn = j0 + u + NBUF - 1;
+        const int pid = nid;
+        nid = page_id_of(c, jn + 1);
+        load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, off);
+        consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, true, true);
+      }
+    };
+    // passes: the peeled first one, then while j + 2 NBUF - 1 < npg
+    const int passes = 1 + (npg - NBUF) / NBUF - ((npg - NBUF) % NBUF == 0 ? 1 : 0);
+    // The first pass is peeled so that the q loads are waited for there; in
+    // the loop only K/V page loads are then outstanding at the loop header
+    // and the compiler's wait counts keep NBUF-1 pages in flight.
+    if (passes - 1 < 3) hook(--hooks_left);
+    ring_pass(0);
+    int k = 1;
+    for (j = NBUF; j + 2 * NBUF - 1 < npg; j += NBUF, ++k) {
+      if (passes - 1 - k < hooks_left) hook(--hooks_left);
+      ring_pass(j);
+    }
+  }
+  // Tail: at most 2*NBUF-1 pages, the last one possibly partial.
+  for (; j < npg; j += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int jj = j + u;
+      if (jj >= npg) break;
+      const int jn = jj + NBUF - 1;
+      if (jn < npg)
+        load_page(buf[(u + NBUF - 1) % NBUF], p, page_id_of(c, jn), hk, page_bytes_of(run, jn, ts2),
+                  off);
+      const int tb = (run.first_page + jj) * 16;
+      consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1,
+                               tb + r + 8 < key1);
+    }
+  }
+  while (hooks_left > 0) hook(--hooks_left);
+}
+
+// Worker wave w runs the pieces worker_ptr[w] .. worker_ptr[w+1]-1 in order
+// (the planner gives every wave the same number of pages). The next piece's
+// tile and page ids are requested while the current piece's last pages
+// stream, so a new piece starts without a dependent round trip. A split
+// unit's pieces publish fp32 partial states; a wave reports a piece's
+// arrival only after its next piece (the partial's stores have long
+// completed by then, so the wait is free), and the last arriving piece
+// merges the unit and clears its counter, so the kernel can be replayed from
+// a graph.
+template <int DT, int G, int NBUF, bool KV8>
+__device__ __forceinline__ void decode_worker(const AttnParams& p, int w) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane >> 3, s = lane & 7;
+  if (w >= p.header[6]) return;  // the grid rounds the worker count up to whole workgroups
+  const int t_end = __builtin_amdgcn_readfirstlane(p.worker_ptr[w + 1]);
+  int t = __builtin_amdgcn_readfirstlane(p.worker_ptr[w]);
+  auto fetch_add = [&](int32_t* ptr) -> int {  // lane 0 only; result read by readlane
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(ptr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+  };
+  float m[G], l[G], acc[G][16];
+  // arrival of a split piece whose partial was published earlier; the last
+  // arrival of the unit merges all its pieces and writes the output
+  auto finish_arrival = [&](const PieceId& pd, int arr) {
+    if (__builtin_amdgcn_readlane(arr, 0) != pd.npieces - 1) return;
+    if (lane == 0) p.counters[pd.base] = 0;
+    gather_partials<G, KV8>(p, pd.base, pd.npieces, r, s, m, l, acc);
+    merge_row_groups<G>(m, l, acc);
+    write_final<DT, G, KV8>(p, pd.row, pd.hk, r, s, m, l, acc);
+  };
+  auto arrive = [&](const PieceId& pd) -> int {
+    // the partial's coherent stores must be complete before the count
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return fetch_add(p.counters + pd.base);
+  };
+
+  PieceId pd = {0, 0, -1, -1, 0};  // pending arrival (slot < 0: none)
+  PieceCtx cur, nxt;
+  PieceRun run, nrun;
+  PageRegs<KV8> buf[NBUF];
+  u32x4 qlo[G], qhi[G];
+  if (t < t_end) {
+    open_piece(p, load_tile(p, t, lane), lane, cur);
+    begin_piece<G, NBUF, KV8>(p, cur, lane, run, buf, qlo, qhi);
+  }
+  while (t < t_end) {
+    // overlapped set-up of the next piece: request its tile (pass 2 from the
+    // end) and its page ids (pass 1); it begins (q and first pages requested)
+    // before this piece's epilogue
+    const int tn = t + 1;
+    int tvn = 0;
+    auto hook = [&](int k) {
+      if (k == 2 && tn < t_end) tvn = load_tile(p, tn, lane);
+      if (k == 1 && tn < t_end) open_piece(p, tvn, lane, nxt);
+    };
+    stream_piece<DT, G, NBUF, KV8>(p, cur, run, lane, buf, qlo, qhi, m, l, acc, hook);
+    const int arr = pd.slot >= 0 ? arrive(pd) : 0;
+    if (tn < t_end) begin_piece<G, NBUF, KV8>(p, nxt, lane, nrun, buf, qlo, qhi);
+    merge_row_groups<G>(m, l, acc);
+    if (cur.id.slot < 0)
+      write_final<DT, G, KV8>(p, cur.id.row, cur.id.hk, r, s, m, l, acc);
+    else
+      write_partial<G, KV8>(p, cur.id.slot, r, s, m, l, acc);
+    if (pd.slot >= 0) finish_arrival(pd, arr);
+    pd = cur.id;
+    t = tn;
+    cur = nxt;
+    run = nrun;
+  }
+  if (pd.slot >= 0) finish_arrival(pd, arrive(pd));
+}
+
+}  // namespace dec
+}  // namespace pkfa

@@ -128,9 +128,11 @@ def test_cascade_call(prefix_len, num_cu):
     assert_close(to_f64(o1), to_f64(l1), *oracle_cascade(wl), what="fa_cascade")
 
 
-def test_cascade_graph_capture_with_side_stream():
-    """The fork/join of fa_cascade captures into one graph; replays (with eager
-    work and synchronisation between them) reproduce the eager bits."""
+@pytest.mark.parametrize("forked", [True, False])
+def test_cascade_graph_capture_with_side_stream(forked):
+    """fa_cascade captures into one graph, with the fork/join of a side stream
+    or as the one-kernel form; replays (with eager work and synchronisation
+    between them) reproduce the eager bits."""
     import torch
     import paged_kv_cache_fa_amd as fa
     wl = make_cascade(256, [40, 3, 700], 32, 8, "bf16", 23, mode="test")
@@ -145,7 +147,7 @@ def test_cascade_graph_capture_with_side_stream():
               torch.empty_like(dw.q), torch.empty(B, H, dtype=torch.float32, device="cuda"))
     out = torch.empty_like(dw.q)
     lse = torch.empty(B, H, dtype=torch.float32, device="cuda")
-    side = torch.cuda.Stream()
+    side = torch.cuda.Stream() if forked else None
     cap = torch.cuda.Stream()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -164,12 +166,17 @@ def test_cascade_graph_capture_with_side_stream():
 
 def test_config4_full_size():
     """Config 4 in the launch configuration the benchmark times: one
-    fa_cascade call with the prefix pass on a side stream."""
+    fa_cascade call on one stream (both passes in one kernel); the same bits
+    with the prefix pass forked onto a side stream."""
     import torch
     print("[config 4] generating", flush=True)
     wl = make_config(4, mode="test")
     dw = DevWorkload(wl)
-    out, lse, plans = run_cascade(dw, fused=True, side_stream=torch.cuda.Stream())
+    out, lse, plans = run_cascade(dw, fused=True)
+    out, lse = out.clone(), lse.clone()
+    o2, l2, _ = run_cascade(dw, *plans, fused=True, side_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
     print(f"[config 4] prefix tiles {plans[0].info().num_tiles} suffix tiles "
           f"{plans[1].info().num_tiles}", flush=True)
     reqs = list(range(0, 256, 5)) + [255]
