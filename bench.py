@@ -19,6 +19,8 @@ Reported alongside in the same JSON line:
   * ``ragged``: the batch-64 decode over a ragged (contiguous-row) KV cache;
   * ``single``: the single-request decode (32 heads, kv_len 2048, fp16) over a
     contiguous K / V;
+  * ``bsr``: block-sparse prefill, 4096 query rows x 16384 keys in 64 x 64
+    blocks, a quarter of the blocks kept, as MFMA utilisation;
   * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
     from HIP events on its stream), with HBM traffic from rocprofv3 counters
     when the stored counter summary matches the current kernel source;
@@ -187,6 +189,42 @@ def ragged_bytes(rw) -> int:
     return kv_bytes(rw.kv_lens, rw.num_kv_heads) + io_bytes(rw.rows, rw.num_qo_heads)
 
 
+class BlockSparseBench(Timed):
+    """Block-sparse attention: the pattern's page table is built once (a
+    static pattern); every step re-plans and runs the append kernel."""
+
+    def __init__(self, bw, device="cuda"):
+        import torch
+        import paged_kv_cache_fa_amd as fa
+        self.fa, self.bw = fa, bw
+        dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[bw.dtype]
+        t = lambda a: torch.from_numpy(a.view(np.int16)).to(device).view(dt)
+        self.q, self.k, self.v = t(bw.q), t(bw.k), t(bw.v)
+        ip, ix, last, lens = fa.block_sparse_pages(bw.block_indptr, bw.block_indices,
+                                                   bw.col_offsets)
+        self.ip_h, self.lens_h, self.ro_h = ip, lens, np.ascontiguousarray(bw.row_offsets)
+        self.ip, self.ix, self.last = _i32(ip, device), _i32(ix, device), _i32(last, device)
+        self.ro = _i32(bw.row_offsets, device)
+        nrb = len(bw.row_offsets) - 1
+        geom = fa.geometry("append", bw.dtype, nrb, bw.num_qo_heads, bw.num_kv_heads,
+                           max_qo_tokens=int(bw.row_offsets[-1]))
+        self.plan = fa.Plan(geom, device=device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[0], bw.num_qo_heads, dtype=torch.float32,
+                               device=device)
+        self.flops = float((np.diff(bw.row_offsets) * lens).sum()) * bw.num_qo_heads * 4 * 128
+
+    def step(self, i: int, ev=None):
+        self.plan.plan(self.ip_h, self.lens_h, self.ro_h, False)
+        if ev is not None:
+            ev[0].record()
+        ts, hs = self.k.stride(0), self.k.stride(1)
+        self.fa.append(self.plan, self.q, self.ro, self.k, self.v, ts, ts, hs, self.ix, self.ip,
+                       self.last, out=self.out, lse=self.lse)
+        if ev is not None:
+            ev[1].record()
+
+
 class AppendBench(Timed):
     def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, **knobs):
         import torch
@@ -319,7 +357,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="decode workload for the headline (1-3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip batch128/cascade/append")
-    ap.add_argument("--parts", default="batch128,cascade,append,fp8,ragged,single",
+    ap.add_argument("--parts", default="batch128,cascade,append,fp8,ragged,single,bsr",
                     help="comma list of the secondary workloads to run after the headline")
     ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
     ap.add_argument("--copy-probe", action="store_true",
@@ -449,6 +487,20 @@ def main():
                       "ms_per_step": round(sr, 5), "kernel_ms": round(kr, 5),
                       "algorithmic_bytes": nr, "kv_copies": len(br.kv)}
         del br, rw, wk
+        torch.cuda.empty_cache()
+    if "bsr" in parts:
+        from workloads import make_block_sparse
+        bw = make_block_sparse([64] * 64, [64] * 256, 0.25, 32, 8, "bf16", seed=7)
+        bb = BlockSparseBench(bw)
+        sb, kb = bb.run(max(5, args.steps // 2), max(2, args.warmup // 2))
+        line["bsr"] = {"workload": "block-sparse prefill: 4096 query rows x 16384 keys, 64 x 64 "
+                                   "blocks, 25% kept (seeded), 32/8 heads, bf16",
+                       "TFLOP/s": round(bb.flops / (kb * 1e-3) / 1e12, 1),
+                       "mfma_utilisation": round(bb.flops / (kb * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
+                                                 4),
+                       "flops": bb.flops, "kernel_ms": round(kb, 5), "ms_per_step": round(sb, 5),
+                       "blocks_kept": int(len(bw.block_indices))}
+        del bb, bw
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -166,6 +166,32 @@ fa_status fa_plan_ragged(fa_plan_t* plan, const fa_geometry* geom, const int32_t
                          void* host_ws, size_t host_ws_bytes, void* dev_ws, size_t dev_ws_bytes,
                          void* stream);
 
+/* Page table of a block-sparse pattern ([Windows] "Core Features", Attention
+ * Kernels: block-sparse and variable block-sparse patterns; [Guide] "What
+ * FlashInfer is", idea 1: one block-sparse format covers them with the page
+ * table). Query rows are cut into row blocks and keys into column blocks:
+ * column block j is rows col_offsets_h[j] .. col_offsets_h[j+1]-1 of K / V
+ * [rows, num_kv_heads, head_dim] (equal sizes: BSR; any sizes: variable
+ * block-sparse). Row block i attends to the keys of column blocks
+ * block_indices_h[block_indptr_h[i] .. block_indptr_h[i+1]-1] (increasing;
+ * every block but a row block's last one a whole number of pages). Host only,
+ * no HIP call.
+ * Output: a paged table over the same K / V whose page ids are row indices
+ * (chunks of page_size rows of the selected blocks): kv_indptr_h int32
+ * [num_row_blocks+1], kv_indices_h int32 [*num_pages] (row of each page),
+ * last_page_len_h and kv_lens_h int32 [num_row_blocks]. Plan it with fa_plan
+ * (decode when every row block is one query row, else append with qo_indptr =
+ * the row blocks' row offsets, non-causal) and run fa_decode / fa_append with
+ * page_stride = token_stride.
+ * *num_pages always receives the page count; kv_indices_h may be NULL (or
+ * kv_indices_cap too small) to ask for it: FA_ERR_CAPACITY. Errors:
+ * FA_ERR_INVALID for a malformed pattern. */
+fa_status fa_block_sparse_pages(const int32_t* block_indptr_h, const int32_t* block_indices_h,
+                                int32_t num_row_blocks, const int32_t* col_offsets_h,
+                                int32_t num_col_blocks, int32_t page_size, int32_t* kv_indptr_h,
+                                int32_t* kv_indices_h, int64_t kv_indices_cap,
+                                int32_t* last_page_len_h, int32_t* kv_lens_h, int64_t* num_pages);
+
 /* Summary of the current plan. */
 fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats);
 

@@ -36,6 +36,7 @@ from .attention import (  # noqa: F401
     ragged_request_kv,
     decode_ragged,
     append_ragged,
+    block_sparse,
     cascade,
     cascade_direct,
 )

@@ -202,6 +202,34 @@ def append_ragged(q_bits: np.ndarray, qo_indptr, k_bits: np.ndarray, v_bits: np.
         k_bits, v_bits, dtype, kv_offsets, b), causal, scale, rows)
 
 
+def block_sparse(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, dtype: str,
+                 block_indptr, block_indices, row_offsets, col_offsets,
+                 scale: Optional[float] = None):
+    """Block-sparse attention ([Windows] "Core Features", Attention Kernels:
+    block-sparse and variable block-sparse patterns). Query rows
+    ``row_offsets[i] .. row_offsets[i+1]-1`` (row block i) attend, without a
+    mask inside the blocks, to the keys of column blocks
+    ``block_indices[block_indptr[i] .. block_indptr[i+1]-1]``; column block j
+    is key rows ``col_offsets[j] .. col_offsets[j+1]-1``. Returns out / lse for
+    every query row."""
+    D = q_bits.shape[-1]
+    scale = default_scale(D) if scale is None else scale
+    row_offsets = np.asarray(row_offsets)
+    outs, lses = [], []
+    for i in range(row_offsets.shape[0] - 1):
+        rows = []
+        for n in range(int(block_indptr[i]), int(block_indptr[i + 1])):
+            j = int(block_indices[n])
+            rows.extend(range(int(col_offsets[j]), int(col_offsets[j + 1])))
+        K = upcast(k_bits[rows], dtype)
+        V = upcast(v_bits[rows], dtype)
+        r0, r1 = int(row_offsets[i]), int(row_offsets[i + 1])
+        o, s = attend(upcast(q_bits[r0:r1], dtype), K, V, scale)
+        outs.append(o)
+        lses.append(s)
+    return np.concatenate(outs), np.concatenate(lses)
+
+
 def _append_rows(q_bits, qo_indptr, dtype, kv_of, causal, scale, rows):
     """Rows of ``append`` / ``append_ragged``; ``kv_of(b)`` gives request b's K, V."""
     D = q_bits.shape[-1]

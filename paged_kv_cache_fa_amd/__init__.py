@@ -9,8 +9,9 @@ library is missing, the import of any entry point raises.
 Entry points (same names as the C ABI): ``workspace_size``, ``plan`` /
 ``plan_ragged`` (return a ``Plan``), ``decode``, ``decode_scaled``,
 ``decode_ragged``, ``append``, ``append_ragged``, ``cascade``, ``merge_state``,
-``merge_states``; and ``single_decode_with_kv_cache``, which plans and runs a
-one-request decode over a contiguous K / V.
+``merge_states``, ``block_sparse_pages``; and ``single_decode_with_kv_cache`` /
+``block_sparse_attention``, which plan and run a one-request decode over a
+contiguous K / V and a block-sparse pattern.
 """
 from __future__ import annotations
 
@@ -267,6 +268,56 @@ def single_decode_with_kv_cache(q, k, v, sm_scale: float = 0.0, k_scale: float =
                              sm_scale=sm_scale, k_scale=k_scale, v_scale=v_scale)
     out = out.reshape(q.shape)
     return (out, lse.reshape(-1)) if return_lse else out
+
+
+def block_sparse_pages(block_indptr, block_indices, col_offsets, page_size: int = 16):
+    """Row-id page table of a block-sparse pattern (see fa_block_sparse_pages):
+    returns (kv_indptr, kv_indices, last_page_len, kv_lens) as int32 arrays."""
+    lib = load()
+    bi, bx, co = _i32(block_indptr), _i32(block_indices), _i32(col_offsets)
+    nrb, ncb = int(bi.shape[0]) - 1, int(co.shape[0]) - 1
+    kv_indptr = np.zeros(nrb + 1, np.int32)
+    last = np.zeros(max(nrb, 1), np.int32)
+    lens = np.zeros(max(nrb, 1), np.int32)
+    n = ctypes.c_int64()
+    bxp = _ptr(bx) if bx.size else None
+    st = lib.fa_block_sparse_pages(_ptr(bi), bxp, nrb, _ptr(co), ncb, page_size, _ptr(kv_indptr),
+                                   None, 0, _ptr(last), _ptr(lens), ctypes.byref(n))
+    if st not in (0, _lib.FA_ERR_CAPACITY):
+        check(st)
+    kv_indices = np.zeros(max(n.value, 1), np.int32)
+    check(lib.fa_block_sparse_pages(_ptr(bi), bxp, nrb, _ptr(co), ncb, page_size,
+                                    _ptr(kv_indptr), _ptr(kv_indices), kv_indices.shape[0],
+                                    _ptr(last), _ptr(lens), ctypes.byref(n)))
+    return kv_indptr, kv_indices[: n.value], last[:nrb], lens[:nrb]
+
+
+def block_sparse_attention(q, k, v, block_indptr, block_indices, row_offsets, col_offsets,
+                           sm_scale: float = 0.0, **knobs):
+    """Block-sparse attention: query rows row_offsets[i] .. row_offsets[i+1]-1
+    (row block i) attend to the keys of their column blocks (see
+    fa_block_sparse_pages). q [rows, Hq, D], k / v [keys, Hkv, D]. Builds the
+    page table and a plan (workspaces allocated here, as torch tensors) and
+    runs fa_decode (one query row per block) or fa_append (non-causal).
+    Returns (out, lse)."""
+    torch = _torch()
+    kv_indptr, kv_indices, last, lens = block_sparse_pages(block_indptr, block_indices,
+                                                           col_offsets)
+    ro = _i32(row_offsets)
+    nrb = int(ro.shape[0]) - 1
+    dev = q.device
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    ts, hs = k.stride(0), k.stride(1)
+    if np.all(np.diff(ro) == 1):
+        g = geometry("decode", q.dtype, max(nrb, 1), q.shape[1], k.shape[1], **knobs)
+        p = Plan(g, device=dev).plan(kv_indptr, lens)
+        return decode(p, q, k, v, ts, ts, hs, t(kv_indices), t(kv_indptr), t(last),
+                      sm_scale=sm_scale)
+    g = geometry("append", q.dtype, max(nrb, 1), q.shape[1], k.shape[1],
+                 max_qo_tokens=max(int(ro[-1]), 1), **knobs)
+    p = Plan(g, device=dev).plan(kv_indptr, lens, ro, False)
+    return append(p, q, t(ro), k, v, ts, ts, hs, t(kv_indices), t(kv_indptr), t(last),
+                  sm_scale=sm_scale)
 
 
 def append(p: Plan, q, qo_indptr, k_pages, v_pages, page_stride: int, token_stride: int,

@@ -27,7 +27,7 @@ FA_MODE_DECODE, FA_MODE_APPEND = 0, 1
 # every symbol declared in include/fa.h
 EXPORTED = [
     "fa_workspace_size", "fa_plan", "fa_plan_info", "fa_plan_tiles", "fa_plan_destroy",
-    "fa_plan_ragged", "fa_decode", "fa_decode_scaled", "fa_decode_ragged", "fa_append",
+    "fa_plan_ragged", "fa_block_sparse_pages", "fa_decode", "fa_decode_scaled", "fa_decode_ragged", "fa_append",
     "fa_append_ragged", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
     "fa_last_error",
 ]
@@ -78,6 +78,7 @@ def load(path: str = LIB_PATH):
         "fa_workspace_size": [GP, ctypes.POINTER(SZ), ctypes.POINTER(SZ)],
         "fa_plan": [PP, GP, P, P, I32, P, I32, P, SZ, P, SZ, P],
         "fa_plan_ragged": [PP, GP, P, I32, P, I32, P, SZ, P, SZ, P],
+        "fa_block_sparse_pages": [P, P, I32, P, I32, I32, P, P, I64, P, P, ctypes.POINTER(I64)],
         "fa_decode_ragged": [PP, P, P, P, I64, I64, P, F32, F32, F32, P, P, P],
         "fa_append_ragged": [PP, P, P, P, P, I64, I64, P, F32, P, P, P],
         "fa_plan_info": [PP, ctypes.POINTER(PlanStats)],

@@ -9,6 +9,8 @@
 // re-plan does not invalidate the captured launch). Run calls enqueue kernels
 // only; their grids depend on the resolved geometry alone.
 #include <hip/hip_runtime_api.h>
+
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -286,6 +288,81 @@ fa_status fa_plan_ragged(fa_plan_t* plan, const fa_geometry* geom, const int32_t
   }
   return plan_and_upload(plan, geom, kv_offsets_h, lens, batch, qo_indptr_h, causal, host_ws,
                          host_ws_bytes, dev_ws, dev_ws_bytes, stream, true);
+}
+
+fa_status fa_block_sparse_pages(const int32_t* block_indptr_h, const int32_t* block_indices_h,
+                                int32_t num_row_blocks, const int32_t* col_offsets_h,
+                                int32_t num_col_blocks, int32_t page_size, int32_t* kv_indptr_h,
+                                int32_t* kv_indices_h, int64_t kv_indices_cap,
+                                int32_t* last_page_len_h, int32_t* kv_lens_h, int64_t* num_pages) {
+  if (num_row_blocks < 0 || num_col_blocks < 0 || page_size <= 0 || !num_pages ||
+      (num_row_blocks > 0 && (!block_indptr_h || !kv_indptr_h || !last_page_len_h ||
+                              !kv_lens_h)) ||
+      !col_offsets_h || col_offsets_h[0] != 0) {
+    set_error("block sparse: bad sizes, NULL table or col_offsets[0] != 0");
+    return FA_ERR_INVALID;
+  }
+  if (num_row_blocks > 0 && block_indptr_h[0] != 0) {
+    set_error("block sparse: block_indptr[0] must be 0");
+    return FA_ERR_INVALID;
+  }
+  for (int32_t j = 0; j < num_col_blocks; ++j)
+    if (col_offsets_h[j + 1] < col_offsets_h[j]) {
+      set_error("block sparse: col_offsets decrease at block %d", j);
+      return FA_ERR_INVALID;
+    }
+  // pass 1: validate and count pages
+  int64_t total = 0;
+  for (int32_t i = 0; i < num_row_blocks; ++i) {
+    const int32_t b0 = block_indptr_h[i], b1 = block_indptr_h[i + 1];
+    if (b1 < b0 || (b1 > b0 && !block_indices_h)) {
+      set_error("block sparse: block_indptr decreases at row block %d", i);
+      return FA_ERR_INVALID;
+    }
+    for (int32_t n = b0; n < b1; ++n) {
+      const int32_t j = block_indices_h[n];
+      if (j < 0 || j >= num_col_blocks || (n > b0 && j <= block_indices_h[n - 1])) {
+        set_error("block sparse: row block %d: column blocks must be increasing and in range", i);
+        return FA_ERR_INVALID;
+      }
+      const int64_t len = (int64_t)col_offsets_h[j + 1] - col_offsets_h[j];
+      if (n + 1 < b1 && len % page_size) {
+        set_error("block sparse: row block %d: column block %d of %lld rows is not the row's "
+                  "last block and not a whole number of pages", i, j, (long long)len);
+        return FA_ERR_INVALID;
+      }
+      total += (len + page_size - 1) / page_size;
+    }
+  }
+  *num_pages = total;
+  if (!kv_indices_h || kv_indices_cap < total) {
+    set_error("block sparse: kv_indices needs %lld entries", (long long)total);
+    return FA_ERR_CAPACITY;
+  }
+  // pass 2: page ids are first rows of page_size-row chunks of the blocks
+  int64_t k = 0;
+  kv_indptr_h[0] = 0;
+  for (int32_t i = 0; i < num_row_blocks; ++i) {
+    int64_t rows = 0;
+    int32_t last = 0;
+    for (int32_t n = block_indptr_h[i]; n < block_indptr_h[i + 1]; ++n) {
+      const int32_t j = block_indices_h[n];
+      const int32_t r0 = col_offsets_h[j], r1 = col_offsets_h[j + 1];
+      for (int32_t r = r0; r < r1; r += page_size) {
+        kv_indices_h[k++] = r;
+        last = std::min(page_size, r1 - r);
+      }
+      rows += r1 - r0;
+    }
+    if (rows > 0x7fffffff) {
+      set_error("block sparse: row block %d sees more than 2^31 keys", i);
+      return FA_ERR_INVALID;
+    }
+    kv_indptr_h[i + 1] = (int32_t)k;
+    kv_lens_h[i] = (int32_t)rows;
+    last_page_len_h[i] = last;
+  }
+  return FA_OK;
 }
 
 fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats) {

@@ -457,10 +457,36 @@ def check_brute_ragged(seed=43):
             _close([lse[b, h]], [bl])
 
 
+# ---------------------------------------------------------------- block-sparse
+def check_brute_block_sparse(seed=44):
+    """Variable block-sparse attention against the pure-Python brute force
+    over an explicit dense mask (row blocks of 1-3 rows, column blocks of
+    2-4 keys, an empty row block)."""
+    from oracle.brute import brute_attention_row
+    from workloads import make_block_sparse
+    bw = make_block_sparse([2, 1, 3, 2], [3, 2, 4, 2, 3], 0.5, 4, 2, "bf16", seed, head_dim=6,
+                           empty_rows=[1])
+    out, lse = OA.block_sparse(bw.q, bw.k, bw.v, "bf16", bw.block_indptr, bw.block_indices,
+                               bw.row_offsets, bw.col_offsets)
+    Q, K, V = (OA.upcast(x, "bf16").tolist() for x in (bw.q, bw.k, bw.v))
+    N = int(bw.col_offsets[-1])
+    for i in range(4):
+        sel = set(bw.block_indices[bw.block_indptr[i]:bw.block_indptr[i + 1]].tolist())
+        # dense mask: key t is visible iff its column block is selected
+        visible = [t for t in range(N)
+                   if int(np.searchsorted(bw.col_offsets, t, side="right") - 1) in sel]
+        for r in range(int(bw.row_offsets[i]), int(bw.row_offsets[i + 1])):
+            for h in range(4):
+                bo, bl = brute_attention_row(Q[r][h], [K[t][h // 2] for t in visible],
+                                             [V[t][h // 2] for t in visible], 1 / math.sqrt(6))
+                _close(out[r, h], np.array(bo))
+                _close([lse[r, h]], [bl])
+
+
 ALL_CHECKS = [
     check_single_token, check_identical_keys, check_q_zero_and_v_ones, check_scale_default,
     check_gqa_map, check_identity_gather, check_count, check_brute_decode, check_brute_append,
     check_causal_prefill, check_permutation_invariance, check_merge_split, check_merge_algebra,
     check_cascade, check_e4m3_definition, check_fp8_scale_placement, check_brute_decode_fp8,
-    check_brute_ragged,
+    check_brute_ragged, check_brute_block_sparse,
 ]

@@ -175,6 +175,45 @@ def test_kv_dtype_geometry():
         assert e.value.code == "UNSUPPORTED"
 
 
+def test_block_sparse_pages_exact():
+    """Row-id page tables of random (variable) block-sparse patterns, against
+    the rows of the selected blocks cut into 16-row pages."""
+    rng = np.random.default_rng(3)
+    for it in range(200):
+        ncb = int(rng.integers(1, 9))
+        sizes = 16 * rng.integers(0, 5, size=ncb)
+        sizes[-1] = int(rng.integers(0, 70))          # the last block may be ragged
+        co = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        nrb = int(rng.integers(0, 6))
+        rows = [np.sort(rng.choice(ncb, size=int(rng.integers(0, ncb + 1)), replace=False))
+                for _ in range(nrb)]
+        bi = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+        bx = np.concatenate(rows + [np.zeros(0, int)]).astype(np.int32)
+        ip, ix, last, lens = fa.block_sparse_pages(bi, bx, co)
+        exp_ix, exp_ip, exp_last, exp_len = [], [0], [], []
+        for r in rows:
+            keys = [t for j in r for t in range(co[j], co[j + 1])]
+            pages = [t for j in r for t in range(co[j], co[j + 1], 16)]
+            exp_ix += pages
+            exp_ip.append(len(exp_ix))
+            exp_len.append(len(keys))
+            exp_last.append(0 if not pages else min(16, co[r[-1] + 1] - pages[-1])
+                            if co[r[-1] + 1] > co[r[-1]] else
+                            min(16, keys[-1] + 1 - pages[-1]) if keys else 0)
+        assert ip.tolist() == exp_ip and ix.tolist() == exp_ix and lens.tolist() == exp_len
+        for i, r in enumerate(rows):
+            n = exp_ip[i + 1] - exp_ip[i]
+            if n:
+                assert (n - 1) * 16 + last[i] == exp_len[i]
+    for bad in (([0, 2], [1, 0], [0, 16, 32]),      # not increasing
+                ([0, 2], [0, 1], [0, 10, 32]),      # a ragged block that is not the last
+                ([0, 1], [2], [0, 16, 32]),         # out of range
+                ([1, 2], [0], [0, 16])):            # indptr not from 0
+        with pytest.raises(fa.FAError) as e:
+            fa.block_sparse_pages(*bad)
+        assert e.value.code == "INVALID"
+
+
 def test_capacity_error():
     g = _geom("decode", 4, 8, 8, max_tiles=16, num_cu=64)
     with pytest.raises(fa.FAError) as e:

@@ -122,6 +122,21 @@ def _ragged_shifted(k_bits, v_bits, dtype, kv_offsets, b, k_scale=1.0, v_scale=1
     return _ragged_kv(k_bits, v_bits, dtype, off, b, k_scale, v_scale)
 
 
+_attend_raw = OA.attend
+
+
+def _block_sparse_extra_key(q_bits, k_bits, v_bits, dtype, block_indptr, block_indices,
+                            row_offsets, col_offsets, scale=None):
+    """Mistake: each column block reaches one key row too far."""
+    co = np.asarray(col_offsets).copy()
+    co[1:] = np.minimum(co[1:] + 1, co[-1])
+    return _block_sparse(q_bits, k_bits, v_bits, dtype, block_indptr, block_indices, row_offsets,
+                         co, scale)
+
+
+_block_sparse = OA.block_sparse
+
+
 def _run_all():
     for chk in P.ALL_CHECKS:
         chk()
@@ -141,6 +156,7 @@ MUTATIONS = [
     ("e4m3_fnuz_nan", OA, "e4m3_value", _e4m3_fnuz_nan),
     ("fp8_scales_swapped", OA, "gather_request_kv", _gather_swapped_scales),
     ("ragged_rows_shifted", OA, "ragged_request_kv", _ragged_shifted),
+    ("block_sparse_extra_key", OA, "block_sparse", _block_sparse_extra_key),
 ]
 
 

@@ -12,6 +12,8 @@ from .gen import (  # noqa: F401
     make_workload,
     make_cascade,
     make_ragged,
+    make_block_sparse,
+    BlockSparseWorkload,
     RaggedWorkload,
     csr_from_page_lists,
     to_storage_bits,

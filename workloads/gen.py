@@ -380,6 +380,60 @@ def make_ragged(kv_lens: Sequence[int], num_qo_heads: int, num_kv_heads: int, dt
         k_scale=FP8_K_SCALE if fp8 else 1.0, v_scale=FP8_V_SCALE if fp8 else 1.0)
 
 
+@dataclass
+class BlockSparseWorkload:
+    """A block-sparse pattern over contiguous q [rows, Hq, D] and k / v [keys,
+    Hkv, D] (stored bits): row block i is q rows row_offsets[i] ..
+    row_offsets[i+1]-1 and attends to column blocks block_indices[
+    block_indptr[i] .. block_indptr[i+1]-1]; column block j is key rows
+    col_offsets[j] .. col_offsets[j+1]-1. Test mode appends NaN key rows."""
+    dtype: str
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    row_offsets: np.ndarray
+    col_offsets: np.ndarray
+    block_indptr: np.ndarray
+    block_indices: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    seed: int
+
+
+def make_block_sparse(row_sizes: Sequence[int], col_sizes: Sequence[int], density: float,
+                      num_qo_heads: int, num_kv_heads: int, dtype: str, seed: int,
+                      head_dim: int = 128, mode: str = "bench", pad_rows: int = 0,
+                      empty_rows: Sequence[int] = ()) -> BlockSparseWorkload:
+    """Draw a pattern (each column block kept with probability ``density``,
+    increasing per row block; the listed row blocks keep none), then Q, K, V
+    as N(0,1) rounded to the storage type. Column blocks other than a row
+    block's last must be whole pages (16 rows): sizes are the caller's."""
+    rng = np.random.default_rng(seed)
+    row_offsets = np.concatenate([[0], np.cumsum(row_sizes)]).astype(np.int32)
+    col_offsets = np.concatenate([[0], np.cumsum(col_sizes)]).astype(np.int32)
+    nrb, ncb = len(row_sizes), len(col_sizes)
+    keep = rng.random((nrb, ncb)) < density
+    for i in empty_rows:
+        keep[i] = False
+    block_indices = np.concatenate([np.nonzero(keep[i])[0] for i in range(nrb)] +
+                                   [np.zeros(0, np.int64)]).astype(np.int32)
+    block_indptr = np.concatenate([[0], np.cumsum(keep.sum(axis=1))]).astype(np.int32)
+    M, N = int(row_offsets[-1]), int(col_offsets[-1])
+    q = to_storage_bits(rng.standard_normal((M, num_qo_heads, head_dim), dtype=np.float32), dtype)
+    kv = []
+    for _ in range(2):
+        arr = np.empty((N + pad_rows, num_kv_heads, head_dim), np.uint16)
+        arr[:N] = to_storage_bits(rng.standard_normal((N, num_kv_heads, head_dim),
+                                                      dtype=np.float32), dtype)
+        arr[N:] = _NAN_BITS[dtype] if mode == "test" else 0
+        kv.append(arr)
+    return BlockSparseWorkload(dtype=dtype, num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+                               head_dim=head_dim, row_offsets=row_offsets, col_offsets=col_offsets,
+                               block_indptr=block_indptr, block_indices=block_indices, q=q,
+                               k=kv[0], v=kv[1], seed=seed)
+
+
 def config_lengths(k: int, rng: np.random.Generator) -> dict:
     """Draw the lengths of config k (the first draws of its generator)."""
     if k == 1:
