@@ -21,6 +21,9 @@ Reported alongside in the same JSON line:
     contiguous K / V;
   * ``bsr``: block-sparse prefill, 4096 query rows x 16384 keys in 64 x 64
     blocks, a quarter of the blocks kept, as MFMA utilisation;
+  * ``pod``: a mixed batch over one pool, the causal append of config 5 plus
+    the batch-64 decode of config 2, in one fa_pod launch against the two
+    kernels back to back;
   * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
     from HIP events on its stream), with HBM traffic from rocprofv3 counters
     when the stored counter summary matches the current kernel source;
@@ -225,6 +228,58 @@ class BlockSparseBench(Timed):
             ev[1].record()
 
 
+class PodBench(Timed):
+    """A mixed batch (prefill / append requests + decode requests, one pool):
+    fa_pod, or fa_append then fa_decode when ``separate``."""
+
+    def __init__(self, wl, n_prefill, device="cuda", separate=False):
+        import torch
+        import paged_kv_cache_fa_amd as fa
+        self.fa, self.wl, self.separate = fa, wl, separate
+        self.pools, q, self.strides = _dev(wl, device, 1 << 30)
+        ip, ix, last, qo = wl.kv_indptr, wl.kv_indices, wl.last_page_len, wl.qo_indptr
+        k = int(ip[n_prefill])
+        self.nrows_p = int(qo[n_prefill])
+        self.q_p, self.q_d = q[: self.nrows_p], q[self.nrows_p:]
+        self.pre_h = (np.ascontiguousarray(ip[: n_prefill + 1]), wl.kv_lens[:n_prefill].copy(),
+                      np.ascontiguousarray(qo[: n_prefill + 1]))
+        self.dec_h = ((ip[n_prefill:] - k).astype(np.int32), wl.kv_lens[n_prefill:].copy())
+        self.ptabs = (_i32(ix[:k], device), _i32(ip[: n_prefill + 1], device),
+                      _i32(last[:n_prefill], device))
+        self.dtabs = (_i32(ix[k:], device), _i32(self.dec_h[0], device),
+                      _i32(last[n_prefill:], device))
+        self.qo = _i32(qo[: n_prefill + 1], device)
+        gp = fa.geometry("append", wl.dtype, n_prefill, wl.num_qo_heads, wl.num_kv_heads,
+                         max_qo_tokens=self.nrows_p)
+        gd = fa.geometry("decode", wl.dtype, wl.batch - n_prefill, wl.num_qo_heads,
+                         wl.num_kv_heads)
+        self.pp, self.dp = fa.Plan(gp, device=device), fa.Plan(gd, device=device)
+        self.out_p = torch.empty_like(self.q_p)
+        self.out_d = torch.empty_like(self.q_d)
+        mk = lambda n: torch.empty(n, wl.num_qo_heads, dtype=torch.float32, device=device)
+        self.lse_p, self.lse_d = mk(self.nrows_p), mk(self.q_d.shape[0])
+
+    def step(self, i: int, ev=None):
+        fa = self.fa
+        pool = self.pools[i % len(self.pools)]
+        k, v = pool[:, 0], pool[:, 1]
+        self.pp.plan(*self.pre_h, True)
+        self.dp.plan(*self.dec_h)
+        if ev is not None:
+            ev[0].record()
+        if self.separate:
+            fa.append(self.pp, self.q_p, self.qo, k, v, *self.strides, *self.ptabs,
+                      out=self.out_p, lse=self.lse_p)
+            fa.decode(self.dp, self.q_d, k, v, *self.strides, *self.dtabs, out=self.out_d,
+                      lse=self.lse_d)
+        else:
+            fa.pod(self.pp, self.q_p, self.qo, *self.ptabs, self.dp, self.q_d, *self.dtabs, k, v,
+                   *self.strides, out_p=self.out_p, lse_p=self.lse_p, out_d=self.out_d,
+                   lse_d=self.lse_d)
+        if ev is not None:
+            ev[1].record()
+
+
 class AppendBench(Timed):
     def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, **knobs):
         import torch
@@ -357,7 +412,7 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="decode workload for the headline (1-3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip batch128/cascade/append")
-    ap.add_argument("--parts", default="batch128,cascade,append,fp8,ragged,single,bsr",
+    ap.add_argument("--parts", default="batch128,cascade,append,fp8,ragged,single,bsr,pod",
                     help="comma list of the secondary workloads to run after the headline")
     ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
     ap.add_argument("--copy-probe", action="store_true",
@@ -368,7 +423,7 @@ def main():
               "(DESIGN.md describes how it would shard).", file=sys.stderr)
         sys.exit(2)
     import torch
-    from workloads import CONFIG_NAMES, make_config
+    from workloads import CONFIG_NAMES, config_lengths, make_config
     knobs = {k: int(v) for k, v in (s.split("=") for s in args.knob)}
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
@@ -501,6 +556,32 @@ def main():
                        "flops": bb.flops, "kernel_ms": round(kb, 5), "ms_per_step": round(sb, 5),
                        "blocks_kept": int(len(bw.block_indices))}
         del bb, bw
+        torch.cuda.empty_cache()
+    if "pod" in parts:
+        from workloads import make_workload
+        r5, r2 = np.random.default_rng(5), np.random.default_rng(2)
+        l5, l2 = config_lengths(5, r5), config_lengths(2, r2)
+        lens = np.concatenate([l5["kv_lens"], l2["kv_lens"]])
+        qo = np.concatenate([l5["qo_lens"], np.ones(len(l2["kv_lens"]), np.int64)])
+        wm = make_workload(lens, 32, 8, "bf16", 52, qo_lens=qo, causal=True, name="mixed")
+        n_pre = len(l5["kv_lens"])
+        res = {}
+        for sep in (False, True):
+            pb = PodBench(wm, n_pre, separate=sep)
+            sp, kp = pb.run(max(5, args.steps // 2), max(2, args.warmup // 2))
+            res[sep] = (sp, kp)
+            del pb
+            torch.cuda.empty_cache()
+        f5 = append_flops(make_config(5))
+        line["pod"] = {"workload": "mixed batch over one pool: config5 causal append (16 x 512 "
+                                   "rows onto 4096) + config2 decode (batch 64), 32/8 heads, bf16",
+                       "kernel_ms": round(res[False][1], 5),
+                       "separate_kernels_ms": round(res[True][1], 5),
+                       "speedup": round(res[True][1] / res[False][1], 3),
+                       "ms_per_step": round(res[False][0], 5),
+                       "tokens_per_s": round((wm.rows) / (res[False][0] * 1e-3), 1),
+                       "append_flops": f5}
+        del wm
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -299,6 +299,23 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
                     const int32_t* kv_indptr_d, const int32_t* last_page_len_d, float sm_scale,
                     void* out, float* lse, void* stream);
 
+/* A mixed batch in one launch ([Windows] "Core Features", Attention Kernels:
+ * POD-attention, prefill and decode fused for mixed batching): the append /
+ * prefill requests of prefill_plan and the decode requests of decode_plan, over
+ * the same page pools, run side by side in the same compute units (decode
+ * workgroups next to append workgroups, as in fa_cascade's one-kernel form).
+ * The results are those of fa_append (q_p, qo_indptr_p_d, kv_*_p_d, out_p,
+ * lse_p) and fa_decode (q_d, kv_*_d, out_d, lse_d), bit for bit. Both plans
+ * need the same dtype and heads, 16-bit K/V pages and num_qo_heads /
+ * num_kv_heads <= 4; pools and strides as in fa_decode. Errors as fa_decode. */
+fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* qo_indptr_p_d,
+                 const int32_t* kv_indices_p_d, const int32_t* kv_indptr_p_d,
+                 const int32_t* last_page_len_p_d, void* out_p, float* lse_p,
+                 const fa_plan_t* decode_plan, const void* q_d, const int32_t* kv_indices_d,
+                 const int32_t* kv_indptr_d, const int32_t* last_page_len_d, void* out_d,
+                 float* lse_d, const void* k_pages, const void* v_pages, int64_t page_stride,
+                 int64_t token_stride, int64_t head_stride, float sm_scale, void* stream);
+
 /* Cascade attention over one shared prefix ([Guide] "Cascade attention for
  * shared prefixes"; [DeepDive] "Why This Design Works": the shared prefix is
  * stored once and read once): for every request b,

@@ -8,7 +8,7 @@ library is missing, the import of any entry point raises.
 
 Entry points (same names as the C ABI): ``workspace_size``, ``plan`` /
 ``plan_ragged`` (return a ``Plan``), ``decode``, ``decode_scaled``,
-``decode_ragged``, ``append``, ``append_ragged``, ``cascade``, ``merge_state``,
+``decode_ragged``, ``append``, ``append_ragged``, ``pod``, ``cascade``, ``merge_state``,
 ``merge_states``, ``block_sparse_pages``; and ``single_decode_with_kv_cache`` /
 ``block_sparse_attention``, which plan and run a one-request decode over a
 contiguous K / V and a block-sparse pattern.
@@ -330,6 +330,23 @@ def append(p: Plan, q, qo_indptr, k_pages, v_pages, page_stride: int, token_stri
                            _ptr(kv_indices), _ptr(kv_indptr), _ptr(last_page_len),
                            float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def pod(prefill_plan: Plan, q_p, qo_indptr_p, kv_indices_p, kv_indptr_p, last_page_len_p,
+        decode_plan: Plan, q_d, kv_indices_d, kv_indptr_d, last_page_len_d, k_pages, v_pages,
+        page_stride: int, token_stride: int, head_stride: int, sm_scale: float = 0.0,
+        out_p=None, lse_p=None, out_d=None, lse_d=None, stream=None):
+    """Prefill and decode requests of a mixed batch in one launch (see fa_pod).
+    Returns ((out_p, lse_p), (out_d, lse_d))."""
+    out_p, lse_p = _alloc_out(q_p, out_p, lse_p, q_p.shape[0], q_p.shape[1])
+    out_d, lse_d = _alloc_out(q_d, out_d, lse_d, q_d.shape[0], q_d.shape[1])
+    check(prefill_plan._lib.fa_pod(
+        ctypes.byref(prefill_plan._plan), _ptr(q_p), _ptr(qo_indptr_p), _ptr(kv_indices_p),
+        _ptr(kv_indptr_p), _ptr(last_page_len_p), _ptr(out_p), _ptr(lse_p),
+        ctypes.byref(decode_plan._plan), _ptr(q_d), _ptr(kv_indices_d), _ptr(kv_indptr_d),
+        _ptr(last_page_len_d), _ptr(out_d), _ptr(lse_d), _ptr(k_pages), _ptr(v_pages),
+        page_stride, token_stride, head_stride, float(sm_scale), _stream(stream)))
+    return (out_p, lse_p), (out_d, lse_d)
 
 
 def cascade(prefix_plan: Plan, suffix_plan: Plan, q, k_pages, v_pages, page_stride: int,

@@ -28,7 +28,7 @@ FA_MODE_DECODE, FA_MODE_APPEND = 0, 1
 EXPORTED = [
     "fa_workspace_size", "fa_plan", "fa_plan_info", "fa_plan_tiles", "fa_plan_destroy",
     "fa_plan_ragged", "fa_block_sparse_pages", "fa_decode", "fa_decode_scaled", "fa_decode_ragged", "fa_append",
-    "fa_append_ragged", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
+    "fa_append_ragged", "fa_pod", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
     "fa_last_error",
 ]
 
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH):
         "fa_block_sparse_pages": [P, P, I32, P, I32, I32, P, P, I64, P, P, ctypes.POINTER(I64)],
         "fa_decode_ragged": [PP, P, P, P, I64, I64, P, F32, F32, F32, P, P, P],
         "fa_append_ragged": [PP, P, P, P, P, I64, I64, P, F32, P, P, P],
+        "fa_pod": [PP, P, P, P, P, P, P, P, PP, P, P, P, P, P, P, P, P, I64, I64, I64, F32, P],
         "fa_plan_info": [PP, ctypes.POINTER(PlanStats)],
         "fa_plan_tiles": [PP, ctypes.POINTER(P), ctypes.POINTER(I32), ctypes.POINTER(P),
                           ctypes.POINTER(I32), ctypes.POINTER(P), ctypes.POINTER(I32)],

@@ -636,6 +636,42 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
   return e == hipSuccess ? FA_OK : hip_fail(e, "cascade merge kernel launch");
 }
 
+fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* qo_indptr_p_d,
+                 const int32_t* kv_indices_p_d, const int32_t* kv_indptr_p_d,
+                 const int32_t* last_page_len_p_d, void* out_p, float* lse_p,
+                 const fa_plan_t* decode_plan, const void* q_d, const int32_t* kv_indices_d,
+                 const int32_t* kv_indptr_d, const int32_t* last_page_len_d, void* out_d,
+                 float* lse_d, const void* k_pages, const void* v_pages, int64_t page_stride,
+                 int64_t token_stride, int64_t head_stride, float sm_scale, void* stream) {
+  const PlanImpl* pp = prefill_plan ? impl(prefill_plan) : nullptr;
+  const PlanImpl* dp = decode_plan ? impl(decode_plan) : nullptr;
+  fa_status st = check_run_args(pp, FA_MODE_APPEND, q_p, k_pages, v_pages, page_stride,
+                                token_stride, head_stride, kv_indices_p_d, kv_indptr_p_d,
+                                last_page_len_p_d, out_p);
+  if (st != FA_OK) return st;
+  st = check_run_args(dp, FA_MODE_DECODE, q_d, k_pages, v_pages, page_stride, token_stride,
+                      head_stride, kv_indices_d, kv_indptr_d, last_page_len_d, out_d);
+  if (st != FA_OK) return st;
+  const fa_geometry& ga = pp->geom;
+  const fa_geometry& gd = dp->geom;
+  const int G = gd.num_qo_heads / gd.num_kv_heads;
+  if (!qo_indptr_p_d || ga.dtype != gd.dtype || ga.num_qo_heads != gd.num_qo_heads ||
+      ga.num_kv_heads != gd.num_kv_heads || gd.kv_dtype != gd.dtype || G > 4) {
+    set_error("pod: the plans need the same dtype and heads, 16-bit K/V pages and "
+              "num_qo_heads / num_kv_heads <= 4, and qo_indptr");
+    return FA_ERR_INVALID;
+  }
+  const AttnParams pa = make_params(pp, q_p, k_pages, v_pages, page_stride, token_stride,
+                                    head_stride, kv_indices_p_d, kv_indptr_p_d, last_page_len_p_d,
+                                    qo_indptr_p_d, sm_scale, out_p, lse_p);
+  const AttnParams pd = make_params(dp, q_d, k_pages, v_pages, page_stride, token_stride,
+                                    head_stride, kv_indices_d, kv_indptr_d, last_page_len_d,
+                                    nullptr, sm_scale, out_d, lse_d);
+  const hipError_t e = launch_pod(pd, dp->num_workers, pa, ga.max_tiles, gd.dtype, G,
+                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : hip_fail(e, "pod kernel launch");
+}
+
 fa_status fa_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
                          void* v_out, float* s_out, int64_t n, int32_t heads, int32_t head_dim,
                          int32_t dtype, void* stream) {

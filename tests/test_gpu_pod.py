@@ -1,0 +1,70 @@
+"""GPU parity for a mixed batch in one launch (fa_pod): prefill / append
+requests and decode requests over one page pool give the bits of fa_append and
+fa_decode run separately, and match the fp64 oracle."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle  # noqa: E402
+from gpu_util import assert_close, to_f64, torch_dtype  # noqa: E402
+from workloads import make_workload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def split_mixed(wl, n_prefill):
+    """CSR tables of the first n_prefill requests and of the rest."""
+    ip, ix, last, qo = wl.kv_indptr, wl.kv_indices, wl.last_page_len, wl.qo_indptr
+    k = int(ip[n_prefill])
+    pre = dict(kv_indptr=ip[: n_prefill + 1].copy(), kv_indices=ix[:k].copy(),
+               last=last[:n_prefill].copy(), kv_lens=wl.kv_lens[:n_prefill].copy(),
+               qo_indptr=qo[: n_prefill + 1].copy())
+    dec = dict(kv_indptr=(ip[n_prefill:] - k).astype(np.int32), kv_indices=ix[k:].copy(),
+               last=last[n_prefill:].copy(), kv_lens=wl.kv_lens[n_prefill:].copy())
+    return pre, dec, int(qo[n_prefill])
+
+
+@pytest.mark.parametrize("group,causal", [(4, True), (1, False), (2, True)])
+def test_pod_mixed_batch(group, causal):
+    import torch
+    import paged_kv_cache_fa_amd as fa
+    pre_lens, pre_qo = [300, 64, 1000], [300, 17, 128] if causal else [40, 17, 128]
+    dec_lens = [1, 15, 16, 17, 33, 257, 5, 900, 2000, 48]
+    hkv = 4
+    print(f"[pod] G={group} causal={causal}", flush=True)
+    wl = make_workload(pre_lens + dec_lens, hkv * group, hkv, "bf16", 80 + group,
+                       qo_lens=pre_qo + [1] * len(dec_lens), causal=causal, mode="test",
+                       extra_pages=3)
+    pre, dec, nrows_p = split_mixed(wl, len(pre_lens))
+    dt = torch_dtype("bf16")
+    pool = torch.from_numpy(wl.pool.view(np.int16)).cuda().view(dt)
+    q = torch.from_numpy(wl.q.view(np.int16)).cuda().view(dt)
+    q_p, q_d = q[:nrows_p], q[nrows_p:]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    _, _, ps, hk, d = wl.pool.shape
+    strides = (2 * ps * hk * d, hk * d, d)
+    k, v = pool[:, 0], pool[:, 1]
+    gp = fa.geometry("append", "bf16", len(pre_lens), hkv * group, hkv, max_qo_tokens=nrows_p,
+                     num_cu=32)
+    gd = fa.geometry("decode", "bf16", len(dec_lens), hkv * group, hkv, num_cu=32)
+    pp = fa.plan(gp, pre["kv_indptr"], pre["kv_lens"], pre["qo_indptr"], causal, device="cuda")
+    dp = fa.plan(gd, dec["kv_indptr"], dec["kv_lens"], device="cuda")
+    ptabs = (t(pre["kv_indices"]), t(pre["kv_indptr"]), t(pre["last"]))
+    dtabs = (t(dec["kv_indices"]), t(dec["kv_indptr"]), t(dec["last"]))
+    (op, lp), (od, ld) = fa.pod(pp, q_p, t(pre["qo_indptr"]), *ptabs, dp, q_d, *dtabs, k, v,
+                                *strides)
+    op, lp, od, ld = op.clone(), lp.clone(), od.clone(), ld.clone()
+    rp_o, rp_l = fa.append(pp, q_p, t(pre["qo_indptr"]), k, v, *strides, *ptabs)
+    rd_o, rd_l = fa.decode(dp, q_d, k, v, *strides, *dtabs)
+    torch.cuda.synchronize()
+    assert torch.equal(op, rp_o) and torch.equal(lp, rp_l), "prefill part differs from fa_append"
+    assert torch.equal(od, rd_o) and torch.equal(ld, rd_l), "decode part differs from fa_decode"
+    ref_p = oracle.append(wl.q[:nrows_p], pre["qo_indptr"], wl.pool, "bf16", pre["kv_indptr"],
+                          pre["kv_indices"], pre["last"], 16, causal=causal)
+    assert_close(to_f64(op), to_f64(lp), *ref_p, what="pod prefill")
+    ref_d = oracle.decode(wl.q[nrows_p:], wl.pool, "bf16", dec["kv_indptr"], dec["kv_indices"],
+                          dec["last"], 16)
+    assert_close(to_f64(od), to_f64(ld), *ref_d, what="pod decode")
