@@ -25,8 +25,11 @@ Reported alongside in the same JSON line:
     the batch-64 decode of config 2, in one fa_pod launch against the two
     kernels back to back;
   * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
-    from HIP events on its stream), with HBM traffic from rocprofv3 counters
-    when the stored counter summary matches the current kernel source;
+    from HIP events around each launch on its stream), with HBM traffic from
+    rocprofv3 counters when the stored counter summary matches the current
+    kernel source (a graph of back-to-back calls measured slower per call:
+    it adds the launch gaps); ``host_plan_us`` is the host cost of one
+    fa_plan call;
   * ``cpu_baseline``: the fp64 numpy oracle on the host cores.
 
 Inputs are synthetic (seeded N(0,1)), resident in HBM before the timed
@@ -155,6 +158,18 @@ class DecodeBench(Timed):
                                   out=self.out, lse=self.lse)
         if ev is not None:
             ev[1].record()
+
+
+def plan_us(b: DecodeBench, n: int = 200) -> float:
+    """Host time of one fa_plan call (build + enqueue of the upload)."""
+    import torch
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(n):
+        b.plan.plan(b.indptr_h, b.lens_h)
+    dt = (time.perf_counter() - t) / n
+    torch.cuda.synchronize()
+    return dt * 1e6
 
 
 class RaggedDecodeBench(Timed):
@@ -436,6 +451,7 @@ def main():
     wl = make_config(args.config)
     b = DecodeBench(wl, **knobs)
     step_ms, kernel_ms = b.run(args.steps, args.warmup)
+    host_plan_us = plan_us(b)
     nbytes = algorithmic_bytes(wl)
     gbs = nbytes / (step_ms * 1e-3) / 1e9
     kgbs = nbytes / (kernel_ms * 1e-3) / 1e9
@@ -467,6 +483,7 @@ def main():
                      "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "decode_kernel (one fa_decode call)",
                      "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes},
+        "host_plan_us": round(host_plan_us, 1),
     }
     del b
     torch.cuda.empty_cache()
