@@ -374,7 +374,18 @@ class CascadeBench(Timed):
             ev[1].record()
 
 
-def stored_traffic(kernel_src: str):
+KERNEL_SOURCES = ("decode.hip", "decode_dev.h", "device_common.h", "kernels.h")
+
+
+def kernel_source_sha256() -> str:
+    """SHA-256 over the decode kernel's source files, in a fixed order."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_fa_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel_src: str = ""):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
     if not os.path.exists(COUNTERS_FILE):
@@ -384,8 +395,7 @@ def stored_traffic(kernel_src: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != sha:
+    if fields.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))
@@ -456,7 +466,7 @@ def main():
     gbs = nbytes / (step_ms * 1e-3) / 1e9
     kgbs = nbytes / (kernel_ms * 1e-3) / 1e9
     st = b.plan.info()
-    traffic = stored_traffic(os.path.join(ROOT, "paged_kv_cache_fa_amd", "csrc", "decode.hip"))
+    traffic = stored_traffic()
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
