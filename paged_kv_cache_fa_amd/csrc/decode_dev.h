@@ -24,7 +24,8 @@
 //    halves, 16 bytes per lane (buffer_load_dwordx4);
 //  * loads go through a per-page buffer resource whose size stops at the
 //    last valid token, so slots past last_page_len read as zero without any
-//    memory access and without branches;
+//    memory access and without branches; K/V loads carry the non-temporal
+//    cache policy (the pages are read once);
 //  * a ring of NBUF pages in registers: page j+NBUF-1 is requested while page
 //    j is consumed;
 //  * scores: packed 2-element dot products (v_dot2_f32_bf16 / _f16) and an
@@ -58,6 +59,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
 constexpr int kCoherent = 16;          // cache policy sc1: device-coherent access
+// Cache policy nt (non-temporal) for K/V page loads: every byte is read once,
+// so the lines are streamed rather than kept (batch-64 GQA decode over
+// 9.7k pages: 123 -> 110 us per launch).
+constexpr int kStream = 2;
 
 // One page of the lane's two tokens (r and r+8). 16-bit pools: k[0], k[1]
 // = token r dims [8s, 8s+8) and [64+8s, 64+8s+8), k[2], k[3] the same for
@@ -97,9 +102,9 @@ __device__ __forceinline__ void load_page(PageRegs<KV8>& pr, const AttnParams& p
   const __amdgpu_buffer_rsrc_t rv =
       page_rsrc(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.v) + base), bytes);
 #pragma unroll
-  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, 0);
+  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, kStream);
 #pragma unroll
-  for (int i = 0; i < N; ++i) pr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, 0);
+  for (int i = 0; i < N; ++i) pr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, kStream);
 }
 
 template <int DT, int G, bool KV8>
