@@ -19,6 +19,11 @@ Reported alongside in the same JSON line:
   * ``ragged``: the batch-64 decode over a ragged (contiguous-row) KV cache;
   * ``single``: the single-request decode (32 heads, kv_len 2048, fp16) over a
     contiguous K / V;
+  * ``ragged`` and ``single`` also give ``graph_ms_per_call``: the median time
+    per call of a captured hipGraph of back-to-back run calls over the
+    rotating K/V copies (plan excluded). The single-request step is bound by
+    the host (binding + plan), and its HIP events then time the host's
+    submission gap rather than the kernel;
   * ``bsr``: block-sparse prefill, 4096 query rows x 16384 keys in 64 x 64
     blocks, a quarter of the blocks kept, as MFMA utilisation;
   * ``pod``: a mixed batch over one pool, the causal append of config 5 plus
@@ -126,6 +131,33 @@ class Timed:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in kev]))
 
+    def graph_call_ms(self, calls: int, replays: int = 20) -> float:
+        """Median time per run call of a captured hipGraph of `calls` back-to-back run
+        calls over the rotating input copies (the plan is made once, before capture)."""
+        import torch
+        self.step(0, None)  # plan + one eager call
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(calls):
+                    self.run_call(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) / calls)
+        del g
+        return float(np.median(ts))
+
 
 class DecodeBench(Timed):
     def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, **knobs):
@@ -145,10 +177,15 @@ class DecodeBench(Timed):
         self.lens_h = np.ascontiguousarray(wl.kv_lens.astype(np.int32))
 
     def step(self, i: int, ev=None):
-        pool = self.pools[i % len(self.pools)]
         self.plan.plan(self.indptr_h, self.lens_h)
         if ev is not None:
             ev[0].record()
+        self.run_call(i)
+        if ev is not None:
+            ev[1].record()
+
+    def run_call(self, i: int):
+        pool = self.pools[i % len(self.pools)]
         args = (self.plan, self.q, pool[:, 0], pool[:, 1], *self.strides, self.kv_indices,
                 self.kv_indptr, self.last)
         if self.wl.kv_dtype is None:
@@ -156,8 +193,6 @@ class DecodeBench(Timed):
         else:
             self.fa.decode_scaled(*args, k_scale=self.wl.k_scale, v_scale=self.wl.v_scale,
                                   out=self.out, lse=self.lse)
-        if ev is not None:
-            ev[1].record()
 
 
 def plan_us(b: DecodeBench, n: int = 200) -> float:
@@ -193,14 +228,17 @@ class RaggedDecodeBench(Timed):
         self.lse = torch.empty(rw.rows, rw.num_qo_heads, dtype=torch.float32, device=device)
 
     def step(self, i: int, ev=None):
-        k, v = self.kv[i % len(self.kv)]
         self.plan.plan_ragged(self.offs_h)
         if ev is not None:
             ev[0].record()
-        self.fa.decode_ragged(self.plan, self.q, k, v, k.stride(0), k.stride(1), self.offs,
-                              out=self.out, lse=self.lse)
+        self.run_call(i)
         if ev is not None:
             ev[1].record()
+
+    def run_call(self, i: int):
+        k, v = self.kv[i % len(self.kv)]
+        self.fa.decode_ragged(self.plan, self.q, k, v, k.stride(0), k.stride(1), self.offs,
+                              out=self.out, lse=self.lse)
 
 
 def ragged_bytes(rw) -> int:
@@ -559,6 +597,7 @@ def main():
         rw = make_ragged(wk.kv_lens, wk.num_qo_heads, wk.num_kv_heads, wk.dtype, seed=k)
         br = RaggedDecodeBench(rw, **knobs)
         sr, kr = br.run(args.steps, args.warmup)
+        gr = br.graph_call_ms(len(br.kv))
         nr = ragged_bytes(rw)
         line[part] = {"workload": f"config{k} lengths as a ragged (contiguous) KV cache: "
                                   f"{CONFIG_NAMES[k]}",
@@ -567,6 +606,8 @@ def main():
                       "kernel_GB/s": round(nr / (kr * 1e-3) / 1e9, 2),
                       "tokens_per_s": round(rw.batch / (sr * 1e-3), 1),
                       "ms_per_step": round(sr, 5), "kernel_ms": round(kr, 5),
+                      "graph_ms_per_call": round(gr, 5),
+                      "graph_GB/s": round(nr / (gr * 1e-3) / 1e9, 2),
                       "algorithmic_bytes": nr, "kv_copies": len(br.kv)}
         del br, rw, wk
         torch.cuda.empty_cache()
