@@ -36,6 +36,9 @@ Reported alongside in the same JSON line:
     kernel source (a graph of back-to-back calls measured slower per call:
     it adds the launch gaps); ``host_plan_us`` is the host cost of one
     fa_plan call;
+  * ``roofline.attainable_GB/s``: a plain streaming read of 1 GiB on the same
+    device (fa_probe_stream_read, best launch size), and the decode kernel's
+    bandwidth as a fraction of it;
   * ``cpu_baseline``: the fp64 numpy oracle on the host cores.
 
 Inputs are synthetic (seeded N(0,1)), resident in HBM before the timed
@@ -243,6 +246,31 @@ class DecodeBench(Timed):
         else:
             self.fa.decode_scaled(*args, k_scale=self.wl.k_scale, v_scale=self.wl.v_scale,
                                   out=self.out, lse=self.lse)
+
+
+def attainable_read_gbs(nbytes: int = 1 << 30, launches: int = 10) -> dict:
+    """HBM bandwidth of a plain streaming read on this device (the library's
+    fa_probe_stream_read over a 1 GiB buffer, 4x the Infinity Cache), the best
+    median over a few launch sizes, each launch timed with HIP events."""
+    import torch
+    import paged_kv_cache_fa_amd as fa
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = (0.0, 0)
+    for wg in (512, 1024, 2048, 4096, 8192):
+        for _ in range(3):
+            fa.probe_stream_read(src, flag, wg)
+        ev = [(HipEvent(), HipEvent()) for _ in range(launches)]
+        for a, b in ev:
+            a.record()
+            fa.probe_stream_read(src, flag, wg)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        best = max(best, (nbytes / (ms * 1e-3) / 1e9, wg))
+    del src, flag
+    torch.cuda.empty_cache()
+    return {"GB/s": round(best[0], 1), "workgroups": best[1]}
 
 
 def plan_us(b: DecodeBench, n: int = 200) -> float:
@@ -550,6 +578,7 @@ def main():
     b = DecodeBench(wl, **knobs)
     step_ms, kernel_ms = b.run(args.steps, args.warmup)
     host_plan_us = plan_us(b)
+    att = attainable_read_gbs()
     nbytes = algorithmic_bytes(wl)
     gbs = nbytes / (step_ms * 1e-3) / 1e9
     kgbs = nbytes / (kernel_ms * 1e-3) / 1e9
@@ -580,7 +609,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "decode_kernel (one fa_decode call)",
-                     "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes},
+                     "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes,
+                     "attainable_GB/s": att["GB/s"],
+                     "frac_of_attainable": round(kgbs / att["GB/s"], 4)},
         "host_plan_us": round(host_plan_us, 1),
     }
     del b

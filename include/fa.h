@@ -375,6 +375,19 @@ fa_status fa_merge_states(const void* v, const float* s, int64_t n, int32_t k, i
                           int32_t head_dim, int32_t dtype, void* v_out, float* s_out,
                           void* stream);
 
+/* Measurement utility, not a step of the attention path: reads `bytes` of
+ * device memory at `src` once with 16-byte non-temporal loads from
+ * `workgroups` workgroups of 256 threads (each a contiguous share), the plain
+ * streaming read that the
+ * decode's HBM bandwidth is compared with. The loads are folded by XOR;
+ * `flag` (device, 4 bytes) is written only in the unlikely case that the fold
+ * equals a fixed key, so the probe adds no write traffic. `bytes` must be a
+ * positive multiple of 16 and `src` 16-byte aligned (the caller owns both
+ * buffers). Launch is asynchronous on `stream`. Errors: FA_ERR_INVALID,
+ * FA_ERR_HIP. */
+fa_status fa_probe_stream_read(const void* src, int64_t bytes, uint32_t* flag, int32_t workgroups,
+                               void* stream);
+
 /* Static description of a status code. */
 const char* fa_status_string(fa_status status);
 

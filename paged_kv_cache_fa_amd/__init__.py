@@ -400,3 +400,11 @@ def merge_states(v, s, v_out=None, s_out=None, stream=None):
     check(load().fa_merge_states(_ptr(v), _ptr(s), n, k, heads, d, dtype_code(v.dtype),
                                  _ptr(v_out), _ptr(s_out), _stream(stream)))
     return v_out, s_out
+
+
+def probe_stream_read(src, flag, workgroups: int = 4096, stream=None):
+    """Read all of the device tensor ``src`` once (see fa_probe_stream_read): a
+    plain streaming read to compare the decode's bandwidth with. ``flag`` is a
+    4-byte device tensor the probe may write."""
+    nbytes = src.numel() * src.element_size()
+    check(load().fa_probe_stream_read(_ptr(src), nbytes, _ptr(flag), workgroups, _stream(stream)))

@@ -29,7 +29,7 @@ EXPORTED = [
     "fa_workspace_size", "fa_plan", "fa_plan_info", "fa_plan_tiles", "fa_plan_destroy",
     "fa_plan_ragged", "fa_block_sparse_pages", "fa_decode", "fa_decode_scaled", "fa_decode_ragged", "fa_append",
     "fa_append_ragged", "fa_pod", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
-    "fa_last_error",
+    "fa_last_error", "fa_probe_stream_read",
 ]
 
 
@@ -93,6 +93,7 @@ def load(path: str = LIB_PATH):
                        P, P, P],
         "fa_merge_state": [P, P, P, P, P, P, I64, I32, I32, I32, P],
         "fa_merge_states": [P, P, I64, I32, I32, I32, I32, P, P, P],
+        "fa_probe_stream_read": [P, I64, P, I32, P],
         "fa_status_string": [I32],
         "fa_last_error": [],
     }

@@ -236,3 +236,16 @@ def test_run_calls_reject_host_only_plans():
     st = lib.fa_decode_scaled(ctypes.byref(p._plan), ptr, ptr, ptr, 2048, 256, 128, ptr, ptr, ptr,
                               0.0, 1.0, 1.0, ptr, None, None)
     assert st == fa._lib.FA_ERR_NOT_PLANNED
+
+
+def test_probe_stream_read_rejects_bad_arguments():
+    # argument checks run before any HIP call, so they are testable without a GPU
+    lib = fa.load()
+    buf = (ctypes.c_uint8 * 64)()
+    flag = (ctypes.c_uint32 * 1)()
+    base = ctypes.addressof(buf)
+    aligned = base + (-base % 16)
+    for src, nbytes, wg in ((None, 32, 8), (aligned, 0, 8), (aligned, 24, 8), (aligned + 4, 32, 8),
+                            (aligned, 32, 0)):
+        assert lib.fa_probe_stream_read(src, nbytes, flag, wg, None) == fa._lib.FA_ERR_INVALID
+        assert b"stream-read probe" in lib.fa_last_error()
