@@ -28,8 +28,8 @@ Reported alongside in the same JSON line:
     submission gap rather than the kernel;
   * ``bsr``: block-sparse prefill, 4096 query rows x 16384 keys in 64 x 64
     blocks, a quarter of the blocks kept, as MFMA utilisation;
-  * ``pod``: a mixed batch over one pool, the causal append of config 5 plus
-    the batch-64 decode of config 2, in one fa_pod launch against the two
+  * ``pod``: a mixed batch over one pool, the causal append of 16 x 512 rows
+    plus the batch-64 decode, in one fa_pod launch against the two
     kernels back to back;
   * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
     from HIP timing events around each launch on its stream, created without
@@ -615,7 +615,7 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"config{args.config}: {CONFIG_NAMES[args.config]}",
+        "config": {"workload": CONFIG_NAMES[args.config],
                    "batch": wl.batch, "num_qo_heads": wl.num_qo_heads,
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "page_size": wl.page_size, "kv_tokens": int(wl.kv_lens.sum()),
@@ -640,7 +640,7 @@ def main():
         b3 = DecodeBench(w3, **knobs)
         s3, k3 = b3.run(args.steps, args.warmup)
         n3 = algorithmic_bytes(w3)
-        line["batch128"] = {"workload": f"config3: {CONFIG_NAMES[3]}",
+        line["batch128"] = {"workload": CONFIG_NAMES[3],
                             "GB/s": round(n3 / (s3 * 1e-3) / 1e9, 2),
                             "pct_of_hbm_peak": round(100 * n3 / (s3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                             "tokens_per_s": round(128 / (s3 * 1e-3), 1),
@@ -652,7 +652,7 @@ def main():
         b4 = CascadeBench(w4)
         s4, k4 = b4.run(max(5, args.steps // 2), max(2, args.warmup // 2))
         n4 = algorithmic_bytes(w4)
-        line["cascade"] = {"workload": f"config4: {CONFIG_NAMES[4]}",
+        line["cascade"] = {"workload": CONFIG_NAMES[4],
                            "GB/s": round(n4 / (s4 * 1e-3) / 1e9, 2),
                            "pct_of_hbm_peak": round(100 * n4 / (s4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                            "tokens_per_s": round(256 / (s4 * 1e-3), 1),
@@ -678,7 +678,7 @@ def main():
         b5 = AppendBench(w5)
         s5, k5 = b5.run(max(5, args.steps // 2), max(2, args.warmup // 2))
         f5 = append_flops(w5)
-        line["append"] = {"workload": f"config5: {CONFIG_NAMES[5]}",
+        line["append"] = {"workload": CONFIG_NAMES[5],
                           "TFLOP/s": round(f5 / (k5 * 1e-3) / 1e12, 1),
                           "mfma_utilisation": round(f5 / (k5 * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
                           "flops": f5, "kernel_ms": round(k5, 5), "ms_per_step": round(s5, 5),
@@ -690,7 +690,7 @@ def main():
         b8 = DecodeBench(w8, **knobs)
         s8, k8 = b8.run(args.steps, args.warmup)
         n8 = algorithmic_bytes(w8)
-        line["fp8"] = {"workload": f"config2 with an E4M3 page pool: {CONFIG_NAMES[2]}",
+        line["fp8"] = {"workload": f"{CONFIG_NAMES[2]}, K/V pages in E4M3",
                        "kv_dtype": "e4m3", "k_scale": w8.k_scale, "v_scale": w8.v_scale,
                        "GB/s": round(n8 / (s8 * 1e-3) / 1e9, 2),
                        "pct_of_hbm_peak": round(100 * n8 / (s8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -711,8 +711,7 @@ def main():
         sr, kr = br.run(args.steps, args.warmup)
         gr = br.graph_call_ms(len(br.kv))
         nr = ragged_bytes(rw)
-        line[part] = {"workload": f"config{k} lengths as a ragged (contiguous) KV cache: "
-                                  f"{CONFIG_NAMES[k]}",
+        line[part] = {"workload": f"{CONFIG_NAMES[k]}, ragged (contiguous) K/V",
                       "GB/s": round(nr / (sr * 1e-3) / 1e9, 2),
                       "pct_of_hbm_peak": round(100 * nr / (sr * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
                       "kernel_GB/s": round(nr / (kr * 1e-3) / 1e9, 2),
@@ -753,8 +752,8 @@ def main():
             del pb
             torch.cuda.empty_cache()
         f5 = append_flops(make_config(5))
-        line["pod"] = {"workload": "mixed batch over one pool: config5 causal append (16 x 512 "
-                                   "rows onto 4096) + config2 decode (batch 64), 32/8 heads, bf16",
+        line["pod"] = {"workload": "mixed batch over one pool: causal append (16 x 512 rows onto "
+                                   "4096) + GQA decode (batch 64, kv U[512,4096]), 32/8 heads, bf16",
                        "kernel_ms": round(res[False][1], 5),
                        "separate_kernels_ms": round(res[True][1], 5),
                        "speedup": round(res[True][1] / res[False][1], 3),

@@ -68,13 +68,13 @@ def test_determinism():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_config5_full_size_sampled_rows():
-    print("[config 5] generating", flush=True)
+def test_causal_append_batch16_full_size_sampled_rows():
+    print("[causal append batch 16 x 512] generating", flush=True)
     wl = make_config(5, mode="test")
     dw = DevWorkload(wl)
     plan, out, lse = run_append(dw)
     st = plan.info()
-    print(f"[config 5] tiles {st.num_tiles} splits {st.num_merge}", flush=True)
+    print(f"[causal append batch 16 x 512] tiles {st.num_tiles} splits {st.num_merge}", flush=True)
     rows = []
     for b in range(wl.batch):
         r0 = int(wl.qo_indptr[b])
@@ -82,7 +82,7 @@ def test_config5_full_size_sampled_rows():
     ref = oracle_append(wl, rows=rows)
     o = to_f64(out)[rows]
     l_ = to_f64(lse)[rows]
-    e = assert_close(o, l_, *ref, what="config 5")
-    print(f"[config 5] sampled {len(rows)} rows: max-abs out {e[0]:.3g} lse {e[1]:.3g}",
+    e = assert_close(o, l_, *ref, what="causal append batch 16 x 512")
+    print(f"[causal append batch 16 x 512] sampled {len(rows)} rows: max-abs out {e[0]:.3g} lse {e[1]:.3g}",
           flush=True)
     assert np.isfinite(to_f64(out)).all()

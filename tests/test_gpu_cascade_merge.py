@@ -164,12 +164,13 @@ def test_cascade_graph_capture_with_side_stream(forked):
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
 
 
-def test_config4_full_size():
-    """Config 4 in the launch configuration the benchmark times: one
-    fa_cascade call on one stream (both passes in one kernel); the same bits
-    with the prefix pass forked onto a side stream."""
+def test_cascade_batch256_full_size():
+    """The batch-256 cascade (16384-token shared prefix) in the launch
+    configuration the benchmark times: one fa_cascade call on one stream (both
+    passes in one kernel); the same bits with the prefix pass forked onto a
+    side stream."""
     import torch
-    print("[config 4] generating", flush=True)
+    print("[cascade batch 256] generating", flush=True)
     wl = make_config(4, mode="test")
     dw = DevWorkload(wl)
     out, lse, plans = run_cascade(dw, fused=True)
@@ -177,9 +178,9 @@ def test_config4_full_size():
     o2, l2, _ = run_cascade(dw, *plans, fused=True, side_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     assert torch.equal(out, o2) and torch.equal(lse, l2)
-    print(f"[config 4] prefix tiles {plans[0].info().num_tiles} suffix tiles "
+    print(f"[cascade batch 256] prefix tiles {plans[0].info().num_tiles} suffix tiles "
           f"{plans[1].info().num_tiles}", flush=True)
     reqs = list(range(0, 256, 5)) + [255]
     ref = oracle_cascade(wl, requests=reqs)
-    e = assert_close(to_f64(out)[reqs], to_f64(lse)[reqs], *ref, what="config 4")
-    print(f"[config 4] {len(reqs)} requests: max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
+    e = assert_close(to_f64(out)[reqs], to_f64(lse)[reqs], *ref, what="cascade batch 256")
+    print(f"[cascade batch 256] {len(reqs)} requests: max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)

@@ -9,7 +9,7 @@ sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 import oracle_pins  # noqa: E402
 from gpu_util import (DevWorkload, assert_close, oracle_decode, run_decode,  # noqa: E402
                       to_f64)
-from workloads import make_config, make_workload  # noqa: E402
+from workloads import CONFIG_NAMES, make_config, make_workload  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -89,16 +89,16 @@ def test_determinism():
 
 
 @pytest.mark.parametrize("k", [1, 2, 3])
-def test_configs_full_size(k):
-    print(f"[config {k}] generating", flush=True)
+def test_benchmark_decode_workloads_full_size(k):
+    print(f"[{CONFIG_NAMES[k]}] generating", flush=True)
     wl = make_config(k, mode="test")
     dw = DevWorkload(wl)
     plan, out, lse = run_decode(dw)
     st = plan.info()
-    print(f"[config {k}] tiles {st.num_tiles} merge {st.num_merge} P {st.chunk_pages}", flush=True)
+    print(f"[{CONFIG_NAMES[k]}] tiles {st.num_tiles} merge {st.num_merge} P {st.chunk_pages}", flush=True)
     ref = oracle_decode(wl)
-    e = assert_close(to_f64(out), to_f64(lse), *ref, what=f"config {k}")
-    print(f"[config {k}] max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
+    e = assert_close(to_f64(out), to_f64(lse), *ref, what=CONFIG_NAMES[k])
+    print(f"[{CONFIG_NAMES[k]}] max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
 
 
 def test_graph_static_replan():

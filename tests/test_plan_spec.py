@@ -208,7 +208,7 @@ def test_decode_configs(k):
     assert len(p["tiles"]) <= p["knobs"]["max_tiles"]
 
 
-def test_append_config5_and_cascade_prefix():
+def test_append_batch16_and_cascade_prefix():
     lens = [4608] * 16
     qo = np.concatenate([[0], np.cumsum([512] * 16)])
     p = plan_spec(_indptr(lens), lens, 16, 32, 8, 128, 16, max_batch=16, qo_indptr=qo,
