@@ -578,8 +578,9 @@ def main():
                     help="run one plain 1 GiB device copy first (scales rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
-              "(DESIGN.md describes how it would shard).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path (requests "
+              "or kv heads would shard across GPUs with no exchange; long sequences by key "
+              "range, with an all-gather of partial states and a local merge).", file=sys.stderr)
         sys.exit(2)
     import torch
     from workloads import CONFIG_NAMES, config_lengths, make_config
