@@ -9,7 +9,7 @@ import pytest
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 from gpu_util import (DevWorkload, assert_close, decode_geometry, oracle_decode,  # noqa: E402
                       run_decode, to_f64)
-from workloads import make_config, make_workload  # noqa: E402
+from workloads import CONFIG_NAMES, make_config, make_workload  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,7 @@ def test_fp8_configs_full_size(k):
     dw = DevWorkload(wl)
     plan, out, lse = run_decode(dw)
     st = plan.info()
-    print(f"[fp8 config {k}] tiles {st.num_tiles} merge {st.num_merge} P {st.chunk_pages}",
+    print(f"[fp8 {CONFIG_NAMES[k]}] tiles {st.num_tiles} merge {st.num_merge} P {st.chunk_pages}",
           flush=True)
     e = assert_close(to_f64(out), to_f64(lse), *oracle_decode(wl), what=f"fp8 config {k}")
     print(f"[fp8 config {k}] max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
