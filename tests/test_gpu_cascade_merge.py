@@ -184,3 +184,32 @@ def test_cascade_batch256_full_size():
     ref = oracle_cascade(wl, requests=reqs)
     e = assert_close(to_f64(out)[reqs], to_f64(lse)[reqs], *ref, what="cascade batch 256")
     print(f"[cascade batch 256] {len(reqs)} requests: max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
+
+
+def test_cascade_equals_decode_over_prefix_and_suffix():
+    """fa_cascade against fa_decode over each request's whole page list (the
+    shared prefix's pages, then its own): the two paths, and the oracle's
+    direct attention over prefix ++ suffix, agree within the tolerances."""
+    import dataclasses
+    from gpu_util import run_decode
+    wl = make_cascade(512, [5, 16, 17, 300, 1, 64, 0, 33], 32, 8, "bf16", 23, mode="test")
+    dw = DevWorkload(wl)
+    out_c, lse_c, _ = run_cascade(dw, fused=True, prefix={"num_cu": 8}, suffix={"num_cu": 8})
+    pre = wl.prefix_indices[wl.prefix_indptr[0]:wl.prefix_indptr[1]]
+    lists = [np.concatenate([pre, wl.kv_indices[wl.kv_indptr[b]:wl.kv_indptr[b + 1]]])
+             for b in range(wl.batch)]
+    indptr = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int32)
+    whole = dataclasses.replace(
+        wl, kv_lens=(wl.kv_lens + wl.prefix_len).astype(np.int32), kv_indptr=indptr,
+        kv_indices=np.concatenate(lists).astype(np.int32), last_page_len=wl.last_page_len.copy(),
+        prefix_len=0, prefix_indptr=None, prefix_indices=None, prefix_last_page_len=None)
+    # a suffix of 0 tokens leaves the prefix's full last page as the request's last page
+    whole.last_page_len[wl.kv_lens == 0] = 16
+    _, out_d, lse_d = run_decode(DevWorkload(whole), num_cu=8)
+    direct = oracle.cascade_direct(wl.q, wl.pool, wl.dtype, wl.prefix_indptr, wl.prefix_indices,
+                                   wl.prefix_last_page_len, wl.kv_indptr, wl.kv_indices,
+                                   wl.last_page_len, wl.page_size)
+    assert_close(to_f64(out_c), to_f64(lse_c), *direct, what="cascade vs direct")
+    assert_close(to_f64(out_d), to_f64(lse_d), *direct, what="decode over prefix ++ suffix")
+    assert_close(to_f64(out_c), to_f64(lse_c), to_f64(out_d), to_f64(lse_d),
+                 what="cascade vs decode")
