@@ -163,23 +163,6 @@ def validate(kv_indptr, kv_lens, batch, num_qo_heads, num_kv_heads, head_dim, pa
             raise PlanSpecError("INVALID", "too many query rows for max_qo_tokens")
 
 
-def _deal(costs):
-    """Deal items (in descending cost, stable) to XCD_BINS bins, each to the
-    bin with the least total cost (lowest index on ties). Returns the item
-    order (bin-major, dealing order inside a bin) and the bin offsets."""
-    bin_of, bcost = [0] * len(costs), [0] * XCD_BINS
-    dealt = sorted(range(len(costs)), key=lambda i: -costs[i])
-    for i in dealt:
-        x = min(range(XCD_BINS), key=lambda j: bcost[j])
-        bin_of[i] = x
-        bcost[x] += costs[i]
-    order = sorted(dealt, key=lambda i: bin_of[i])      # stable: keeps dealing order
-    ptr = [0]
-    for x in range(XCD_BINS):
-        ptr.append(ptr[-1] + sum(1 for i in order if bin_of[i] == x))
-    return order, ptr
-
-
 def _decode_plan(kv_indptr, kv_lens, batch, Hkv, ps, k, c0):
     S = k["num_cu"] * k["tiles_per_cu"]
     NS = max(1, S * k["pieces_per_worker"] // Hkv)

@@ -5,7 +5,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpkfa.so")
+# The in-tree build; PKFA_LIB names another build of the same ABI to load
+# instead (the tests use it for an AddressSanitizer build of the host paths).
+LIB_PATH = os.environ.get("PKFA_LIB") or os.path.join(HERE, "libpkfa.so")
 
 FA_OK = 0
 FA_ERR_INVALID = -1

@@ -114,7 +114,6 @@ AttnParams make_params(const PlanImpl* pl, const void* q, const void* k, const v
   p.kv_offsets = nullptr;
   p.num_qo_heads = pl->geom.num_qo_heads;
   p.num_kv_heads = pl->geom.num_kv_heads;
-  p.causal = pl->causal;
   p.defer_merge = 0;
   return p;
 }
@@ -196,17 +195,20 @@ fa_status plan_and_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_
     set_error("device workspace needs %zu bytes, 256-byte aligned", pl->lay.dev_bytes);
     return FA_ERR_WORKSPACE;
   }
-  // Queue heads and arrival counters return to zero at the end of every run
-  // call; clear them once per device workspace (fresh memory holds garbage).
+  // Arrival counters return to zero at the end of every run call; clear them
+  // when this plan first uses a device workspace, and again whenever a new
+  // geometry moves or grows the counter region (fresh memory holds garbage).
   const size_t cbytes = pl->lay.dev_part_lse - pl->lay.dev_counters;
   hipError_t e = hipSuccess;
-  if (pl->zeroed_ws != dev_ws || pl->zeroed_bytes < cbytes) {
+  if (pl->zeroed_ws != dev_ws || pl->zeroed_off != pl->lay.dev_counters ||
+      pl->zeroed_bytes < cbytes) {
     e = hipMemsetAsync(static_cast<uint8_t*>(dev_ws) + pl->lay.dev_counters, 0, cbytes, s);
     if (e != hipSuccess) {
       pl->planned = 0;
       return hip_fail(e, "hipMemsetAsync (arrival counters)");
     }
     pl->zeroed_ws = dev_ws;
+    pl->zeroed_off = pl->lay.dev_counters;
     pl->zeroed_bytes = cbytes;
   }
   const size_t bytes = pl->lay.tiles + (size_t)pl->num_tiles * kTileInts * 4;
@@ -630,9 +632,11 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
     if (e == hipSuccess) e = hipStreamWaitEvent(s, static_cast<hipEvent_t>(sp->join2_event), 0);
     if (e != hipSuccess) return hip_fail(e, "cascade join");
   }
+  // grid from the suffix geometry's max_batch; the kernel reads the batch of
+  // the current suffix plan from its uploaded header
   e = launch_cascade_merge(pa.header, pa.merge, pa.part_o, pa.part_lse, prefix_out, prefix_lse,
-                           suffix_out, suffix_lse, out, lse, sp->batch, gs.num_qo_heads, G,
-                           gs.num_kv_heads, gp.qo_tile, gs.dtype, s);
+                           suffix_out, suffix_lse, out, lse, ps.header, gs.max_batch,
+                           gs.num_qo_heads, G, gs.num_kv_heads, gp.qo_tile, gs.dtype, s);
   return e == hipSuccess ? FA_OK : hip_fail(e, "cascade merge kernel launch");
 }
 

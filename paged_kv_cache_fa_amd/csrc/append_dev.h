@@ -161,8 +161,11 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
   const int g = col / PT, pos = col % PT;
   const int head = hk * G + g;
   const bool qvalid = pos < rows;
-  const int qpos_min = p.causal ? kv_len - qo_len + (q0 - qo_beg) : 0x7fffffff;
-  const int qpos = p.causal ? qpos_min + pos : 0x7fffffff;
+  // the mask mode comes from the uploaded plan (header word 4), so a captured
+  // launch follows a re-plan that switches it
+  const bool causal = __builtin_amdgcn_readfirstlane(p.header[4]) != 0;
+  const int qpos_min = causal ? kv_len - qo_len + (q0 - qo_beg) : 0x7fffffff;
+  const int qpos = causal ? qpos_min + pos : 0x7fffffff;
 
   // Q^T operand: 8 blocks of 16 dims, this lane supplies dims 16 kb + 8 h .. +8
   u32x4 qf[8];

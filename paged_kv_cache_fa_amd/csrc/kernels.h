@@ -32,7 +32,6 @@ struct AttnParams {
   float v_scale;              // per-tensor V scale, applied to the final output
   int32_t num_qo_heads;
   int32_t num_kv_heads;
-  int32_t causal;
   int32_t defer_merge;        // append: split tiles only publish their partial states
 };
 
@@ -54,13 +53,14 @@ hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, c
                               hipStream_t s);
 // Cascade combine: out[r, h] = merge of the shared-prefix state of (r, h)
 // (the prefix plan's deferred chunk partials, or prefix_out / prefix_lse when
-// that plan did not split) with the suffix state.
+// that plan did not split) with the suffix state, for the suffix plan's
+// current batch (header word 2, at most max_n rows: the grid's size).
 hipError_t launch_cascade_merge(const int32_t* prefix_header, const int32_t* prefix_merge,
                                 const float* part_o, const float* part_lse, const void* prefix_out,
                                 const float* prefix_lse, const void* suffix_out,
-                                const float* suffix_lse, void* out, float* lse, int64_t n,
-                                int heads, int group, int num_kv_heads, int qo_tile, int dtype,
-                                hipStream_t s);
+                                const float* suffix_lse, void* out, float* lse,
+                                const int32_t* suffix_header, int64_t max_n, int heads, int group,
+                                int num_kv_heads, int qo_tile, int dtype, hipStream_t s);
 hipError_t launch_merge_states(const void* v, const float* s, int64_t n, int k, int heads,
                                int head_dim, int dtype, void* vo, float* so, hipStream_t st);
 

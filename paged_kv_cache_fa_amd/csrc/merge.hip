@@ -132,8 +132,9 @@ template <int DT>
 __global__ __launch_bounds__(256) void cascade_merge_kernel(
     const int32_t* header, const int32_t* merge, const float* part_o, const float* part_lse,
     const void* po, const float* pls, const void* so, const float* sls, void* vo, float* lo,
-    int64_t n, int heads, int group, int num_kv_heads, int qo_tile) {
+    const int32_t* suffix_header, int heads, int group, int num_kv_heads, int qo_tile) {
   const int num_merge = header[1];
+  const int64_t n = suffix_header[2];  // the suffix plan's batch (graph replays follow re-plans)
   const int64_t total = n * heads * 16;
   for (int64_t it = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; it < total;
        it += (int64_t)gridDim.x * blockDim.x) {
@@ -219,20 +220,20 @@ hipError_t launch_merge_states(const void* v, const float* sv, int64_t n, int k,
 hipError_t launch_cascade_merge(const int32_t* prefix_header, const int32_t* prefix_merge,
                                 const float* part_o, const float* part_lse, const void* prefix_out,
                                 const float* prefix_lse, const void* suffix_out,
-                                const float* suffix_lse, void* out, float* lse, int64_t n,
-                                int heads, int group, int num_kv_heads, int qo_tile, int dtype,
-                                hipStream_t s) {
-  const int64_t total = n * heads * 16;
+                                const float* suffix_lse, void* out, float* lse,
+                                const int32_t* suffix_header, int64_t max_n, int heads, int group,
+                                int num_kv_heads, int qo_tile, int dtype, hipStream_t s) {
+  const int64_t total = max_n * heads * 16;
   if (total <= 0) return hipSuccess;
   const int grid = grid_for(total);
   if (dtype == FA_BF16)
     hipLaunchKernelGGL(cascade_merge_kernel<FA_BF16>, dim3(grid), dim3(256), 0, s, prefix_header,
                        prefix_merge, part_o, part_lse, prefix_out, prefix_lse, suffix_out,
-                       suffix_lse, out, lse, n, heads, group, num_kv_heads, qo_tile);
+                       suffix_lse, out, lse, suffix_header, heads, group, num_kv_heads, qo_tile);
   else
     hipLaunchKernelGGL(cascade_merge_kernel<FA_F16>, dim3(grid), dim3(256), 0, s, prefix_header,
                        prefix_merge, part_o, part_lse, prefix_out, prefix_lse, suffix_out,
-                       suffix_lse, out, lse, n, heads, group, num_kv_heads, qo_tile);
+                       suffix_lse, out, lse, suffix_header, heads, group, num_kv_heads, qo_tile);
   return hipGetLastError();
 }
 

@@ -51,8 +51,9 @@ struct PlanImpl {
   void* host_ws;
   void* dev_ws;
   void* upload_event;  // hipEvent_t recorded after the copy out of host_ws
-  void* zeroed_ws;     // device workspace whose counters were cleared
-  size_t zeroed_bytes;
+  void* zeroed_ws;     // device workspace whose counters were cleared,
+  size_t zeroed_off;   // at this offset,
+  size_t zeroed_bytes; // this many bytes
   void* fork_event;    // hipEvent_t fork / join events for the cascade call's streams
   void* join_event;
   void* join2_event;

@@ -145,8 +145,10 @@ def test_graph_static_replan():
             last_buf.copy_(torch.from_numpy(wl_.last_page_len).cuda())
             q_buf.copy_(torch.from_numpy(wl_.q.view(np.int16)).cuda().view(q_buf.dtype))
             torch.cuda.synchronize()
+            # the upload and the replay are ordered by stream s
             plan.plan(wl_.kv_indptr, wl_.kv_lens, stream=s)
-            g.replay()
+            with torch.cuda.stream(s):
+                g.replay()
             torch.cuda.synchronize()
             wref = wl_
             wref_pool = pool_np
