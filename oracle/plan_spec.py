@@ -81,6 +81,7 @@ SUPPORTED_PAGE_SIZE = (16,)
 SUPPORTED_GROUP = (1, 2, 4, 8)
 MAX_PIECE_PAGES = 128
 XCD_BINS = 8
+APPEND_COLS = 256  # query columns of an append tile (G heads x APPEND_COLS / G rows)
 PIECES_PER_WORKER = 1
 PIECE_COST_PAGES = {"16-bit": 4, "e4m3": 8}
 
@@ -103,15 +104,16 @@ def default_knobs(num_kv_heads: int, max_batch: int, max_qo_tokens: int, is_appe
                   max_merge: int = 0, pieces_per_worker: int = 0, group: int = 1) -> dict:
     """Fill zero knobs with defaults; capacities are the worst case of the procedure.
 
-    An append q tile holds at most ``128 / group`` rows (the library's tiles
-    have 128 query columns = group heads x rows); that is also the default."""
+    An append q tile holds at most ``APPEND_COLS / group`` rows (the library's
+    tiles have APPEND_COLS query columns = group heads x rows); that is also
+    the default."""
     num_cu = num_cu or 256
     pieces_per_worker = 0 if is_append else (pieces_per_worker or PIECES_PER_WORKER)
     tiles_per_cu = tiles_per_cu or (2 if is_append else 4)
     min_chunk_pages = min_chunk_pages or 1
-    qo_tile = (qo_tile or 128 // group) if is_append else 1
-    if is_append and qo_tile > 128 // group:
-        raise PlanSpecError("UNSUPPORTED", "qo_tile larger than 128 / group")
+    qo_tile = (qo_tile or APPEND_COLS // group) if is_append else 1
+    if is_append and qo_tile > APPEND_COLS // group:
+        raise PlanSpecError("UNSUPPORTED", "qo_tile larger than APPEND_COLS / group")
     target = num_cu * tiles_per_cu
     if is_append:
         n_qtiles = max_batch + _cdiv(max_qo_tokens, qo_tile)

@@ -8,9 +8,9 @@ namespace {
 template <int DT, int G>
 __global__ __launch_bounds__(app::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void append_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * app::kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * app::VLayout<3>::kBufElems];
   __shared__ int s_flag;
-  app::append_worker<DT, G>(p, (int)blockIdx.x, (int)gridDim.x, smem, s_flag);
+  app::append_worker<DT, G, 3>(p, (int)blockIdx.x, (int)gridDim.x, smem, s_flag);
 }
 
 template <int DT>

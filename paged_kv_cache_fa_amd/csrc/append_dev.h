@@ -14,17 +14,18 @@
 //  * tiles come in 8 bins, one per XCD: the planner deals each (request, kv
 //    head) group to one bin, so the q tiles that read the same keys run side
 //    by side on one XCD and share its L2;
-//  * one 256-thread workgroup (4 waves) per tile {request, kv head, up to
-//    128/G query positions, key chunk}. The tile's 128 query columns are the
-//    G heads of the kv head's group x 128/G positions (GQA packing): every
-//    K/V block staged in LDS feeds all of them. Wave w owns columns
-//    32w .. 32w+31;
-//  * blocks of 64 keys: each thread fetches 16 bytes of 4 token rows of K and
-//    of V (one row from each of the block's 4 pages, so every load's page is
-//    uniform across the workgroup) through a per-page buffer resource that
-//    ends at the last valid token: keys past the end read as zero. The
-//    registers are written to a double-buffered LDS after the current block's
-//    math, one barrier per block;
+//  * one 512-thread workgroup (8 waves, 2 per SIMD) per tile {request, kv
+//    head, up to 256/G query positions, key chunk}. The tile's 256 query
+//    columns are the G heads of the kv head's group x 256/G positions (GQA
+//    packing): every K/V block staged in LDS feeds all of them, so a block is
+//    fetched once per 256 columns. Wave w owns columns 32w .. 32w+31;
+//  * blocks of 64 keys: waves 0-3 stage K and waves 4-7 stage V (one of each
+//    per SIMD); each of their threads fetches 16 bytes of 4 token rows (one
+//    row from each of the block's 4 pages, so every load's page is uniform
+//    across the wave) through a per-page buffer resource that ends at the
+//    last valid token: keys past the end read as zero. The registers are
+//    written to a double-buffered LDS after the current block's math, one
+//    barrier per block;
 //  * inside a block, key k sits in LDS slot 4 (k mod 16) + k / 16, so one
 //    thread's 4 rows form 4 consecutive slots: V is stored transposed
 //    (dim-major, 4 slots per 8-byte store) without any exchange. The
@@ -60,12 +61,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCols = 32 * kWaves;  // query columns of a tile
 constexpr int kBlockKeys = 64;
 constexpr int kKStride = 136;  // 16-bit elements per K slot row in LDS (128 dims + 8 pad)
 constexpr int kKElems = kBlockKeys * kKStride;
-constexpr int kVElems = 128 * kBlockKeys;  // V^T: 128 dim rows x 64 slots (swizzled)
-constexpr int kBufElems = kKElems + kVElems;
 constexpr int kCoherent = 16;          // cache policy sc1: device-coherent access
 constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 2^8
 
@@ -94,20 +95,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p)
 // MFMA A operand of a lane of half h for slot tile kt, group kh is the 8
 // slots {32 kt + 16 kh + 4 h + e, 32 kt + 16 kh + 8 + 4 h + e : e < 4}, i.e.
 // the 4-slot groups tr and tr + 2 (tr = 8 kt + 4 kh + h): they share the
-// 16-byte unit 4 kt + 2 kh + h (first and second half). Units are XOR-swizzled
-// with vswz(d), which depends on d mod 32 only (the 4 dim tiles of a lane
-// differ by immediate offsets); the 8 rows read together (consecutive d) get
-// distinct units, and so do the 16 transposing 8-byte stores issued together.
-__device__ __forceinline__ int vswz(int d) { return (((d >> 3) & 3) << 1) ^ (d & 7); }
-// Byte offset inside row d of 4-slot group tr (slots 4 tr .. 4 tr + 3).
-__device__ __forceinline__ int vgroup_off(int tr, int d) {
-  return 16 * ((2 * (tr >> 2) + (tr & 1)) ^ vswz(d)) + 8 * ((tr >> 1) & 1);
-}
+// 16-byte unit c = 4 kt + 2 kh + h (first and second half). Unit c of row d
+// sits at position c ^ swz(d) of a row of kRow elements; swz depends on
+// d mod 32 only (the 4 dim tiles of a lane differ by immediate offsets).
+// Two layouts, chosen by measuring the LDS bank-conflict counter on the
+// operand reads (16 consecutive rows, one unit each, per lane half) and the
+// staging threads' transposing 8-byte stores:
+//  * kRow 96 (64 slots + 32 padding, 192 bytes), swz(d) = (d / 4) mod 8:
+//    no conflict cycles on either (the pipelined loop, one workgroup per CU);
+//  * kRow 64 (unpadded), swz(d) = 2 ((d / 8) mod 4) ^ (d mod 8): conflict-free
+//    stores, about 4 conflict cycles per operand read; it keeps two LDS
+//    stages within half a CU's LDS (the loop that shares its CU).
+template <int STAGES>
+struct VLayout {
+  static constexpr bool kPadded = STAGES == 3;
+  static constexpr int kRow = kPadded ? 96 : 64;
+  static constexpr int kElems = 128 * kRow;
+  static constexpr int kBufElems = kKElems + kElems;  // one LDS stage: K slots + V^T
+  __device__ __forceinline__ static int swz(int d) {
+    return kPadded ? (d >> 2) & 7 : (((d >> 3) & 3) << 1) ^ (d & 7);
+  }
+  // swz(8 dg + 2 w + hi) = swz_base(dg) ^ swz_step(w, hi) for w < 4, hi < 2
+  __device__ __forceinline__ static int swz_base(int dg) {
+    return kPadded ? (2 * dg) & 6 : (dg & 3) << 1;
+  }
+  __device__ __forceinline__ static constexpr int swz_step(int w, int hi) {
+    return kPadded ? w >> 1 : (2 * w) ^ hi;
+  }
+};
 
 // Key (0..63 within the block) held in register r of score tile kt by a lane
-// of half h: slot 32 kt + 8 (r / 4) + 4 h + r % 4, key = slot / 4 + 16 (slot % 4).
-__device__ __forceinline__ constexpr int reg_key(int kt, int r, int h) {
-  return 8 * kt + 2 * (r >> 2) + h + 16 * (r & 3);
+// of half h: slot 32 kt + 8 (r / 4) + 4 h + r % 4, key = slot / 4 + 16 (slot % 4),
+// i.e. reg_key0(kt, r) + h (a compile-time constant plus the lane half).
+__device__ __forceinline__ constexpr int reg_key0(int kt, int r) {
+  return 8 * kt + 2 * (r >> 2) + 16 * (r & 3);
 }
 
 // Max / sum of a value over the lane pair (l, l ^ 32), in every lane.
@@ -120,10 +141,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DT, int G>
+// STAGES: LDS buffers of the block loop, 3 (software pipeline: the scores of
+// block j+1 beside the softmax of block j) or 2 (one block at a time, for a
+// workgroup that shares its CU).
+template <int DT, int G, int STAGES>
 __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, uint16_t* smem,
                                             int& s_flag) {
-  constexpr int PT = 128 / G;  // query positions per tile
+  constexpr int PT = kCols / G;  // query positions per tile
+  using VL = VLayout<STAGES>;
+  constexpr int kBufElems = VL::kBufElems;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -187,15 +213,19 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
   const int nblocks = key1 > key0 ? (key1 - key0 + kBlockKeys - 1) / kBlockKeys : 0;
   const int first_page = key0 >> 4;  // chunks start on a page boundary
 
-  // --- K/V staging: thread = (token row tr of each of the 4 pages, dims 8 dg..) --
-  // tid bits [1:0] and [5:4] give dg, bits [3:2] and [7:6] give tr: a wave
-  // reads 4 whole token rows per load, and 16 lanes that store together cover
-  // 4 dg x 4 tr (conflict-free V^T stores under vswz).
-  const int dg = (tid & 3) | ((tid >> 2) & 12), tr = ((tid >> 2) & 3) | ((tid >> 4) & 12);
+  // --- K/V staging: waves 0-3 stage K, waves 4-7 V (wave-uniform role);
+  // thread st = tid mod 256 of a role = (token row tr of each of the 4 pages,
+  // dims 8 dg..): st bits [1:0] and [5:4] give dg, bits [3:2] and [7:6] give
+  // tr: a wave reads 4 whole token rows per load, and 16 lanes that store
+  // together cover 4 dg x 4 tr (conflict-free V^T stores under vswz).
+  const bool stage_v = wave >= 4;
+  const int st = tid & 255;
+  const int dg = (st & 3) | ((st >> 2) & 12), tr = ((st >> 2) & 3) | ((st >> 4) & 12);
   const uint32_t row_bytes = (uint32_t)p.token_stride * 2u;
   const uint32_t ld_off = (uint32_t)tr * row_bytes + 16u * dg;
   const int64_t head_off = (int64_t)hk * p.head_stride;
-  u32x4 stk[4], stv[4];
+  const uint16_t* src = stage_v ? p.v : p.k;
+  u32x4 stg[4];
   int pid[4];
   // page ids of a block: lanes 0..3 load them (index clamped to the request's
   // last page: a block past the end fetches nothing, see nbytes below), and
@@ -215,121 +245,203 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
       const int nbytes =
           __builtin_amdgcn_readfirstlane(min(max(key1 - kstart, 0), 16) * (int)row_bytes);
       const int64_t base = (int64_t)pid[i] * p.page_stride + head_off;
-      const __amdgpu_buffer_rsrc_t rk =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + base), 0, nbytes, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rv =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + base), 0, nbytes, 0x00020000);
-      stk[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ld_off, 0, 0);
-      stv[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, ld_off, 0, 0);
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(src + base), 0, nbytes, 0x00020000);
+      stg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, ld_off, 0, 0);
     }
   };
   auto store = [&](int buf) {
     uint16_t* sk = smem + buf * kBufElems;
     uint16_t* sv = sk + kKElems;
+    if (!stage_v) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(sk + (4 * tr + i) * kKStride + 8 * dg) = stk[i];
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(sk + (4 * tr + i) * kKStride + 8 * dg) = stg[i];
+      return;
+    }
+    // Dims d = 8 dg + 2 w and d + 1 go to V^T rows d, d + 1: the thread's 4
+    // slots 4 tr .. 4 tr + 3 are the first (tr bit 1 clear) or second half of
+    // unit 2 (tr >> 2) + (tr & 1), at position unit ^ swz(row). u and the
+    // row base are recomputed here on every call (the empty asm hides that
+    // they do not change), so the compiler does not keep 8 loop-invariant
+    // addresses live through the block loop.
+    int u = (2 * (tr >> 2) + (tr & 1)) ^ VL::swz_base(dg);
+    int vbase = 2 * VL::kRow * 8 * dg + 8 * ((tr >> 1) & 1);
+    asm volatile("" : "+v"(u), "+v"(vbase));
+    char* sv8 = reinterpret_cast<char*>(sv) + vbase;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = stv[0][w], a1 = stv[1][w], a2 = stv[2][w], a3 = stv[3][w];
+      const uint32_t a0 = stg[0][w], a1 = stg[1][w], a2 = stg[2][w], a3 = stg[3][w];
       const u32x2 lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
                         __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
       const u32x2 hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
                         __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-      const int d = 8 * dg + 2 * w;
-      char* sv8 = reinterpret_cast<char*>(sv);
-      *reinterpret_cast<u32x2*>(sv8 + d * 2 * kBlockKeys + vgroup_off(tr, d)) = lo;
-      *reinterpret_cast<u32x2*>(sv8 + (d + 1) * 2 * kBlockKeys + vgroup_off(tr, d + 1)) = hi;
+      *reinterpret_cast<u32x2*>(sv8 + 2 * w * 2 * VL::kRow + 16 * (u ^ VL::swz_step(w, 0))) = lo;
+      *reinterpret_cast<u32x2*>(sv8 + (2 * w + 1) * 2 * VL::kRow + 16 * (u ^ VL::swz_step(w, 1))) =
+          hi;
     }
   };
 
-  // one block of 64 keys from LDS buffer buf
-  // one block of 64 keys from LDS buffer buf, processed as two halves of 32
-  // slots: the softmax of one half overlaps the MFMAs of the other
-  auto block = [&](int buf, int blk, bool need_mask) {
-    const uint16_t* sk = smem + buf * kBufElems;
-    const uint16_t* sv = sk + kKElems;
-    f32x16 s[2];
+  // S^T of one 64-key block from its LDS buffer (two 32-slot halves, each a
+  // chain of 8 MFMAs over the 128 dims). The K operands are read from LDS
+  // KPRE at a time ahead of their MFMAs, so a chain waits for LDS 8 / KPRE
+  // times.
+  constexpr int KPRE = 4;
+  auto scores_half = [&](const uint16_t* sk, int kt, f32x16& s_out) {
+    const uint16_t* krow = sk + (32 * kt + jq) * kKStride + 8 * h;
+    f32x16 acc = {};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const uint16_t* krow = sk + (32 * kt + jq) * kKStride + 8 * h;
-      s[kt] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(krow), qf[0], f32x16{});
+    for (int k4 = 0; k4 < 8; k4 += KPRE) {
+      u32x4 ka[KPRE];
 #pragma unroll
-      for (int kb = 1; kb < 8; ++kb)
-        s[kt] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(krow + 16 * kb), qf[kb], s[kt]);
+      for (int i = 0; i < KPRE; ++i) ka[i] = *reinterpret_cast<const u32x4*>(krow + 16 * (k4 + i));
+#pragma unroll
+      for (int i = 0; i < KPRE; ++i) acc = Mfma<DT>::run(ka[i], qf[k4 + i], acc);
     }
-    if (need_mask) {  // wave-uniform
-      const int kb0 = key0 + blk * kBlockKeys;
-      const int lim = min(key1 - 1, qpos) - kb0;  // last visible key of this column, in-block
+    s_out = acc;
+  };
+
+  // The online softmax of one block, in three steps that both loops run in
+  // the same order (so they give the same bits): the mask, the row max with
+  // the (lazy) rescale of the running state, and the probabilities with
+  // O^T += V^T P^T.
+  auto mask_block = [&](f32x16 (&s)[2], int blk) {
+    const int kb0 = key0 + blk * kBlockKeys;
+    if (kb0 + kBlockKeys > key1 || kb0 + kBlockKeys - 1 > qpos_min) {  // wave-uniform
+      // last visible key of this column, in-block, less the lane half
+      const int lim = min(key1 - 1, qpos) - kb0 - h;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          s[kt][r] = reg_key(kt, r, h) > lim ? kNegInf : s[kt][r];
+          s[kt][r] = reg_key0(kt, r) > lim ? kNegInf : s[kt][r];
     }
+  };
+  auto row_max = [&](const f32x16 (&s)[2]) {
+    float mx = kNegInf;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      float mx = kNegInf;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      mx = pair_max(mx);
-      const float mxs = mx * scale;
-      const bool need = mxs > m + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? fast_exp2(m - mxs) : 1.f;
-        m = need ? mxs : m;
-        l *= alpha;
+    mx = pair_max(mx);
+    const float mxs = mx * scale;
+    const bool need = mxs > m + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m - mxs) : 1.f;
+      m = need ? mxs : m;
+      l *= alpha;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-      const float ms = m == kNegInf ? 0.f : m;
-      // O^T += V^T P^T over the half's 2 slot groups of 16 (the row sum is
-      // kept in fp32: the LSE must not carry the operand rounding)
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+  };
+  auto exp_pv = [&](const f32x16 (&s)[2], const uint16_t* sv) {
+    const float ms = m == kNegInf ? 0.f : m;
+    // probabilities, packed to the input type as the B operand of P V (the
+    // row sum is kept in fp32: the LSE must not carry the operand rounding)
+    u32x4 pb[2][2];
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        u32x4 pb;
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kt][8 * kh + 2 * e], scale, -ms));
           const float p1 = fast_exp2(__builtin_fmaf(s[kt][8 * kh + 2 * e + 1], scale, -ms));
           l += p0 + p1;
-          pb[e] = Elt<DT>::pack(p0, p1);
+          pb[kt][kh][e] = Elt<DT>::pack(p0, p1);
         }
-        const int unit = (4 * kt + 2 * kh + h) ^ vswz(jq);
+    // O^T += V^T P^T over the block's 4 slot groups of 16
+    const uint16_t* vrow = sv + jq * VL::kRow;
+    const int sw = VL::swz(jq);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint16_t* vp = sv + (32 * db + jq) * kBlockKeys + 8 * unit;
-          o[db] = Mfma<DT>::run(*reinterpret_cast<const u32x4*>(vp), pb, o[db]);
-        }
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int unit = (4 * kt + 2 * kh + h) ^ sw;
+        u32x4 va[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          va[db] = *reinterpret_cast<const u32x4*>(vrow + 32 * db * VL::kRow + 8 * unit);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = Mfma<DT>::run(va[db], pb[kt][kh], o[db]);
       }
-    }
   };
 
-  // Software pipeline: while block blk is computed from LDS, block blk+1 is in
-  // flight into registers and the page ids of block blk+2 are loaded (issued
-  // first, so waiting for them never waits for the K/V loads). The last
-  // iteration fetches and stages one block past the end: its buffer
-  // resources have zero size, so it reads nothing and stores zeros.
-  if (nblocks > 0) {
-    take_pids(load_pid_vec(0));
-    fetch(0);
-    store(0);
-    take_pids(load_pid_vec(1));
-  }
-  __syncthreads();
-
-  for (int blk = 0; blk < nblocks; ++blk) {
-    const int buf = blk & 1;
-    const int pv = load_pid_vec(blk + 2);
-    fetch(blk + 1);
-    const int kb0 = key0 + blk * kBlockKeys;
-    const bool need_mask = kb0 + kBlockKeys > key1 || kb0 + kBlockKeys - 1 > qpos_min;
-    block(buf, blk, need_mask);
-    store(buf ^ 1);
-    take_pids(pv);
+  if constexpr (STAGES == 2) {
+    // Two LDS buffers (the one-launch cascade / mixed-batch kernel, where an
+    // append workgroup shares its CU with decode workers): block blk is
+    // computed from buffer blk mod 2 while block blk+1 is in flight into
+    // registers and the page ids of block blk+2 are loaded; one barrier per
+    // block. The last iteration stages one block past the end (zero-size
+    // buffer resources: nothing is read, zeros are stored).
+    if (nblocks > 0) {
+      take_pids(load_pid_vec(0));
+      fetch(0);
+      store(0);
+      take_pids(load_pid_vec(1));
+    }
     __syncthreads();
+    for (int blk = 0; blk < nblocks; ++blk) {
+      const int buf = blk & 1;
+      const int pv = load_pid_vec(blk + 2);
+      fetch(blk + 1);
+      const uint16_t* sk = smem + buf * kBufElems;
+      f32x16 sc[2];
+      scores_half(sk, 0, sc[0]);
+      scores_half(sk, 1, sc[1]);
+      mask_block(sc, blk);
+      row_max(sc);
+      exp_pv(sc, sk + kKElems);
+      store(buf ^ 1);
+      take_pids(pv);
+      __syncthreads();
+    }
+  } else {
+    // Software pipeline over three LDS buffers: block j is in buffer j mod 3.
+    // Iteration j runs block j's softmax and P V beside block j+1's scores
+    // (staged by iteration j-1), while block j+2's K/V (requested at its top,
+    // page ids requested an iteration earlier) are written to buffer
+    // (j+2) mod 3 at its end; that buffer last held block j-1, which every wave
+    // finished before the previous barrier. Blocks past the end have
+    // zero-size buffer resources: they read nothing and stage zeros, and their
+    // scores are never used.
+    auto buf_of = [&](int j) { return smem + (j % 3) * kBufElems; };
+    f32x16 sa[2], sb[2];
+    if (nblocks > 0) {
+      take_pids(load_pid_vec(0));
+      fetch(0);
+      store(0);
+      take_pids(load_pid_vec(1));
+      fetch(1);
+      store(1);
+      take_pids(load_pid_vec(2));
+    }
+    __syncthreads();
+    if (nblocks > 0) {
+      scores_half(buf_of(0), 0, sa[0]);
+      scores_half(buf_of(0), 1, sa[1]);
+    }
+    auto iteration = [&](int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
+      const int pv = load_pid_vec(j + 3);
+      fetch(j + 2);
+      // block j's softmax and P V; block j+1's scores issued beside it:
+      // half 0 before the row max, half 1 before the exponentials
+      const uint16_t* sk_next = buf_of(j + 1);
+      mask_block(s, j);
+      scores_half(sk_next, 0, s_next[0]);
+      row_max(s);
+      scores_half(sk_next, 1, s_next[1]);
+      exp_pv(s, buf_of(j) + kKElems);
+      store((j + 2) % 3);
+      take_pids(pv);
+      __syncthreads();
+    };
+    for (int j = 0; j < nblocks; j += 2) {
+      iteration(j, sa, sb);
+      if (j + 1 < nblocks) iteration(j + 1, sb, sa);
+    }
   }
 
   // --- epilogue --------------------------------------------------------------
@@ -429,13 +541,13 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
 // positions i / 8, i / 8 + gridDim.x / 8, ... of the bin.
 // Workgroup `block` of `nblocks` runs the tiles of bin block mod 8, strided
 // by nblocks / 8 (nblocks a multiple of 8).
-template <int DT, int G>
+template <int DT, int G, int STAGES>
 __device__ __forceinline__ void append_worker(const AttnParams& p, int block, int nblocks,
                                               uint16_t* smem, int& s_flag) {
   const int x = block % kAppendBins, stride = nblocks / kAppendBins;
   const int t1 = p.worker_ptr[x + 1];
   for (int t = p.worker_ptr[x] + block / kAppendBins; t < t1; t += stride)
-    append_tile<DT, G>(p, t, smem, s_flag);
+    append_tile<DT, G, STAGES>(p, t, smem, s_flag);
 }
 
 }  // namespace app

@@ -92,11 +92,11 @@ fa_status resolve_geometry(const fa_geometry* in, fa_geometry* out) {
   if (!g.tiles_per_cu) g.tiles_per_cu = app ? 2 : 4;
   if (!g.min_chunk_pages) g.min_chunk_pages = 1;
   g.pieces_per_worker = app ? 0 : (g.pieces_per_worker ? g.pieces_per_worker : kPiecesPerWorker);
-  // an append tile holds 128 query columns: the G heads x 128 / G positions
-  g.qo_tile = app ? (g.qo_tile ? g.qo_tile : 128 / G) : 1;
-  if (app && g.qo_tile > 128 / G) {
+  // an append tile holds kAppendCols query columns: the G heads x kAppendCols / G positions
+  g.qo_tile = app ? (g.qo_tile ? g.qo_tile : kAppendCols / G) : 1;
+  if (app && g.qo_tile > kAppendCols / G) {
     set_error("qo_tile %d exceeds the %d query positions of an append tile for group %d",
-              g.qo_tile, 128 / G, G);
+              g.qo_tile, kAppendCols / G, G);
     return FA_ERR_UNSUPPORTED;
   }
   const int64_t target = (int64_t)g.num_cu * g.tiles_per_cu;

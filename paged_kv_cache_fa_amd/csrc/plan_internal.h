@@ -17,6 +17,7 @@ constexpr int kSupportedHeadDim = 128;
 constexpr int kSupportedPageSize = 16;
 constexpr int kMaxPiecePages = 128;  // decode pieces: the kernel holds 128 page ids per wave
 constexpr int kXcdBins = 8;          // append tile bins, one per XCD (workgroup i runs on XCD i % 8)
+constexpr int kAppendCols = 256;     // query columns of an append tile: G heads x 256 / G positions
 constexpr int kPiecesPerWorker = 1;  // decode: work lists per worker wave
 // decode: set-up and epilogue of one piece, in pages of streaming time
 constexpr int kPieceCostPages16 = 4;

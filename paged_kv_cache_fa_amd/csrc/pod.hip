@@ -5,12 +5,12 @@
 // mixed prefill + decode batches of POD-attention named in section
 // "Features (from the repository README)").
 //
-// Workgroups 0 .. dec_blocks-1 are decode workers (4 independent waves, the
+// Workgroups 0 .. dec_blocks-1 are decode workers (8 independent waves, the
 // suffix plan's work lists); the rest run the prefix plan's append tiles
 // (bins by workgroup index mod 8, as in the append kernel). Both roles are
-// compiled for 2 waves per SIMD (at most 256 registers each), so a CU holds
-// one decode and one append workgroup at once: the append waves' matrix
-// work overlaps the decode waves' memory streaming. The decode role keeps a
+// compiled for 2 waves per SIMD (at most 256 registers each), so decode and
+// append waves share the CUs: the append waves' matrix work overlaps the
+// decode waves' memory streaming. The decode role keeps a
 // 2-page ring to fit the register budget. Split units merge as in the two
 // kernels (the prefix pass defers to the cascade combine).
 #include "append_dev.h"
@@ -20,25 +20,25 @@ namespace pkfa {
 namespace {
 
 template <int DT, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(app::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pod_kernel(AttnParams dp, AttnParams ap, int dec_blocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * app::kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * app::VLayout<2>::kBufElems];
   __shared__ int s_flag;
   const int blk = (int)blockIdx.x;
   if (blk < dec_blocks)
     dec::decode_worker<DT, G, 2, false>(
-        dp, blk * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)));
+        dp, blk * app::kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)));
   else
-    app::append_worker<DT, G>(ap, blk - dec_blocks, (int)gridDim.x - dec_blocks, smem, s_flag);
+    app::append_worker<DT, G, 2>(ap, blk - dec_blocks, (int)gridDim.x - dec_blocks, smem, s_flag);
 }
 
 template <int DT>
 hipError_t launch_dt(const AttnParams& dp, const AttnParams& ap, int group, int dec_blocks,
                      int grid, hipStream_t s) {
   switch (group) {
-    case 1: hipLaunchKernelGGL((pod_kernel<DT, 1>), dim3(grid), dim3(256), 0, s, dp, ap, dec_blocks); break;
-    case 2: hipLaunchKernelGGL((pod_kernel<DT, 2>), dim3(grid), dim3(256), 0, s, dp, ap, dec_blocks); break;
-    case 4: hipLaunchKernelGGL((pod_kernel<DT, 4>), dim3(grid), dim3(256), 0, s, dp, ap, dec_blocks); break;
+    case 1: hipLaunchKernelGGL((pod_kernel<DT, 1>), dim3(grid), dim3(app::kThreads), 0, s, dp, ap, dec_blocks); break;
+    case 2: hipLaunchKernelGGL((pod_kernel<DT, 2>), dim3(grid), dim3(app::kThreads), 0, s, dp, ap, dec_blocks); break;
+    case 4: hipLaunchKernelGGL((pod_kernel<DT, 4>), dim3(grid), dim3(app::kThreads), 0, s, dp, ap, dec_blocks); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
@@ -50,7 +50,8 @@ hipError_t launch_pod(const AttnParams& dp, int workers, const AttnParams& ap, i
                       int dtype, int group, hipStream_t s) {
   // decode workgroups first (a multiple of 8, so the append part keeps its
   // XCD bins), then the append grid of the append kernel
-  const int dec_blocks = (workers + 31) / 32 * 8;
+  constexpr int kPerBlock = app::kWaves;
+  const int dec_blocks = (workers + 8 * kPerBlock - 1) / (8 * kPerBlock) * 8;
   const int app_blocks = (max_tiles + kAppendBins - 1) / kAppendBins * kAppendBins;
   const int grid = dec_blocks + app_blocks;
   if (grid <= 0) return hipSuccess;

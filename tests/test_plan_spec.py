@@ -214,11 +214,13 @@ def test_append_batch16_and_cascade_prefix():
     p = plan_spec(_indptr(lens), lens, 16, 32, 8, 128, 16, max_batch=16, qo_indptr=qo,
                   causal=True, max_qo_tokens=8192)
     check_append_invariants(p, lens, 8, qo, True)
-    assert p["num_slots"] == 0 and len(p["tiles"]) == 16 * 8 * 16
+    # q tiles of 256 / G = 64 rows: 8 per (request, kv head), no key split
+    assert p["num_slots"] == 0 and len(p["tiles"]) == 16 * 8 * 8
     p = plan_spec([0, 1024], [16384], 1, 32, 8, 128, 16, max_batch=1, qo_indptr=[0, 256],
                   causal=False, max_qo_tokens=256)
     check_append_invariants(p, [16384], 8, [0, 256], False)
-    assert p["chunk_pages"] == 128 and len(p["tiles"]) == 512
+    # 4 q tiles x 8 kv heads x 1024 pages over 512 tiles: chunks of 64 pages
+    assert p["chunk_pages"] == 64 and len(p["tiles"]) == 512
 
 
 def test_random_geometries():
@@ -238,7 +240,7 @@ def test_random_geometries():
             ql = np.minimum(rng.integers(0, 70, size=B), lens)
             qo = np.concatenate([[0], np.cumsum(ql)]).astype(np.int64)
             causal = bool(rng.integers(0, 2))
-            qt = min(int(rng.choice([8, 16, 32])), 128 // G)
+            qt = min(int(rng.choice([8, 16, 32, 64])), 256 // G)
             p = plan_spec(_indptr(lens), lens, B, G * Hkv, Hkv, 128, 16, max_batch=max(B, 1),
                           qo_indptr=qo, causal=causal, max_qo_tokens=max(int(qo[-1]), 1),
                           qo_tile=qt, **knobs)
