@@ -241,6 +241,30 @@ fa_status fa_decode(const fa_plan_t* plan, const void* q, const void* k_pages,
                     const int32_t* last_page_len_d, float sm_scale, void* out, float* lse,
                     void* stream);
 
+/* For callers that cannot allocate (serving loops or harnesses that forbid
+ * device allocation): fa_plan + fa_decode in one call, with no caller-owned
+ * workspace and no allocation of any kind. The plan image, the arrival
+ * counters and the fp32 partial states live in a file-scope device array of
+ * 16 MiB per GPU and the host plan workspace in a static host array of 1 MiB
+ * per GPU, both held until the process ends.
+ *  geom, kv_indptr_h, kv_lens_h, batch  as in fa_plan (decode geometry only).
+ *  q, pages, strides, page tables, sm_scale, out, lse  as in fa_decode.
+ * The call plans on the host, copies the plan into the GPU's array on
+ * `stream` and waits on `stream` until that copy is done (work queued earlier
+ * on the stream included), then queues the decode kernel. It cannot be
+ * captured into a graph. Calls on one GPU share its arrays: calls that overlap
+ * (other streams or host threads on the same GPU) race. The results are those
+ * of fa_plan + fa_decode with the same geometry, bit for bit. Errors: those
+ * of fa_plan and fa_decode; FA_ERR_CAPACITY (nothing queued) when the
+ * geometry's workspaces (fa_workspace_size) exceed the static arrays. */
+fa_status fa_decode_noalloc(const fa_geometry* geom, const int32_t* kv_indptr_h,
+                            const int32_t* kv_lens_h, int32_t batch, const void* q,
+                            const void* k_pages, const void* v_pages, int64_t page_stride,
+                            int64_t token_stride, int64_t head_stride,
+                            const int32_t* kv_indices_d, const int32_t* kv_indptr_d,
+                            const int32_t* last_page_len_d, float sm_scale, void* out, float* lse,
+                            void* stream);
+
 /* Decode over a paged KV cache whose stored values carry one scale per tensor
  * ([Tool] "FlashInfer", "What it does": FP8 compute for attention; [Guide]
  * "Features (from the repository README)": FP8 with per-tensor scaling).

@@ -7,7 +7,7 @@ tensors (used for memory and streams only); there is no CPU fallback — if the
 library is missing, the import of any entry point raises.
 
 Entry points (same names as the C ABI): ``workspace_size``, ``plan`` /
-``plan_ragged`` (return a ``Plan``), ``decode``, ``decode_scaled``,
+``plan_ragged`` (return a ``Plan``), ``decode``, ``decode_noalloc``, ``decode_scaled``,
 ``decode_ragged``, ``append``, ``append_ragged``, ``pod``, ``cascade``, ``merge_state``,
 ``merge_states``, ``block_sparse_pages``; and ``single_decode_with_kv_cache`` /
 ``block_sparse_attention``, which plan and run a one-request decode over a
@@ -211,6 +211,23 @@ def decode(p: Plan, q, k_pages, v_pages, page_stride: int, token_stride: int, he
                            page_stride, token_stride, head_stride, _ptr(kv_indices),
                            _ptr(kv_indptr), _ptr(last_page_len), float(sm_scale), _ptr(out),
                            _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def decode_noalloc(geom: Geometry, kv_indptr_h, kv_lens_h, q, k_pages, v_pages, page_stride: int,
+                   token_stride: int, head_stride: int, kv_indices, kv_indptr, last_page_len,
+                   sm_scale: float = 0.0, out=None, lse=None, stream=None):
+    """fa_plan + fa_decode in one call with the library's static per-GPU
+    workspaces (see fa_decode_noalloc): no workspace is passed and nothing is
+    allocated by the library. Returns (out, lse)."""
+    lib = load()
+    ip, lens = _i32(kv_indptr_h), _i32(kv_lens_h)
+    out, lse = _alloc_out(q, out, lse, q.shape[0], q.shape[1])
+    check(lib.fa_decode_noalloc(ctypes.byref(geom), _ptr(ip), _ptr(lens), int(lens.shape[0]),
+                                _ptr(q), _ptr(k_pages), _ptr(v_pages), page_stride, token_stride,
+                                head_stride, _ptr(kv_indices), _ptr(kv_indptr),
+                                _ptr(last_page_len), float(sm_scale), _ptr(out), _ptr(lse),
+                                _stream(stream)))
     return out, lse
 
 

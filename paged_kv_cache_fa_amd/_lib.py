@@ -29,7 +29,8 @@ FA_MODE_DECODE, FA_MODE_APPEND = 0, 1
 # every symbol declared in include/fa.h
 EXPORTED = [
     "fa_workspace_size", "fa_plan", "fa_plan_info", "fa_plan_tiles", "fa_plan_destroy",
-    "fa_plan_ragged", "fa_block_sparse_pages", "fa_decode", "fa_decode_scaled", "fa_decode_ragged", "fa_append",
+    "fa_plan_ragged", "fa_block_sparse_pages", "fa_decode", "fa_decode_noalloc", "fa_decode_scaled",
+    "fa_decode_ragged", "fa_append",
     "fa_append_ragged", "fa_pod", "fa_cascade", "fa_merge_state", "fa_merge_states", "fa_status_string",
     "fa_last_error", "fa_probe_stream_read",
 ]
@@ -89,6 +90,7 @@ def load(path: str = LIB_PATH):
                           ctypes.POINTER(I32), ctypes.POINTER(P), ctypes.POINTER(I32)],
         "fa_plan_destroy": [PP],
         "fa_decode": [PP, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
+        "fa_decode_noalloc": [GP, P, P, I32, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
         "fa_decode_scaled": [PP, P, P, P, I64, I64, I64, P, P, P, F32, F32, F32, P, P, P],
         "fa_append": [PP, P, P, P, P, I64, I64, I64, P, P, P, F32, P, P, P],
         "fa_cascade": [PP, PP, P, P, P, I64, I64, I64, P, P, P, P, P, P, P, F32, P, P, P, P, P, P,

@@ -148,13 +148,17 @@ fa_status fa_workspace_size(const fa_geometry* geom, size_t* host_bytes, size_t*
   return FA_OK;
 }
 
-namespace {
+}  // extern "C"
 
-// fa_plan and fa_plan_ragged: build on the host, upload into dev_ws.
-fa_status plan_and_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
-                          const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
-                          int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
-                          size_t dev_ws_bytes, void* stream, bool ragged) {
+namespace pkfa {
+
+// fa_plan and fa_plan_ragged (and the no-allocation decode): build on the
+// host, upload into dev_ws. Without events no HIP event is created: the call
+// instead waits on the stream until the upload has read host_ws.
+fa_status plan_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
+                      const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
+                      int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
+                      size_t dev_ws_bytes, void* stream, bool ragged, bool events) {
   if (!plan) {
     set_error("plan is NULL");
     return FA_ERR_INVALID;
@@ -174,7 +178,7 @@ fa_status plan_and_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_
       return FA_ERR_CAPTURING;
     }
     // the previous copy out of host_ws must finish before host_ws is rewritten
-    if (pl->upload_event) {
+    if (events && pl->upload_event) {
       e = hipEventSynchronize(static_cast<hipEvent_t>(pl->upload_event));
       if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     }
@@ -232,6 +236,16 @@ fa_status plan_and_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_
     pl->planned = 0;
     return hip_fail(e, "plan upload");
   }
+  if (!events) {
+    // no event guards host_ws: wait here until the upload has read it
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      pl->planned = 0;
+      return hip_fail(e, "hipStreamSynchronize (plan upload)");
+    }
+    pl->uploaded = 1;
+    return FA_OK;
+  }
   for (void** slot : {&pl->upload_event, &pl->fork_event, &pl->join_event, &pl->join2_event}) {
     if (*slot) continue;
     hipEvent_t ev;
@@ -251,14 +265,16 @@ fa_status plan_and_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_
   return FA_OK;
 }
 
-}  // namespace
+}  // namespace pkfa
+
+extern "C" {
 
 fa_status fa_plan(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
                   const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
                   int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
                   size_t dev_ws_bytes, void* stream) {
-  return plan_and_upload(plan, geom, kv_indptr_h, kv_lens_h, batch, qo_indptr_h, causal, host_ws,
-                         host_ws_bytes, dev_ws, dev_ws_bytes, stream, false);
+  return plan_upload(plan, geom, kv_indptr_h, kv_lens_h, batch, qo_indptr_h, causal, host_ws,
+                     host_ws_bytes, dev_ws, dev_ws_bytes, stream, false, true);
 }
 
 fa_status fa_plan_ragged(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_offsets_h,
@@ -288,8 +304,8 @@ fa_status fa_plan_ragged(fa_plan_t* plan, const fa_geometry* geom, const int32_t
     }
     lens[b] = (int32_t)L;
   }
-  return plan_and_upload(plan, geom, kv_offsets_h, lens, batch, qo_indptr_h, causal, host_ws,
-                         host_ws_bytes, dev_ws, dev_ws_bytes, stream, true);
+  return plan_upload(plan, geom, kv_offsets_h, lens, batch, qo_indptr_h, causal, host_ws,
+                     host_ws_bytes, dev_ws, dev_ws_bytes, stream, true, true);
 }
 
 fa_status fa_block_sparse_pages(const int32_t* block_indptr_h, const int32_t* block_indices_h,

@@ -79,4 +79,12 @@ fa_status build_plan(PlanImpl* p, const fa_geometry& g, const int32_t* kv_indptr
 
 void set_error(const char* fmt, ...);
 
+// fa_plan's body (api.cpp): plan into host_ws and upload into dev_ws on
+// `stream` (a hipStream_t). With events false no HIP event is created: the
+// call waits on the stream until the upload has read host_ws.
+fa_status plan_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_t* kv_indptr_h,
+                      const int32_t* kv_lens_h, int32_t batch, const int32_t* qo_indptr_h,
+                      int32_t causal, void* host_ws, size_t host_ws_bytes, void* dev_ws,
+                      size_t dev_ws_bytes, void* stream, bool ragged, bool events);
+
 }  // namespace pkfa

@@ -41,6 +41,7 @@ hipError_t hipEventDestroy(hipEvent_t) { reached("hipEventDestroy"); }
 hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t, unsigned int) {
   reached("hipStreamWaitEvent");
 }
+hipError_t hipStreamSynchronize(hipStream_t) { reached("hipStreamSynchronize"); }
 // A heap read at index i of a 4-element array: out of bounds for i >= 4. The
 // sanitizer test calls it with i = 4 to show that the build is instrumented.
 int pkfa_sanitizer_canary(int i) {
@@ -49,6 +50,13 @@ int pkfa_sanitizer_canary(int i) {
   const int v = a[i];
   free(a);
   return v;
+}
+// the no-allocation decode keeps its static device array in a HIP source
+fa_status fa_decode_noalloc(const fa_geometry*, const int32_t*, const int32_t*, int32_t,
+                            const void*, const void*, const void*, int64_t, int64_t, int64_t,
+                            const int32_t*, const int32_t*, const int32_t*, float, void*, float*,
+                            void*) {
+  reached("fa_decode_noalloc");
 }
 // the streaming-read probe lives with its kernel in a HIP source
 fa_status fa_probe_stream_read(const void*, int64_t, uint32_t*, int32_t, void*) {
