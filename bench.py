@@ -4,44 +4,45 @@ Headline (the JSON ``value``): batched paged decode, batch 64, GQA 32 q / 8 kv
 heads, head_dim 128, bf16, page 16, kv_len uniform in [512, 4096], pages
 scattered by a seeded permutation. One step = the host plan (balanced
 split-KV work list, uploaded to the device workspace) + the decode kernel
-(which also merges split requests). ``value`` is the achieved algorithmic
-HBM bandwidth of the step in GB/s: bytes of the valid K/V of every request,
-plus q, out and lse, divided by the wall time per step.
+(which also merges split requests), steps back to back with nothing else
+queued between them. ``value`` is the achieved algorithmic HBM bandwidth of
+the step in GB/s: bytes of the valid K/V of every request, plus q, out and
+lse, divided by the wall time per step.
 
-Reported alongside in the same JSON line:
+Every line reports a ``roofline`` block for its dominant kernel: its
+algorithmic bytes (or FLOPs) per run call over the call's time measured with
+HIP timing events on the launch stream (each call re-planned first, outside
+the events), against the 8 TB/s HBM or the 2.5 PFLOP/s bf16 MFMA peak, with
+``traffic`` (HBM bytes per call from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+by a 1 GiB copy) when ``profiles/<line>_hbm_counters.txt`` was taken on this
+line and on the current kernel sources. Decode lines also give the timing
+protocol for a run call alone, ``graph_ms_per_call``: one hipGraph of R
+back-to-back calls over the rotating pool copies, median of 20 replays / R.
+
+Lines after the headline:
+  * ``single``: config 1 as defined (one request, 32/32 heads, 2048 tokens in
+    128 pages under a seeded permutation, fp16), a graph of 32 back-to-back
+    calls over 32 pool copies (its eager step is bound by the host);
   * ``batch128``: the skewed batch-128 decode (4 x 32768 + 124 log-normal);
-  * ``cascade``: batch 256 sharing a 16384-token prefix (prefix pass on MFMA +
-    suffix decode + merge_state), as HBM GB/s with the prefix counted once;
-    ``no_cascade_decode`` times the same batch as one plain decode whose
-    requests each read the prefix pages (17.9 GB), for the speedup;
-  * ``append``: causal append of 16 x 512 rows onto 4096 cached tokens, as
-    MFMA utilisation (584.2 GFLOP of unmasked work per step);
-  * ``fp8``: the batch-64 decode with an E4M3 page pool (per-tensor scales,
-    bf16 q / out), as HBM GB/s with one byte per K/V element;
-  * ``ragged``: the batch-64 decode over a ragged (contiguous-row) KV cache;
-  * ``single``: the single-request decode (32 heads, kv_len 2048, fp16) over a
-    contiguous K / V;
-  * ``ragged`` and ``single`` also give ``graph_ms_per_call``: the median time
-    per call of a captured hipGraph of back-to-back run calls over the
-    rotating K/V copies (plan excluded). The single-request step is bound by
-    the host (binding + plan), and its HIP events then time the host's
-    submission gap rather than the kernel;
-  * ``bsr``: block-sparse prefill, 4096 query rows x 16384 keys in 64 x 64
-    blocks, a quarter of the blocks kept, as MFMA utilisation;
-  * ``pod``: a mixed batch over one pool, the causal append of 16 x 512 rows
-    plus the batch-64 decode, in one fa_pod launch against the two
-    kernels back to back;
-  * ``roofline``: the decode kernel against the 8 TB/s HBM peak (kernel time
-    from HIP timing events around each launch on its stream, created without
-    the system-scope fence), with HBM traffic from
-    rocprofv3 counters when the stored counter summary matches the current
-    kernel source (a graph of back-to-back calls measured slower per call:
-    it adds the launch gaps); ``host_plan_us`` is the host cost of one
-    fa_plan call;
-  * ``roofline.attainable_GB/s``: a plain streaming read of 1 GiB on the same
-    device (fa_probe_stream_read, best launch size), and the decode kernel's
-    bandwidth as a fraction of it;
-  * ``cpu_baseline``: the fp64 numpy oracle on the host cores.
+  * ``cascade``: batch 256 sharing a 16384-token prefix (one fa_cascade call:
+    prefix pass on MFMA + suffix decode + merge), HBM GB/s with the prefix
+    counted once; ``no_cascade_decode`` times the same batch as one plain
+    decode whose requests each re-read the prefix pages (17.9 GB);
+  * ``append``: causal append of 16 x 512 rows onto 4096 cached tokens, MFMA
+    utilisation (584.2 GFLOP of unmasked work per call);
+  * ``fp8``: the batch-64 decode over an E4M3 page pool (per-tensor scales);
+  * ``ragged`` / ``single_ragged``: configs 2 and 1 over a ragged (contiguous)
+    K/V;
+  * ``bsr``: block-sparse prefill, 4096 x 16384 in 64 x 64 blocks, 25% kept;
+  * ``pod``: causal append + batch-64 decode in one fa_pod launch against the
+    two kernels back to back;
+  * ``host_plan_us`` (the host cost of one fa_plan), the streaming-read ceiling
+    ``roofline.attainable_GB/s`` (fa_probe_stream_read over 1 GiB) and
+    ``cpu_baseline`` (the fp64 numpy oracle on the host cores).
+
+``--profile LINE`` runs only one line's run call (for rocprofv3 kernel-trace and
+counter runs) and ``--profile LINE --summarize DIR`` turns that run's CSV output
+into the text summaries kept under profiles/.
 
 Inputs are synthetic (seeded N(0,1)), resident in HBM before the timed
 region; steps rotate over enough copies of the page pool (>= 1 GiB in total)
@@ -65,7 +66,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2516.6  # bf16 dense: 256 CU x 4096 FLOP/clk x 2.4 GHz
 METRIC = "paged decode achieved HBM GB/s (% of peak) and tokens/sec at batch 64/128"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_batch64_hbm_counters.txt")
 
 
 def kv_bytes(lens, hkv, d=128, elt=2) -> int:
@@ -114,14 +114,17 @@ def append_flops(wl) -> float:
     return float(pairs) * wl.num_qo_heads * 4 * wl.head_dim
 
 
-def _dev(wl, device, min_rotation_bytes):
+def _dev(wl, device, min_rotation_bytes, min_copies=1):
+    """Device copies of the pool (enough copies to rotate over min_rotation_bytes,
+    at least min_copies), q and the pool strides."""
     import torch
     dt = {"bf16": torch.bfloat16, "fp16": torch.float16}[wl.dtype]
     if wl.kv_dtype == "e4m3":
         pool = torch.from_numpy(wl.pool).to(device)
     else:
         pool = torch.from_numpy(wl.pool.view(np.int16)).to(device).view(dt)
-    copies = max(1, math.ceil(min_rotation_bytes / max(1, pool.numel() * pool.element_size())))
+    copies = max(min_copies,
+                 math.ceil(min_rotation_bytes / max(1, pool.numel() * pool.element_size())))
     pools = [pool] + [pool.clone() for _ in range(copies - 1)]
     q = torch.from_numpy(wl.q.view(np.int16)).to(device).view(dt)
     _, _, ps, hkv, d = wl.pool.shape
@@ -183,30 +186,52 @@ class HipEvent:
 
 
 class Timed:
-    """Run steps; time the whole step (torch events around all steps) and one named
-    kernel call per step (HIP timing events around it, on its stream)."""
+    """Timing of one workload line. A bench object provides ``replan()`` (the
+    host plan + its upload, on torch's current stream) and ``run_call(i)``
+    (the run calls of one step over input copy i)."""
 
-    def run(self, steps: int, warmup: int):
+    def step(self, i: int):
+        self.replan()
+        self.run_call(i)
+
+    def steps_ms(self, steps: int, warmup: int) -> float:
+        """Whole steps (re-plan + run), back to back with nothing else queued
+        between them: torch events around all steps, mean per step."""
         import torch
         for i in range(warmup):
-            self.step(i, None)
+            self.step(i)
         torch.cuda.synchronize()
-        kev = [(HipEvent(), HipEvent()) for _ in range(steps)]
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         t0.record()
         for i in range(steps):
-            self.step(warmup + i, kev[i])
+            self.step(warmup + i)
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in kev]))
+        return t0.elapsed_time(t1) / steps
 
-    def graph_call_ms(self, calls: int, replays: int = 20) -> float:
-        """Median time per run call of a captured hipGraph of `calls` back-to-back run
-        calls over the rotating input copies (the plan is made once, before capture)."""
+    def kernel_ms(self, launches: int, warmup: int = 2) -> float:
+        """The run calls alone: each step re-plans, then HIP timing events on
+        the launch stream bracket its run calls; mean over the launches."""
         import torch
-        self.step(0, None)  # plan + one eager call
+        for i in range(warmup):
+            self.step(i)
+        ev = [(HipEvent(), HipEvent()) for _ in range(launches)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(ev):
+            self.replan()
+            a.record()
+            self.run_call(warmup + i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    def graph_ms(self, calls: int, replays: int = 20) -> float:
+        """The timing protocol for a run call alone: one hipGraph of `calls`
+        back-to-back run calls over the rotating input copies (plan made once,
+        before capture), replayed `replays` times; median time per call."""
+        import torch
+        self.step(0)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -231,11 +256,13 @@ class Timed:
 
 
 class DecodeBench(Timed):
-    def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, **knobs):
+    """fa_plan + fa_decode (fa_decode_scaled for an E4M3 pool) over a paged pool."""
+
+    def __init__(self, wl, device="cuda", min_rotation_bytes=1 << 30, min_copies=1, **knobs):
         import torch
         import paged_kv_cache_fa_amd as fa
         self.fa, self.wl = fa, wl
-        self.pools, self.q, self.strides = _dev(wl, device, min_rotation_bytes)
+        self.pools, self.q, self.strides = _dev(wl, device, min_rotation_bytes, min_copies)
         self.kv_indptr = _i32(wl.kv_indptr, device)
         self.kv_indices = _i32(wl.kv_indices, device)
         self.last = _i32(wl.last_page_len, device)
@@ -247,13 +274,8 @@ class DecodeBench(Timed):
         self.indptr_h = np.ascontiguousarray(wl.kv_indptr)
         self.lens_h = np.ascontiguousarray(wl.kv_lens.astype(np.int32))
 
-    def step(self, i: int, ev=None):
+    def replan(self):
         self.plan.plan(self.indptr_h, self.lens_h)
-        if ev is not None:
-            ev[0].record()
-        self.run_call(i)
-        if ev is not None:
-            ev[1].record()
 
     def run_call(self, i: int):
         pool = self.pools[i % len(self.pools)]
@@ -297,7 +319,7 @@ def plan_us(b: DecodeBench, n: int = 200) -> float:
     torch.cuda.synchronize()
     t = time.perf_counter()
     for _ in range(n):
-        b.plan.plan(b.indptr_h, b.lens_h)
+        b.replan()
     dt = (time.perf_counter() - t) / n
     torch.cuda.synchronize()
     return dt * 1e6
@@ -323,13 +345,8 @@ class RaggedDecodeBench(Timed):
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(rw.rows, rw.num_qo_heads, dtype=torch.float32, device=device)
 
-    def step(self, i: int, ev=None):
+    def replan(self):
         self.plan.plan_ragged(self.offs_h)
-        if ev is not None:
-            ev[0].record()
-        self.run_call(i)
-        if ev is not None:
-            ev[1].record()
 
     def run_call(self, i: int):
         k, v = self.kv[i % len(self.kv)]
@@ -366,15 +383,13 @@ class BlockSparseBench(Timed):
                                device=device)
         self.flops = float((np.diff(bw.row_offsets) * lens).sum()) * bw.num_qo_heads * 4 * 128
 
-    def step(self, i: int, ev=None):
+    def replan(self):
         self.plan.plan(self.ip_h, self.lens_h, self.ro_h, False)
-        if ev is not None:
-            ev[0].record()
+
+    def run_call(self, i: int):
         ts, hs = self.k.stride(0), self.k.stride(1)
         self.fa.append(self.plan, self.q, self.ro, self.k, self.v, ts, ts, hs, self.ix, self.ip,
                        self.last, out=self.out, lse=self.lse)
-        if ev is not None:
-            ev[1].record()
 
 
 class PodBench(Timed):
@@ -398,8 +413,11 @@ class PodBench(Timed):
         self.dtabs = (_i32(ix[k:], device), _i32(self.dec_h[0], device),
                       _i32(last[n_prefill:], device))
         self.qo = _i32(qo[: n_prefill + 1], device)
+        # fa_pod's append workgroups take q tiles of 128 / G rows; the two
+        # separate kernels run the append kernel's own (wider) default tiles
+        tile = {} if separate else {"qo_tile": 128 // (wl.num_qo_heads // wl.num_kv_heads)}
         gp = fa.geometry("append", wl.dtype, n_prefill, wl.num_qo_heads, wl.num_kv_heads,
-                         max_qo_tokens=self.nrows_p)
+                         max_qo_tokens=self.nrows_p, **tile)
         gd = fa.geometry("decode", wl.dtype, wl.batch - n_prefill, wl.num_qo_heads,
                          wl.num_kv_heads)
         self.pp, self.dp = fa.Plan(gp, device=device), fa.Plan(gd, device=device)
@@ -408,14 +426,14 @@ class PodBench(Timed):
         mk = lambda n: torch.empty(n, wl.num_qo_heads, dtype=torch.float32, device=device)
         self.lse_p, self.lse_d = mk(self.nrows_p), mk(self.q_d.shape[0])
 
-    def step(self, i: int, ev=None):
+    def replan(self):
+        self.pp.plan(*self.pre_h, True)
+        self.dp.plan(*self.dec_h)
+
+    def run_call(self, i: int):
         fa = self.fa
         pool = self.pools[i % len(self.pools)]
         k, v = pool[:, 0], pool[:, 1]
-        self.pp.plan(*self.pre_h, True)
-        self.dp.plan(*self.dec_h)
-        if ev is not None:
-            ev[0].record()
         if self.separate:
             fa.append(self.pp, self.q_p, self.qo, k, v, *self.strides, *self.ptabs,
                       out=self.out_p, lse=self.lse_p)
@@ -425,8 +443,6 @@ class PodBench(Timed):
             fa.pod(self.pp, self.q_p, self.qo, *self.ptabs, self.dp, self.q_d, *self.dtabs, k, v,
                    *self.strides, out_p=self.out_p, lse_p=self.lse_p, out_d=self.out_d,
                    lse_d=self.lse_d)
-        if ev is not None:
-            ev[1].record()
 
 
 class AppendBench(Timed):
@@ -445,16 +461,14 @@ class AppendBench(Timed):
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty(wl.rows, wl.num_qo_heads, dtype=torch.float32, device=device)
 
-    def step(self, i: int, ev=None):
+    def replan(self):
         wl = self.wl
-        pool = self.pools[i % len(self.pools)]
         self.plan.plan(wl.kv_indptr, wl.kv_lens, wl.qo_indptr, wl.causal)
-        if ev is not None:
-            ev[0].record()
+
+    def run_call(self, i: int):
+        pool = self.pools[i % len(self.pools)]
         self.fa.append(self.plan, self.q, self.qo_indptr, pool[:, 0], pool[:, 1], *self.strides,
                        self.kv_indices, self.kv_indptr, self.last, out=self.out, lse=self.lse)
-        if ev is not None:
-            ev[1].record()
 
 
 class CascadeBench(Timed):
@@ -476,8 +490,10 @@ class CascadeBench(Timed):
         self.p_indices = _i32(wl.prefix_indices, device)
         self.p_last = _i32(wl.prefix_last_page_len, device)
         self.qo = _i32([0, B], device)
+        # prefix q tiles of 128 / G rows: the one-launch cascade kernel's append workgroups
+        pk = {"qo_tile": 128 // (wl.num_qo_heads // wl.num_kv_heads), **(prefix_knobs or {})}
         gp = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads, max_qo_tokens=B,
-                         **(prefix_knobs or {}))
+                         **pk)
         gs = fa.geometry("decode", wl.dtype, B, wl.num_qo_heads, wl.num_kv_heads,
                          **(suffix_knobs or {}))
         self.pplan = fa.Plan(gp, device=device)
@@ -487,49 +503,63 @@ class CascadeBench(Timed):
         self.op, self.lp = mk()
         self.os, self.ls = mk()
         self.out, self.lse = mk()
-        # One stream: measured on MI355X, running the prefix pass on a side
-        # stream beside the suffix decode is slower (they compete for each
-        # CU's registers and caches) than running the two back to back.
-        self.side = None
 
-    def step(self, i: int, ev=None):
-        wl, fa = self.wl, self.fa
-        pool = self.pools[i % len(self.pools)]
-        k, v = pool[:, 0], pool[:, 1]
+    def replan(self):
+        wl = self.wl
         self.pplan.plan(wl.prefix_indptr, [wl.prefix_len], [0, wl.batch], False)
         self.splan.plan(wl.kv_indptr, wl.kv_lens)
-        if ev is not None:
-            ev[0].record()
-        fa.cascade(self.pplan, self.splan, self.q, k, v, *self.strides, self.qo, self.p_indices,
-                   self.p_indptr, self.p_last, self.kv_indices, self.kv_indptr, self.last,
-                   states=(self.op, self.lp, self.os, self.ls), out=self.out, lse=self.lse,
-                   side_stream=self.side)
-        if ev is not None:
-            ev[1].record()
+
+    def run_call(self, i: int):
+        # one stream: measured on MI355X, running the prefix pass on a side
+        # stream beside the suffix decode is slower than the one-kernel form
+        pool = self.pools[i % len(self.pools)]
+        k, v = pool[:, 0], pool[:, 1]
+        self.fa.cascade(self.pplan, self.splan, self.q, k, v, *self.strides, self.qo,
+                        self.p_indices, self.p_indptr, self.p_last, self.kv_indices,
+                        self.kv_indptr, self.last, states=(self.op, self.lp, self.os, self.ls),
+                        out=self.out, lse=self.lse)
 
 
-KERNEL_SOURCES = ("decode.hip", "decode_dev.h", "device_common.h", "kernels.h")
+# --- stored rocprofv3 counter summaries ---------------------------------------------------------
+
+# kernel sources whose hash keys a stored counter summary, per line
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "decode_dev.h", "device_common.h", "kernels.h"),
+    "cascade": ("pod.hip", "append_dev.h", "decode_dev.h", "merge.hip", "device_common.h",
+                "kernels.h"),
+    "append": ("append.hip", "append_dev.h", "device_common.h", "kernels.h"),
+}
+LINE_KERNEL = {"decode_batch64": "decode", "decode_batch128": "decode",
+               "decode_fp8_batch64": "decode", "decode_single_kv2048": "decode",
+               "cascade_batch256": "cascade", "append_causal_batch16": "append"}
 
 
-def kernel_source_sha256() -> str:
-    """SHA-256 over the decode kernel's source files, in a fixed order."""
+def kernel_source_sha256(kind: str = "decode") -> str:
+    """SHA-256 over the source files of a line's kernels, in a fixed order."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         h.update(open(os.path.join(ROOT, "paged_kv_cache_fa_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
 
-def stored_traffic(kernel_src: str = ""):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
-    if not os.path.exists(COUNTERS_FILE):
+def counters_file(line: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{line}_hbm_counters.txt")
+
+
+def stored_traffic(line: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled) from the committed
+    counter summary of this line, if it was taken on this workload and on the
+    current kernel sources; else None."""
+    path = counters_file(line)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(COUNTERS_FILE):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
+    for text in open(path):
+        if ":" in text and not text.startswith("#"):
+            k, v = text.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_sha256():
+    if fields.get("line") != line or \
+            fields.get("kernel_source_sha256") != kernel_source_sha256(LINE_KERNEL[line]):
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))
@@ -563,206 +593,403 @@ def cpu_baseline(wl, min_seconds: float = 10.0) -> dict:
                       f"({done_req / t_used * 1:.1f} tokens/s), {t_used:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="decode workload for the headline (1-3)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only-headline", action="store_true", help="skip batch128/cascade/append")
-    ap.add_argument("--parts", default="batch128,cascade,append,fp8,ragged,single,bsr,pod",
-                    help="comma list of the secondary workloads to run after the headline")
-    ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="run one plain 1 GiB device copy first (scales rocprofv3 byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: this library has no multi-GPU path (requests "
-              "or kv heads would shard across GPUs with no exchange; long sequences by key "
-              "range, with an all-gather of partial states and a local merge).", file=sys.stderr)
-        sys.exit(2)
+def hbm_roofline(line, nbytes, kernel_ms, kernel_name, **extra) -> dict:
+    gbs = nbytes / (kernel_ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(line),
+         "kernel": kernel_name, "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes}
+    r.update(extra)
+    return r
+
+
+def mfma_roofline(flops, kernel_ms, kernel_name, **extra) -> dict:
+    tf = flops / (kernel_ms * 1e-3) / 1e12
+    r = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+         "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "traffic": None, "kernel": kernel_name,
+         "kernel_ms": round(kernel_ms, 5), "algorithmic_flops": flops}
+    r.update(extra)
+    return r
+
+
+# --- workload lines -------------------------------------------------------------------------------
+
+def line_decode(k, steps, warmup, kv_dtype=None, knobs=None):
+    """A batched paged decode (configs 2 and 3, or config 2 over an E4M3 pool):
+    whole steps (re-plan + decode), the decode call alone with HIP events, and
+    the graph protocol (R back-to-back calls over the rotating pool copies)."""
+    from workloads import CONFIG_NAMES, make_config
+    wl = make_config(k, kv_dtype=kv_dtype) if kv_dtype else make_config(k)
+    b = DecodeBench(wl, **(knobs or {}))
+    step_ms = b.steps_ms(steps, warmup)
+    kern_ms = b.kernel_ms(steps)
+    graph_ms = b.graph_ms(len(b.pools))
+    nbytes = algorithmic_bytes(wl)
+    st = b.plan.info()
+    line = "decode_fp8_batch64" if kv_dtype else {2: "decode_batch64", 3: "decode_batch128"}[k]
+    res = {"workload": CONFIG_NAMES[k] + (", K/V pages in E4M3" if kv_dtype else ""),
+           "GB/s": round(nbytes / (step_ms * 1e-3) / 1e9, 2),
+           "pct_of_hbm_peak": round(100 * nbytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+           "tokens_per_s": round(wl.batch / (step_ms * 1e-3), 1),
+           "ms_per_step": round(step_ms, 5),
+           "roofline": hbm_roofline(line, nbytes, kern_ms, "decode_kernel (one fa_decode call)",
+                                    graph_ms_per_call=round(graph_ms, 5),
+                                    graph_frac=round(nbytes / (graph_ms * 1e-3) / 1e9 /
+                                                     HBM_PEAK_GBS, 4)),
+           "plan": {"tiles": st.num_tiles, "split_units": st.num_merge,
+                    "workers": st.num_workers, "piece_pages": st.chunk_pages},
+           "pool_copies": len(b.pools), "kv_tokens": int(wl.kv_lens.sum())}
+    if kv_dtype:
+        res.update(kv_dtype=kv_dtype, k_scale=wl.k_scale, v_scale=wl.v_scale)
+    return res, b, wl
+
+
+def line_single(steps, warmup):
+    """Config 1 as defined: one request, q [32, 128] fp16, K/V of 2048 tokens
+    x 32 kv heads in 128 pages of 16 tokens under a seeded random page
+    permutation; a graph of 32 back-to-back fa_decode calls over 32 pool
+    copies (the timing protocol), and the eager step for context."""
+    from workloads import CONFIG_NAMES, make_config
+    wl = make_config(1)
+    b = DecodeBench(wl, min_copies=32)
+    graph_ms = b.graph_ms(len(b.pools))
+    step_ms = b.steps_ms(steps, warmup)
+    kern_ms = b.kernel_ms(steps)
+    nbytes = algorithmic_bytes(wl)
+    st = b.plan.info()
+    return {"workload": CONFIG_NAMES[1] + ", 128 pages in a seeded permutation",
+            "GB/s": round(nbytes / (graph_ms * 1e-3) / 1e9, 2),
+            "pct_of_hbm_peak": round(100 * nbytes / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "tokens_per_s": round(1 / (graph_ms * 1e-3), 1),
+            "graph_ms_per_call": round(graph_ms, 5), "eager_ms_per_step": round(step_ms, 5),
+            "roofline": hbm_roofline("decode_single_kv2048", nbytes, graph_ms,
+                                     "decode_kernel (graph of 32 back-to-back fa_decode calls)",
+                                     event_kernel_ms=round(kern_ms, 5)),
+            "plan": {"tiles": st.num_tiles, "split_units": st.num_merge,
+                     "piece_pages": st.chunk_pages},
+            "pool_copies": len(b.pools)}
+
+
+def line_cascade(steps, warmup):
+    from workloads import CONFIG_NAMES, make_config
+    w4 = make_config(4)
+    b4 = CascadeBench(w4)
+    n = max(5, steps // 2)
+    step_ms = b4.steps_ms(n, max(2, warmup // 2))
+    kern_ms = b4.kernel_ms(n)
+    n4 = algorithmic_bytes(w4)
+    res = {"workload": CONFIG_NAMES[4],
+           "GB/s": round(n4 / (step_ms * 1e-3) / 1e9, 2),
+           "pct_of_hbm_peak": round(100 * n4 / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+           "tokens_per_s": round(w4.batch / (step_ms * 1e-3), 1),
+           "ms_per_step": round(step_ms, 5),
+           "roofline": hbm_roofline("cascade_batch256", n4, kern_ms,
+                                    "pod_kernel + cascade_merge_kernel (one fa_cascade call)")}
+    del b4
     import torch
-    from workloads import CONFIG_NAMES, config_lengths, make_config
-    knobs = {k: int(v) for k, v in (s.split("=") for s in args.knob)}
-    if args.copy_probe:
+    torch.cuda.empty_cache()
+    # context: the same batch as one plain decode (each request re-reads the prefix)
+    wn = no_cascade_view(w4)
+    bn = DecodeBench(wn, max_tiles=40000, max_partials=40000, max_merge=4096)
+    kn = bn.kernel_ms(5)
+    nn = algorithmic_bytes(wn)
+    # (its re-read prefix pages mostly come from the 256 MB Infinity Cache, so this
+    # effective rate is not an HBM figure)
+    res["no_cascade_decode"] = {"kernel_ms": round(kn, 5), "algorithmic_bytes": nn,
+                                "effective_GB/s": round(nn / (kn * 1e-3) / 1e9, 2)}
+    res["speedup_over_no_cascade"] = round(kn / kern_ms, 2)
+    return res
+
+
+def line_append(steps, warmup):
+    from workloads import CONFIG_NAMES, make_config
+    w5 = make_config(5)
+    b5 = AppendBench(w5)
+    n = max(5, steps // 2)
+    step_ms = b5.steps_ms(n, max(2, warmup // 2))
+    kern_ms = b5.kernel_ms(n)
+    f5 = append_flops(w5)
+    return {"workload": CONFIG_NAMES[5],
+            "TFLOP/s": round(f5 / (step_ms * 1e-3) / 1e12, 1),
+            "tokens_per_s": round(w5.rows / (step_ms * 1e-3), 1),
+            "ms_per_step": round(step_ms, 5),
+            "roofline": mfma_roofline(f5, kern_ms, "append_kernel (one fa_append call)",
+                                      algorithmic_bytes=algorithmic_bytes(w5))}
+
+
+def line_ragged(k, steps, warmup):
+    from workloads import CONFIG_NAMES, make_config, make_ragged
+    wk = make_config(k)
+    rw = make_ragged(wk.kv_lens, wk.num_qo_heads, wk.num_kv_heads, wk.dtype, seed=k)
+    br = RaggedDecodeBench(rw)
+    sr = br.steps_ms(steps, warmup)
+    kr = br.kernel_ms(steps)
+    gr = br.graph_ms(len(br.kv))
+    nr = ragged_bytes(rw)
+    return {"workload": f"{CONFIG_NAMES[k]}, ragged (contiguous) K/V",
+            "GB/s": round(nr / (sr * 1e-3) / 1e9, 2), "ms_per_step": round(sr, 5),
+            "kernel_ms": round(kr, 5), "kernel_GB/s": round(nr / (kr * 1e-3) / 1e9, 2),
+            "graph_ms_per_call": round(gr, 5), "graph_GB/s": round(nr / (gr * 1e-3) / 1e9, 2),
+            "algorithmic_bytes": nr, "kv_copies": len(br.kv)}
+
+
+def line_bsr(steps, warmup):
+    from workloads import make_block_sparse
+    bw = make_block_sparse([64] * 64, [64] * 256, 0.25, 32, 8, "bf16", seed=7)
+    bb = BlockSparseBench(bw)
+    n = max(5, steps // 2)
+    sb = bb.steps_ms(n, max(2, warmup // 2))
+    kb = bb.kernel_ms(n)
+    return {"workload": "block-sparse prefill: 4096 query rows x 16384 keys, 64 x 64 blocks, "
+                        "25% kept (seeded), 32/8 heads, bf16",
+            "ms_per_step": round(sb, 5), "blocks_kept": int(len(bw.block_indices)),
+            "roofline": mfma_roofline(bb.flops, kb, "append_kernel (one fa_append call)")}
+
+
+def line_pod(steps, warmup):
+    import torch
+    from workloads import config_lengths, make_config, make_workload
+    r5, r2 = np.random.default_rng(5), np.random.default_rng(2)
+    l5, l2 = config_lengths(5, r5), config_lengths(2, r2)
+    lens = np.concatenate([l5["kv_lens"], l2["kv_lens"]])
+    qo = np.concatenate([l5["qo_lens"], np.ones(len(l2["kv_lens"]), np.int64)])
+    wm = make_workload(lens, 32, 8, "bf16", 52, qo_lens=qo, causal=True, name="mixed")
+    n_pre = len(l5["kv_lens"])
+    res = {}
+    n = max(5, steps // 2)
+    for sep in (False, True):
+        pb = PodBench(wm, n_pre, separate=sep)
+        res[sep] = (pb.steps_ms(n, max(2, warmup // 2)), pb.kernel_ms(n))
+        del pb
+        torch.cuda.empty_cache()
+    f5 = append_flops(make_config(5))
+    return {"workload": "mixed batch over one pool: causal append (16 x 512 rows onto 4096) + "
+                        "GQA decode (batch 64, kv U[512,4096]), 32/8 heads, bf16",
+            "kernel_ms": round(res[False][1], 5), "separate_kernels_ms": round(res[True][1], 5),
+            "speedup": round(res[True][1] / res[False][1], 3),
+            "ms_per_step": round(res[False][0], 5),
+            "tokens_per_s": round(wm.rows / (res[False][0] * 1e-3), 1), "append_flops": f5}
+
+
+# --- profiling support ----------------------------------------------------------------------------
+
+PROFILE_LINES = ("decode_batch64", "decode_batch128", "decode_fp8_batch64",
+                 "decode_single_kv2048", "cascade_batch256", "append_causal_batch16")
+
+
+def profile_line(line: str, steps: int, warmup: int, copy_probe: bool):
+    """Run one line's run call `warmup + steps` times, each after a re-plan (as
+    the roofline timing does), and nothing else (plus an optional plain 1 GiB
+    device copy first, whose byte counters scale the kernel's), for a
+    rocprofv3 kernel-trace or counter run."""
+    import torch
+    from workloads import make_config
+    if copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        torch.cuda.empty_cache()
+    mk = {"decode_batch64": lambda: DecodeBench(make_config(2)),
+          "decode_batch128": lambda: DecodeBench(make_config(3)),
+          "decode_fp8_batch64": lambda: DecodeBench(make_config(2, kv_dtype="e4m3")),
+          "decode_single_kv2048": lambda: DecodeBench(make_config(1), min_copies=32),
+          "cascade_batch256": lambda: CascadeBench(make_config(4)),
+          "append_causal_batch16": lambda: AppendBench(make_config(5))}[line]
+    b = mk()
+    torch.cuda.synchronize()
+    for i in range(warmup + steps):
+        b.replan()       # as in the roofline timing: every run call is re-planned first
+        b.run_call(i)
+    torch.cuda.synchronize()
+    print(f"profiled {line}: {warmup} + {steps} run calls", flush=True)
 
-    wl = make_config(args.config)
-    b = DecodeBench(wl, **knobs)
-    step_ms, kernel_ms = b.run(args.steps, args.warmup)
+
+def line_work(line: str):
+    """(algorithmic bytes, algorithmic FLOPs) of one run call of a line."""
+    from workloads import make_config
+    k = {"decode_batch64": 2, "decode_batch128": 3, "decode_fp8_batch64": 2,
+         "decode_single_kv2048": 1, "cascade_batch256": 4, "append_causal_batch16": 5}[line]
+    wl = make_config(k, kv_dtype="e4m3") if line == "decode_fp8_batch64" else make_config(k)
+    return algorithmic_bytes(wl), (append_flops(wl) if k == 5 else None)
+
+
+def summarize(line: str, run_dir: str, command: str, warmup: int) -> str:
+    """Text summary of rocprofv3 runs of `--profile line` (kernel trace and / or
+    counters, CSV output under the comma-separated directories run_dir), for
+    profiles/."""
+    import csv
+    import glob
+    import re
+    out = [f"# rocprofv3 summary: {line} (one MI355X, gfx950)", f"# command: {command}",
+           f"line: {line}"]
+    nbytes, flops = line_work(line)
+    dirs = run_dir.split(",")
+    traces = [f for d in dirs for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"),
+                                                 recursive=True)]
+    counters = [f for d in dirs for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                                                   recursive=True)]
+    totals = {}
+    short = lambda n: re.sub(r"\(.*", "", re.sub(r"^(void )?pkfa::\(anonymous namespace\)::", "", n))
+    if traces:
+        rows = sorted(csv.DictReader(open(traces[0])), key=lambda r: int(r["Start_Timestamp"]))
+        by = {}
+        for r in rows:
+            by.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for name, ds in by.items():
+            if name.startswith("__amd") or "upload_kernel" in name:
+                continue
+            ds = ds[warmup:] if len(ds) > warmup else ds
+            out.append(f"kernel: {short(name)}  launches {len(ds)}  avg_us {np.mean(ds):.2f}  "
+                       f"min_us {np.min(ds):.2f}  max_us {np.max(ds):.2f}")
+        main_k = [n for n in by if not n.startswith("__amd") and "upload" not in n]
+        # the run call's time: all its kernels per call (cascade: two kernels)
+        per_call = sum(np.mean(by[n][warmup:] if len(by[n]) > warmup else by[n]) for n in main_k)
+        out.append(f"run_call_avg_us: {per_call:.2f}")
+        if flops:
+            out.append(f"algorithmic_flops_per_call: {flops:.0f}")
+            tf = flops / (per_call * 1e-6) / 1e12
+            out.append(f"achieved: {tf:.1f} TFLOP/s = {tf / MFMA_PEAK_TFLOPS:.4f} of "
+                       f"{MFMA_PEAK_TFLOPS} TFLOP/s bf16 dense MFMA peak")
+        else:
+            gbs = nbytes / (per_call * 1e-6) / 1e9
+            out.append(f"algorithmic_bytes_per_call: {nbytes}")
+            out.append(f"achieved: {gbs:.1f} GB/s = {gbs / HBM_PEAK_GBS:.4f} of "
+                       f"{HBM_PEAK_GBS:.0f} GB/s HBM peak")
+    for path in counters:
+        rows = list(csv.DictReader(open(path)))
+        per = {}
+        for r in rows:
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            per.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+            per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        copies = [v for (d, n), v in sorted(per.items()) if n == "__amd_rocclr_copyBuffer"
+                  and max(v.values()) > 1e5]
+        mine = [(d, n, v) for (d, n), v in sorted(per.items())
+                if not n.startswith("__amd") and "upload_kernel" not in n]
+        mine = mine[warmup * (2 if line == "cascade_batch256" else 1):]
+        names = sorted({c for _, _, v in mine for c in v})
+        for c in names:
+            by_k = {}
+            for _, n, v in mine:
+                if c in v:
+                    by_k.setdefault(short(n), []).append(v[c])
+            for kname, vals in by_k.items():
+                out.append(f"counter {c} {kname}: mean {np.mean(vals):.0f} over {len(vals)} "
+                           f"dispatches")
+        fetch = sum(np.mean([v["FETCH_SIZE"] for _, _, v in mine if "FETCH_SIZE" in v and n == kk])
+                    for kk in {n for _, n, v in mine if "FETCH_SIZE" in v}) if any(
+                        "FETCH_SIZE" in v for _, _, v in mine) else None
+        write = sum(np.mean([v["WRITE_SIZE"] for _, _, v in mine if "WRITE_SIZE" in v and n == kk])
+                    for kk in {n for _, n, v in mine if "WRITE_SIZE" in v}) if any(
+                        "WRITE_SIZE" in v for _, _, v in mine) else None
+        if copies and (fetch is not None or write is not None):
+            c = copies[0]
+            kib = 1 << 20  # the probe copies 1 GiB = 1048576 KiB
+            if fetch is not None and "FETCH_SIZE" in c:
+                f_scale = kib / c["FETCH_SIZE"]
+                out.append(f"fetch_scale (1 GiB copy: {c['FETCH_SIZE']:.0f} KiB read): {f_scale:.4f}")
+                out.append(f"fetch_bytes_per_call: {fetch * f_scale * 1024:.0f}")
+                totals["fetch"] = fetch * f_scale * 1024
+            if write is not None and "WRITE_SIZE" in c:
+                w_scale = kib / c["WRITE_SIZE"]
+                out.append(f"write_scale (1 GiB copy: {c['WRITE_SIZE']:.0f} KiB written): {w_scale:.4f}")
+                out.append(f"write_bytes_per_call: {write * w_scale * 1024:.0f}")
+                totals["write"] = write * w_scale * 1024
+    if "fetch" in totals and "write" in totals:
+        hbm = totals["fetch"] + totals["write"]
+        out.append(f"hbm_bytes_per_launch: {hbm:.0f}")
+        out.append(f"algorithmic_bytes_per_launch: {nbytes}")
+        out.append(f"traffic_over_algorithmic: {hbm / nbytes:.4f}")
+    out.append(f"kernel_source_sha256: {kernel_source_sha256(LINE_KERNEL[line])}")
+    return "\n".join(out) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true", help="skip the secondary lines")
+    ap.add_argument("--parts",
+                    default="single,batch128,cascade,append,fp8,ragged,single_ragged,bsr,pod",
+                    help="comma list of the secondary lines to run after the headline")
+    ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
+    ap.add_argument("--profile", choices=PROFILE_LINES,
+                    help="run only this line's run call (for rocprofv3), print no JSON")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="with --profile: one plain 1 GiB device copy first (scales byte counters)")
+    ap.add_argument("--summarize", metavar="DIRS",
+                    help="with --profile: print a text summary of the rocprofv3 output in DIRS "
+                         "(comma-separated)")
+    ap.add_argument("--command", default="", help="with --summarize: the command that made DIR")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path (requests "
+              "or kv heads would shard across GPUs with no exchange; long sequences by key "
+              "range, with an all-gather of partial states and a local merge).", file=sys.stderr)
+        sys.exit(2)
+    if args.profile and args.summarize:
+        sys.stdout.write(summarize(args.profile, args.summarize, args.command, args.warmup))
+        return
+    import torch
+    if args.profile:
+        profile_line(args.profile, args.steps, args.warmup, args.copy_probe)
+        return
+    from workloads import CONFIG_NAMES
+    knobs = {k: int(v) for k, v in (s.split("=") for s in args.knob)}
+
+    head, b, wl = line_decode(2, args.steps, args.warmup, knobs=knobs)
     host_plan_us = plan_us(b)
+    del b
+    torch.cuda.empty_cache()
     att = attainable_read_gbs()
-    nbytes = algorithmic_bytes(wl)
-    gbs = nbytes / (step_ms * 1e-3) / 1e9
-    kgbs = nbytes / (kernel_ms * 1e-3) / 1e9
-    st = b.plan.info()
-    traffic = stored_traffic()
+    rl = head["roofline"]
+    rl["attainable_GB/s"] = att["GB/s"]
+    rl["frac_of_attainable"] = round(rl["achieved"] / att["GB/s"], 4)
+    nbytes = rl["algorithmic_bytes"]
+    step_ms = head["ms_per_step"]
     line = {
         "metric": METRIC,
-        "value": round(gbs, 2),
+        "value": head["GB/s"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 5),
+        "ms_per_step": step_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[args.config],
-                   "batch": wl.batch, "num_qo_heads": wl.num_qo_heads,
-                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
-                   "page_size": wl.page_size, "kv_tokens": int(wl.kv_lens.sum()),
-                   "algorithmic_bytes": nbytes, "pool_copies": len(b.pools),
-                   "tiles": st.num_tiles, "split_units": st.num_merge,
-                   "workers": st.num_workers, "piece_pages": st.chunk_pages},
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(wl.batch / (step_ms * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(kgbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(kgbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel (one fa_decode call)",
-                     "kernel_ms": round(kernel_ms, 5), "algorithmic_bytes": nbytes,
-                     "attainable_GB/s": att["GB/s"],
-                     "frac_of_attainable": round(kgbs / att["GB/s"], 4)},
+        "config": {"workload": CONFIG_NAMES[2], "batch": wl.batch,
+                   "num_qo_heads": wl.num_qo_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "page_size": wl.page_size,
+                   "kv_tokens": head["kv_tokens"], "algorithmic_bytes": nbytes,
+                   "pool_copies": head["pool_copies"], **head["plan"]},
+        "pct_of_hbm_peak": head["pct_of_hbm_peak"],
+        "tokens_per_s": head["tokens_per_s"],
+        "roofline": rl,
         "host_plan_us": round(host_plan_us, 1),
     }
-    del b
-    torch.cuda.empty_cache()
     parts = set() if args.only_headline else set(filter(None, args.parts.split(",")))
-    if "batch128" in parts:
-        w3 = make_config(3)
-        b3 = DecodeBench(w3, **knobs)
-        s3, k3 = b3.run(args.steps, args.warmup)
-        n3 = algorithmic_bytes(w3)
-        line["batch128"] = {"workload": CONFIG_NAMES[3],
-                            "GB/s": round(n3 / (s3 * 1e-3) / 1e9, 2),
-                            "pct_of_hbm_peak": round(100 * n3 / (s3 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                            "tokens_per_s": round(128 / (s3 * 1e-3), 1),
-                            "ms_per_step": round(s3, 5), "kernel_ms": round(k3, 5)}
-        del b3, w3
-        torch.cuda.empty_cache()
-    if "cascade" in parts:
-        w4 = make_config(4)
-        b4 = CascadeBench(w4)
-        s4, k4 = b4.run(max(5, args.steps // 2), max(2, args.warmup // 2))
-        n4 = algorithmic_bytes(w4)
-        line["cascade"] = {"workload": CONFIG_NAMES[4],
-                           "GB/s": round(n4 / (s4 * 1e-3) / 1e9, 2),
-                           "pct_of_hbm_peak": round(100 * n4 / (s4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                           "tokens_per_s": round(256 / (s4 * 1e-3), 1),
-                           "ms_per_step": round(s4, 5), "kernel_ms": round(k4, 5),
-                           "algorithmic_bytes": n4}
-        del b4
-        torch.cuda.empty_cache()
-        # context: the same batch as one plain decode (each request re-reads the prefix)
-        wn = no_cascade_view(w4)
-        bn = DecodeBench(wn, max_tiles=40000, max_partials=40000, max_merge=4096)
-        sn, kn = bn.run(5, 2)
-        nn = algorithmic_bytes(wn)
-        # (its re-read prefix pages mostly come from the 256 MB Infinity Cache, so this
-        # effective rate is not an HBM figure)
-        line["cascade"]["no_cascade_decode"] = {
-            "kernel_ms": round(kn, 5), "ms_per_step": round(sn, 5), "algorithmic_bytes": nn,
-            "effective_GB/s": round(nn / (kn * 1e-3) / 1e9, 2)}
-        line["cascade"]["speedup_over_no_cascade"] = round(kn / k4, 2)
-        del bn, wn, w4
-        torch.cuda.empty_cache()
-    if "append" in parts:
-        w5 = make_config(5)
-        b5 = AppendBench(w5)
-        s5, k5 = b5.run(max(5, args.steps // 2), max(2, args.warmup // 2))
-        f5 = append_flops(w5)
-        line["append"] = {"workload": CONFIG_NAMES[5],
-                          "TFLOP/s": round(f5 / (k5 * 1e-3) / 1e12, 1),
-                          "mfma_utilisation": round(f5 / (k5 * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
-                          "flops": f5, "kernel_ms": round(k5, 5), "ms_per_step": round(s5, 5),
-                          "tokens_per_s": round(w5.rows / (s5 * 1e-3), 1)}
-        del b5, w5
-        torch.cuda.empty_cache()
-    if "fp8" in parts:
-        w8 = make_config(2, kv_dtype="e4m3")
-        b8 = DecodeBench(w8, **knobs)
-        s8, k8 = b8.run(args.steps, args.warmup)
-        n8 = algorithmic_bytes(w8)
-        line["fp8"] = {"workload": f"{CONFIG_NAMES[2]}, K/V pages in E4M3",
-                       "kv_dtype": "e4m3", "k_scale": w8.k_scale, "v_scale": w8.v_scale,
-                       "GB/s": round(n8 / (s8 * 1e-3) / 1e9, 2),
-                       "pct_of_hbm_peak": round(100 * n8 / (s8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                       "kernel_GB/s": round(n8 / (k8 * 1e-3) / 1e9, 2),
-                       "kernel_frac": round(n8 / (k8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                       "tokens_per_s": round(w8.batch / (s8 * 1e-3), 1),
-                       "ms_per_step": round(s8, 5), "kernel_ms": round(k8, 5),
-                       "algorithmic_bytes": n8}
-        del b8, w8
-        torch.cuda.empty_cache()
-    from workloads import make_ragged
-    for part, k in (("ragged", 2), ("single", 1)):
-        if part not in parts:
-            continue
-        wk = make_config(k)
-        rw = make_ragged(wk.kv_lens, wk.num_qo_heads, wk.num_kv_heads, wk.dtype, seed=k)
-        br = RaggedDecodeBench(rw, **knobs)
-        sr, kr = br.run(args.steps, args.warmup)
-        gr = br.graph_call_ms(len(br.kv))
-        nr = ragged_bytes(rw)
-        line[part] = {"workload": f"{CONFIG_NAMES[k]}, ragged (contiguous) K/V",
-                      "GB/s": round(nr / (sr * 1e-3) / 1e9, 2),
-                      "pct_of_hbm_peak": round(100 * nr / (sr * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-                      "kernel_GB/s": round(nr / (kr * 1e-3) / 1e9, 2),
-                      "tokens_per_s": round(rw.batch / (sr * 1e-3), 1),
-                      "ms_per_step": round(sr, 5), "kernel_ms": round(kr, 5),
-                      "graph_ms_per_call": round(gr, 5),
-                      "graph_GB/s": round(nr / (gr * 1e-3) / 1e9, 2),
-                      "algorithmic_bytes": nr, "kv_copies": len(br.kv)}
-        del br, rw, wk
-        torch.cuda.empty_cache()
-    if "bsr" in parts:
-        from workloads import make_block_sparse
-        bw = make_block_sparse([64] * 64, [64] * 256, 0.25, 32, 8, "bf16", seed=7)
-        bb = BlockSparseBench(bw)
-        sb, kb = bb.run(max(5, args.steps // 2), max(2, args.warmup // 2))
-        line["bsr"] = {"workload": "block-sparse prefill: 4096 query rows x 16384 keys, 64 x 64 "
-                                   "blocks, 25% kept (seeded), 32/8 heads, bf16",
-                       "TFLOP/s": round(bb.flops / (kb * 1e-3) / 1e12, 1),
-                       "mfma_utilisation": round(bb.flops / (kb * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS,
-                                                 4),
-                       "flops": bb.flops, "kernel_ms": round(kb, 5), "ms_per_step": round(sb, 5),
-                       "blocks_kept": int(len(bw.block_indices))}
-        del bb, bw
-        torch.cuda.empty_cache()
-    if "pod" in parts:
-        from workloads import make_workload
-        r5, r2 = np.random.default_rng(5), np.random.default_rng(2)
-        l5, l2 = config_lengths(5, r5), config_lengths(2, r2)
-        lens = np.concatenate([l5["kv_lens"], l2["kv_lens"]])
-        qo = np.concatenate([l5["qo_lens"], np.ones(len(l2["kv_lens"]), np.int64)])
-        wm = make_workload(lens, 32, 8, "bf16", 52, qo_lens=qo, causal=True, name="mixed")
-        n_pre = len(l5["kv_lens"])
-        res = {}
-        for sep in (False, True):
-            pb = PodBench(wm, n_pre, separate=sep)
-            sp, kp = pb.run(max(5, args.steps // 2), max(2, args.warmup // 2))
-            res[sep] = (sp, kp)
-            del pb
+    runners = [("single", lambda: line_single(args.steps, args.warmup)),
+               ("batch128", lambda: line_decode(3, args.steps, args.warmup, knobs=knobs)[0]),
+               ("cascade", lambda: line_cascade(args.steps, args.warmup)),
+               ("append", lambda: line_append(args.steps, args.warmup)),
+               ("fp8", lambda: line_decode(2, args.steps, args.warmup, kv_dtype="e4m3",
+                                           knobs=knobs)[0]),
+               ("ragged", lambda: line_ragged(2, args.steps, args.warmup)),
+               ("single_ragged", lambda: line_ragged(1, args.steps, args.warmup)),
+               ("bsr", lambda: line_bsr(args.steps, args.warmup)),
+               ("pod", lambda: line_pod(args.steps, args.warmup))]
+    for name, fn in runners:
+        if name in parts:
+            line[name] = fn()
             torch.cuda.empty_cache()
-        f5 = append_flops(make_config(5))
-        line["pod"] = {"workload": "mixed batch over one pool: causal append (16 x 512 rows onto "
-                                   "4096) + GQA decode (batch 64, kv U[512,4096]), 32/8 heads, bf16",
-                       "kernel_ms": round(res[False][1], 5),
-                       "separate_kernels_ms": round(res[True][1], 5),
-                       "speedup": round(res[True][1] / res[False][1], 3),
-                       "ms_per_step": round(res[False][0], 5),
-                       "tokens_per_s": round((wm.rows) / (res[False][0] * 1e-3), 1),
-                       "append_flops": f5}
-        del wm
-        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

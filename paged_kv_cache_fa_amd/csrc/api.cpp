@@ -628,7 +628,7 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
                               prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
                               prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
   pa.defer_merge = 1;  // the prefix chunks are merged together with the suffix below
-  if (!fork_pre && !fork_suf && kCascadeOneLaunch && G <= 4) {
+  if (!fork_pre && !fork_suf && kCascadeOneLaunch && G <= 4 && gp.qo_tile <= kPodCols / G) {
     // both passes in one launch, sharing the CUs
     e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, s);
     if (e != hipSuccess) return hip_fail(e, "cascade kernel launch");
@@ -676,9 +676,11 @@ fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* 
   const fa_geometry& gd = dp->geom;
   const int G = gd.num_qo_heads / gd.num_kv_heads;
   if (!qo_indptr_p_d || ga.dtype != gd.dtype || ga.num_qo_heads != gd.num_qo_heads ||
-      ga.num_kv_heads != gd.num_kv_heads || gd.kv_dtype != gd.dtype || G > 4) {
-    set_error("pod: the plans need the same dtype and heads, 16-bit K/V pages and "
-              "num_qo_heads / num_kv_heads <= 4, and qo_indptr");
+      ga.num_kv_heads != gd.num_kv_heads || gd.kv_dtype != gd.dtype || G > 4 ||
+      ga.qo_tile > kPodCols / G) {
+    set_error("pod: the plans need the same dtype and heads, 16-bit K/V pages, "
+              "num_qo_heads / num_kv_heads <= 4, a prefill qo_tile of at most 128 / G and "
+              "qo_indptr");
     return FA_ERR_INVALID;
   }
   const AttnParams pa = make_params(pp, q_p, k_pages, v_pages, page_stride, token_stride,

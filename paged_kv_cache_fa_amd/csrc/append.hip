@@ -5,21 +5,24 @@
 namespace pkfa {
 namespace {
 
+constexpr int kWaves = 8;  // one 512-thread workgroup per CU, 2 waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+
 template <int DT, int G>
-__global__ __launch_bounds__(app::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void append_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[3 * app::VLayout<3>::kBufElems];
   __shared__ int s_flag;
-  app::append_worker<DT, G, 3>(p, (int)blockIdx.x, (int)gridDim.x, smem, s_flag);
+  app::append_worker<DT, G, 3, kWaves>(p, (int)blockIdx.x, (int)gridDim.x, smem, s_flag);
 }
 
 template <int DT>
 hipError_t launch_dt(const AttnParams& p, int group, int grid, hipStream_t s) {
   switch (group) {
-    case 1: hipLaunchKernelGGL((append_kernel<DT, 1>), dim3(grid), dim3(app::kThreads), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((append_kernel<DT, 2>), dim3(grid), dim3(app::kThreads), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((append_kernel<DT, 4>), dim3(grid), dim3(app::kThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((append_kernel<DT, 8>), dim3(grid), dim3(app::kThreads), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((append_kernel<DT, 1>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((append_kernel<DT, 2>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((append_kernel<DT, 4>), dim3(grid), dim3(kThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((append_kernel<DT, 8>), dim3(grid), dim3(kThreads), 0, s, p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

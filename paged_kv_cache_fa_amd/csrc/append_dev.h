@@ -61,9 +61,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kCols = 32 * kWaves;  // query columns of a tile
+// Workgroups of WAVES waves (a template parameter): 8 in the append kernel
+// (one workgroup per CU, 2 waves per SIMD), 4 in the one-launch mixed kernel,
+// whose append workgroups share each CU with decode workgroups. A workgroup
+// covers 32 WAVES query columns.
 constexpr int kBlockKeys = 64;
 constexpr int kKStride = 136;  // 16-bit elements per K slot row in LDS (128 dims + 8 pad)
 constexpr int kKElems = kBlockKeys * kKStride;
@@ -143,11 +144,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // STAGES: LDS buffers of the block loop, 3 (software pipeline: the scores of
 // block j+1 beside the softmax of block j) or 2 (one block at a time, for a
-// workgroup that shares its CU).
-template <int DT, int G, int STAGES>
+// workgroup that shares its CU). A tile's rows must fit the workgroup's
+// 32 WAVES / G positions (the planner's qo_tile).
+template <int DT, int G, int STAGES, int WAVES>
 __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, uint16_t* smem,
                                             int& s_flag) {
-  constexpr int PT = kCols / G;  // query positions per tile
+  constexpr int kCols = 32 * WAVES;  // query columns of the workgroup
+  constexpr int PT = kCols / G;      // query positions per tile
   using VL = VLayout<STAGES>;
   constexpr int kBufElems = VL::kBufElems;
   const int tid = threadIdx.x;
@@ -213,19 +216,28 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
   const int nblocks = key1 > key0 ? (key1 - key0 + kBlockKeys - 1) / kBlockKeys : 0;
   const int first_page = key0 >> 4;  // chunks start on a page boundary
 
-  // --- K/V staging: waves 0-3 stage K, waves 4-7 V (wave-uniform role);
-  // thread st = tid mod 256 of a role = (token row tr of each of the 4 pages,
-  // dims 8 dg..): st bits [1:0] and [5:4] give dg, bits [3:2] and [7:6] give
-  // tr: a wave reads 4 whole token rows per load, and 16 lanes that store
-  // together cover 4 dg x 4 tr (conflict-free V^T stores under vswz).
-  const bool stage_v = wave >= 4;
-  const int st = tid & 255;
-  const int dg = (st & 3) | ((st >> 2) & 12), tr = ((st >> 2) & 3) | ((st >> 4) & 12);
+  // --- K/V staging: the first half of the waves stage K, the second half V
+  // (a wave-uniform role; one of each per SIMD). The 256 (token row tr of each
+  // of the block's 4 pages, 16-byte dim group dg) pairs of a role are dealt
+  // to its 32 WAVES threads in kPasses passes: pair st (st bits [1:0] and
+  // [5:4] give dg, bits [3:2] and [7:6] give tr) is thread st mod 32 WAVES,
+  // pass st / (32 WAVES). A wave reads 4 whole token rows per load, and 16
+  // lanes that store together cover 4 dg x 4 tr.
+  constexpr int kRoleThreads = 32 * WAVES;
+  constexpr int kPasses = 256 / kRoleThreads;
+  const bool stage_v = wave >= WAVES / 2;
+  const int st0 = tid % kRoleThreads;
+  const int dg = (st0 & 3) | ((st0 >> 2) & 12);
+  int trp[kPasses];
+#pragma unroll
+  for (int r = 0; r < kPasses; ++r) {
+    const int st = st0 + r * kRoleThreads;
+    trp[r] = ((st >> 2) & 3) | ((st >> 4) & 12);
+  }
   const uint32_t row_bytes = (uint32_t)p.token_stride * 2u;
-  const uint32_t ld_off = (uint32_t)tr * row_bytes + 16u * dg;
   const int64_t head_off = (int64_t)hk * p.head_stride;
   const uint16_t* src = stage_v ? p.v : p.k;
-  u32x4 stg[4];
+  u32x4 stg[4 * kPasses];
   int pid[4];
   // page ids of a block: lanes 0..3 load them (index clamped to the request's
   // last page: a block past the end fetches nothing, see nbytes below), and
@@ -245,9 +257,12 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
       const int nbytes =
           __builtin_amdgcn_readfirstlane(min(max(key1 - kstart, 0), 16) * (int)row_bytes);
       const int64_t base = (int64_t)pid[i] * p.page_stride + head_off;
-      const __amdgpu_buffer_rsrc_t r =
+      const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)(src + base), 0, nbytes, 0x00020000);
-      stg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, ld_off, 0, 0);
+#pragma unroll
+      for (int r = 0; r < kPasses; ++r)
+        stg[4 * r + i] = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, (uint32_t)trp[r] * row_bytes + 16u * dg, 0, 0);
     }
   };
   auto store = [&](int buf) {
@@ -255,30 +270,39 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
     uint16_t* sv = sk + kKElems;
     if (!stage_v) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(sk + (4 * tr + i) * kKStride + 8 * dg) = stg[i];
+      for (int r = 0; r < kPasses; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x4*>(sk + (4 * trp[r] + i) * kKStride + 8 * dg) = stg[4 * r + i];
       return;
     }
     // Dims d = 8 dg + 2 w and d + 1 go to V^T rows d, d + 1: the thread's 4
     // slots 4 tr .. 4 tr + 3 are the first (tr bit 1 clear) or second half of
-    // unit 2 (tr >> 2) + (tr & 1), at position unit ^ swz(row). u and the
-    // row base are recomputed here on every call (the empty asm hides that
-    // they do not change), so the compiler does not keep 8 loop-invariant
-    // addresses live through the block loop.
-    int u = (2 * (tr >> 2) + (tr & 1)) ^ VL::swz_base(dg);
-    int vbase = 2 * VL::kRow * 8 * dg + 8 * ((tr >> 1) & 1);
-    asm volatile("" : "+v"(u), "+v"(vbase));
+    // unit 2 (tr >> 2) + (tr & 1), at position unit ^ swz(row) (tr bit 1 is
+    // the same in every pass). u and the row base are recomputed here on
+    // every call (the empty asm hides that they do not change), so the
+    // compiler does not keep 8 loop-invariant addresses live through the
+    // block loop.
+    int vbase = 2 * VL::kRow * 8 * dg + 8 * ((trp[0] >> 1) & 1);
+    asm volatile("" : "+v"(vbase));
     char* sv8 = reinterpret_cast<char*>(sv) + vbase;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = stg[0][w], a1 = stg[1][w], a2 = stg[2][w], a3 = stg[3][w];
-      const u32x2 lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                        __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-      const u32x2 hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                        __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-      *reinterpret_cast<u32x2*>(sv8 + 2 * w * 2 * VL::kRow + 16 * (u ^ VL::swz_step(w, 0))) = lo;
-      *reinterpret_cast<u32x2*>(sv8 + (2 * w + 1) * 2 * VL::kRow + 16 * (u ^ VL::swz_step(w, 1))) =
-          hi;
+    for (int r = 0; r < kPasses; ++r) {
+      int u = (2 * (trp[r] >> 2) + (trp[r] & 1)) ^ VL::swz_base(dg);
+      asm volatile("" : "+v"(u));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a0 = stg[4 * r][w], a1 = stg[4 * r + 1][w], a2 = stg[4 * r + 2][w],
+                       a3 = stg[4 * r + 3][w];
+        const u32x2 lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                          __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+        const u32x2 hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                          __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+        *reinterpret_cast<u32x2*>(sv8 + 2 * w * 2 * VL::kRow + 16 * (u ^ VL::swz_step(w, 0))) =
+            lo;
+        *reinterpret_cast<u32x2*>(sv8 + (2 * w + 1) * 2 * VL::kRow +
+                                  16 * (u ^ VL::swz_step(w, 1))) = hi;
+      }
     }
   };
 
@@ -541,13 +565,13 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
 // positions i / 8, i / 8 + gridDim.x / 8, ... of the bin.
 // Workgroup `block` of `nblocks` runs the tiles of bin block mod 8, strided
 // by nblocks / 8 (nblocks a multiple of 8).
-template <int DT, int G, int STAGES>
+template <int DT, int G, int STAGES, int WAVES>
 __device__ __forceinline__ void append_worker(const AttnParams& p, int block, int nblocks,
                                               uint16_t* smem, int& s_flag) {
   const int x = block % kAppendBins, stride = nblocks / kAppendBins;
   const int t1 = p.worker_ptr[x + 1];
   for (int t = p.worker_ptr[x] + block / kAppendBins; t < t1; t += stride)
-    append_tile<DT, G, STAGES>(p, t, smem, s_flag);
+    append_tile<DT, G, STAGES, WAVES>(p, t, smem, s_flag);
 }
 
 }  // namespace app

@@ -42,7 +42,9 @@ hipError_t launch_decode(const AttnParams& p, int dtype, bool kv_e4m3, int group
                          hipStream_t s);
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
 // Cascade's two passes in one launch: decode workers (dp, `workers` waves)
-// and append tiles (ap, its max_tiles grid); group 1, 2 or 4.
+// and append tiles (ap, its max_tiles grid); group 1, 2 or 4, append tiles of
+// at most kPodCols / group query positions.
+constexpr int kPodCols = 128;
 hipError_t launch_pod(const AttnParams& dp, int workers, const AttnParams& ap, int max_tiles,
                       int dtype, int group, hipStream_t s);
 // Copy n_words 32-bit words from device-visible pinned host memory into device

@@ -5,12 +5,13 @@
 // mixed prefill + decode batches of POD-attention named in section
 // "Features (from the repository README)").
 //
-// Workgroups 0 .. dec_blocks-1 are decode workers (8 independent waves, the
+// Workgroups 0 .. dec_blocks-1 are decode workers (4 independent waves, the
 // suffix plan's work lists); the rest run the prefix plan's append tiles
-// (bins by workgroup index mod 8, as in the append kernel). Both roles are
-// compiled for 2 waves per SIMD (at most 256 registers each), so decode and
-// append waves share the CUs: the append waves' matrix work overlaps the
-// decode waves' memory streaming. The decode role keeps a
+// (bins by workgroup index mod 8, as in the append kernel) with 4 waves, so
+// their tiles hold at most 128 / G query positions. Both roles are compiled
+// for 2 waves per SIMD (at most 256 registers each) and a CU holds one
+// decode and one append workgroup at once: the append waves' matrix work
+// overlaps the decode waves' memory streaming. The decode role keeps a
 // 2-page ring to fit the register budget. Split units merge as in the two
 // kernels (the prefix pass defers to the cascade combine).
 #include "append_dev.h"
@@ -19,26 +20,29 @@
 namespace pkfa {
 namespace {
 
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
 template <int DT, int G>
-__global__ __launch_bounds__(app::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pod_kernel(AttnParams dp, AttnParams ap, int dec_blocks) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * app::VLayout<2>::kBufElems];
   __shared__ int s_flag;
   const int blk = (int)blockIdx.x;
   if (blk < dec_blocks)
     dec::decode_worker<DT, G, 2, false>(
-        dp, blk * app::kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)));
+        dp, blk * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)));
   else
-    app::append_worker<DT, G, 2>(ap, blk - dec_blocks, (int)gridDim.x - dec_blocks, smem, s_flag);
+    app::append_worker<DT, G, 2, kWaves>(ap, blk - dec_blocks, (int)gridDim.x - dec_blocks, smem, s_flag);
 }
 
 template <int DT>
 hipError_t launch_dt(const AttnParams& dp, const AttnParams& ap, int group, int dec_blocks,
                      int grid, hipStream_t s) {
   switch (group) {
-    case 1: hipLaunchKernelGGL((pod_kernel<DT, 1>), dim3(grid), dim3(app::kThreads), 0, s, dp, ap, dec_blocks); break;
-    case 2: hipLaunchKernelGGL((pod_kernel<DT, 2>), dim3(grid), dim3(app::kThreads), 0, s, dp, ap, dec_blocks); break;
-    case 4: hipLaunchKernelGGL((pod_kernel<DT, 4>), dim3(grid), dim3(app::kThreads), 0, s, dp, ap, dec_blocks); break;
+    case 1: hipLaunchKernelGGL((pod_kernel<DT, 1>), dim3(grid), dim3(kThreads), 0, s, dp, ap, dec_blocks); break;
+    case 2: hipLaunchKernelGGL((pod_kernel<DT, 2>), dim3(grid), dim3(kThreads), 0, s, dp, ap, dec_blocks); break;
+    case 4: hipLaunchKernelGGL((pod_kernel<DT, 4>), dim3(grid), dim3(kThreads), 0, s, dp, ap, dec_blocks); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
@@ -50,7 +54,7 @@ hipError_t launch_pod(const AttnParams& dp, int workers, const AttnParams& ap, i
                       int dtype, int group, hipStream_t s) {
   // decode workgroups first (a multiple of 8, so the append part keeps its
   // XCD bins), then the append grid of the append kernel
-  constexpr int kPerBlock = app::kWaves;
+  constexpr int kPerBlock = kWaves;
   const int dec_blocks = (workers + 8 * kPerBlock - 1) / (8 * kPerBlock) * 8;
   const int app_blocks = (max_tiles + kAppendBins - 1) / kAppendBins * kAppendBins;
   const int grid = dec_blocks + app_blocks;

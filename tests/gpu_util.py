@@ -124,8 +124,12 @@ def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, fused=False
     wl = dw.wl
     B = wl.batch
     if prefix_plan is None:
+        # prefix q tiles of 128 / G rows fit the one-launch cascade kernel's
+        # append workgroups (wider tiles run the two-launch form)
+        pk = dict(knobs.get("prefix", {}))
+        pk.setdefault("qo_tile", 128 // (wl.num_qo_heads // wl.num_kv_heads))
         g = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads,
-                        max_qo_tokens=B, **knobs.get("prefix", {}))
+                        max_qo_tokens=B, **pk)
         prefix_plan = fa.Plan(g, device=dw.device)
         prefix_plan.plan(wl.prefix_indptr, [wl.prefix_len], [0, B], False)
     if suffix_plan is None:

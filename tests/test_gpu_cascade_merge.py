@@ -213,3 +213,15 @@ def test_cascade_equals_decode_over_prefix_and_suffix():
     assert_close(to_f64(out_d), to_f64(lse_d), *direct, what="decode over prefix ++ suffix")
     assert_close(to_f64(out_c), to_f64(lse_c), to_f64(out_d), to_f64(lse_d),
                  what="cascade vs decode")
+
+
+def test_cascade_wide_prefix_tiles_two_launches():
+    """A prefix plan with q tiles wider than the one-launch kernel's 128 / G
+    positions (the planner's default for append) runs as the suffix decode and
+    the append kernel in order, then the combine; same results as the oracle."""
+    wl = make_cascade(512, [5, 16, 300, 0, 900], 32, 8, "bf16", 24, mode="test")
+    dw = DevWorkload(wl)
+    out, lse, plans = run_cascade(dw, fused=True, prefix={"qo_tile": 64, "num_cu": 8},
+                                  suffix={"num_cu": 8})
+    assert plans[0].info().resolved.qo_tile == 64
+    assert_close(to_f64(out), to_f64(lse), *oracle_cascade(wl), what="cascade wide tiles")

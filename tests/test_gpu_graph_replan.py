@@ -201,7 +201,7 @@ def test_cascade_graph_replan():
     slots = Slots(wls, prefix=True)
     s = torch.cuda.Stream()
     B = max(w.batch for w in wls)
-    gp = fa.geometry("append", "bf16", 1, 32, 8, max_qo_tokens=B, num_cu=8)
+    gp = fa.geometry("append", "bf16", 1, 32, 8, max_qo_tokens=B, num_cu=8, qo_tile=32)
     pplan = fa.Plan(gp, device="cuda")
     splan = fa.Plan(fa.geometry("decode", "bf16", B, 32, 8, num_cu=8), device="cuda")
 

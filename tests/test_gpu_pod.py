@@ -48,7 +48,7 @@ def test_pod_mixed_batch(group, causal):
     strides = (2 * ps * hk * d, hk * d, d)
     k, v = pool[:, 0], pool[:, 1]
     gp = fa.geometry("append", "bf16", len(pre_lens), hkv * group, hkv, max_qo_tokens=nrows_p,
-                     num_cu=32)
+                     num_cu=32, qo_tile=128 // group)
     gd = fa.geometry("decode", "bf16", len(dec_lens), hkv * group, hkv, num_cu=32)
     pp = fa.plan(gp, pre["kv_indptr"], pre["kv_lens"], pre["qo_indptr"], causal, device="cuda")
     dp = fa.plan(gd, dec["kv_indptr"], dec["kv_lens"], device="cuda")
@@ -68,3 +68,25 @@ def test_pod_mixed_batch(group, causal):
     ref_d = oracle.decode(wl.q[nrows_p:], wl.pool, "bf16", dec["kv_indptr"], dec["kv_indices"],
                           dec["last"], 16)
     assert_close(to_f64(od), to_f64(ld), *ref_d, what="pod decode")
+
+
+def test_pod_refuses_wide_prefill_tiles():
+    """fa_pod's append workgroups hold 128 / G query positions: a prefill plan
+    with wider q tiles (the append kernel's default) is refused."""
+    import torch
+    import paged_kv_cache_fa_amd as fa
+    wl = make_workload([300, 40], 16, 4, "bf16", 3, qo_lens=[100, 1], causal=True, mode="test")
+    pre, dec, nrows_p = split_mixed(wl, 1)
+    gp = fa.geometry("append", "bf16", 1, 16, 4, max_qo_tokens=nrows_p)   # qo_tile 256 / 4
+    gd = fa.geometry("decode", "bf16", 1, 16, 4)
+    pp = fa.plan(gp, pre["kv_indptr"], pre["kv_lens"], pre["qo_indptr"], True, device="cuda")
+    dp = fa.plan(gd, dec["kv_indptr"], dec["kv_lens"], device="cuda")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    pool = torch.zeros(wl.pool.shape, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(wl.q.shape, dtype=torch.bfloat16, device="cuda")
+    _, _, ps, hk, d = wl.pool.shape
+    with pytest.raises(fa.FAError) as e:
+        fa.pod(pp, q[:nrows_p], t(pre["qo_indptr"]), t(pre["kv_indices"]), t(pre["kv_indptr"]),
+               t(pre["last"]), dp, q[nrows_p:], t(dec["kv_indices"]), t(dec["kv_indptr"]),
+               t(dec["last"]), pool[:, 0], pool[:, 1], 2 * ps * hk * d, hk * d, d)
+    assert e.value.code == "INVALID"
