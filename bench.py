@@ -65,6 +65,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2516.6  # bf16 dense: 256 CU x 4096 FLOP/clk x 2.4 GHz
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
 METRIC = "paged decode achieved HBM GB/s (% of peak) and tokens/sec at batch 64/128"
 
 
@@ -815,6 +816,12 @@ def line_work(line: str):
     return algorithmic_bytes(wl), (append_flops(wl) if k == 5 else None)
 
 
+def is_path_kernel(name: str) -> bool:
+    """A kernel of the attention path (not the plan upload, nor a runtime or
+    torch kernel)."""
+    return "pkfa::" in name and "upload_kernel" not in name and "stream_read" not in name
+
+
 def summarize(line: str, run_dir: str, command: str, warmup: int) -> str:
     """Text summary of rocprofv3 runs of `--profile line` (kernel trace and / or
     counters, CSV output under the comma-separated directories run_dir), for
@@ -839,12 +846,12 @@ def summarize(line: str, run_dir: str, command: str, warmup: int) -> str:
             by.setdefault(r["Kernel_Name"], []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         for name, ds in by.items():
-            if name.startswith("__amd") or "upload_kernel" in name:
+            if not is_path_kernel(name):
                 continue
             ds = ds[warmup:] if len(ds) > warmup else ds
             out.append(f"kernel: {short(name)}  launches {len(ds)}  avg_us {np.mean(ds):.2f}  "
                        f"min_us {np.min(ds):.2f}  max_us {np.max(ds):.2f}")
-        main_k = [n for n in by if not n.startswith("__amd") and "upload" not in n]
+        main_k = [n for n in by if is_path_kernel(n)]
         # the run call's time: all its kernels per call (cascade: two kernels)
         per_call = sum(np.mean(by[n][warmup:] if len(by[n]) > warmup else by[n]) for n in main_k)
         out.append(f"run_call_avg_us: {per_call:.2f}")
@@ -867,8 +874,7 @@ def summarize(line: str, run_dir: str, command: str, warmup: int) -> str:
             per[key][r["Counter_Name"]] += float(r["Counter_Value"])
         copies = [v for (d, n), v in sorted(per.items()) if n == "__amd_rocclr_copyBuffer"
                   and max(v.values()) > 1e5]
-        mine = [(d, n, v) for (d, n), v in sorted(per.items())
-                if not n.startswith("__amd") and "upload_kernel" not in n]
+        mine = [(d, n, v) for (d, n), v in sorted(per.items()) if is_path_kernel(n)]
         mine = mine[warmup * (2 if line == "cascade_batch256" else 1):]
         names = sorted({c for _, _, v in mine for c in v})
         for c in names:
@@ -879,12 +885,15 @@ def summarize(line: str, run_dir: str, command: str, warmup: int) -> str:
             for kname, vals in by_k.items():
                 out.append(f"counter {c} {kname}: mean {np.mean(vals):.0f} over {len(vals)} "
                            f"dispatches")
-        fetch = sum(np.mean([v["FETCH_SIZE"] for _, _, v in mine if "FETCH_SIZE" in v and n == kk])
-                    for kk in {n for _, n, v in mine if "FETCH_SIZE" in v}) if any(
-                        "FETCH_SIZE" in v for _, _, v in mine) else None
-        write = sum(np.mean([v["WRITE_SIZE"] for _, _, v in mine if "WRITE_SIZE" in v and n == kk])
-                    for kk in {n for _, n, v in mine if "WRITE_SIZE" in v}) if any(
-                        "WRITE_SIZE" in v for _, _, v in mine) else None
+        def per_call(counter):
+            # sum over the call's kernels of each kernel's mean per dispatch
+            by_name = {}
+            for _, n, v in mine:
+                if counter in v:
+                    by_name.setdefault(n, []).append(v[counter])
+            return sum(np.mean(x) for x in by_name.values()) if by_name else None
+
+        fetch, write = per_call("FETCH_SIZE"), per_call("WRITE_SIZE")
         if copies and (fetch is not None or write is not None):
             c = copies[0]
             kib = 1 << 20  # the probe copies 1 GiB = 1048576 KiB
@@ -898,6 +907,27 @@ def summarize(line: str, run_dir: str, command: str, warmup: int) -> str:
                 out.append(f"write_scale (1 GiB copy: {c['WRITE_SIZE']:.0f} KiB written): {w_scale:.4f}")
                 out.append(f"write_bytes_per_call: {write * w_scale * 1024:.0f}")
                 totals["write"] = write * w_scale * 1024
+        # MFMA occupancy of the dominant kernel: busy cycles of the matrix units
+        # over (GPU-active cycles of one XCD x 1024 SIMDs); GRBM_GUI_ACTIVE is
+        # summed over the 8 XCDs, and its cycles over the dispatch's duration give
+        # the clock the kernel actually ran at
+        busy = [v for _, n, v in mine if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "GRBM_GUI_ACTIVE" in v]
+        if busy:
+            act = np.mean([v["GRBM_GUI_ACTIVE"] for v in busy]) / N_XCD
+            mb = np.mean([v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in busy])
+            out.append(f"mfma_busy_frac (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/{N_XCD} x "
+                       f"{N_SIMD} SIMDs)): {mb / (act * N_SIMD):.4f}")
+            spans = {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+                     for r in rows}
+            durs = [spans[d] for d, n, v in mine
+                    if "SQ_VALU_MFMA_BUSY_CYCLES" in v and "GRBM_GUI_ACTIVE" in v]
+            if durs:
+                out.append(f"active_clock_GHz (GRBM_GUI_ACTIVE/{N_XCD} over the dispatch time "
+                           f"under counter collection): {act / np.mean(durs) / 1e9:.3f}")
+            if "SQ_BUSY_CU_CYCLES" in busy[0]:
+                cu = np.mean([v["SQ_BUSY_CU_CYCLES"] for v in busy])
+                out.append(f"cu_busy_frac (SQ_BUSY_CU_CYCLES / (GRBM_GUI_ACTIVE/{N_XCD} x "
+                           f"{N_CU} CUs)): {cu / (act * N_CU):.4f}")
     if "fetch" in totals and "write" in totals:
         hbm = totals["fetch"] + totals["write"]
         out.append(f"hbm_bytes_per_launch: {hbm:.0f}")

@@ -117,8 +117,11 @@ typedef struct {
   fa_geometry resolved;    /* geometry with every default filled in */
 } fa_plan_stats;
 
-/* Host and device workspace sizes in bytes for a geometry. Either output may
- * be NULL. Errors: FA_ERR_INVALID / FA_ERR_UNSUPPORTED for a bad geometry. */
+/* Host and device workspace sizes in bytes for a geometry ([DeepDive]
+ * "Snippet One": the caller allocates the decode wrapper's workspace buffer
+ * once and the plan and run calls work inside it; here the two sizes are
+ * exact for the geometry instead of a fixed 128 MB). Either output may be
+ * NULL. Errors: FA_ERR_INVALID / FA_ERR_UNSUPPORTED for a bad geometry. */
 fa_status fa_workspace_size(const fa_geometry* geom, size_t* host_bytes, size_t* device_bytes);
 
 /* Build the split-KV work plan on the host ([Guide] "What FlashInfer is",
@@ -195,7 +198,9 @@ fa_status fa_block_sparse_pages(const int32_t* block_indptr_h, const int32_t* bl
 /* Summary of the current plan. */
 fa_status fa_plan_info(const fa_plan_t* plan, fa_plan_stats* stats);
 
-/* Host copies of the current plan, valid until the next fa_plan on this plan.
+/* Host copies of the current plan ([Guide] "What FlashInfer is", idea 3: the
+ * load-balanced tile assignment that the plan phase computes; exposed so a
+ * caller can inspect the balance), valid until the next fa_plan on this plan.
  * tiles int32 [num_tiles][8]:
  *   decode  {request, kv_head, kv_indptr[request], first_slot, key_begin, key_end, slot,
  *           n_pieces};
@@ -412,7 +417,10 @@ fa_status fa_merge_states(const void* v, const float* s, int64_t n, int32_t k, i
 fa_status fa_probe_stream_read(const void* src, int64_t bytes, uint32_t* flag, int32_t workgroups,
                                void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code. Error reporting of this interface
+ * itself: the pages define no error codes (their Python calls raise), so
+ * every entry point returns one of the FA_ codes above and these two calls
+ * turn it into text. */
 const char* fa_status_string(fa_status status);
 
 /* Detail of the last error raised on the calling thread ("" if none). */

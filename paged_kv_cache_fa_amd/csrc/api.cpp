@@ -10,7 +10,10 @@
 // only; their grids depend on the resolved geometry alone.
 #include <hip/hip_runtime_api.h>
 
+#include <sched.h>
+
 #include <algorithm>
+#include <atomic>
 #include <math.h>
 #include <string.h>
 
@@ -30,6 +33,23 @@ const char* last_error();
 using namespace pkfa;
 
 namespace {
+
+// Wait until the copy kernel of this plan's last upload out of pinned host
+// memory has read the image: each of its workgroups stores the upload's
+// sequence number into its word of the host workspace's flag area.
+void wait_upload_flags(PlanImpl* pl) {
+  if (!pl->flag_ws) return;
+  const volatile uint32_t* f = reinterpret_cast<const volatile uint32_t*>(
+      static_cast<const uint8_t*>(pl->flag_ws) + pl->lay.host_flags);
+  for (int spin = 0;; ++spin) {
+    int i = 0;
+    while (i < pl->flag_n && f[i] == pl->flag_seq) ++i;
+    if (i == pl->flag_n) break;
+    if (spin > 256) sched_yield();
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  pl->flag_ws = nullptr;
+}
 
 fa_status hip_fail(hipError_t e, const char* what) {
   set_error("%s: %s", what, hipGetErrorString(e));
@@ -169,6 +189,9 @@ fa_status plan_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_t* k
     pl->magic = kPlanMagic;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // a copy kernel still reading host_ws must finish before it is rewritten (a
+  // copy out of another host workspace leaves this one alone)
+  if (pl->flag_ws == host_ws) wait_upload_flags(pl);
   if (dev_ws) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     hipError_t e = hipStreamIsCapturing(s, &cs);
@@ -227,14 +250,34 @@ fa_status plan_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_t* k
       pl->upload_src = attr.devicePointer;
     (void)hipGetLastError();  // a pageable pointer leaves an error behind; drop it
   }
+  // With events (fa_plan), a copy kernel out of pinned memory reports through
+  // the flag area of host_ws; the next fa_plan on this plan waits for it.
+  const bool flags = events && pl->upload_src;
+  if (flags && (pl->flags_cleared_ws != host_ws || pl->flags_cleared_off != pl->lay.host_flags)) {
+    // new flag words: clear whatever the memory held (no copy of this plan
+    // is pending on them: fa_plan waited above for any copy out of host_ws)
+    memset(static_cast<uint8_t*>(host_ws) + pl->lay.host_flags, 0, kUploadMaxGrid * 4);
+    pl->flags_cleared_ws = host_ws;
+    pl->flags_cleared_off = pl->lay.host_flags;
+  }
+  const uint32_t seq = pl->flag_seq + 1 == 0 ? 1 : pl->flag_seq + 1;
   if (pl->upload_src)
     e = launch_upload(static_cast<uint32_t*>(dev_ws), static_cast<const uint32_t*>(pl->upload_src),
-                      (int64_t)(bytes / 4), s);
+                      (int64_t)(bytes / 4),
+                      flags ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(pl->upload_src) +
+                                                          pl->lay.host_flags)
+                            : nullptr,
+                      seq, s);
   else
     e = hipMemcpyAsync(dev_ws, host_ws, bytes, hipMemcpyHostToDevice, s);
   if (e != hipSuccess) {
     pl->planned = 0;
     return hip_fail(e, "plan upload");
+  }
+  if (flags) {
+    pl->flag_ws = host_ws;
+    pl->flag_seq = seq;
+    pl->flag_n = upload_grid((int64_t)(bytes / 4));
   }
   if (!events) {
     // no event guards host_ws: wait here until the upload has read it
@@ -256,10 +299,12 @@ fa_status plan_upload(fa_plan_t* plan, const fa_geometry* geom, const int32_t* k
     }
     *slot = ev;
   }
-  e = hipEventRecord(static_cast<hipEvent_t>(pl->upload_event), s);
-  if (e != hipSuccess) {
-    pl->planned = 0;
-    return hip_fail(e, "hipEventRecord");
+  if (!flags) {
+    e = hipEventRecord(static_cast<hipEvent_t>(pl->upload_event), s);
+    if (e != hipSuccess) {
+      pl->planned = 0;
+      return hip_fail(e, "hipEventRecord");
+    }
   }
   pl->uploaded = 1;
   return FA_OK;
@@ -426,6 +471,8 @@ fa_status fa_plan_destroy(fa_plan_t* plan) {
   if (!plan) return FA_OK;
   PlanImpl* pl = impl(plan);
   if (pl->magic == kPlanMagic) {
+    // a pending copy still reads the host workspace and will write its flags
+    wait_upload_flags(pl);
     for (void* ev : {pl->upload_event, pl->fork_event, pl->join_event, pl->join2_event})
       if (ev) (void)hipEventDestroy(static_cast<hipEvent_t>(ev));
   }

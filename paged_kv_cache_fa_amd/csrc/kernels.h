@@ -49,7 +49,11 @@ hipError_t launch_pod(const AttnParams& dp, int workers, const AttnParams& ap, i
                       int dtype, int group, hipStream_t s);
 // Copy n_words 32-bit words from device-visible pinned host memory into device
 // memory with a small kernel (both 16-byte aligned).
-hipError_t launch_upload(uint32_t* dst, const uint32_t* src, int64_t n_words, hipStream_t s);
+// Copy n_words from src (device-visible host memory) to dst; when flags is not
+// null, workgroup i stores seq into flags[i] once its reads are done.
+int upload_grid(int64_t n_words);
+hipError_t launch_upload(uint32_t* dst, const uint32_t* src, int64_t n_words, uint32_t* flags,
+                         uint32_t seq, hipStream_t s);
 hipError_t launch_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
                               void* vo, float* so, int64_t n, int heads, int head_dim, int dtype,
                               hipStream_t s);

@@ -18,8 +18,10 @@
 //
 // Append (MFMA-bound, one workgroup per tile): every q tile is cut into
 // chunks of P = max(min_chunk_pages, ceil(units / target)) pages, so tiles
-// cost about the same; tiles are ordered by descending cost so in-order
-// dispatch starts the longest first.
+// cost about the same. The (request, kv head) groups are dealt, largest
+// first, to 8 bins of least cost, one per XCD, so the q tiles that read the
+// same keys run on one XCD and share its L2; within a bin a group's tiles are
+// listed in descending cost, and workgroup i runs tiles of bin i mod 8.
 //
 // Launch shapes depend only on capacities derived from the geometry, never on
 // the lengths, which keeps a captured graph valid across plans.
@@ -153,7 +155,8 @@ Layout compute_layout(const fa_geometry& g) {
   L.host_units = align_up(L.host_seg + (size_t)bins * 4, 8);
   // per (request, kv head): 2 int32 (decode) or int64 cost + 3 int32 (append)
   L.host_lens = L.host_units + (size_t)g.max_batch * g.num_kv_heads * 24;
-  L.host_bytes = L.host_lens + ((size_t)g.max_batch + 1) * 4;
+  L.host_flags = align_up(L.host_lens + ((size_t)g.max_batch + 1) * 4, 256);
+  L.host_bytes = L.host_flags + (size_t)kUploadMaxGrid * 4;
   return L;
 }
 

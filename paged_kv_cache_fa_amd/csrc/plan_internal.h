@@ -19,6 +19,7 @@ constexpr int kMaxPiecePages = 128;  // decode pieces: the kernel holds 128 page
 constexpr int kXcdBins = 8;          // append tile bins, one per XCD (workgroup i runs on XCD i % 8)
 constexpr int kAppendCols = 256;     // query columns of an append tile: G heads x 256 / G positions
 constexpr int kPiecesPerWorker = 1;  // decode: work lists per worker wave
+constexpr int kUploadMaxGrid = 64;   // workgroups of the plan copy kernel (one flag word each)
 // decode: set-up and epilogue of one piece, in pages of streaming time
 constexpr int kPieceCostPages16 = 4;
 constexpr int kPieceCostPagesE4M3 = 8;
@@ -33,11 +34,13 @@ constexpr int kPieceCostPagesE4M3 = 8;
 // Host only: scratch for sorting and dealing tiles (decode: pieces, dealing
 // order, bin heap, bin of each dealt piece, bin offsets; append: per-group
 // cost / order / bin / sequence), per-request / per-unit counts, and the
-// request lengths of a ragged plan.
+// request lengths of a ragged plan, and the completion words of the copy
+// kernel that reads the image out of pinned host memory ([kUploadMaxGrid]).
 struct Layout {
   size_t header, merge, worker_ptr, offsets, tiles, upload_end;
   size_t dev_counters, dev_part_lse, dev_part_o, dev_bytes;
-  size_t host_unsorted, host_order, host_cost, host_bin, host_seg, host_units, host_lens, host_bytes;
+  size_t host_unsorted, host_order, host_cost, host_bin, host_seg, host_units, host_lens,
+      host_flags, host_bytes;
   int32_t workers;
 };
 
@@ -60,6 +63,15 @@ struct PlanImpl {
   void* join2_event;
   void* upload_host;   // host workspace whose device mapping was looked up
   void* upload_src;    // its device-visible address (pinned memory), or null
+  // Completion words of the last copy kernel out of pinned host memory: each
+  // of its `flag_n` workgroups stores `flag_seq` into its word of the host
+  // workspace's flag area once its reads are done. flag_ws is null when no
+  // such copy is pending.
+  void* flag_ws;
+  uint32_t flag_seq;
+  int32_t flag_n;
+  void* flags_cleared_ws;  // host workspace whose flag area holds no stale
+  size_t flags_cleared_off;  // word at this offset
 };
 static_assert(sizeof(PlanImpl) <= sizeof(fa_plan_t), "plan object too large");
 

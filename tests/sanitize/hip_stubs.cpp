@@ -72,7 +72,8 @@ hipError_t launch_append(const AttnParams&, int, int, int, hipStream_t) { reache
 hipError_t launch_pod(const AttnParams&, int, const AttnParams&, int, int, int, hipStream_t) {
   reached("launch_pod");
 }
-hipError_t launch_upload(uint32_t*, const uint32_t*, int64_t, hipStream_t) {
+int upload_grid(int64_t) { return 1; }
+hipError_t launch_upload(uint32_t*, const uint32_t*, int64_t, uint32_t*, uint32_t, hipStream_t) {
   reached("launch_upload");
 }
 hipError_t launch_merge_state(const void*, const float*, const void*, const float*, void*, float*,
