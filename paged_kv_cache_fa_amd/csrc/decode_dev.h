@@ -37,6 +37,12 @@
 //    codes are widened exactly to the q type in registers (v_cvt_scalef32_pk
 //    with scale 1) and take the same dot2 path; the K scale joins the score
 //    scale and the V scale the final normalisation;
+//  * with many products per byte (G = 8, or E4M3 pages at G = 4) the scores
+//    run on the matrix cores instead (MQK): K is loaded in the A layout of
+//    v_mfma_f32_16x16x32 (token = lane % 16), q is the B operand (head =
+//    lane % 16, zero past G), four MFMAs give S^T for the page's 16 tokens,
+//    and the wave passes the scores through 1.25 KB of LDS to the row groups
+//    that own the tokens; V, P*V and everything after stay as above;
 //  * each row group keeps its own online-softmax state (reference max in log2
 //    units, sum, 16 fp32 accumulators per head); the reference is only moved
 //    (and the accumulators rescaled) when a wave-wide vote finds a score more
@@ -82,6 +88,49 @@ __device__ __forceinline__ int acc_dim(int s, int i) {
   return KV8 ? 16 * s + 4 * i : (i < 2 ? 8 * s + 4 * i : 64 + 8 * s + 4 * (i - 2));
 }
 
+// q operands of a piece. VALU scores: lo[g], hi[g] = dims acc_dim(s, 0..1)
+// and acc_dim(s, 2..3) of head g. Matrix-core scores (MQK): b[i] = the B
+// operand of the i-th 16x16x32 MFMA: head n = lane % 16 (zero for n >= G),
+// dims kdim(i, lane / 16) .. +8.
+template <int G, bool MQK>
+struct QOps {
+  u32x4 lo[G], hi[G];
+};
+template <int G>
+struct QOps<G, true> {
+  u32x4 b[4];
+};
+
+// MQK: the K page in the 16x16x32 MFMA A layout (row = token lane % 16, 8
+// dims per lane): the dims of lane group g = lane / 16 in MFMA i. 16-bit
+// pools: 32i + 8g (4 loads of 16 B, each covering 64 contiguous bytes of
+// 16 token rows); E4M3: lane group g loads bytes [16g, 16g+16) and [64+16g,
+// 64+16g+16) of the row, which widen to the operands of MFMAs 0, 1 and 2, 3.
+template <bool KV8>
+__device__ __forceinline__ int kdim(int i, int g) {
+  return KV8 ? (i < 2 ? 16 * g + 8 * i : 64 + 16 * g + 8 * (i - 2)) : 32 * i + 8 * g;
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == FA_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// MQK score exchange in LDS, per wave: S[token][head], rows of 20 floats
+// (the 16 lanes of a head column and the 8 rows a read touches fall in
+// distinct banks).
+constexpr int kScoreRow = 20;
+constexpr int kScoreFloats = 16 * kScoreRow;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
@@ -94,7 +143,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p)
 
 template <bool KV8>
 __device__ __forceinline__ void load_page(PageRegs<KV8>& pr, const AttnParams& p, int pid, int hk,
-                                          uint32_t bytes, const uint32_t (&off)[4]) {
+                                          uint32_t bytes, const uint32_t (&koff)[4],
+                                          const uint32_t (&off)[4]) {
   constexpr int N = PageRegs<KV8>::N;
   const int64_t base = ((int64_t)pid * p.page_stride + (int64_t)hk * p.head_stride) * (KV8 ? 1 : 2);
   const __amdgpu_buffer_rsrc_t rk =
@@ -102,18 +152,80 @@ __device__ __forceinline__ void load_page(PageRegs<KV8>& pr, const AttnParams& p
   const __amdgpu_buffer_rsrc_t rv =
       page_rsrc(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.v) + base), bytes);
 #pragma unroll
-  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, kStream);
+  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, kStream);
 #pragma unroll
   for (int i = 0; i < N; ++i) pr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, kStream);
 }
 
+// Scores of the lane's two tokens (r and r+8) for the G heads, on the matrix
+// cores: S^T = K Q^T over 16 tokens x 16 head columns (4 MFMAs of 32 dims),
+// then through the wave's LDS rows to the row groups that own the tokens.
 template <int DT, int G, bool KV8>
-__device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const u32x4 (&qlo)[G],
-                                             const u32x4 (&qhi)[G], float (&m)[G], float (&l)[G],
+__device__ __forceinline__ void mfma_scores(const PageRegs<KV8>& pr, const QOps<G, true>& q,
+                                            float* sc, int lane, float (&xa)[G], float (&xb)[G]) {
+  using E = Elt<DT>;
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 a;
+    if constexpr (KV8) {
+      const u32x4 w = pr.k[i >> 1];
+      const int d = (i & 1) * 2;
+      a[0] = E::template from_e4m3<false>(w[d]);
+      a[1] = E::template from_e4m3<true>(w[d]);
+      a[2] = E::template from_e4m3<false>(w[d + 1]);
+      a[3] = E::template from_e4m3<true>(w[d + 1]);
+    } else {
+      a = pr.k[i];
+    }
+    c = mfma16x16x32<DT>(a, q.b[i], c);
+  }
+  // lane holds C[token 4 (lane / 16) + j][head lane % 16]
+  const int n = lane & 15, t0 = (lane >> 4) * 4;
+  if (n < G) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[(t0 + j) * kScoreRow + n] = c[j];
+  }
+  const int r = lane >> 3;
+  const float* ra = sc + r * kScoreRow;
+  const float* rb = sc + (r + 8) * kScoreRow;
+  if constexpr (G >= 4) {
+#pragma unroll
+    for (int g = 0; g < G; g += 4) {
+      const f32x4 va = *reinterpret_cast<const f32x4*>(ra + g);
+      const f32x4 vb = *reinterpret_cast<const f32x4*>(rb + g);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        xa[g + u] = va[u];
+        xb[g + u] = vb[u];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      xa[g] = ra[g];
+      xb[g] = rb[g];
+    }
+  }
+}
+
+template <int DT, int G, bool KV8, bool MQK>
+__device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const QOps<G, MQK>& q,
+                                             float* sc, int lane, float (&m)[G], float (&l)[G],
                                              float (&acc)[G][16], float scale, bool va, bool vb) {
   using E = Elt<DT>;
+  float sa[G], sb[G];
+  if constexpr (MQK) {
+    float xa[G], xb[G];
+    mfma_scores<DT, G, KV8>(pr, q, sc, lane, xa, xb);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      sa[g] = va ? xa[g] * scale : kNegInf;
+      sb[g] = vb ? xb[g] * scale : kNegInf;
+    }
+  } else {
   // key pairs of tokens r (ka) and r+8 (kb) in the q layout: pair i < 4 meets
-  // qlo[g][i], pair 4 + i meets qhi[g][i]
+  // q.lo[g][i], pair 4 + i meets q.hi[g][i]
   uint32_t ka[8], kb[8];
   if constexpr (KV8) {
     // E4M3 codes widened to the q type; dword i holds dims 16s+4i .. 16s+4i+3
@@ -133,24 +245,24 @@ __device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const u32x
       kb[4 + i] = pr.k[3][i];
     }
   }
-  float sa[G], sb[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float x = 0.f, y = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x = E::dot2(qlo[g][i], ka[i], x);
-      y = E::dot2(qlo[g][i], kb[i], y);
+      x = E::dot2(q.lo[g][i], ka[i], x);
+      y = E::dot2(q.lo[g][i], kb[i], y);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x = E::dot2(qhi[g][i], ka[4 + i], x);
-      y = E::dot2(qhi[g][i], kb[4 + i], y);
+      x = E::dot2(q.hi[g][i], ka[4 + i], x);
+      y = E::dot2(q.hi[g][i], kb[4 + i], y);
     }
     const float xs = octet_sum(x) * scale;
     const float ys = octet_sum(y) * scale;
     sa[g] = va ? xs : kNegInf;
     sb[g] = vb ? ys : kNegInf;
+  }
   }
   bool need = false;
 #pragma unroll
@@ -403,6 +515,22 @@ __device__ __forceinline__ uint32_t page_offsets(const AttnParams& p, int lane, 
   return ts2;
 }
 
+// The lane's K load offsets in a page: the V layout's, or (MQK) the MFMA A
+// layout's (token lane % 16, dims kdim(i, lane / 16)).
+template <bool KV8, bool MQK>
+__device__ __forceinline__ void page_offsets_k(uint32_t ts2, const uint32_t (&off)[4], int lane,
+                                               uint32_t (&koff)[4]) {
+  if constexpr (MQK) {
+    const uint32_t t = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      koff[i] = t * ts2 + (KV8 ? (uint32_t)kdim<true>(2 * i, g) : 2u * (uint32_t)kdim<false>(i, g));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) koff[i] = off[i];
+  }
+}
+
 __device__ __forceinline__ int page_id_of(const PieceCtx& c, int j) {
   return j < 64 ? __builtin_amdgcn_readlane(c.ids0, j & 63) : __builtin_amdgcn_readlane(c.ids1, j & 63);
 }
@@ -417,10 +545,10 @@ __device__ __forceinline__ uint32_t page_bytes_of(const PieceRun& run, int j, ui
 // Start a piece: check it against the device page table, request its q rows
 // and its first NBUF-1 pages into the ring. The caller runs this before the
 // previous piece's epilogue, which then overlaps the first loads' latency.
-template <int G, int NBUF, bool KV8>
+template <int G, int NBUF, bool KV8, bool MQK>
 __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx& c, int lane,
                                             PieceRun& run, PageRegs<KV8> (&buf)[NBUF],
-                                            u32x4 (&qlo)[G], u32x4 (&qhi)[G]) {
+                                            QOps<G, MQK>& q) {
   // The context's fields are wave-uniform; readfirstlane says so to the
   // compiler (it loses track across the loop that hands pieces over), so the
   // page buffer resources stay scalar.
@@ -441,20 +569,31 @@ __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx&
   run.npg = agrees ? __builtin_amdgcn_readfirstlane(c.npg_plan) : 0;
   const int s = lane & 7;
   const uint16_t* qp = p.q + ((int64_t)run.row * p.num_qo_heads + run.hk * G) * 128;
+  if constexpr (MQK) {
+    const int n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    qlo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 0));
-    qhi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 2));
+    for (int i = 0; i < 4; ++i)
+      q.b[i] = n < G ? *reinterpret_cast<const u32x4*>(qp + n * 128 + kdim<KV8>(i, g))
+                     : u32x4{0u, 0u, 0u, 0u};
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      q.lo[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 0));
+      q.hi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 2));
+    }
   }
-  uint32_t off[4];
+  uint32_t off[4], koff[4];
   const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
+  page_offsets_k<KV8, MQK>(ts2, off, lane, koff);
   if (run.npg >= 2 * NBUF) {
 #pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u) load_page(buf[u], p, page_id_of(c, u), run.hk, 16u * ts2, off);
+    for (int u = 0; u < NBUF - 1; ++u)
+      load_page(buf[u], p, page_id_of(c, u), run.hk, 16u * ts2, koff, off);
   } else {
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u)
-      if (u < run.npg) load_page(buf[u], p, page_id_of(c, u), run.hk, page_bytes_of(run, u, ts2), off);
+      if (u < run.npg)
+        load_page(buf[u], p, page_id_of(c, u), run.hk, page_bytes_of(run, u, ts2), koff, off);
   }
 }
 
@@ -464,16 +603,17 @@ __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx&
 // (k = 2, 1, 0 for the last three passes; all three run after the loop if
 // the piece has fewer), where the caller overlaps the set-up of its next
 // piece with the loads.
-template <int DT, int G, int NBUF, bool KV8, typename Hook>
+template <int DT, int G, int NBUF, bool KV8, bool MQK, typename Hook>
 __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx& c,
                                              const PieceRun& run, int lane,
-                                             PageRegs<KV8> (&buf)[NBUF], const u32x4 (&qlo)[G],
-                                             const u32x4 (&qhi)[G], float (&m)[G], float (&l)[G],
+                                             PageRegs<KV8> (&buf)[NBUF], const QOps<G, MQK>& q,
+                                             float* sc, float (&m)[G], float (&l)[G],
                                              float (&acc)[G][16], Hook&& hook) {
   const int r = lane >> 3;
   const int hk = run.hk, npg = run.npg, key1 = run.key1;
-  uint32_t off[4];
+  uint32_t off[4], koff[4];
   const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
+  page_offsets_k<KV8, MQK>(ts2, off, lane, koff);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = kNegInf;
@@ -496,8 +636,8 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
         const int jn = j0 + u + NBUF - 1;
         const int pid = nid;
         nid = page_id_of(c, jn + 1);
-        load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, off);
-        consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, true, true);
+        load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, koff, off);
+        consume_page<DT, G, KV8, MQK>(buf[u], q, sc, lane, m, l, acc, scale, true, true);
       }
     };
     // passes: the peeled first one, then while j + 2 NBUF - 1 < npg
@@ -522,10 +662,10 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
       const int jn = jj + NBUF - 1;
       if (jn < npg)
         load_page(buf[(u + NBUF - 1) % NBUF], p, page_id_of(c, jn), hk, page_bytes_of(run, jn, ts2),
-                  off);
+                  koff, off);
       const int tb = (run.first_page + jj) * 16;
-      consume_page<DT, G, KV8>(buf[u], qlo, qhi, m, l, acc, scale, tb + r < key1,
-                               tb + r + 8 < key1);
+      consume_page<DT, G, KV8, MQK>(buf[u], q, sc, lane, m, l, acc, scale, tb + r < key1,
+                                    tb + r + 8 < key1);
     }
   }
   while (hooks_left > 0) hook(--hooks_left);
@@ -540,8 +680,8 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
 // completed by then, so the wait is free), and the last arriving piece
 // merges the unit and clears its counter, so the kernel can be replayed from
 // a graph.
-template <int DT, int G, int NBUF, bool KV8>
-__device__ __forceinline__ void decode_worker(const AttnParams& p, int w) {
+template <int DT, int G, int NBUF, bool KV8, bool MQK = false>
+__device__ __forceinline__ void decode_worker(const AttnParams& p, int w, float* sc = nullptr) {
   const int lane = threadIdx.x & 63;
   const int r = lane >> 3, s = lane & 7;
   if (w >= p.header[6]) return;  // the grid rounds the worker count up to whole workgroups
@@ -574,10 +714,10 @@ __device__ __forceinline__ void decode_worker(const AttnParams& p, int w) {
   PieceCtx cur, nxt;
   PieceRun run, nrun;
   PageRegs<KV8> buf[NBUF];
-  u32x4 qlo[G], qhi[G];
+  QOps<G, MQK> q;
   if (t < t_end) {
     open_piece(p, load_tile(p, t, lane), lane, cur);
-    begin_piece<G, NBUF, KV8>(p, cur, lane, run, buf, qlo, qhi);
+    begin_piece<G, NBUF, KV8, MQK>(p, cur, lane, run, buf, q);
   }
   while (t < t_end) {
     // overlapped set-up of the next piece: request its tile (pass 2 from the
@@ -589,9 +729,9 @@ __device__ __forceinline__ void decode_worker(const AttnParams& p, int w) {
       if (k == 2 && tn < t_end) tvn = load_tile(p, tn, lane);
       if (k == 1 && tn < t_end) open_piece(p, tvn, lane, nxt);
     };
-    stream_piece<DT, G, NBUF, KV8>(p, cur, run, lane, buf, qlo, qhi, m, l, acc, hook);
+    stream_piece<DT, G, NBUF, KV8, MQK>(p, cur, run, lane, buf, q, sc, m, l, acc, hook);
     const int arr = pd.slot >= 0 ? arrive(pd) : 0;
-    if (tn < t_end) begin_piece<G, NBUF, KV8>(p, nxt, lane, nrun, buf, qlo, qhi);
+    if (tn < t_end) begin_piece<G, NBUF, KV8, MQK>(p, nxt, lane, nrun, buf, q);
     merge_row_groups<G>(m, l, acc);
     if (cur.id.slot < 0)
       write_final<DT, G, KV8>(p, cur.id.row, cur.id.hk, r, s, m, l, acc);

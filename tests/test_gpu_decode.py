@@ -101,6 +101,20 @@ def test_benchmark_decode_workloads_full_size(k):
     print(f"[{CONFIG_NAMES[k]}] max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
 
 
+@pytest.mark.parametrize("kv_dtype", [None, "e4m3"])
+def test_group8_batch64_full_size(kv_dtype):
+    """GQA group 8 (64 q / 8 kv heads) on the batch-64 lengths, every row: the
+    group size whose scores run on the matrix cores."""
+    from workloads import config_lengths
+    lens = config_lengths(2, np.random.default_rng(2))["kv_lens"]
+    print(f"[group 8 batch 64 {kv_dtype}] generating", flush=True)
+    wl = make_workload(lens, 64, 8, "bf16", 12, mode="test", kv_dtype=kv_dtype)
+    dw = DevWorkload(wl)
+    plan, out, lse = run_decode(dw)
+    e = assert_close(to_f64(out), to_f64(lse), *oracle_decode(wl), what=f"group 8 {kv_dtype}")
+    print(f"[group 8 batch 64 {kv_dtype}] max-abs out {e[0]:.3g} lse {e[1]:.3g}", flush=True)
+
+
 def test_graph_static_replan():
     """Capture decode once, re-plan with new lengths (same geometry), replay."""
     import torch
