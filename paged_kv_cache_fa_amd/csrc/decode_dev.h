@@ -10,7 +10,7 @@
 // the log-sum-exp merge ([Guide] section "Cascade attention for shared
 // prefixes").
 //
-// MI355X design (decode is HBM-bound, so no MFMA):
+// MI355X design (decode is HBM-bound):
 //  * one wave64 per worker, 4 independent waves per 256-thread workgroup, no
 //    barriers; the planner cuts requests into pieces and deals them, largest
 //    first, to static per-wave work lists of the same cost (pages plus a
@@ -37,12 +37,12 @@
 //    codes are widened exactly to the q type in registers (v_cvt_scalef32_pk
 //    with scale 1) and take the same dot2 path; the K scale joins the score
 //    scale and the V scale the final normalisation;
-//  * with many products per byte (G = 8, or E4M3 pages at G = 4) the scores
-//    run on the matrix cores instead (MQK): K is loaded in the A layout of
-//    v_mfma_f32_16x16x32 (token = lane % 16), q is the B operand (head =
-//    lane % 16, zero past G), four MFMAs give S^T for the page's 16 tokens,
-//    and the wave passes the scores through 1.25 KB of LDS to the row groups
-//    that own the tokens; V, P*V and everything after stay as above;
+//  * for G >= 4 both products run on the matrix cores instead (MPV, see
+//    consume_page_mpv): at 4 or 8 heads per kv head the VALU dot products
+//    would take most of the vector issue rate at HBM speed (G = 8: 138 us
+//    on the batch-64 lengths against 103 us this way; G = 4: 108 -> 102 us;
+//    E4M3 pages at G = 4: 73 -> 60 us), while for G <= 2 the VALU path is as
+//    fast or faster;
 //  * each row group keeps its own online-softmax state (reference max in log2
 //    units, sum, 16 fp32 accumulators per head); the reference is only moved
 //    (and the accumulators rescaled) when a wave-wide vote finds a score more
@@ -88,11 +88,11 @@ __device__ __forceinline__ int acc_dim(int s, int i) {
   return KV8 ? 16 * s + 4 * i : (i < 2 ? 8 * s + 4 * i : 64 + 8 * s + 4 * (i - 2));
 }
 
-// q operands of a piece. VALU scores: lo[g], hi[g] = dims acc_dim(s, 0..1)
-// and acc_dim(s, 2..3) of head g. Matrix-core scores (MQK): b[i] = the B
-// operand of the i-th 16x16x32 MFMA: head n = lane % 16 (zero for n >= G),
-// dims kdim(i, lane / 16) .. +8.
-template <int G, bool MQK>
+// q operands of a piece. VALU path: lo[g], hi[g] = dims acc_dim(s, 0..1)
+// and acc_dim(s, 2..3) of head g. MPV: b[i] = the B operand of the i-th
+// 16x16x32 MFMA of the scores: head n = lane % 16 (zero for n >= G), dims
+// 32i + 8 (lane / 16) .. +8.
+template <int G, bool MPV>
 struct QOps {
   u32x4 lo[G], hi[G];
 };
@@ -100,16 +100,6 @@ template <int G>
 struct QOps<G, true> {
   u32x4 b[4];
 };
-
-// MQK: the K page in the 16x16x32 MFMA A layout (row = token lane % 16, 8
-// dims per lane): the dims of lane group g = lane / 16 in MFMA i. 16-bit
-// pools: 32i + 8g (4 loads of 16 B, each covering 64 contiguous bytes of
-// 16 token rows); E4M3: lane group g loads bytes [16g, 16g+16) and [64+16g,
-// 64+16g+16) of the row, which widen to the operands of MFMAs 0, 1 and 2, 3.
-template <bool KV8>
-__device__ __forceinline__ int kdim(int i, int g) {
-  return KV8 ? (i < 2 ? 16 * g + 8 * i : 64 + 16 * g + 8 * (i - 2)) : 32 * i + 8 * g;
-}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -125,12 +115,6 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// MQK score exchange in LDS, per wave: S[token][head], rows of 20 floats
-// (the 16 lanes of a head column and the 8 rows a read touches fall in
-// distinct banks).
-constexpr int kScoreRow = 20;
-constexpr int kScoreFloats = 16 * kScoreRow;
-
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
@@ -143,8 +127,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p)
 
 template <bool KV8>
 __device__ __forceinline__ void load_page(PageRegs<KV8>& pr, const AttnParams& p, int pid, int hk,
-                                          uint32_t bytes, const uint32_t (&koff)[4],
-                                          const uint32_t (&off)[4]) {
+                                          uint32_t bytes, const uint32_t (&off)[4]) {
   constexpr int N = PageRegs<KV8>::N;
   const int64_t base = ((int64_t)pid * p.page_stride + (int64_t)hk * p.head_stride) * (KV8 ? 1 : 2);
   const __amdgpu_buffer_rsrc_t rk =
@@ -152,78 +135,17 @@ __device__ __forceinline__ void load_page(PageRegs<KV8>& pr, const AttnParams& p
   const __amdgpu_buffer_rsrc_t rv =
       page_rsrc(reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.v) + base), bytes);
 #pragma unroll
-  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, kStream);
+  for (int i = 0; i < N; ++i) pr.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, off[i], 0, kStream);
 #pragma unroll
   for (int i = 0; i < N; ++i) pr.v[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, off[i], 0, kStream);
 }
 
-// Scores of the lane's two tokens (r and r+8) for the G heads, on the matrix
-// cores: S^T = K Q^T over 16 tokens x 16 head columns (4 MFMAs of 32 dims),
-// then through the wave's LDS rows to the row groups that own the tokens.
 template <int DT, int G, bool KV8>
-__device__ __forceinline__ void mfma_scores(const PageRegs<KV8>& pr, const QOps<G, true>& q,
-                                            float* sc, int lane, float (&xa)[G], float (&xb)[G]) {
-  using E = Elt<DT>;
-  f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 a;
-    if constexpr (KV8) {
-      const u32x4 w = pr.k[i >> 1];
-      const int d = (i & 1) * 2;
-      a[0] = E::template from_e4m3<false>(w[d]);
-      a[1] = E::template from_e4m3<true>(w[d]);
-      a[2] = E::template from_e4m3<false>(w[d + 1]);
-      a[3] = E::template from_e4m3<true>(w[d + 1]);
-    } else {
-      a = pr.k[i];
-    }
-    c = mfma16x16x32<DT>(a, q.b[i], c);
-  }
-  // lane holds C[token 4 (lane / 16) + j][head lane % 16]
-  const int n = lane & 15, t0 = (lane >> 4) * 4;
-  if (n < G) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sc[(t0 + j) * kScoreRow + n] = c[j];
-  }
-  const int r = lane >> 3;
-  const float* ra = sc + r * kScoreRow;
-  const float* rb = sc + (r + 8) * kScoreRow;
-  if constexpr (G >= 4) {
-#pragma unroll
-    for (int g = 0; g < G; g += 4) {
-      const f32x4 va = *reinterpret_cast<const f32x4*>(ra + g);
-      const f32x4 vb = *reinterpret_cast<const f32x4*>(rb + g);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        xa[g + u] = va[u];
-        xb[g + u] = vb[u];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      xa[g] = ra[g];
-      xb[g] = rb[g];
-    }
-  }
-}
-
-template <int DT, int G, bool KV8, bool MQK>
-__device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const QOps<G, MQK>& q,
-                                             float* sc, int lane, float (&m)[G], float (&l)[G],
-                                             float (&acc)[G][16], float scale, bool va, bool vb) {
+__device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const QOps<G, false>& q,
+                                             float (&m)[G], float (&l)[G], float (&acc)[G][16],
+                                             float scale, bool va, bool vb) {
   using E = Elt<DT>;
   float sa[G], sb[G];
-  if constexpr (MQK) {
-    float xa[G], xb[G];
-    mfma_scores<DT, G, KV8>(pr, q, sc, lane, xa, xb);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      sa[g] = va ? xa[g] * scale : kNegInf;
-      sb[g] = vb ? xb[g] * scale : kNegInf;
-    }
-  } else {
   // key pairs of tokens r (ka) and r+8 (kb) in the q layout: pair i < 4 meets
   // q.lo[g][i], pair 4 + i meets q.hi[g][i]
   uint32_t ka[8], kb[8];
@@ -262,7 +184,6 @@ __device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const QOps
     const float ys = octet_sum(y) * scale;
     sa[g] = va ? xs : kNegInf;
     sb[g] = vb ? ys : kNegInf;
-  }
   }
   bool need = false;
 #pragma unroll
@@ -310,6 +231,226 @@ __device__ __forceinline__ void consume_page(const PageRegs<KV8>& pr, const QOps
     const uint32_t pp = E::pack(pa, pb);
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[g][e] = E::dot2(pp, pv[e], acc[g][e]);
+  }
+}
+
+// ---- all matrix-core path (MPV) -----------------------------------------
+// Lane l = 16 gq + c: column c is a head (zero q past G), lane group gq.
+// K and V are loaded in the row-group layout of the VALU path (each load
+// instruction reads the 128-byte halves of 8 token rows; the MFMA operand
+// layouts read 64 bytes of 16 rows per instruction, which measured 16%
+// slower at batch 64) and pass through a per-wave LDS page. Per page:
+// S^T = K Q^T (4 x 16x16x32, K read back as A operands with ds_read_b128)
+// leaves the scores of tokens 4gq .. 4gq+3 for head c in the lane, which is
+// also the B-operand layout of P^T for O^T += V^T P^T (8 x 16x16x16, dims
+// 16n .. 16n+15; V^T read by ds_read_b64_tr_b16). The online-softmax state
+// is per head column (max across the 4 lane groups by two lane swaps) and
+// O^T stays in 32 accumulators: the lane holds dims 16n + 4gq .. +3 of head c.
+template <int G, bool MPV>
+struct WaveState {
+  float m[G], l[G], acc[G][16];
+};
+template <int G>
+struct WaveState<G, true> {
+  float m, l;
+  f32x4 o[8];
+};
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x16(v4s a, u32x2 b, f32x4 c) {
+  if constexpr (DT == FA_BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(v4s, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
+
+// Per-wave V page in LDS: 16 token rows of 256 B (16-bit elements) at a
+// stride of 288 B; the 16-byte chunk k (dims 8k .. 8k+7) of row r sits in
+// slot k ^ (4 (r & 3) + r / 4). Of the layouts measured with
+// SQ_LDS_BANK_CONFLICT (row strides 256, 272, 288, 320 B with six chunk
+// swizzles), this one is free of bank conflicts for both the 16-byte row
+// writes and the transposed 8-byte reads.
+constexpr int kVRowBytes = 288;
+constexpr int kVPageBytes = 16 * kVRowBytes;
+__device__ __forceinline__ uint32_t vslot(int r, int k) {
+  return (uint32_t)(r * kVRowBytes + ((k ^ (((r & 3) << 2) | (r >> 2))) << 4));
+}
+
+template <int DT, int G, bool KV8>
+__device__ __forceinline__ void consume_page_mpv(const PageRegs<KV8>& pr, const QOps<G, true>& q,
+                                                 uint8_t* vl, int lane, WaveState<G, true>& st,
+                                                 float scale, int nvalid) {
+  using E = Elt<DT>;
+  const int t = lane & 15, gq = lane >> 4;
+  // K and V were loaded in the row-group layout (lane = 8 r + s holds tokens
+  // r and r+8, 16 bytes of each per load: every load instruction reads whole
+  // 128-byte halves of 8 token rows); they reach the MFMA layouts through
+  // the wave's LDS page (E4M3 codes widened to the q type on the way in).
+  const int r = lane >> 3, sg = lane & 7;
+  auto to_lds = [&](const u32x4 (&w)[PageRegs<KV8>::N]) {
+    if constexpr (KV8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u32x4 x;
+          x[0] = E::template from_e4m3<false>(w[i][2 * h]);
+          x[1] = E::template from_e4m3<true>(w[i][2 * h]);
+          x[2] = E::template from_e4m3<false>(w[i][2 * h + 1]);
+          x[3] = E::template from_e4m3<true>(w[i][2 * h + 1]);
+          *reinterpret_cast<u32x4*>(vl + vslot(r + 8 * i, 2 * sg + h)) = x;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(vl + vslot(r + 8 * (i >> 1), 8 * (i & 1) + sg)) = w[i];
+    }
+  };
+  // scores S^T[token 4gq + j][head t]: A operand i = dims 32i + 8gq of token t
+  to_lds(pr.k);
+  u32x4 ka[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const u32x4*>(vl + vslot(t, 4 * i + gq));
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = mfma16x16x32<DT>(ka[i], q.b[i], c);
+  // the V page replaces K in LDS (LDS operations of a wave run in order)
+  to_lds(pr.v);
+  // online softmax per head column
+  float sv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sv[j] = 4 * gq + j < nvalid ? c[j] * scale : kNegInf;
+  float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mx = pair32_max(pair16_max(mx));
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack)) {
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - (mn == kNegInf ? 0.f : mn));
+    st.l *= alpha;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
+    st.m = mn;
+  }
+  const float ms = st.m == kNegInf ? 0.f : st.m;
+  float pj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pj[j] = fast_exp2(sv[j] - ms);
+  st.l += (pj[0] + pj[1]) + (pj[2] + pj[3]);
+  const u32x2 pb = {E::pack(pj[0], pj[1]), E::pack(pj[2], pj[3])};
+  // O^T += V^T P^T: lane reads dim 16n + t of tokens 4gq .. 4gq+3
+  const int e = t >> 2, qq = t & 3;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const uint32_t a = vslot(4 * gq + e, 2 * n + (qq >> 1)) + 8u * (uint32_t)(qq & 1);
+    const v4s va =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(vl + a));
+    st.o[n] = mfma16x16x16<DT>(va, pb, st.o[n]);
+  }
+}
+
+// Sum the lane groups' partial row sums (the max is already common).
+template <int G>
+__device__ __forceinline__ void finish_state(WaveState<G, true>& st) {
+  st.l = pair32_sum(pair16_sum(st.l));
+}
+
+template <int DT, int G, bool KV8>
+__device__ __forceinline__ void write_final_mpv(const AttnParams& p, int row, int hk, int lane,
+                                                const WaveState<G, true>& st) {
+  const int c = lane & 15, gq = lane >> 4;
+  if (c >= G) return;
+  const int Hq = p.num_qo_heads;
+  const int h = hk * G + c;
+  const bool live = st.l > 0.f;
+  const float inv = live ? p.v_scale / st.l : 0.f;
+  uint16_t* op = p.out + ((int64_t)row * Hq + h) * 128 + 4 * gq;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const u32x2 w = {Elt<DT>::pack(st.o[n][0] * inv, st.o[n][1] * inv),
+                     Elt<DT>::pack(st.o[n][2] * inv, st.o[n][3] * inv)};
+    *reinterpret_cast<u32x2*>(op + 16 * n) = w;
+  }
+  if (gq == 0 && p.lse) p.lse[(int64_t)row * Hq + h] = live ? (st.m + fast_log2(st.l)) * kLn2 : kNegInf;
+}
+
+template <int G>
+__device__ __forceinline__ void write_partial_mpv(const AttnParams& p, int64_t slot, int lane,
+                                                  const WaveState<G, true>& st) {
+  const int c = lane & 15, gq = lane >> 4;
+  if (c >= G) return;
+  const int64_t sh = slot * G + c;
+  const bool live = st.l > 0.f;
+  const float inv = live ? 1.f / st.l : 0.f;
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
+  const uint32_t o = (uint32_t)sh * 512u + 16u * (uint32_t)gq;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    u32x4 u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u[k] = __float_as_uint(st.o[n][k] * inv);
+    __builtin_amdgcn_raw_buffer_store_b128(u, rs, o + 64u * n, 0, kCoherent);
+  }
+  if (gq == 0)
+    __hip_atomic_store(p.part_lse + sh, live ? st.m + fast_log2(st.l) : kNegInf, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Online merge of the fp32 partial states in slots base .. base+C-1: the 16 /
+// G copies of each head column (lanes c, c + G, ...) take every (16/G)-th
+// piece, then the copies are merged across lanes. Leaves a finished state
+// (l summed) in the lanes of column c < G.
+template <int G>
+__device__ __forceinline__ void gather_partials_mpv(const AttnParams& p, int64_t base, int C,
+                                                    int lane, WaveState<G, true>& st) {
+  constexpr int NC = 16 / G;  // copies of a head column
+  const int c = lane & 15, gq = lane >> 4;
+  const int hc = c % G, copy = c / G;
+  st.m = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t rs = part_rsrc(p);
+  for (int k = copy; k < C; k += NC) {
+    const int64_t sh = (base + k) * G + hc;
+    const float s2 = __hip_atomic_load(p.part_lse + sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t o = (uint32_t)sh * 512u + 16u * (uint32_t)gq;
+    f32x4 v[8];
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      v[n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, o + 64u * n, 0,
+                                                                             kCoherent));
+    const float mn = fmaxf(st.m, s2);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float f = fast_exp2(st.m - ms);
+    const float w = fast_exp2(s2 - ms);
+    st.l = st.l * f + w;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] = st.o[n] * f + w * v[n];
+    st.m = mn;
+  }
+  // merge the copies: lanes c ^ (G << b) inside each row of 16
+#pragma unroll
+  for (int b = G; b < 16; b <<= 1) {
+    const float m2 = __shfl_xor(st.m, b, 64);
+    const float mn = fmaxf(st.m, m2);
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float f = fast_exp2(st.m - ms);
+    st.l = st.l * f;
+    st.l += __shfl_xor(st.l, b, 64);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float x = st.o[n][k] * f;
+        st.o[n][k] = x + __shfl_xor(x, b, 64);
+      }
+    }
+    st.m = mn;
   }
 }
 
@@ -515,22 +656,6 @@ __device__ __forceinline__ uint32_t page_offsets(const AttnParams& p, int lane, 
   return ts2;
 }
 
-// The lane's K load offsets in a page: the V layout's, or (MQK) the MFMA A
-// layout's (token lane % 16, dims kdim(i, lane / 16)).
-template <bool KV8, bool MQK>
-__device__ __forceinline__ void page_offsets_k(uint32_t ts2, const uint32_t (&off)[4], int lane,
-                                               uint32_t (&koff)[4]) {
-  if constexpr (MQK) {
-    const uint32_t t = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      koff[i] = t * ts2 + (KV8 ? (uint32_t)kdim<true>(2 * i, g) : 2u * (uint32_t)kdim<false>(i, g));
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) koff[i] = off[i];
-  }
-}
-
 __device__ __forceinline__ int page_id_of(const PieceCtx& c, int j) {
   return j < 64 ? __builtin_amdgcn_readlane(c.ids0, j & 63) : __builtin_amdgcn_readlane(c.ids1, j & 63);
 }
@@ -545,10 +670,10 @@ __device__ __forceinline__ uint32_t page_bytes_of(const PieceRun& run, int j, ui
 // Start a piece: check it against the device page table, request its q rows
 // and its first NBUF-1 pages into the ring. The caller runs this before the
 // previous piece's epilogue, which then overlaps the first loads' latency.
-template <int G, int NBUF, bool KV8, bool MQK>
+template <int G, int NBUF, bool KV8, bool MPV>
 __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx& c, int lane,
                                             PieceRun& run, PageRegs<KV8> (&buf)[NBUF],
-                                            QOps<G, MQK>& q) {
+                                            QOps<G, MPV>& q) {
   // The context's fields are wave-uniform; readfirstlane says so to the
   // compiler (it loses track across the loop that hands pieces over), so the
   // page buffer resources stay scalar.
@@ -569,11 +694,11 @@ __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx&
   run.npg = agrees ? __builtin_amdgcn_readfirstlane(c.npg_plan) : 0;
   const int s = lane & 7;
   const uint16_t* qp = p.q + ((int64_t)run.row * p.num_qo_heads + run.hk * G) * 128;
-  if constexpr (MQK) {
+  if constexpr (MPV) {
     const int n = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      q.b[i] = n < G ? *reinterpret_cast<const u32x4*>(qp + n * 128 + kdim<KV8>(i, g))
+      q.b[i] = n < G ? *reinterpret_cast<const u32x4*>(qp + n * 128 + 32 * i + 8 * g)
                      : u32x4{0u, 0u, 0u, 0u};
   } else {
 #pragma unroll
@@ -582,18 +707,17 @@ __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx&
       q.hi[g] = *reinterpret_cast<const u32x4*>(qp + g * 128 + acc_dim<KV8>(s, 2));
     }
   }
-  uint32_t off[4], koff[4];
+  uint32_t off[4];
   const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
-  page_offsets_k<KV8, MQK>(ts2, off, lane, koff);
   if (run.npg >= 2 * NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u)
-      load_page(buf[u], p, page_id_of(c, u), run.hk, 16u * ts2, koff, off);
+      load_page(buf[u], p, page_id_of(c, u), run.hk, 16u * ts2, off);
   } else {
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u)
       if (u < run.npg)
-        load_page(buf[u], p, page_id_of(c, u), run.hk, page_bytes_of(run, u, ts2), koff, off);
+        load_page(buf[u], p, page_id_of(c, u), run.hk, page_bytes_of(run, u, ts2), off);
   }
 }
 
@@ -603,25 +727,36 @@ __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx&
 // (k = 2, 1, 0 for the last three passes; all three run after the loop if
 // the piece has fewer), where the caller overlaps the set-up of its next
 // piece with the loads.
-template <int DT, int G, int NBUF, bool KV8, bool MQK, typename Hook>
+template <int DT, int G, int NBUF, bool KV8, bool MPV, typename Hook>
 __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx& c,
                                              const PieceRun& run, int lane,
-                                             PageRegs<KV8> (&buf)[NBUF], const QOps<G, MQK>& q,
-                                             float* sc, float (&m)[G], float (&l)[G],
-                                             float (&acc)[G][16], Hook&& hook) {
+                                             PageRegs<KV8> (&buf)[NBUF], const QOps<G, MPV>& q,
+                                             void* lds, WaveState<G, MPV>& st, Hook&& hook) {
   const int r = lane >> 3;
   const int hk = run.hk, npg = run.npg, key1 = run.key1;
-  uint32_t off[4], koff[4];
+  uint32_t off[4];
   const uint32_t ts2 = page_offsets<KV8>(p, lane, off);
-  page_offsets_k<KV8, MQK>(ts2, off, lane, koff);
+  if constexpr (MPV) {
+    st.m = kNegInf;
+    st.l = 0.f;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
+    for (int n = 0; n < 8; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[g][e] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      st.m[g] = kNegInf;
+      st.l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.acc[g][e] = 0.f;
+    }
   }
-  const float scale = p.scale_log2;
+  auto consume = [&](const PageRegs<KV8>& pr, int nvalid) {
+    if constexpr (MPV)
+      consume_page_mpv<DT, G, KV8>(pr, q, static_cast<uint8_t*>(lds), lane, st, p.scale_log2,
+                                   nvalid);
+    else
+      consume_page<DT, G, KV8>(pr, q, st.m, st.l, st.acc, p.scale_log2, r < nvalid, r + 8 < nvalid);
+  };
   int j = 0;
   int hooks_left = 3;
   if (npg >= 2 * NBUF) {
@@ -636,8 +771,8 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
         const int jn = j0 + u + NBUF - 1;
         const int pid = nid;
         nid = page_id_of(c, jn + 1);
-        load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, koff, off);
-        consume_page<DT, G, KV8, MQK>(buf[u], q, sc, lane, m, l, acc, scale, true, true);
+        load_page(buf[(u + NBUF - 1) % NBUF], p, pid, hk, full, off);
+        consume(buf[u], 16);
       }
     };
     // passes: the peeled first one, then while j + 2 NBUF - 1 < npg
@@ -662,10 +797,9 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
       const int jn = jj + NBUF - 1;
       if (jn < npg)
         load_page(buf[(u + NBUF - 1) % NBUF], p, page_id_of(c, jn), hk, page_bytes_of(run, jn, ts2),
-                  koff, off);
+                  off);
       const int tb = (run.first_page + jj) * 16;
-      consume_page<DT, G, KV8, MQK>(buf[u], q, sc, lane, m, l, acc, scale, tb + r < key1,
-                                    tb + r + 8 < key1);
+      consume(buf[u], key1 - tb);
     }
   }
   while (hooks_left > 0) hook(--hooks_left);
@@ -680,8 +814,8 @@ __device__ __forceinline__ void stream_piece(const AttnParams& p, const PieceCtx
 // completed by then, so the wait is free), and the last arriving piece
 // merges the unit and clears its counter, so the kernel can be replayed from
 // a graph.
-template <int DT, int G, int NBUF, bool KV8, bool MQK = false>
-__device__ __forceinline__ void decode_worker(const AttnParams& p, int w, float* sc = nullptr) {
+template <int DT, int G, int NBUF, bool KV8, bool MPV>
+__device__ __forceinline__ void decode_worker(const AttnParams& p, int w, void* lds) {
   const int lane = threadIdx.x & 63;
   const int r = lane >> 3, s = lane & 7;
   if (w >= p.header[6]) return;  // the grid rounds the worker count up to whole workgroups
@@ -692,15 +826,20 @@ __device__ __forceinline__ void decode_worker(const AttnParams& p, int w, float*
     if (lane == 0) v = __hip_atomic_fetch_add(ptr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return v;
   };
-  float m[G], l[G], acc[G][16];
+  WaveState<G, MPV> st;
   // arrival of a split piece whose partial was published earlier; the last
   // arrival of the unit merges all its pieces and writes the output
   auto finish_arrival = [&](const PieceId& pd, int arr) {
     if (__builtin_amdgcn_readlane(arr, 0) != pd.npieces - 1) return;
     if (lane == 0) p.counters[pd.base] = 0;
-    gather_partials<G, KV8>(p, pd.base, pd.npieces, r, s, m, l, acc);
-    merge_row_groups<G>(m, l, acc);
-    write_final<DT, G, KV8>(p, pd.row, pd.hk, r, s, m, l, acc);
+    if constexpr (MPV) {
+      gather_partials_mpv<G>(p, pd.base, pd.npieces, lane, st);
+      write_final_mpv<DT, G, KV8>(p, pd.row, pd.hk, lane, st);
+    } else {
+      gather_partials<G, KV8>(p, pd.base, pd.npieces, r, s, st.m, st.l, st.acc);
+      merge_row_groups<G>(st.m, st.l, st.acc);
+      write_final<DT, G, KV8>(p, pd.row, pd.hk, r, s, st.m, st.l, st.acc);
+    }
   };
   auto arrive = [&](const PieceId& pd) -> int {
     // the partial's coherent stores must be complete before the count
@@ -714,10 +853,10 @@ __device__ __forceinline__ void decode_worker(const AttnParams& p, int w, float*
   PieceCtx cur, nxt;
   PieceRun run, nrun;
   PageRegs<KV8> buf[NBUF];
-  QOps<G, MQK> q;
+  QOps<G, MPV> q;
   if (t < t_end) {
     open_piece(p, load_tile(p, t, lane), lane, cur);
-    begin_piece<G, NBUF, KV8, MQK>(p, cur, lane, run, buf, q);
+    begin_piece<G, NBUF, KV8, MPV>(p, cur, lane, run, buf, q);
   }
   while (t < t_end) {
     // overlapped set-up of the next piece: request its tile (pass 2 from the
@@ -729,14 +868,22 @@ __device__ __forceinline__ void decode_worker(const AttnParams& p, int w, float*
       if (k == 2 && tn < t_end) tvn = load_tile(p, tn, lane);
       if (k == 1 && tn < t_end) open_piece(p, tvn, lane, nxt);
     };
-    stream_piece<DT, G, NBUF, KV8, MQK>(p, cur, run, lane, buf, q, sc, m, l, acc, hook);
+    stream_piece<DT, G, NBUF, KV8, MPV>(p, cur, run, lane, buf, q, lds, st, hook);
     const int arr = pd.slot >= 0 ? arrive(pd) : 0;
-    if (tn < t_end) begin_piece<G, NBUF, KV8, MQK>(p, nxt, lane, nrun, buf, q);
-    merge_row_groups<G>(m, l, acc);
-    if (cur.id.slot < 0)
-      write_final<DT, G, KV8>(p, cur.id.row, cur.id.hk, r, s, m, l, acc);
-    else
-      write_partial<G, KV8>(p, cur.id.slot, r, s, m, l, acc);
+    if (tn < t_end) begin_piece<G, NBUF, KV8, MPV>(p, nxt, lane, nrun, buf, q);
+    if constexpr (MPV) {
+      finish_state<G>(st);
+      if (cur.id.slot < 0)
+        write_final_mpv<DT, G, KV8>(p, cur.id.row, cur.id.hk, lane, st);
+      else
+        write_partial_mpv<G>(p, cur.id.slot, lane, st);
+    } else {
+      merge_row_groups<G>(st.m, st.l, st.acc);
+      if (cur.id.slot < 0)
+        write_final<DT, G, KV8>(p, cur.id.row, cur.id.hk, r, s, st.m, st.l, st.acc);
+      else
+        write_partial<G, KV8>(p, cur.id.slot, r, s, st.m, st.l, st.acc);
+    }
     if (pd.slot >= 0) finish_arrival(pd, arr);
     pd = cur.id;
     t = tn;

@@ -29,9 +29,15 @@ void pod_kernel(AttnParams dp, AttnParams ap, int dec_blocks) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * app::VLayout<2>::kBufElems];
   __shared__ int s_flag;
   const int blk = (int)blockIdx.x;
-  if (blk < dec_blocks)
-    dec::decode_worker<DT, G, 2, false>(
-        dp, blk * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)));
+  if (blk < dec_blocks) {
+    // the decode role takes the decode kernel's path for this group size
+    // (bit-identical results); its LDS pages alias the append role's buffer
+    constexpr bool kMPV = G >= 4;
+    static_assert(!kMPV || 4 * dec::kVPageBytes <= sizeof(smem), "decode LDS pages do not fit");
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    dec::decode_worker<DT, G, 2, false, kMPV>(dp, blk * kWaves + wave,
+                                               reinterpret_cast<uint8_t*>(smem) + wave * dec::kVPageBytes);
+  }
   else
     app::append_worker<DT, G, 2, kWaves>(ap, blk - dec_blocks, (int)gridDim.x - dec_blocks, smem, s_flag);
 }
