@@ -36,6 +36,8 @@ Lines after the headline:
   * ``bsr``: block-sparse prefill, 4096 x 16384 in 64 x 64 blocks, 25% kept;
   * ``pod``: causal append + batch-64 decode in one fa_pod launch against the
     two kernels back to back;
+  * ``groups``: the batch-64 decode lengths at GQA group sizes 1, 2, 4, 8
+    (16-bit and E4M3 pools), the decode call alone;
   * ``host_plan_us`` (the host cost of one fa_plan), the streaming-read ceiling
     ``roofline.attainable_GB/s`` (fa_probe_stream_read over 1 GiB) and
     ``cpu_baseline`` (the fp64 numpy oracle on the host cores).
@@ -746,6 +748,30 @@ def line_bsr(steps, warmup):
             "roofline": mfma_roofline(bb.flops, kb, "append_kernel (one fa_append call)")}
 
 
+def line_groups(steps, warmup):
+    """The batch-64 decode lengths at every GQA group size (8 kv heads, 8 to 64
+    q heads; 16-bit and E4M3 pools): the decode call alone, HIP events after a
+    re-plan, one line per group size and pool type. G <= 2 runs the VALU
+    path, G >= 4 the matrix-core path."""
+    import torch
+    from workloads import config_lengths, make_workload
+    lens = config_lengths(2, np.random.default_rng(2))["kv_lens"]
+    res = {}
+    for kvd in (None, "e4m3"):
+        for g in (1, 2, 4, 8):
+            wl = make_workload(lens, 8 * g, 8, "bf16", 2, kv_dtype=kvd)
+            b = DecodeBench(wl)
+            k = b.kernel_ms(max(10, steps // 2), warmup=3)
+            n = algorithmic_bytes(wl)
+            res[f"{kvd or 'bf16'}_G{g}"] = {"kernel_ms": round(k, 5),
+                                           "GB/s": round(n / (k * 1e-3) / 1e9, 1),
+                                           "frac": round(n / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del b, wl
+            torch.cuda.empty_cache()
+    return {"workload": "batch-64 decode lengths (kv U[512,4096], seed 2), 8 kv heads, "
+                        "G = 1, 2, 4, 8 query heads per kv head, bf16 q", "lines": res}
+
+
 def line_pod(steps, warmup):
     import torch
     from workloads import config_lengths, make_config, make_workload
@@ -945,7 +971,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the secondary lines")
     ap.add_argument("--parts",
-                    default="single,batch128,cascade,append,fp8,ragged,single_ragged,bsr,pod",
+                    default="single,batch128,cascade,append,fp8,ragged,single_ragged,bsr,pod,groups",
                     help="comma list of the secondary lines to run after the headline")
     ap.add_argument("--knob", action="append", default=[], help="decode plan knob name=value")
     ap.add_argument("--profile", choices=PROFILE_LINES,
@@ -1015,7 +1041,8 @@ def main():
                ("ragged", lambda: line_ragged(2, args.steps, args.warmup)),
                ("single_ragged", lambda: line_ragged(1, args.steps, args.warmup)),
                ("bsr", lambda: line_bsr(args.steps, args.warmup)),
-               ("pod", lambda: line_pod(args.steps, args.warmup))]
+               ("pod", lambda: line_pod(args.steps, args.warmup)),
+               ("groups", lambda: line_groups(args.steps, args.warmup))]
     for name, fn in runners:
         if name in parts:
             line[name] = fn()
