@@ -139,8 +139,12 @@ fa_status fa_workspace_size(const fa_geometry* geom, size_t* host_bytes, size_t*
  *               0 .. kv_len - qo_len + i (its new tokens are already in the
  *               pages); ignored for decode.
  *  host_ws      caller host memory of fa_workspace_size's host_bytes (pinned
- *               memory recommended). fa_plan waits for its own previous copy
- *               out of it before writing it again.
+ *               memory recommended). Pinned: a copy kernel on `stream` reads
+ *               the image out of it and then stores a sequence number into
+ *               completion words at its end; pageable: hipMemcpyAsync and a
+ *               HIP event. Either way fa_plan waits for its own previous copy
+ *               out of host_ws before writing it again; other plans must not
+ *               use the same host_ws.
  *  dev_ws       caller device memory of device_bytes, 256-byte aligned, or
  *               NULL to plan on the host only (no HIP call is made; the plan
  *               can then be inspected but not run).
@@ -217,7 +221,11 @@ fa_status fa_plan_tiles(const fa_plan_t* plan, const int32_t** tiles_h, int32_t*
                         const int32_t** merge_h, int32_t* num_merge,
                         const int32_t** worker_ptr_h, int32_t* num_workers);
 
-/* Release the HIP events a plan keeps (host workspace reuse, cascade fork/join). */
+/* Release the HIP events a plan keeps (cascade fork/join, pageable host
+ * workspaces). If the plan's last copy out of a pinned host workspace is
+ * still pending, waits until the copy kernel has read the image and written
+ * its completion words, so the host workspace can be freed afterwards (the
+ * device workspace, as always, only once the work queued on it is done). */
 fa_status fa_plan_destroy(fa_plan_t* plan);
 
 /* Batched decode over the paged KV cache ([DeepDive] "Snippet One", batch
