@@ -517,16 +517,20 @@ __device__ __forceinline__ void gather_partials(const AttnParams& p, int64_t bas
     for (int e = 0; e < 16; ++e) acc[g][e] = acc[g][e] * f + w * v[e];
     m[g] = mn;
   };
-  // two chunks per row group per round, both requested before either is used
-  for (int c = r; c < C; c += 16) {
-    const bool two = c + 8 < C;
+  // up to four chunks per row group per round (c, c+8, c+16, c+24), all
+  // requested before any is used: a unit of up to 32 pieces is one round trip
+  for (int c = r; c < C; c += 32) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float sa2, sb2 = kNegInf, va[16], vb[16];
-      load_state(c, g, sa2, va);
-      if (two) load_state(c + 8, g, sb2, vb);
-      add_state(g, sa2, va);
-      if (two) add_state(g, sb2, vb);
+      float s2[4], v[4][16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s2[u] = kNegInf;
+        if (c + 8 * u < C) load_state(c + 8 * u, g, s2[u], v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c + 8 * u < C) add_state(g, s2[u], v[u]);
     }
   }
 }
