@@ -20,8 +20,8 @@ protocol for a run call alone, ``graph_ms_per_call``: one hipGraph of R
 back-to-back calls over the rotating pool copies, median of 20 replays / R.
 
 Lines after the headline:
-  * ``single``: config 1 as defined (one request, 32/32 heads, 2048 tokens in
-    128 pages under a seeded permutation, fp16), a graph of 32 back-to-back
+  * ``single``: the single-request decode (one request, 32/32 heads, 2048
+    tokens in 128 pages under a seeded permutation, fp16), a graph of 32 back-to-back
     calls over 32 pool copies (its eager step is bound by the host);
   * ``batch128``: the skewed batch-128 decode (4 x 32768 + 124 log-normal);
   * ``cascade``: batch 256 sharing a 16384-token prefix (one fa_cascade call:
@@ -31,8 +31,8 @@ Lines after the headline:
   * ``append``: causal append of 16 x 512 rows onto 4096 cached tokens, MFMA
     utilisation (584.2 GFLOP of unmasked work per call);
   * ``fp8``: the batch-64 decode over an E4M3 page pool (per-tensor scales);
-  * ``ragged`` / ``single_ragged``: configs 2 and 1 over a ragged (contiguous)
-    K/V;
+  * ``ragged`` / ``single_ragged``: the batch-64 and single-request decodes
+    over a ragged (contiguous) K/V;
   * ``bsr``: block-sparse prefill, 4096 x 16384 in 64 x 64 blocks, 25% kept;
   * ``pod``: causal append + batch-64 decode in one fa_pod launch against the
     two kernels back to back;
@@ -617,7 +617,8 @@ def mfma_roofline(flops, kernel_ms, kernel_name, **extra) -> dict:
 # --- workload lines -------------------------------------------------------------------------------
 
 def line_decode(k, steps, warmup, kv_dtype=None, knobs=None):
-    """A batched paged decode (configs 2 and 3, or config 2 over an E4M3 pool):
+    """A batched paged decode (batch 64 or the skewed batch 128, or batch 64
+    over an E4M3 pool):
     whole steps (re-plan + decode), the decode call alone with HIP events, and
     the graph protocol (R back-to-back calls over the rotating pool copies)."""
     from workloads import CONFIG_NAMES, make_config
@@ -647,7 +648,7 @@ def line_decode(k, steps, warmup, kv_dtype=None, knobs=None):
 
 
 def line_single(steps, warmup):
-    """Config 1 as defined: one request, q [32, 128] fp16, K/V of 2048 tokens
+    """The single-request decode: one request, q [32, 128] fp16, K/V of 2048 tokens
     x 32 kv heads in 128 pages of 16 tokens under a seeded random page
     permutation; a graph of 32 back-to-back fa_decode calls over 32 pool
     copies (the timing protocol), and the eager step for context."""

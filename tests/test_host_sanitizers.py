@@ -7,9 +7,9 @@ kernel launcher is a stand-in that aborts (``tests/sanitize/hip_stubs.cpp``): a
 plan without a device workspace and every argument check make no HIP call.
 The CPU ABI tests (the 400 random geometries bit-exact against the plan spec,
 the benchmark configurations, the error codes, the block-sparse page tables)
-then run in a subprocess that loads this build (``PKFA_LIB``) with the ASan
-runtime preloaded. A canary with a planted out-of-bounds read, present only in
-this build, shows that the instrumentation is live.
+then run in a subprocess that loads the sanitizer library (``PKFA_LIB``) with
+the ASan runtime preloaded. A canary with a planted out-of-bounds read, present
+only in that library, shows that the instrumentation is live.
 """
 import os
 import shutil

@@ -457,12 +457,12 @@ def make_config(k: int, seed: Optional[int] = None, mode: str = "bench",
                 kv_dtype: Optional[str] = None) -> Workload:
     """The five benchmark workloads (seed defaults to the config number).
 
-    ``kv_dtype="e4m3"`` gives the decode configs 2 and 3 with an FP8 pool
+    ``kv_dtype="e4m3"`` gives the batch-64 and batch-128 decodes with an FP8 pool
     (same lengths, page table and draws; q stays bf16)."""
     if seed is None:
         seed = k
     if kv_dtype is not None and k not in (2, 3):
-        raise ValueError("an FP8 pool is defined for the decode configs 2 and 3 only")
+        raise ValueError("an FP8 pool is defined for the batch-64 and batch-128 decodes only")
     rng = np.random.default_rng(seed)
     name = f"config{k}" + ("" if kv_dtype is None else f"_{kv_dtype}")
     ln = config_lengths(k, rng)
