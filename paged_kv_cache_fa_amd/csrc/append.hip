@@ -11,9 +11,9 @@ constexpr int kThreads = 64 * kWaves;
 template <int DT, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void append_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * app::VLayout<3>::kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * app::VLayout::kBufElems];
   __shared__ int s_flag;
-  app::append_worker<DT, G, 3, kWaves>(p, (int)blockIdx.x, (int)gridDim.x, smem, s_flag);
+  app::append_worker<DT, G, 4, kWaves>(p, (int)blockIdx.x, (int)gridDim.x, smem, s_flag);
 }
 
 template <int DT>

@@ -23,9 +23,10 @@
 //    per SIMD); each of their threads fetches 16 bytes of 4 token rows (one
 //    row from each of the block's 4 pages, so every load's page is uniform
 //    across the wave) through a per-page buffer resource that ends at the
-//    last valid token: keys past the end read as zero. The registers are
-//    written to a double-buffered LDS after the current block's math, one
-//    barrier per block;
+//    last valid token: keys past the end read as zero. A block's registers
+//    are written to LDS at the top of the next iteration (four LDS stages,
+//    so a block is requested two iterations before its scores are needed),
+//    one barrier per block;
 //  * inside a block, key k sits in LDS slot 4 (k mod 16) + k / 16, so one
 //    thread's 4 rows form 4 consecutive slots: V is stored transposed
 //    (dim-major, 4 slots per 8-byte store) without any exchange. The
@@ -99,29 +100,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnParams& p)
 // 16-byte unit c = 4 kt + 2 kh + h (first and second half). Unit c of row d
 // sits at position c ^ swz(d) of a row of kRow elements; swz depends on
 // d mod 32 only (the 4 dim tiles of a lane differ by immediate offsets).
-// Two layouts, chosen by measuring the LDS bank-conflict counter on the
-// operand reads (16 consecutive rows, one unit each, per lane half) and the
-// staging threads' transposing 8-byte stores:
-//  * kRow 96 (64 slots + 32 padding, 192 bytes), swz(d) = (d / 4) mod 8:
-//    no conflict cycles on either (the pipelined loop, one workgroup per CU);
-//  * kRow 64 (unpadded), swz(d) = 2 ((d / 8) mod 4) ^ (d mod 8): conflict-free
-//    stores, about 4 conflict cycles per operand read; it keeps two LDS
-//    stages within half a CU's LDS (the loop that shares its CU).
-template <int STAGES>
+// Rows are 64 slots (128 bytes) with no padding, so four LDS stages of K and
+// V^T fit beside each other. swz is linear over the bits of d mod 32:
+// swz(d) = 2 d0 ^ 3 d1 ^ 5 d2 ^ 7 d3 ^ 2 d4 (d_i the bits of d). Of the
+// swizzles measured on the LDS counters (SQ_LDS_BANK_CONFLICT and
+// SQ_LDS_IDX_ACTIVE per instruction, the exact store and read patterns of
+// this kernel, row strides of 128 to 192 bytes), it is one of those with no
+// conflict cycles on the operand reads (3.9 LDS cycles per instruction,
+// against 7.7 with conflicts) and the fewest cycles on the transposing
+// 8-byte stores (4.0 per instruction, against 5.3 to 16).
 struct VLayout {
-  static constexpr bool kPadded = STAGES == 3;
-  static constexpr int kRow = kPadded ? 96 : 64;
+  static constexpr int kRow = 64;
   static constexpr int kElems = 128 * kRow;
   static constexpr int kBufElems = kKElems + kElems;  // one LDS stage: K slots + V^T
   __device__ __forceinline__ static int swz(int d) {
-    return kPadded ? (d >> 2) & 7 : (((d >> 3) & 3) << 1) ^ (d & 7);
+    return ((d & 1) * 2) ^ (((d >> 1) & 1) * 3) ^ (((d >> 2) & 1) * 5) ^ (((d >> 3) & 1) * 7) ^
+           (((d >> 4) & 1) * 2);
   }
   // swz(8 dg + 2 w + hi) = swz_base(dg) ^ swz_step(w, hi) for w < 4, hi < 2
   __device__ __forceinline__ static int swz_base(int dg) {
-    return kPadded ? (2 * dg) & 6 : (dg & 3) << 1;
+    return ((dg & 1) * 7) ^ (((dg >> 1) & 1) * 2);
   }
   __device__ __forceinline__ static constexpr int swz_step(int w, int hi) {
-    return kPadded ? w >> 1 : (2 * w) ^ hi;
+    return ((w & 1) * 3) ^ (((w >> 1) & 1) * 5) ^ (hi * 2);
   }
 };
 
@@ -142,16 +143,16 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// STAGES: LDS buffers of the block loop, 3 (software pipeline: the scores of
-// block j+1 beside the softmax of block j) or 2 (one block at a time, for a
-// workgroup that shares its CU). A tile's rows must fit the workgroup's
+// STAGES: LDS buffers of the block loop, 4 (software pipeline: the scores of
+// block j+1 beside the softmax of block j, stores a block ahead) or 2 (one
+// block at a time, for a workgroup that shares its CU). A tile's rows must fit the workgroup's
 // 32 WAVES / G positions (the planner's qo_tile).
 template <int DT, int G, int STAGES, int WAVES>
 __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, uint16_t* smem,
                                             int& s_flag) {
   constexpr int kCols = 32 * WAVES;  // query columns of the workgroup
   constexpr int PT = kCols / G;      // query positions per tile
-  using VL = VLayout<STAGES>;
+  using VL = VLayout;
   constexpr int kBufElems = VL::kBufElems;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -423,15 +424,18 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
       __syncthreads();
     }
   } else {
-    // Software pipeline over three LDS buffers: block j is in buffer j mod 3.
-    // Iteration j runs block j's softmax and P V beside block j+1's scores
-    // (staged by iteration j-1), while block j+2's K/V (requested at its top,
-    // page ids requested an iteration earlier) are written to buffer
-    // (j+2) mod 3 at its end; that buffer last held block j-1, which every wave
-    // finished before the previous barrier. Blocks past the end have
-    // zero-size buffer resources: they read nothing and stage zeros, and their
-    // scores are never used.
-    auto buf_of = [&](int j) { return smem + (j % 3) * kBufElems; };
+    static_assert(STAGES == 4, "the block loop runs 2 or 4 LDS stages");
+    // Software pipeline over four LDS buffers: block j is in buffer j mod 4.
+    // Iteration j first stores block j+2 (requested at the top of iteration
+    // j-1, so its loads have landed) into buffer (j+2) mod 4, which last held
+    // block j-2 (read by every wave before the barrier that ended iteration
+    // j-2), and requests block j+3 into the staging registers (its page ids
+    // were loaded an iteration earlier). Then it runs block j's softmax and
+    // P V beside block j+1's scores. The stores complete while the iteration
+    // computes, away from the barrier that ends it, which publishes them.
+    // Blocks past the end have zero-size buffer resources: they read nothing
+    // and stage zeros, and their scores are never used.
+    auto buf_of = [&](int j) { return smem + (j & 3) * kBufElems; };
     f32x16 sa[2], sb[2];
     if (nblocks > 0) {
       take_pids(load_pid_vec(0));
@@ -441,6 +445,8 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
       fetch(1);
       store(1);
       take_pids(load_pid_vec(2));
+      fetch(2);
+      take_pids(load_pid_vec(3));
     }
     __syncthreads();
     if (nblocks > 0) {
@@ -448,8 +454,9 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
       scores_half(buf_of(0), 1, sa[1]);
     }
     auto iteration = [&](int j, f32x16 (&s)[2], f32x16 (&s_next)[2]) {
-      const int pv = load_pid_vec(j + 3);
-      fetch(j + 2);
+      store((j + 2) & 3);
+      const int pv = load_pid_vec(j + 4);
+      fetch(j + 3);
       // block j's softmax and P V; block j+1's scores issued beside it:
       // half 0 before the row max, half 1 before the exponentials
       const uint16_t* sk_next = buf_of(j + 1);
@@ -458,7 +465,6 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
       row_max(s);
       scores_half(sk_next, 1, s_next[1]);
       exp_pv(s, buf_of(j) + kKElems);
-      store((j + 2) % 3);
       take_pids(pv);
       __syncthreads();
     };

@@ -26,7 +26,7 @@ constexpr int kThreads = 64 * kWaves;
 template <int DT, int G>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void pod_kernel(AttnParams dp, AttnParams ap, int dec_blocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * app::VLayout<2>::kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * app::VLayout::kBufElems];
   __shared__ int s_flag;
   const int blk = (int)blockIdx.x;
   if (blk < dec_blocks) {
