@@ -18,6 +18,7 @@ namespace pkfa {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBatch = 8;  // states of one (row, head) whose loads are in flight together
 
 // 8 consecutive values of type DT (FA_F32 or a 16-bit type) <-> fp32.
 template <int DT>
@@ -53,17 +54,20 @@ struct Vec8<FA_F32> {
   }
 };
 
-// Running merge state in log2 units.
+// Running merge state in log2 units. A state with s = -inf leaves it as it
+// is (f = 1, nothing added, whatever its v holds); the update has no branch,
+// so the loads of several states can be in flight before the first is added.
 struct Online {
   float m = kNegInf, sum = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   __device__ __forceinline__ void add(float s2, const float (&v)[8]) {
-    if (s2 == kNegInf) return;
-    const float mn = fmaxf(m, s2);
-    const float f = fast_exp2(m - mn);  // m = -inf -> 0
-    const float w = fast_exp2(s2 - mn);
+    const bool live = s2 != kNegInf;
+    const float mn = live ? fmaxf(m, s2) : m;
+    const float ms = mn == kNegInf ? 0.f : mn;
+    const float f = fast_exp2(m - ms);  // m = -inf -> 0
+    const float w = live ? fast_exp2(s2 - ms) : 0.f;
     sum = sum * f + w;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = acc[i] * f + w * v[i];
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] * f + (live ? w * v[i] : 0.f);
     m = mn;
   }
   __device__ __forceinline__ void finish(float (&out)[8], float& lse2) const {
@@ -112,11 +116,20 @@ __global__ __launch_bounds__(256) void merge_states_kernel(const void* v, const 
     const int64_t row = rh / heads, h = rh % heads;
     const int d = (int)(it % chunks) * 8;
     Online st;
-    for (int c = 0; c < k; ++c) {
-      const int64_t sh = (row * k + c) * heads + h;
-      float x[8];
-      Vec8<DT>::load(v, sh * head_dim + d, x);
-      st.add(s[sh] * kLog2e, x);
+    // up to kBatch states requested at once, then merged in order
+    for (int c0 = 0; c0 < k; c0 += kBatch) {
+      float s2[kBatch], x[kBatch][8];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (c0 + i < k) {
+          const int64_t sh = (row * k + c0 + i) * heads + h;
+          Vec8<DT>::load(v, sh * head_dim + d, x[i]);
+          s2[i] = s[sh] * kLog2e;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (c0 + i < k) st.add(s2[i], x[i]);
     }
     float o[8], lse2;
     st.finish(o, lse2);
@@ -143,23 +156,37 @@ __global__ __launch_bounds__(256) void cascade_merge_kernel(
     const int h = (int)(rh % heads);
     const int d = (int)(it & 15) * 8;
     Online st;
-    float x[8];
+    // the suffix state is requested first; the prefix chunks then come in
+    // batches of kBatch, all of a batch in flight at once
+    float xs[8];
+    Vec8<DT>::load(so, rh * 128 + d, xs);
+    const float ss = sls[rh] * kLog2e;
     if (num_merge > 0) {
       const int hk = h / group, g = h % group;
-      const int32_t* e = merge + ((int64_t)(r / qo_tile) * num_kv_heads + hk) * 4;
-      const int q0 = e[0], base = e[2], C = e[3];
+      // one 16-byte load of the merge entry {q0, -, base, C}
+      const u32x4 e = *reinterpret_cast<const u32x4*>(merge + ((int64_t)(r / qo_tile) * num_kv_heads + hk) * 4);
+      const int q0 = (int)e[0], base = (int)e[2], C = (int)e[3];
       const int rows = (int)min((int64_t)qo_tile, n - q0);
-      for (int c = 0; c < C; ++c) {
-        const int64_t sh = (int64_t)(base + c * rows + (r - q0)) * group + g;
-        Vec8<FA_F32>::load(part_o, sh * 128 + d, x);
-        st.add(part_lse[sh], x);
+      for (int c0 = 0; c0 < C; c0 += kBatch) {
+        float s2[kBatch], x[kBatch][8];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          if (c0 + i < C) {
+            const int64_t sh = (int64_t)(base + (c0 + i) * rows + (r - q0)) * group + g;
+            Vec8<FA_F32>::load(part_o, sh * 128 + d, x[i]);
+            s2[i] = part_lse[sh];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+          if (c0 + i < C) st.add(s2[i], x[i]);
       }
     } else {
+      float x[8];
       Vec8<DT>::load(po, rh * 128 + d, x);
       st.add(pls[rh] * kLog2e, x);
     }
-    Vec8<DT>::load(so, rh * 128 + d, x);
-    st.add(sls[rh] * kLog2e, x);
+    st.add(ss, xs);
     float o[8], lse2;
     st.finish(o, lse2);
     Vec8<DT>::store(vo, rh * 128 + d, o);
