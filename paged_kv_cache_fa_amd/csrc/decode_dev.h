@@ -91,7 +91,8 @@ __device__ __forceinline__ int acc_dim(int s, int i) {
 // q operands of a piece. VALU path: lo[g], hi[g] = dims acc_dim(s, 0..1)
 // and acc_dim(s, 2..3) of head g. MPV: b[i] = the B operand of the i-th
 // 16x16x32 MFMA of the scores: head n = lane % 16 (zero for n >= G), dims
-// 32i + 8 (lane / 16) .. +8.
+// 32i + 8 (lane / 16) .. +8 (E4M3 pools: dims 32 (lane / 16) + 8i .. +8, so
+// that a lane's four K operands come from 32 consecutive code bytes).
 template <int G, bool MPV>
 struct QOps {
   u32x4 lo[G], hi[G];
@@ -312,11 +313,31 @@ __device__ __forceinline__ void consume_page_mpv(const PageRegs<KV8>& pr, const 
         *reinterpret_cast<u32x4*>(vl + vslot(r + 8 * (i >> 1), 8 * (i & 1) + sg)) = w[i];
     }
   };
-  // scores S^T[token 4gq + j][head t]: A operand i = dims 32i + 8gq of token t
-  to_lds(pr.k);
+  // scores S^T[token 4gq + j][head t]: A operand i = dims 32i + 8gq of token t.
+  // E4M3: dims 32gq + 8i. The K codes go to LDS as they are (rows of 128
+  // bytes, 16-byte chunk c of row r at c ^ ((r / 2) mod 8), so the 16 rows
+  // a lane group reads fall in distinct banks); a lane reads its 32 code
+  // bytes in two 16-byte reads and widens them itself: half the LDS traffic
+  // of widening before the store.
   u32x4 ka[4];
+  if constexpr (KV8) {
+    auto kslot = [](int row, int c) { return (uint32_t)(row * 128 + ((c ^ ((row >> 1) & 7)) << 4)); };
+    *reinterpret_cast<u32x4*>(vl + kslot(r, sg)) = pr.k[0];
+    *reinterpret_cast<u32x4*>(vl + kslot(r + 8, sg)) = pr.k[1];
+    const u32x4 c0 = *reinterpret_cast<const u32x4*>(vl + kslot(t, 2 * gq));
+    const u32x4 c1 = *reinterpret_cast<const u32x4*>(vl + kslot(t, 2 * gq + 1));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const u32x4*>(vl + vslot(t, 4 * i + gq));
+    for (int i = 0; i < 4; ++i) {
+      const u32x4& c = i < 2 ? c0 : c1;
+      const int w = 2 * (i & 1);
+      ka[i] = u32x4{E::template from_e4m3<false>(c[w]), E::template from_e4m3<true>(c[w]),
+                    E::template from_e4m3<false>(c[w + 1]), E::template from_e4m3<true>(c[w + 1])};
+    }
+  } else {
+    to_lds(pr.k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ka[i] = *reinterpret_cast<const u32x4*>(vl + vslot(t, 4 * i + gq));
+  }
   f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) c = mfma16x16x32<DT>(ka[i], q.b[i], c);
@@ -702,7 +723,8 @@ __device__ __forceinline__ void begin_piece(const AttnParams& p, const PieceCtx&
     const int n = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      q.b[i] = n < G ? *reinterpret_cast<const u32x4*>(qp + n * 128 + 32 * i + 8 * g)
+      q.b[i] = n < G ? *reinterpret_cast<const u32x4*>(qp + n * 128 + (KV8 ? 32 * g + 8 * i
+                                                                           : 32 * i + 8 * g))
                      : u32x4{0u, 0u, 0u, 0u};
   } else {
 #pragma unroll
