@@ -416,11 +416,10 @@ class PodBench(Timed):
         self.dtabs = (_i32(ix[k:], device), _i32(self.dec_h[0], device),
                       _i32(last[n_prefill:], device))
         self.qo = _i32(qo[: n_prefill + 1], device)
-        # fa_pod's append workgroups take q tiles of 128 / G rows; the two
-        # separate kernels run the append kernel's own (wider) default tiles
-        tile = {} if separate else {"qo_tile": 128 // (wl.num_qo_heads // wl.num_kv_heads)}
+        # both forms take the append kernel's default q tiles (256 / G rows),
+        # which fa_pod runs in the append kernel's workgroup shape
         gp = fa.geometry("append", wl.dtype, n_prefill, wl.num_qo_heads, wl.num_kv_heads,
-                         max_qo_tokens=self.nrows_p, **tile)
+                         max_qo_tokens=self.nrows_p)
         gd = fa.geometry("decode", wl.dtype, wl.batch - n_prefill, wl.num_qo_heads,
                          wl.num_kv_heads)
         self.pp, self.dp = fa.Plan(gp, device=device), fa.Plan(gd, device=device)

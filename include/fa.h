@@ -339,12 +339,16 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
 /* A mixed batch in one launch ([Windows] "Core Features", Attention Kernels:
  * POD-attention, prefill and decode fused for mixed batching): the append /
  * prefill requests of prefill_plan and the decode requests of decode_plan, over
- * the same page pools, run side by side in the same compute units (decode
- * workgroups next to append workgroups, as in fa_cascade's one-kernel form).
- * The results are those of fa_append (q_p, qo_indptr_p_d, kv_*_p_d, out_p,
- * lse_p) and fa_decode (q_d, kv_*_d, out_d, lse_d), bit for bit. Both plans
- * need the same dtype and heads, 16-bit K/V pages and num_qo_heads /
- * num_kv_heads <= 4; pools and strides as in fa_decode. Errors as fa_decode. */
+ * the same page pools, in one kernel. The prefill plan's q tile picks its
+ * shape: tiles of at most 128 / G query positions run beside the decode
+ * workgroups in the same compute units (fa_cascade's one-kernel form); wider
+ * tiles, up to the append kernel's 256 / G (the default qo_tile of an append
+ * geometry), run the append kernel's workgroups, and each compute unit runs
+ * decode or append work at a time. The results are those of fa_append (q_p,
+ * qo_indptr_p_d, kv_*_p_d, out_p, lse_p) and fa_decode (q_d, kv_*_d, out_d,
+ * lse_d), bit for bit. Both plans need the same dtype and heads, 16-bit K/V
+ * pages and num_qo_heads / num_kv_heads <= 4; pools and strides as in
+ * fa_decode. Errors as fa_decode. */
 fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* qo_indptr_p_d,
                  const int32_t* kv_indices_p_d, const int32_t* kv_indptr_p_d,
                  const int32_t* last_page_len_p_d, void* out_p, float* lse_p,

@@ -677,7 +677,7 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
   pa.defer_merge = 1;  // the prefix chunks are merged together with the suffix below
   if (!fork_pre && !fork_suf && kCascadeOneLaunch && G <= 4 && gp.qo_tile <= kPodCols / G) {
     // both passes in one launch, sharing the CUs
-    e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, s);
+    e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, false, s);
     if (e != hipSuccess) return hip_fail(e, "cascade kernel launch");
   } else {
     e = launch_decode(ps, gs.dtype, false, G, sp->num_workers, s_suf);
@@ -724,19 +724,22 @@ fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* 
   const int G = gd.num_qo_heads / gd.num_kv_heads;
   if (!qo_indptr_p_d || ga.dtype != gd.dtype || ga.num_qo_heads != gd.num_qo_heads ||
       ga.num_kv_heads != gd.num_kv_heads || gd.kv_dtype != gd.dtype || G > 4 ||
-      ga.qo_tile > kPodCols / G) {
+      ga.qo_tile > kPodWideCols / G) {
     set_error("pod: the plans need the same dtype and heads, 16-bit K/V pages, "
-              "num_qo_heads / num_kv_heads <= 4, a prefill qo_tile of at most 128 / G and "
+              "num_qo_heads / num_kv_heads <= 4, a prefill qo_tile of at most 256 / G and "
               "qo_indptr");
     return FA_ERR_INVALID;
   }
+  // prefill tiles wider than the shared form's take the append kernel's
+  // workgroup shape (one role per CU at a time)
+  const bool wide = ga.qo_tile > kPodCols / G;
   const AttnParams pa = make_params(pp, q_p, k_pages, v_pages, page_stride, token_stride,
                                     head_stride, kv_indices_p_d, kv_indptr_p_d, last_page_len_p_d,
                                     qo_indptr_p_d, sm_scale, out_p, lse_p);
   const AttnParams pd = make_params(dp, q_d, k_pages, v_pages, page_stride, token_stride,
                                     head_stride, kv_indices_d, kv_indptr_d, last_page_len_d,
                                     nullptr, sm_scale, out_d, lse_d);
-  const hipError_t e = launch_pod(pd, dp->num_workers, pa, ga.max_tiles, gd.dtype, G,
+  const hipError_t e = launch_pod(pd, dp->num_workers, pa, ga.max_tiles, gd.dtype, G, wide,
                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : hip_fail(e, "pod kernel launch");
 }

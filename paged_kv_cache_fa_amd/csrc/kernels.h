@@ -41,12 +41,16 @@ constexpr int kAppendBins = 8;  // append tile bins = XCDs (workgroup i runs bin
 hipError_t launch_decode(const AttnParams& p, int dtype, bool kv_e4m3, int group, int workers,
                          hipStream_t s);
 hipError_t launch_append(const AttnParams& p, int dtype, int group, int max_tiles, hipStream_t s);
-// Cascade's two passes in one launch: decode workers (dp, `workers` waves)
-// and append tiles (ap, its max_tiles grid); group 1, 2 or 4, append tiles of
-// at most kPodCols / group query positions.
+// Decode workers (dp, `workers` waves) and append tiles (ap, its max_tiles
+// grid) in one launch; group 1, 2 or 4. Shared form (wide = false): 4-wave
+// workgroups, a decode and an append workgroup per CU, append tiles of at
+// most kPodCols / group query positions. Wide form: the append kernel's
+// 8-wave workgroups and LDS ring (tiles of up to kPodWideCols / group
+// positions), one workgroup and so one role per CU at a time.
 constexpr int kPodCols = 128;
+constexpr int kPodWideCols = 256;
 hipError_t launch_pod(const AttnParams& dp, int workers, const AttnParams& ap, int max_tiles,
-                      int dtype, int group, hipStream_t s);
+                      int dtype, int group, bool wide, hipStream_t s);
 // Copy n_words 32-bit words from device-visible pinned host memory into device
 // memory with a small kernel (both 16-byte aligned).
 // Copy n_words from src (device-visible host memory) to dst; when flags is not

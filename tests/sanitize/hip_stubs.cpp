@@ -69,7 +69,8 @@ hipError_t launch_decode(const AttnParams&, int, bool, int, int, hipStream_t) {
   reached("launch_decode");
 }
 hipError_t launch_append(const AttnParams&, int, int, int, hipStream_t) { reached("launch_append"); }
-hipError_t launch_pod(const AttnParams&, int, const AttnParams&, int, int, int, hipStream_t) {
+hipError_t launch_pod(const AttnParams&, int, const AttnParams&, int, int, int, bool,
+                      hipStream_t) {
   reached("launch_pod");
 }
 int upload_grid(int64_t) { return 1; }

@@ -27,14 +27,19 @@ def split_mixed(wl, n_prefill):
     return pre, dec, int(qo[n_prefill])
 
 
-@pytest.mark.parametrize("group,causal", [(4, True), (1, False), (2, True)])
-def test_pod_mixed_batch(group, causal):
+@pytest.mark.parametrize("group,causal,wide", [(4, True, False), (1, False, False),
+                                               (2, True, False), (4, True, True),
+                                               (1, False, True), (2, False, True)])
+def test_pod_mixed_batch(group, causal, wide):
+    """Both launch shapes: prefill tiles of 128 / G rows (decode and append
+    workgroups share each CU) and of 256 / G rows (the append kernel's
+    workgroups, one role per CU at a time)."""
     import torch
     import paged_kv_cache_fa_amd as fa
     pre_lens, pre_qo = [300, 64, 1000], [300, 17, 128] if causal else [40, 17, 128]
     dec_lens = [1, 15, 16, 17, 33, 257, 5, 900, 2000, 48]
     hkv = 4
-    print(f"[pod] G={group} causal={causal}", flush=True)
+    print(f"[pod] G={group} causal={causal} wide={wide}", flush=True)
     wl = make_workload(pre_lens + dec_lens, hkv * group, hkv, "bf16", 80 + group,
                        qo_lens=pre_qo + [1] * len(dec_lens), causal=causal, mode="test",
                        extra_pages=3)
@@ -48,7 +53,7 @@ def test_pod_mixed_batch(group, causal):
     strides = (2 * ps * hk * d, hk * d, d)
     k, v = pool[:, 0], pool[:, 1]
     gp = fa.geometry("append", "bf16", len(pre_lens), hkv * group, hkv, max_qo_tokens=nrows_p,
-                     num_cu=32, qo_tile=128 // group)
+                     num_cu=32, qo_tile=(256 if wide else 128) // group)
     gd = fa.geometry("decode", "bf16", len(dec_lens), hkv * group, hkv, num_cu=32)
     pp = fa.plan(gp, pre["kv_indptr"], pre["kv_lens"], pre["qo_indptr"], causal, device="cuda")
     dp = fa.plan(gd, dec["kv_indptr"], dec["kv_lens"], device="cuda")
@@ -70,15 +75,14 @@ def test_pod_mixed_batch(group, causal):
     assert_close(to_f64(od), to_f64(ld), *ref_d, what="pod decode")
 
 
-def test_pod_refuses_wide_prefill_tiles():
-    """fa_pod's append workgroups hold 128 / G query positions: a prefill plan
-    with wider q tiles (the append kernel's default) is refused."""
+def test_pod_refuses_group_8():
+    """fa_pod runs groups of at most 4 query heads per kv head."""
     import torch
     import paged_kv_cache_fa_amd as fa
-    wl = make_workload([300, 40], 16, 4, "bf16", 3, qo_lens=[100, 1], causal=True, mode="test")
+    wl = make_workload([300, 40], 32, 4, "bf16", 3, qo_lens=[100, 1], causal=True, mode="test")
     pre, dec, nrows_p = split_mixed(wl, 1)
-    gp = fa.geometry("append", "bf16", 1, 16, 4, max_qo_tokens=nrows_p)   # qo_tile 256 / 4
-    gd = fa.geometry("decode", "bf16", 1, 16, 4)
+    gp = fa.geometry("append", "bf16", 1, 32, 4, max_qo_tokens=nrows_p)
+    gd = fa.geometry("decode", "bf16", 1, 32, 4)
     pp = fa.plan(gp, pre["kv_indptr"], pre["kv_lens"], pre["qo_indptr"], True, device="cuda")
     dp = fa.plan(gd, dec["kv_indptr"], dec["kv_lens"], device="cuda")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
