@@ -197,10 +197,16 @@ class Timed:
         self.replan()
         self.run_call(i)
 
+    def warm(self, warmup: int) -> int:
+        """Untimed steps before a timed run: at least one per rotated input
+        copy (the first launch over a copy is slow, a one-time cost)."""
+        return max(warmup, len(getattr(self, "pools", ())))
+
     def steps_ms(self, steps: int, warmup: int) -> float:
         """Whole steps (re-plan + run), back to back with nothing else queued
         between them: torch events around all steps, mean per step."""
         import torch
+        warmup = self.warm(warmup)
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
@@ -217,6 +223,7 @@ class Timed:
         """The run calls alone: each step re-plans, then HIP timing events on
         the launch stream bracket its run calls; mean over the launches."""
         import torch
+        warmup = self.warm(warmup)
         for i in range(warmup):
             self.step(i)
         ev = [(HipEvent(), HipEvent()) for _ in range(launches)]
