@@ -63,9 +63,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 // Workgroups of WAVES waves (a template parameter): 8 in the append kernel
-// (one workgroup per CU, 2 waves per SIMD), 4 in the one-launch mixed kernel,
-// whose append workgroups share each CU with decode workgroups. A workgroup
-// covers 32 WAVES query columns.
+// and the wide one-launch form (one workgroup per CU, 2 waves per SIMD), 4 in
+// the shared one-launch form, whose append workgroups share each CU with
+// decode workgroups. A workgroup covers 32 WAVES query columns.
 constexpr int kBlockKeys = 64;
 constexpr int kKStride = 136;  // 16-bit elements per K slot row in LDS (128 dims + 8 pad)
 constexpr int kKElems = kBlockKeys * kKStride;
