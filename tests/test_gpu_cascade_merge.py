@@ -58,6 +58,23 @@ def test_merge_states(dtype, k):
                  what=f"merge_states {dtype} k={k}")
 
 
+@pytest.mark.parametrize("k", [3, 17])
+def test_merge_states_ignores_empty_values(k):
+    """A state with lse = -inf leaves the merge as it is, whatever its values
+    hold (NaN here): the same bits as with finite values in those states."""
+    import torch
+    import paged_kv_cache_fa_amd as fa
+    rng = np.random.default_rng(40 + k)
+    v, s, _, _ = _states(rng, (23, k, 4), "fp32", empty_frac=0.3)
+    v_nan = v.clone()
+    v_nan[torch.isinf(s)] = float("nan")
+    vo, so = fa.merge_states(v, s)
+    vn, sn = fa.merge_states(v_nan, s)
+    torch.cuda.synchronize()
+    assert torch.equal(vo, vn) and torch.equal(so, sn)
+    assert bool(torch.isfinite(vo).all())
+
+
 def test_merge_recovers_unsplit_attention():
     """Two decode passes over disjoint halves of each request's keys, merged on
     the GPU, equal the oracle over the whole request."""
