@@ -529,42 +529,87 @@ __device__ __forceinline__ void append_tile(const AttnParams& p, int tile_id, ui
     s_flag = last;
   }
   __syncthreads();
-  if (!s_flag || !qvalid) return;
+  if (!s_flag) return;
 
-  // last workgroup of the split: merge the chunks of every column; lane (h, jq)
-  // owns dims 64 h .. 64 h + 63 of its column
-  float acc[64];
+  // last workgroup of the split: merge the chunks. The chunk-c states of this
+  // tile are one run of rows G entries (entry pos G + g) of 512 bytes from
+  // entry (base + c rows) G. First each entry's max and sum over the chunks
+  // (thread = entry), then the weighted sum with the weights known, a wave
+  // reading 2 whole entries per load: thread tid takes 16-byte unit tid mod 32
+  // of entries tid / 32 + 2 WAVES r, r < 16.
+  const int nent = rows * G;
+  float* s_max = reinterpret_cast<float*>(smem);
+  float* s_inv = s_max + kCols;
+  if (tid < nent) {
+    float mx = kNegInf, sum = 0.f;
+#pragma unroll 1
+    for (int c0 = 0; c0 < nchunk; c0 += 8) {
+      float s2[8];
 #pragma unroll
-  for (int i = 0; i < 64; ++i) acc[i] = 0.f;
-  float gm = kNegInf, gl = 0.f;
+      for (int i = 0; i < 8; ++i) {
+        const int c = min(c0 + i, nchunk - 1);
+        s2[i] = __hip_atomic_load(p.part_lse + (int64_t)(base + c * rows) * G + tid,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool live = c0 + i < nchunk && s2[i] != kNegInf;
+        const float mn = live ? fmaxf(mx, s2[i]) : mx;
+        const float ms = mn == kNegInf ? 0.f : mn;
+        sum = sum * fast_exp2(mx - ms) + (live ? fast_exp2(s2[i] - ms) : 0.f);
+        mx = mn;
+      }
+    }
+    const bool live = sum > 0.f;
+    s_max[tid] = mx == kNegInf ? 0.f : mx;
+    s_inv[tid] = live ? 1.f / sum : 0.f;
+    if (p.lse)
+      p.lse[(int64_t)(q0 + tid / G) * Hq + hk * G + tid % G] =
+          live ? (mx + fast_log2(sum)) * kLn2 : kNegInf;
+  }
+  __syncthreads();
+
+  constexpr int kStep = 2 * WAVES;  // entries per load
+  const int unit = tid & 31, e0 = tid >> 5;
+  const __amdgpu_buffer_rsrc_t rl =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.part_lse, 0, 0x7fffffff, 0x00020000);
+  // lane 2 r + hh (and 32 + 2 r + hh) fetches the weight of the wave's entry
+  // 2 wave + hh + kStep r; round r reads it from there
+  const int el = min(2 * wave + (lane & 1) + kStep * ((lane & 31) >> 1), nent - 1);
+  const float mx_l = s_max[el], inv_l = s_inv[el];
+  float acc[16][4];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[r][i] = 0.f;
+#pragma unroll 1
   for (int c = 0; c < nchunk; ++c) {
-    const int64_t sh = (int64_t)(base + c * rows + pos) * G + g;
-    const float s2 = __hip_atomic_load(p.part_lse + sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t ob = (uint32_t)sh * 512u + 256u * h;
+    const uint32_t ebase = (uint32_t)((base + c * rows) * G);  // wave-uniform
     u32x4 raw[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, ob + 16 * i, 0, kCoherent);
-    const float mn = fmaxf(gm, s2);
-    const float ms = mn == kNegInf ? 0.f : mn;
-    const float f = fast_exp2(gm - ms);
-    const float w = fast_exp2(s2 - ms);
-    gl = gl * f + w;
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t e = (uint32_t)min(e0 + kStep * r, nent - 1);
+      raw[r] = __builtin_amdgcn_raw_buffer_load_b128(rs, e * 512u + 16u * unit, ebase * 512u, kCoherent);
+    }
+    const float s2 = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)el * 4u, ebase * 4u, kCoherent));
+    const float w_l = fast_exp2(s2 - mx_l) * inv_l;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) acc[i] = acc[i] * f + w * __uint_as_float(raw[i >> 2][i & 3]);
-    gm = mn;
+    for (int r = 0; r < 16; ++r) {
+      const float w = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (2 * r + h), __float_as_int(w_l)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[r][i] += w * __uint_as_float(raw[r][i]);
+    }
   }
-  const bool glive = gl > 0.f;
-  const float ginv = glive ? 1.f / gl : 0.f;
-  uint16_t* op = p.out + ((int64_t)(q0 + pos) * Hq + head) * 128 + 64 * h;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = Elt<DT>::pack(acc[8 * i + 2 * e] * ginv, acc[8 * i + 2 * e + 1] * ginv);
-    *reinterpret_cast<u32x4*>(op + 8 * i) = w;
+  for (int r = 0; r < 16; ++r) {
+    const int e = e0 + kStep * r;
+    if (e < nent) {
+      uint16_t* op = p.out + ((int64_t)(q0 + e / G) * Hq + hk * G + e % G) * 128 + 4 * unit;
+      *reinterpret_cast<u32x2*>(op) = u32x2{Elt<DT>::pack(acc[r][0], acc[r][1]),
+                                            Elt<DT>::pack(acc[r][2], acc[r][3])};
+    }
   }
-  if (h == 0 && p.lse)
-    p.lse[(int64_t)(q0 + pos) * Hq + head] = glive ? (gm + fast_log2(gl)) * kLn2 : kNegInf;
 }
 
 // Workgroup i runs tiles of bin i mod 8 (the XCD the hardware gives it), at

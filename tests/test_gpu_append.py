@@ -44,6 +44,20 @@ def test_split_chunks(num_cu, tiles_per_cu):
     _case(lens, qo, 32, 8, "bf16", 7, num_cu=num_cu, tiles_per_cu=tiles_per_cu)
 
 
+@pytest.mark.parametrize("group,dtype,lens,qo,num_cu,tiles_per_cu", [
+    (1, "fp16", [3000, 130], [70, 9], 64, 8),    # over a hundred chunks per tile
+    (2, "bf16", [900], [900], 16, 8),            # causal prefill: early rows see empty chunks
+    (8, "bf16", [1500, 40], [33, 40], 32, 8),    # one partial tile of 32 columns per request
+    (4, "fp16", [2500], [200], 8, 4),            # a ragged last tile (200 = 3 x 64 + 8)
+])
+def test_split_chunks_groups(group, dtype, lens, qo, num_cu, tiles_per_cu):
+    # the last workgroup of a split merges the chunks: every group size, chunk
+    # counts past the merge's batch of 8, rows with no visible key in a chunk
+    plan = _case(lens, qo, 2 * group, 2, dtype, 60 + group, num_cu=num_cu,
+                 tiles_per_cu=tiles_per_cu)
+    assert plan.info().num_merge > 0
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_prefix_style_non_causal(causal):
     # many query rows against one long request (the shared-prefix pass shape)
