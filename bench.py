@@ -499,8 +499,10 @@ class CascadeBench(Timed):
         self.p_indices = _i32(wl.prefix_indices, device)
         self.p_last = _i32(wl.prefix_last_page_len, device)
         self.qo = _i32([0, B], device)
-        # prefix q tiles of 128 / G rows: the one-launch cascade kernel's append workgroups
-        pk = {"qo_tile": 128 // (wl.num_qo_heads // wl.num_kv_heads), **(prefix_knobs or {})}
+        # prefix q tiles of the append default (256 / G rows), one per CU: the
+        # one-launch kernel's wide form, two rounds of tiles on the half of the
+        # CUs that the suffix decode leaves
+        pk = {"tiles_per_cu": 1, **(prefix_knobs or {})}
         gp = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads, max_qo_tokens=B,
                          **pk)
         gs = fa.geometry("decode", wl.dtype, B, wl.num_qo_heads, wl.num_kv_heads,

@@ -81,7 +81,7 @@ typedef struct {
   int32_t num_cu;          /* compute units to spread tiles over (default 256) */
   int32_t tiles_per_cu;    /* decode: worker waves per compute unit (default 4); append: tiles per CU (default 2) */
   int32_t min_chunk_pages; /* smallest split-KV chunk / decode piece size in pages (default 1) */
-  int32_t qo_tile;         /* append: query rows per tile, 1..128/G (default 128/G,
+  int32_t qo_tile;         /* append: query rows per tile, 1..256/G (default 256/G,
                               G = num_qo_heads / num_kv_heads); decode: 1 */
   int32_t max_tiles;       /* capacities; the defaults cover every plan whose total pages
                               (plus 4 or 8 per request) stay within 128 pages per bin (decode:
@@ -341,7 +341,7 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
  * prefill requests of prefill_plan and the decode requests of decode_plan, over
  * the same page pools, in one kernel. The prefill plan's q tile picks its
  * shape: tiles of at most 128 / G query positions run beside the decode
- * workgroups in the same compute units (fa_cascade's one-kernel form); wider
+ * workgroups in the same compute units; wider
  * tiles, up to the append kernel's 256 / G (the default qo_tile of an append
  * geometry), run the append kernel's workgroups, and each compute unit runs
  * decode or append work at a time. The results are those of fa_append (q_p,
@@ -374,18 +374,22 @@ fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* 
  *               partial states in the prefix plan's workspace.)
  *  out / lse    device [batch, num_qo_heads, head_dim] / fp32 (lse may be NULL).
  * With both extra streams NULL (or equal to `stream`) and num_qo_heads /
- * num_kv_heads <= 4, one kernel on `stream` runs both passes side by side in
- * the same compute units (decode workgroups next to append workgroups: the
- * matrix work of the prefix overlaps the suffix streaming). Otherwise the
+ * num_kv_heads <= 4, one kernel on `stream` runs both passes side by side
+ * (fa_pod's two shapes, picked by the prefix plan's q tile: up to 128 / G
+ * positions, the prefix workgroups share each compute unit with a decode
+ * workgroup; up to 256 / G, the append geometry's default, the decode takes
+ * half the compute units and the prefix tiles the other half at full rate,
+ * then all of them). Otherwise the
  * suffix decode runs on `suffix_stream` and the prefix pass on
  * `prefix_stream` (each NULL or equal to `stream` = run on `stream`); streams
  * other than `stream` are forked from it and joined back with events of the
  * suffix plan (capturable). Then one combine kernel on `stream` merges, per
  * (request, head), the prefix chunks and the suffix state by log-sum-exp.
- * (Measured on MI355X at batch 256 / 16k prefix: the one-kernel form takes
- * 231 us per call against 265 us for the two passes in order with 256 / G
- * prefix tiles; the passes on separate streams, sharing or splitting the
- * compute units, were slower than in order.) Other
+ * (Measured on MI355X at batch 256 / 16k prefix, G = 4, with 1 GiB of pool
+ * copies rotated: the kernel spans 152-166 us with 256 / G prefix tiles and
+ * one tile per compute unit (tiles_per_cu 1), 181-192 us with 128 / G tiles
+ * sharing the compute units; the passes on separate streams, sharing or
+ * splitting the compute units, were slower than in order.) Other
  * arguments as fa_decode. Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED,
  * FA_ERR_HIP. */
 fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan, const void* q,

@@ -675,9 +675,10 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
                               prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
                               prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
   pa.defer_merge = 1;  // the prefix chunks are merged together with the suffix below
-  if (!fork_pre && !fork_suf && kCascadeOneLaunch && G <= 4 && gp.qo_tile <= kPodCols / G) {
-    // both passes in one launch, sharing the CUs
-    e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, false, s);
+  if (!fork_pre && !fork_suf && kCascadeOneLaunch && G <= 4 && gp.qo_tile <= kPodWideCols / G) {
+    // both passes in one launch: q tiles of up to 128 / G positions share each
+    // CU with a decode workgroup, wider ones take whole CUs beside the decode's
+    e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, gp.qo_tile > kPodCols / G, s);
     if (e != hipSuccess) return hip_fail(e, "cascade kernel launch");
   } else {
     e = launch_decode(ps, gs.dtype, false, G, sp->num_workers, s_suf);

@@ -8,15 +8,17 @@
 // Workgroups 0 .. dec_blocks-1 are decode workers (independent waves, the
 // decode plan's work lists); the rest run the append plan's tiles (bins by
 // workgroup index mod 8, as in the append kernel). Two shapes:
-//  * shared (cascade): 4-wave workgroups compiled for 2 waves per SIMD (at
+//  * shared: 4-wave workgroups compiled for 2 waves per SIMD (at
 //    most 256 registers each), two LDS stages, so a CU holds one decode and
 //    one append workgroup at once and the append waves' matrix work overlaps
 //    the decode waves' memory streaming; append tiles hold at most 128 / G
 //    query positions, and the decode role keeps a 2-page ring;
-//  * wide (mixed batch): the append kernel's 8-wave workgroups and four-stage
-//    LDS ring (tiles of up to 256 / G positions); one workgroup fills a CU's
-//    LDS, so each CU runs one role at a time and picks up append tiles once
-//    its decode workgroup is done.
+//  * wide: the append kernel's 8-wave workgroups and four-stage LDS ring
+//    (tiles of up to 256 / G positions); one workgroup fills a CU's LDS, so
+//    each CU runs one role at a time. A decode workgroup runs 8 worker waves,
+//    so a decode plan of 4 worker waves per CU holds half the CUs (which
+//    still stream near the HBM peak) while the append tiles run at full rate
+//    on the other half and then move onto the decode's CUs as they finish.
 // Split units merge as in the two kernels (a cascade's prefix pass defers to
 // the cascade combine).
 #include "append_dev.h"

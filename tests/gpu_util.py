@@ -124,10 +124,9 @@ def run_cascade(dw: DevWorkload, prefix_plan=None, suffix_plan=None, fused=False
     wl = dw.wl
     B = wl.batch
     if prefix_plan is None:
-        # prefix q tiles of 128 / G rows fit the one-launch cascade kernel's
-        # append workgroups (wider tiles run the two-launch form)
+        # the append geometry's default q tile (256 / G rows: the one-launch
+        # kernel's wide form); {"qo_tile": 128 // G} picks its shared form
         pk = dict(knobs.get("prefix", {}))
-        pk.setdefault("qo_tile", 128 // (wl.num_qo_heads // wl.num_kv_heads))
         g = fa.geometry("append", wl.dtype, 1, wl.num_qo_heads, wl.num_kv_heads,
                         max_qo_tokens=B, **pk)
         prefix_plan = fa.Plan(g, device=dw.device)

@@ -110,10 +110,16 @@ def test_merge_recovers_unsplit_attention():
     assert_close(to_f64(out), lse.cpu().numpy().astype(np.float64), *ref, what="split+merge")
 
 
-def test_cascade_small():
+# the prefix plan's q tile picks the one-launch kernel's shape: 128 / G rows
+# share each CU with a decode workgroup, 256 / G (the default) take whole CUs
+FORMS = {"shared": {"qo_tile": 32}, "wide": {}}
+
+
+@pytest.mark.parametrize("form", sorted(FORMS))
+def test_cascade_small(form):
     wl = make_cascade(256, [5, 16, 17, 300, 1], 32, 8, "bf16", 21, mode="test")
     dw = DevWorkload(wl)
-    out, lse, _ = run_cascade(dw, prefix={"num_cu": 4}, suffix={"num_cu": 4})
+    out, lse, _ = run_cascade(dw, prefix={"num_cu": 4, **FORMS[form]}, suffix={"num_cu": 4})
     ref = oracle_cascade(wl)
     assert_close(to_f64(out), to_f64(lse), *ref, what="cascade small")
     direct = oracle.cascade_direct(wl.q, wl.pool, wl.dtype, wl.prefix_indptr, wl.prefix_indices,
@@ -122,8 +128,9 @@ def test_cascade_small():
     assert_close(to_f64(out), to_f64(lse), *direct, what="cascade vs direct")
 
 
+@pytest.mark.parametrize("form", sorted(FORMS))
 @pytest.mark.parametrize("prefix_len,num_cu", [(512, 8), (96, 1), (2048, 64)])
-def test_cascade_call(prefix_len, num_cu):
+def test_cascade_call(prefix_len, num_cu, form):
     """fa_cascade matches the oracle whether the prefix pass splits its keys
     (chunk partials merged with the suffix in the combine kernel) or not, and
     gives the same bits serially and with the passes forked onto other streams."""
@@ -131,8 +138,9 @@ def test_cascade_call(prefix_len, num_cu):
     wl = make_cascade(prefix_len, [5, 16, 17, 300, 1, 64, 900, 0], 32, 8, "bf16", 22,
                       mode="test")
     dw = DevWorkload(wl)
-    _, _, plans = run_cascade(dw, prefix={"num_cu": num_cu}, suffix={"num_cu": 8})
-    print(f"[cascade] prefix {prefix_len}: {plans[0].info().num_merge} split units", flush=True)
+    _, _, plans = run_cascade(dw, prefix={"num_cu": num_cu, **FORMS[form]}, suffix={"num_cu": 8})
+    print(f"[cascade] prefix {prefix_len} {form}: {plans[0].info().num_merge} split units",
+          flush=True)
     o1, l1, _ = run_cascade(dw, *plans, fused=True)
     o1, l1 = o1.clone(), l1.clone()
     o2, l2, _ = run_cascade(dw, *plans, fused=True, side_stream=torch.cuda.Stream())
@@ -145,8 +153,8 @@ def test_cascade_call(prefix_len, num_cu):
     assert_close(to_f64(o1), to_f64(l1), *oracle_cascade(wl), what="fa_cascade")
 
 
-@pytest.mark.parametrize("forked", [True, False])
-def test_cascade_graph_capture_with_side_stream(forked):
+@pytest.mark.parametrize("forked,form", [(True, "wide"), (False, "wide"), (False, "shared")])
+def test_cascade_graph_capture_with_side_stream(forked, form):
     """fa_cascade captures into one graph, with the fork/join of a side stream
     or as the one-kernel form; replays (with eager work and synchronisation
     between them) reproduce the eager bits."""
@@ -154,7 +162,7 @@ def test_cascade_graph_capture_with_side_stream(forked):
     import paged_kv_cache_fa_amd as fa
     wl = make_cascade(256, [40, 3, 700], 32, 8, "bf16", 23, mode="test")
     dw = DevWorkload(wl)
-    _, _, plans = run_cascade(dw, prefix={"num_cu": 8}, suffix={"num_cu": 8})
+    _, _, plans = run_cascade(dw, prefix={"num_cu": 8, **FORMS[form]}, suffix={"num_cu": 8})
     ref_o, ref_l, _ = run_cascade(dw, *plans, fused=True)  # eager fa_cascade
     ref_o, ref_l = ref_o.clone(), ref_l.clone()
     assert plans[0].info().num_merge > 0  # the prefix chunks go through the combine kernel
@@ -181,25 +189,36 @@ def test_cascade_graph_capture_with_side_stream(forked):
         assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
 
 
-def test_cascade_batch256_full_size():
-    """The batch-256 cascade (16384-token shared prefix) in the launch
-    configuration the benchmark times: one fa_cascade call on one stream (both
-    passes in one kernel); the same bits with the prefix pass forked onto a
+_FULL = {}
+
+
+def _full_cascade():
+    if not _FULL:
+        print("[cascade batch 256] generating", flush=True)
+        wl = make_config(4, mode="test")
+        _FULL["wl"], _FULL["dw"] = wl, DevWorkload(wl)
+        _FULL["ref"] = oracle_cascade(wl)
+    return _FULL["wl"], _FULL["dw"], _FULL["ref"]
+
+
+@pytest.mark.parametrize("form,knobs", [("wide", {"tiles_per_cu": 1}), ("shared", {"qo_tile": 32})])
+def test_cascade_batch256_full_size(form, knobs):
+    """The batch-256 cascade (16384-token shared prefix) as one fa_cascade
+    call on one stream (both passes in one kernel), in the launch
+    configuration the benchmark times (wide: 64-row prefix tiles, one per CU)
+    and in the shared form; the same bits with the prefix pass forked onto a
     side stream."""
     import torch
-    print("[cascade batch 256] generating", flush=True)
-    wl = make_config(4, mode="test")
-    dw = DevWorkload(wl)
-    out, lse, plans = run_cascade(dw, fused=True)
+    wl, dw, ref = _full_cascade()
+    out, lse, plans = run_cascade(dw, fused=True, prefix=knobs)
     out, lse = out.clone(), lse.clone()
     o2, l2, _ = run_cascade(dw, *plans, fused=True, side_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     assert torch.equal(out, o2) and torch.equal(lse, l2)
-    print(f"[cascade batch 256] prefix tiles {plans[0].info().num_tiles} suffix tiles "
+    print(f"[cascade batch 256 {form}] prefix tiles {plans[0].info().num_tiles} suffix tiles "
           f"{plans[1].info().num_tiles}", flush=True)
-    ref = oracle_cascade(wl)
-    e = assert_close(to_f64(out), to_f64(lse), *ref, what="cascade batch 256")
-    print(f"[cascade batch 256] all {wl.batch} requests: max-abs out {e[0]:.3g} "
+    e = assert_close(to_f64(out), to_f64(lse), *ref, what=f"cascade batch 256 {form}")
+    print(f"[cascade batch 256 {form}] all {wl.batch} requests: max-abs out {e[0]:.3g} "
           f"lse {e[1]:.3g}", flush=True)
 
 
@@ -232,13 +251,25 @@ def test_cascade_equals_decode_over_prefix_and_suffix():
                  what="cascade vs decode")
 
 
-def test_cascade_wide_prefix_tiles_two_launches():
-    """A prefix plan with q tiles wider than the one-launch kernel's 128 / G
-    positions (the planner's default for append) runs as the suffix decode and
-    the append kernel in order, then the combine; same results as the oracle."""
+def test_cascade_wide_prefix_tiles():
+    """A prefix plan with q tiles of 256 / G positions (the planner's default
+    for append) runs the one-launch kernel's wide form; same results as the
+    oracle."""
     wl = make_cascade(512, [5, 16, 300, 0, 900], 32, 8, "bf16", 24, mode="test")
     dw = DevWorkload(wl)
     out, lse, plans = run_cascade(dw, fused=True, prefix={"qo_tile": 64, "num_cu": 8},
                                   suffix={"num_cu": 8})
     assert plans[0].info().resolved.qo_tile == 64
     assert_close(to_f64(out), to_f64(lse), *oracle_cascade(wl), what="cascade wide tiles")
+
+
+@pytest.mark.parametrize("qo_tile", [32, 16])
+def test_cascade_group8_two_launches(qo_tile):
+    """Eight query heads per kv head: no one-launch form, so fa_cascade runs the
+    suffix decode and the append kernel in order, then the combine."""
+    wl = make_cascade(704, [5, 16, 300, 0, 33], 32, 4, "bf16", 25, mode="test")
+    dw = DevWorkload(wl)
+    out, lse, plans = run_cascade(dw, fused=True, prefix={"qo_tile": qo_tile, "num_cu": 8},
+                                  suffix={"num_cu": 8})
+    assert plans[0].info().num_merge > 0
+    assert_close(to_f64(out), to_f64(lse), *oracle_cascade(wl), what="cascade G = 8")

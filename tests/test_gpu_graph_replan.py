@@ -190,9 +190,11 @@ def test_append_graph_replan_causal_switch():
     _replay_check(s, g, replan, slots, wls * 2, ref_of, lambda wl: wl.rows)
 
 
-def test_cascade_graph_replan():
-    """fa_cascade (one kernel for both passes + the combine): new suffix lengths,
-    a new prefix length (split into chunks or not) and a smaller batch."""
+@pytest.mark.parametrize("qo_tile", [32, 64])
+def test_cascade_graph_replan(qo_tile):
+    """fa_cascade (one kernel for both passes, in its shared or wide form, + the
+    combine): new suffix lengths, a new prefix length (split into chunks or
+    not) and a smaller batch."""
     import torch
     import paged_kv_cache_fa_amd as fa
     wls = [make_cascade(512, [5, 16, 17, 300, 1, 64], 32, 8, "bf16", 41, mode="test"),
@@ -201,7 +203,7 @@ def test_cascade_graph_replan():
     slots = Slots(wls, prefix=True)
     s = torch.cuda.Stream()
     B = max(w.batch for w in wls)
-    gp = fa.geometry("append", "bf16", 1, 32, 8, max_qo_tokens=B, num_cu=8, qo_tile=32)
+    gp = fa.geometry("append", "bf16", 1, 32, 8, max_qo_tokens=B, num_cu=8, qo_tile=qo_tile)
     pplan = fa.Plan(gp, device="cuda")
     splan = fa.Plan(fa.geometry("decode", "bf16", B, 32, 8, num_cu=8), device="cuda")
 
