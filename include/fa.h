@@ -385,9 +385,12 @@ fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* 
  * other than `stream` are forked from it and joined back with events of the
  * suffix plan (capturable). Then one combine kernel on `stream` merges, per
  * (request, head), the prefix chunks and the suffix state by log-sum-exp.
+ * In the wide shape a decode plan of 4 worker waves per compute unit holds
+ * half of them, so a prefix plan of one round of tiles for the other half
+ * (num_cu 128, tiles_per_cu 1 on 256 compute units) fits it best.
  * (Measured on MI355X at batch 256 / 16k prefix, G = 4, with 1 GiB of pool
- * copies rotated: the kernel spans 152-166 us with 256 / G prefix tiles and
- * one tile per compute unit (tiles_per_cu 1), 181-192 us with 128 / G tiles
+ * copies rotated, per call in one run: 179-184 us with that prefix plan,
+ * 196-200 us with two rounds of 256 / G tiles, 204 us with 128 / G tiles
  * sharing the compute units; the passes on separate streams, sharing or
  * splitting the compute units, were slower than in order.) Other
  * arguments as fa_decode. Errors: FA_ERR_INVALID, FA_ERR_NOT_PLANNED,

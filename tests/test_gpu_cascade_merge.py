@@ -201,12 +201,13 @@ def _full_cascade():
     return _FULL["wl"], _FULL["dw"], _FULL["ref"]
 
 
-@pytest.mark.parametrize("form,knobs", [("wide", {"tiles_per_cu": 1}), ("shared", {"qo_tile": 32})])
+@pytest.mark.parametrize("form,knobs", [("wide", {"num_cu": 128, "tiles_per_cu": 1}),
+                                        ("shared", {"qo_tile": 32})])
 def test_cascade_batch256_full_size(form, knobs):
     """The batch-256 cascade (16384-token shared prefix) as one fa_cascade
     call on one stream (both passes in one kernel), in the launch
-    configuration the benchmark times (wide: 64-row prefix tiles, one per CU)
-    and in the shared form; the same bits with the prefix pass forked onto a
+    configuration the benchmark times (wide: 64-row prefix tiles, one round
+    of 128) and in the shared form; the same bits with the prefix pass forked onto a
     side stream."""
     import torch
     wl, dw, ref = _full_cascade()
