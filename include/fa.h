@@ -346,9 +346,10 @@ fa_status fa_append(const fa_plan_t* plan, const void* q, const int32_t* qo_indp
  * geometry), run the append kernel's workgroups, and each compute unit runs
  * decode or append work at a time. The results are those of fa_append (q_p,
  * qo_indptr_p_d, kv_*_p_d, out_p, lse_p) and fa_decode (q_d, kv_*_d, out_d,
- * lse_d), bit for bit. Both plans need the same dtype and heads, 16-bit K/V
- * pages and num_qo_heads / num_kv_heads <= 4; pools and strides as in
- * fa_decode. Errors as fa_decode. */
+ * lse_d), bit for bit. Both plans need the same dtype and heads and 16-bit
+ * K/V pages; with num_qo_heads / num_kv_heads = 8 only the wider tiles are
+ * built (qo_tile 17..32). Pools and strides as in fa_decode. Errors as
+ * fa_decode. */
 fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* qo_indptr_p_d,
                  const int32_t* kv_indices_p_d, const int32_t* kv_indptr_p_d,
                  const int32_t* last_page_len_p_d, void* out_p, float* lse_p,
@@ -373,13 +374,12 @@ fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* 
  *               does not split its keys; split prefix chunks stay as fp32
  *               partial states in the prefix plan's workspace.)
  *  out / lse    device [batch, num_qo_heads, head_dim] / fp32 (lse may be NULL).
- * With both extra streams NULL (or equal to `stream`) and num_qo_heads /
- * num_kv_heads <= 4, one kernel on `stream` runs both passes side by side
- * (fa_pod's two shapes, picked by the prefix plan's q tile: up to 128 / G
- * positions, the prefix workgroups share each compute unit with a decode
- * workgroup; up to 256 / G, the append geometry's default, the decode takes
- * half the compute units and the prefix tiles the other half at full rate,
- * then all of them). Otherwise the
+ * With both extra streams NULL (or equal to `stream`), one kernel on `stream`
+ * runs both passes side by side (fa_pod's two shapes, picked by the prefix
+ * plan's q tile: up to 128 / G positions, G <= 4, the prefix workgroups
+ * share each compute unit with a decode workgroup; up to 256 / G, the append
+ * geometry's default, the decode takes half the compute units and the prefix
+ * tiles the other half at full rate, then all of them). Otherwise the
  * suffix decode runs on `suffix_stream` and the prefix pass on
  * `prefix_stream` (each NULL or equal to `stream` = run on `stream`); streams
  * other than `stream` are forked from it and joined back with events of the

@@ -675,10 +675,13 @@ fa_status fa_cascade(const fa_plan_t* prefix_plan, const fa_plan_t* suffix_plan,
                               prefix_indices_d, prefix_indptr_d, prefix_last_page_len_d,
                               prefix_qo_indptr_d, sm_scale, prefix_out, prefix_lse);
   pa.defer_merge = 1;  // the prefix chunks are merged together with the suffix below
-  if (!fork_pre && !fork_suf && kCascadeOneLaunch && G <= 4 && gp.qo_tile <= kPodWideCols / G) {
+  const bool wide = gp.qo_tile > kPodCols / G;
+  if (!fork_pre && !fork_suf && kCascadeOneLaunch && gp.qo_tile <= kPodWideCols / G &&
+      (G <= 4 || wide)) {
     // both passes in one launch: q tiles of up to 128 / G positions share each
-    // CU with a decode workgroup, wider ones take whole CUs beside the decode's
-    e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, gp.qo_tile > kPodCols / G, s);
+    // CU with a decode workgroup (G <= 4), wider ones take whole CUs beside
+    // the decode's
+    e = launch_pod(ps, sp->num_workers, pa, gp.max_tiles, gs.dtype, G, wide, s);
     if (e != hipSuccess) return hip_fail(e, "cascade kernel launch");
   } else {
     e = launch_decode(ps, gs.dtype, false, G, sp->num_workers, s_suf);
@@ -723,17 +726,17 @@ fa_status fa_pod(const fa_plan_t* prefill_plan, const void* q_p, const int32_t* 
   const fa_geometry& ga = pp->geom;
   const fa_geometry& gd = dp->geom;
   const int G = gd.num_qo_heads / gd.num_kv_heads;
+  // prefill tiles wider than the shared form's take the append kernel's
+  // workgroup shape (one role per CU at a time); G = 8 has only that shape
+  const bool wide = ga.qo_tile > kPodCols / G;
   if (!qo_indptr_p_d || ga.dtype != gd.dtype || ga.num_qo_heads != gd.num_qo_heads ||
-      ga.num_kv_heads != gd.num_kv_heads || gd.kv_dtype != gd.dtype || G > 4 ||
+      ga.num_kv_heads != gd.num_kv_heads || gd.kv_dtype != gd.dtype || (G > 4 && !wide) ||
       ga.qo_tile > kPodWideCols / G) {
-    set_error("pod: the plans need the same dtype and heads, 16-bit K/V pages, "
-              "num_qo_heads / num_kv_heads <= 4, a prefill qo_tile of at most 256 / G and "
-              "qo_indptr");
+    set_error("pod: the plans need the same dtype and heads, 16-bit K/V pages, a prefill "
+              "qo_tile of at most 256 / G (more than 128 / G for num_qo_heads / num_kv_heads "
+              "= 8) and qo_indptr");
     return FA_ERR_INVALID;
   }
-  // prefill tiles wider than the shared form's take the append kernel's
-  // workgroup shape (one role per CU at a time)
-  const bool wide = ga.qo_tile > kPodCols / G;
   const AttnParams pa = make_params(pp, q_p, k_pages, v_pages, page_stride, token_stride,
                                     head_stride, kv_indices_p_d, kv_indptr_p_d, last_page_len_p_d,
                                     qo_indptr_p_d, sm_scale, out_p, lse_p);

@@ -12,7 +12,7 @@
 //    most 256 registers each), two LDS stages, so a CU holds one decode and
 //    one append workgroup at once and the append waves' matrix work overlaps
 //    the decode waves' memory streaming; append tiles hold at most 128 / G
-//    query positions, and the decode role keeps a 2-page ring;
+//    query positions (G <= 4), and the decode role keeps a 2-page ring;
 //  * wide: the append kernel's 8-wave workgroups and four-stage LDS ring
 //    (tiles of up to 256 / G positions); one workgroup fills a CU's LDS, so
 //    each CU runs one role at a time. A decode workgroup runs 8 worker waves,
@@ -55,6 +55,15 @@ hipError_t launch_dt(const AttnParams& dp, const AttnParams& ap, int group, int 
     case 1: hipLaunchKernelGGL((pod_kernel<DT, 1, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, dp, ap, dec_blocks); break;
     case 2: hipLaunchKernelGGL((pod_kernel<DT, 2, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, dp, ap, dec_blocks); break;
     case 4: hipLaunchKernelGGL((pod_kernel<DT, 4, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, dp, ap, dec_blocks); break;
+    case 8:
+      // the shared form's 128 columns would hold 16 positions of 8 heads; only
+      // the wide form is built for G = 8
+      if constexpr (WAVES == 8) {
+        hipLaunchKernelGGL((pod_kernel<DT, 8, WAVES>), dim3(grid), dim3(64 * WAVES), 0, s, dp, ap, dec_blocks);
+        break;
+      } else {
+        return hipErrorNotSupported;
+      }
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();

@@ -265,9 +265,10 @@ def test_cascade_wide_prefix_tiles():
 
 
 @pytest.mark.parametrize("qo_tile", [32, 16])
-def test_cascade_group8_two_launches(qo_tile):
-    """Eight query heads per kv head: no one-launch form, so fa_cascade runs the
-    suffix decode and the append kernel in order, then the combine."""
+def test_cascade_group8(qo_tile):
+    """Eight query heads per kv head: prefix tiles of 32 rows run the one-kernel
+    wide form; tiles of 16 rows (the shared form's, not built for G = 8) run
+    the suffix decode and the append kernel in order; then the combine."""
     wl = make_cascade(704, [5, 16, 300, 0, 33], 32, 4, "bf16", 25, mode="test")
     dw = DevWorkload(wl)
     out, lse, plans = run_cascade(dw, fused=True, prefix={"qo_tile": qo_tile, "num_cu": 8},

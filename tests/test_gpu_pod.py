@@ -29,11 +29,12 @@ def split_mixed(wl, n_prefill):
 
 @pytest.mark.parametrize("group,causal,wide", [(4, True, False), (1, False, False),
                                                (2, True, False), (4, True, True),
-                                               (1, False, True), (2, False, True)])
+                                               (1, False, True), (2, False, True),
+                                               (8, True, True), (8, False, True)])
 def test_pod_mixed_batch(group, causal, wide):
     """Both launch shapes: prefill tiles of 128 / G rows (decode and append
     workgroups share each CU) and of 256 / G rows (the append kernel's
-    workgroups, one role per CU at a time)."""
+    workgroups, one role per CU at a time; the only shape for G = 8)."""
     import torch
     import paged_kv_cache_fa_amd as fa
     pre_lens, pre_qo = [300, 64, 1000], [300, 17, 128] if causal else [40, 17, 128]
@@ -75,13 +76,14 @@ def test_pod_mixed_batch(group, causal, wide):
     assert_close(to_f64(od), to_f64(ld), *ref_d, what="pod decode")
 
 
-def test_pod_refuses_group_8():
-    """fa_pod runs groups of at most 4 query heads per kv head."""
+def test_pod_refuses_group_8_shared_shape():
+    """With 8 query heads per kv head fa_pod runs only the wide shape: prefill
+    tiles of at most 128 / G = 16 rows are refused."""
     import torch
     import paged_kv_cache_fa_amd as fa
     wl = make_workload([300, 40], 32, 4, "bf16", 3, qo_lens=[100, 1], causal=True, mode="test")
     pre, dec, nrows_p = split_mixed(wl, 1)
-    gp = fa.geometry("append", "bf16", 1, 32, 4, max_qo_tokens=nrows_p)
+    gp = fa.geometry("append", "bf16", 1, 32, 4, max_qo_tokens=nrows_p, qo_tile=16)
     gd = fa.geometry("decode", "bf16", 1, 32, 4)
     pp = fa.plan(gp, pre["kv_indptr"], pre["kv_lens"], pre["qo_indptr"], True, device="cuda")
     dp = fa.plan(gd, dec["kv_indptr"], dec["kv_lens"], device="cuda")
