@@ -35,13 +35,26 @@ def test_pod_mixed_batch(group, causal, wide):
     """Both launch shapes: prefill tiles of 128 / G rows (decode and append
     workgroups share each CU) and of 256 / G rows (the append kernel's
     workgroups, one role per CU at a time; the only shape for G = 8)."""
-    import torch
-    import paged_kv_cache_fa_amd as fa
     pre_lens, pre_qo = [300, 64, 1000], [300, 17, 128] if causal else [40, 17, 128]
     dec_lens = [1, 15, 16, 17, 33, 257, 5, 900, 2000, 48]
+    _pod_case(group, causal, wide, pre_lens, pre_qo, dec_lens, 80 + group)
+
+
+@pytest.mark.parametrize("group,wide", [(4, False), (4, True), (8, True)])
+def test_pod_empty_requests(group, wide):
+    """Prefill requests with no query rows (one with no cached tokens either)
+    beside ordinary ones and short decode requests, in each launch shape."""
+    _pod_case(group, True, wide, [300, 64, 500, 0], [0, 17, 0, 0], [1, 5, 2, 900, 16, 1],
+              90 + group)
+
+
+def _pod_case(group, causal, wide, pre_lens, pre_qo, dec_lens, seed):
+    import torch
+    import paged_kv_cache_fa_amd as fa
     hkv = 4
-    print(f"[pod] G={group} causal={causal} wide={wide}", flush=True)
-    wl = make_workload(pre_lens + dec_lens, hkv * group, hkv, "bf16", 80 + group,
+    print(f"[pod] G={group} causal={causal} wide={wide} prefill {pre_lens} rows {pre_qo} "
+          f"decode {dec_lens}", flush=True)
+    wl = make_workload(pre_lens + dec_lens, hkv * group, hkv, "bf16", seed,
                        qo_lens=pre_qo + [1] * len(dec_lens), causal=causal, mode="test",
                        extra_pages=3)
     pre, dec, nrows_p = split_mixed(wl, len(pre_lens))
@@ -53,8 +66,9 @@ def test_pod_mixed_batch(group, causal, wide):
     _, _, ps, hk, d = wl.pool.shape
     strides = (2 * ps * hk * d, hk * d, d)
     k, v = pool[:, 0], pool[:, 1]
-    gp = fa.geometry("append", "bf16", len(pre_lens), hkv * group, hkv, max_qo_tokens=nrows_p,
-                     num_cu=32, qo_tile=(256 if wide else 128) // group)
+    gp = fa.geometry("append", "bf16", len(pre_lens), hkv * group, hkv,
+                     max_qo_tokens=max(nrows_p, 1), num_cu=32,
+                     qo_tile=(256 if wide else 128) // group)
     gd = fa.geometry("decode", "bf16", len(dec_lens), hkv * group, hkv, num_cu=32)
     pp = fa.plan(gp, pre["kv_indptr"], pre["kv_lens"], pre["qo_indptr"], causal, device="cuda")
     dp = fa.plan(gd, dec["kv_indptr"], dec["kv_lens"], device="cuda")
